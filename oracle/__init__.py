@@ -1,0 +1,324 @@
+"""CPU oracle for the DeepSeekMoE layer forward -- TEST INFRASTRUCTURE ONLY.
+
+Plain, slow and written from the pages; see ``moe_oracle.c`` for the
+per-step definitions and citations.  Only the tests, the smoke check and the
+benchmark's CPU-baseline leg may import this package.  It shares no code with
+the HIP library (``sigmoid_top_routing_02_amd``) and never imports it.
+
+The Python side only marshals numpy arrays into the C functions and strings
+the steps of the layer together in the order of the output equation
+(nlp-lineage summary, "The notation").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "moe_oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so with gcc (plain C, no fast-math, no contraction)."""
+    if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+        tmp = LIB + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+               "-shared", "-fPIC", "-Wall", "-o", tmp, SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, LIB)
+    return LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+            build(force=True)
+        L = ctypes.CDLL(LIB)
+        P = ctypes.c_void_p
+        i64, i32, f32 = ctypes.c_int64, ctypes.c_int, ctypes.c_float
+        L.oracle_exp_spec.argtypes = [f32]
+        L.oracle_exp_spec.restype = f32
+        L.oracle_sigmoid_spec.argtypes = [f32]
+        L.oracle_sigmoid_spec.restype = f32
+        L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+        L.oracle_e4m3_decode.restype = ctypes.c_double
+        L.oracle_e4m3_encode.argtypes = [f32]
+        L.oracle_e4m3_encode.restype = ctypes.c_uint8
+        L.oracle_sigmoid_spec_n.argtypes = [P, i64, P]
+        L.oracle_exp_spec_n.argtypes = [P, i64, P]
+        L.oracle_e4m3_encode_n.argtypes = [P, i64, P]
+        L.oracle_router_scores.argtypes = [P, P, i64, i32, i32, P]
+        L.oracle_topk_from_scores.argtypes = [P, P, i64, i32, i32, P, P]
+        L.oracle_dispatch.argtypes = [P, i64, i32, i32, i32, P, P, P, P]
+        L.oracle_dispatch.restype = i32
+        L.oracle_quant_1x128.argtypes = [P, i64, i32, P, P]
+        L.oracle_quant_128x128.argtypes = [P, i64, i32, P, P]
+        L.oracle_gemm_blockscaled.argtypes = [P, P, P, i64, P, P, i32, i32, P]
+        L.oracle_swiglu.argtypes = [P, P, i64, P]
+        L.oracle_combine.argtypes = [P, P, i64, P, P, i64, i32, i32, P]
+        L.oracle_bias_update.argtypes = [P, P, i32, i64, f32]
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+# ---------------------------------------------------------------- scalars
+def exp_spec(y: float) -> float:
+    return lib().oracle_exp_spec(float(y))
+
+
+def sigmoid_spec(x: float) -> float:
+    return lib().oracle_sigmoid_spec(float(x))
+
+
+def e4m3_decode(code: int) -> float:
+    return lib().oracle_e4m3_decode(int(code))
+
+
+def e4m3_encode(x: float) -> int:
+    return int(lib().oracle_e4m3_encode(float(x)))
+
+
+def e4m3_encode_array(x: np.ndarray) -> np.ndarray:
+    """Element-wise E4M3 encoding (no scaling) of an FP32 array."""
+    flat = _c(x, np.float32).reshape(-1)
+    out = np.empty(flat.size, np.uint8)
+    lib().oracle_e4m3_encode_n(_p(flat), flat.size, _p(out))
+    return out.reshape(np.shape(x))
+
+
+def sigmoid_spec_array(x: np.ndarray) -> np.ndarray:
+    flat = _c(x, np.float32).reshape(-1)
+    out = np.empty(flat.size, np.float32)
+    lib().oracle_sigmoid_spec_n(_p(flat), flat.size, _p(out))
+    return out.reshape(np.shape(x))
+
+
+def exp_spec_array(x: np.ndarray) -> np.ndarray:
+    flat = _c(x, np.float32).reshape(-1)
+    out = np.empty(flat.size, np.float32)
+    lib().oracle_exp_spec_n(_p(flat), flat.size, _p(out))
+    return out.reshape(np.shape(x))
+
+
+# ---------------------------------------------------------------- router
+def router_scores(u_bf16: np.ndarray, e_bf16: np.ndarray) -> np.ndarray:
+    """s[t,i] = sigmoid_spec(FP32 sequential dot(u_t, e_i)); bf16 inputs as uint16."""
+    u = _c(u_bf16, np.uint16)
+    e = _c(e_bf16, np.uint16)
+    T, d = u.shape
+    E = e.shape[0]
+    s = np.empty((T, E), np.float32)
+    lib().oracle_router_scores(_p(u), _p(e), T, d, E, _p(s))
+    return s
+
+
+def topk_from_scores(s: np.ndarray, bias: np.ndarray, K: int):
+    s = _c(s, np.float32)
+    b = _c(bias, np.float32)
+    T, E = s.shape
+    idx = np.empty((T, K), np.int32)
+    gate = np.empty((T, K), np.float32)
+    lib().oracle_topk_from_scores(_p(s), _p(b), T, E, K, _p(idx), _p(gate))
+    return idx, gate
+
+
+def router_topk(u_bf16, e_bf16, bias, K: int):
+    s = router_scores(u_bf16, e_bf16)
+    idx, gate = topk_from_scores(s, bias, K)
+    return idx, gate, s
+
+
+# ---------------------------------------------------------------- dispatch
+def dispatch(idx, E, include_shared):
+    """count[E], group_offset[E+1(+1)], row_token[R], slot_row[T,K] (see moe_oracle.c)."""
+    idx = _c(idx, np.int32)
+    T, K = idx.shape
+    R = T * K + (T if include_shared else 0)
+    count = np.empty(E, np.int32)
+    go = np.empty(E + 1 + (1 if include_shared else 0), np.int32)
+    row_token = np.empty(max(R, 1), np.int32)
+    slot_row = np.empty((T, K), np.int32)
+    rc = lib().oracle_dispatch(_p(idx), T, K, E, int(bool(include_shared)), _p(count), _p(go),
+                               _p(row_token), _p(slot_row))
+    if rc != 0:
+        raise ValueError("expert index out of range")
+    return count, go, row_token[:R], slot_row
+
+
+# ---------------------------------------------------------------- quant
+def quant_1x128(x: np.ndarray):
+    x = _c(x, np.float32)
+    rows, cols = x.shape
+    assert cols % 128 == 0
+    q = np.empty((rows, cols), np.uint8)
+    sc = np.empty((rows, cols // 128), np.float32)
+    lib().oracle_quant_1x128(_p(x), rows, cols, _p(q), _p(sc))
+    return q, sc
+
+
+def quant_128x128(w: np.ndarray):
+    w = _c(w, np.float32)
+    rows, cols = w.shape
+    assert rows % 128 == 0 and cols % 128 == 0
+    q = np.empty((rows, cols), np.uint8)
+    sc = np.empty((rows // 128, cols // 128), np.float32)
+    lib().oracle_quant_128x128(_p(w), rows, cols, _p(q), _p(sc))
+    return q, sc
+
+
+def e4m3_table() -> np.ndarray:
+    return np.array([e4m3_decode(c) for c in range(256)], dtype=np.float64)
+
+
+def dequant_1x128(q: np.ndarray, sc: np.ndarray) -> np.ndarray:
+    v = e4m3_table()[q]
+    return v * np.repeat(sc.astype(np.float64), 128, axis=1)
+
+
+# ---------------------------------------------------------------- GEMM
+def gemm_blockscaled(qa, sa, qb, sb, a_rows=None) -> np.ndarray:
+    """C[m,n] = sum_j sa[am,j] sb[n//128,j] sum_{k in slice j} qa[am,k] qb[n,k] (FP64)."""
+    qa = _c(qa, np.uint8)
+    sa = _c(sa, np.float32)
+    qb = _c(qb, np.uint8)
+    sb = _c(sb, np.float32)
+    K = qa.shape[1]
+    N = qb.shape[0]
+    assert qb.shape[1] == K and K % 128 == 0 and N % 128 == 0
+    if a_rows is None:
+        M = qa.shape[0]
+        rows_p = None
+    else:
+        a_rows = _c(a_rows, np.int32)
+        M = a_rows.shape[0]
+        rows_p = _p(a_rows)
+    out = np.empty((M, N), np.float64)
+    if M:
+        lib().oracle_gemm_blockscaled(_p(qa), _p(sa), rows_p, M, _p(qb), _p(sb), N, K, _p(out))
+    return out
+
+
+def swiglu(zg: np.ndarray, zu: np.ndarray) -> np.ndarray:
+    zg = _c(zg, np.float64)
+    zu = _c(zu, np.float64)
+    h = np.empty_like(zg)
+    lib().oracle_swiglu(_p(zg), _p(zu), zg.size, _p(h))
+    return h
+
+
+# ---------------------------------------------------------------- combine / bias
+def combine(u_bf16, y, shared_row0: int, gate, slot_row) -> np.ndarray:
+    u = _c(u_bf16, np.uint16)
+    y = _c(y, np.float64)
+    g = _c(gate, np.float32)
+    sr = _c(slot_row, np.int32)
+    T, d = u.shape
+    K = g.shape[1]
+    out = np.empty((T, d), np.float64)
+    lib().oracle_combine(_p(u), _p(y), int(shared_row0), _p(g), _p(sr), T, K, d, _p(out))
+    return out
+
+
+def bias_update(bias, count, total_assignments: int, gamma: float) -> np.ndarray:
+    b = _c(bias, np.float32).copy()
+    c = _c(count, np.int32)
+    lib().oracle_bias_update(_p(b), _p(c), b.shape[0], int(total_assignments), float(gamma))
+    return b
+
+
+# ---------------------------------------------------------------- composite layer
+def expert_ffn_rows(uq, us, token_rows, w1, w3, w2):
+    """FFN of one expert for the given tokens, on quantised operands.
+
+    uq/us: quantised u (E4M3 codes [T,d], scales [T,d/128]); token_rows: the
+    tokens routed to this expert; w1, w3 [I,d], w2 [d,I] FP32 masters, which the
+    oracle quantises itself per 128x128 block.  Returns z_gate, z_up (FP64),
+    h (FP32, the SwiGLU output rounded to binary32), its 1x128 codes and
+    scales, and Y (FP64)."""
+    q1, s1 = quant_128x128(w1)
+    q3, s3 = quant_128x128(w3)
+    q2, s2 = quant_128x128(w2)
+    zg = gemm_blockscaled(uq, us, q1, s1, a_rows=token_rows)
+    zu = gemm_blockscaled(uq, us, q3, s3, a_rows=token_rows)
+    h = swiglu(zg, zu).astype(np.float32)
+    hq, hs = quant_1x128(h)
+    y = gemm_blockscaled(hq, hs, q2, s2)
+    return dict(zg=zg, zu=zu, h=h, hq=hq, hs=hs, y=y)
+
+
+def layer_forward(u_bf16, e_bf16, bias, K, weights_fn, shared: bool = True):
+    """Whole layer on the CPU.
+
+    weights_fn(expert) -> (w1, w3, w2) FP32 masters; expert E is the shared one.
+    Returns a dict with every intermediate (router, dispatch, quantised u,
+    per-row h codes, Y in GEMM-row order, and h' in FP64)."""
+    u = _c(u_bf16, np.uint16)
+    T, d = u.shape
+    E = e_bf16.shape[0]
+    idx, gate, s = router_topk(u, e_bf16, bias, K)
+    count, go, row_token, slot_row = dispatch(idx, E, shared)
+    uf = (u.astype(np.uint32) << 16).view(np.float32)
+    uq, us = quant_1x128(uf)
+    R = row_token.shape[0]
+    y = np.zeros((R, d), np.float64)
+    I = None
+    hq_all = hs_all = h_all = None
+    groups = E + (1 if shared else 0)
+    for g in range(groups):
+        r0, r1 = int(go[g]), int(go[g + 1])
+        if r1 == r0:
+            continue
+        w1, w3, w2 = weights_fn(g)
+        if I is None:
+            I = w1.shape[0]
+            hq_all = np.zeros((R, I), np.uint8)
+            hs_all = np.zeros((R, I // 128), np.float32)
+            h_all = np.zeros((R, I), np.float32)
+        f = expert_ffn_rows(uq, us, row_token[r0:r1], w1, w3, w2)
+        y[r0:r1] = f["y"]
+        hq_all[r0:r1] = f["hq"]
+        hs_all[r0:r1] = f["hs"]
+        h_all[r0:r1] = f["h"]
+    out = combine(u, y, T * K if shared else -1, gate, slot_row)
+    return dict(idx=idx, gate=gate, s=s, count=count, group_offset=go, row_token=row_token,
+                slot_row=slot_row, uq=uq, us=us, h=h_all, hq=hq_all, hs=hs_all, y=y, out=out)
+
+
+def layer_forward_unquantised(u_bf16, e_bf16, bias, K, weights_fn, shared: bool = True):
+    """The same layer with no FP8 anywhere: FP64 FFNs on the FP32 masters and
+    bf16 u (routing is unchanged: it never used FP8).  Used to report the
+    quantisation error, not as a parity target."""
+    u = _c(u_bf16, np.uint16)
+    T, d = u.shape
+    E = e_bf16.shape[0]
+    idx, gate, s = router_topk(u, e_bf16, bias, K)
+    count, go, row_token, slot_row = dispatch(idx, E, shared)
+    uf = (u.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    R = row_token.shape[0]
+    y = np.zeros((R, d), np.float64)
+    for g in range(E + (1 if shared else 0)):
+        r0, r1 = int(go[g]), int(go[g + 1])
+        if r1 == r0:
+            continue
+        w1, w3, w2 = (np.asarray(w, np.float64) for w in weights_fn(g))
+        x = uf[row_token[r0:r1]]
+        h = swiglu(x @ w1.T, x @ w3.T)
+        y[r0:r1] = h @ w2.T
+    out = combine(u, y, T * K if shared else -1, gate, slot_row)
+    return dict(idx=idx, gate=gate, y=y, out=out)

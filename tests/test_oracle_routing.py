@@ -1,0 +1,247 @@
+"""Pins for the oracle's router (affinity, biased top-K, gates), dispatch and
+bias update.
+
+What pins them (none of it re-runs the oracle's own formula):
+  * exact special cases: small-integer bf16 inputs make every logit an exact
+    integer in any summation order, so the score must be sigmoid_spec of the
+    integer numpy dot product;
+  * brute force over all K-subsets (tiny E) and numpy's lexsort;
+  * the page facts: exactly K distinct experts, gates sum to 1 over the chosen
+    ones, the bias changes the choice but never the gate values
+    ("DeepSeek-V3 Technical Report" notes, bias and MoE-routing paragraphs;
+    nlp-lineage summary, "The notation");
+  * numpy bincount / cumsum / stable argsort for the dispatch;
+  * the sign table of the bias update.
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+
+def _bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Exact float32 -> bf16 bits (inputs here are chosen bf16-representable)."""
+    b = np.ascontiguousarray(x, np.float32).view(np.uint32)
+    assert np.all(b & 0xFFFF == 0), "value not exactly representable in bf16"
+    return (b >> 16).astype(np.uint16)
+
+
+def _rand_bf16(rng, shape, std=1.0):
+    x = (rng.standard_normal(shape) * std).astype(np.float32)
+    return (x.view(np.uint32) >> 16).astype(np.uint16)  # truncation: still a valid bf16 sample
+
+
+def test_router_scores_exact_integer_case(oracle_mod):
+    rng = np.random.default_rng(10)
+    T, d, E = 9, 256, 12
+    u = rng.integers(-3, 4, (T, d)).astype(np.float32)
+    e = rng.integers(-2, 3, (E, d)).astype(np.float32) / 64.0
+    s = oracle_mod.router_scores(_bf16_bits(u), _bf16_bits(e))
+    logits = (u.astype(np.int64) @ (e * 64).astype(np.int64).T).astype(np.float64) / 64.0
+    expect = oracle_mod.sigmoid_spec_array(logits.astype(np.float32))
+    np.testing.assert_array_equal(s, expect)
+    # and within 4 ulps of the FP64 sigmoid of the exact logits
+    ref = 1 / (1 + np.exp(-logits))
+    assert np.max(np.abs(s - ref) / np.spacing(np.abs(ref).astype(np.float32))) <= 4
+
+
+def test_router_scores_close_to_fp64(oracle_mod):
+    rng = np.random.default_rng(11)
+    T, d, E = 16, 512, 8
+    u = _rand_bf16(rng, (T, d))
+    e = _rand_bf16(rng, (E, d), d ** -0.5)
+    s = oracle_mod.router_scores(u, e)
+    uf = (u.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    ef = (e.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    ref = 1 / (1 + np.exp(-(uf @ ef.T)))
+    assert np.max(np.abs(s - ref)) < 1e-5
+
+
+def _keys(s, b):
+    return (s + b[None, :]).astype(np.float32)
+
+
+def test_topk_brute_force_tiny(oracle_mod):
+    """For E <= 8, the chosen set is the K-subset with the largest keys under
+    the (key desc, index asc) order; slot order is that ranking."""
+    rng = np.random.default_rng(12)
+    for E, K in [(5, 2), (6, 3), (8, 4), (8, 8), (7, 1)]:
+        T = 40
+        s = rng.uniform(0, 1, (T, E)).astype(np.float32)
+        s[:, 1] = s[:, 3]            # force exact ties
+        b = rng.uniform(-0.05, 0.05, E).astype(np.float32)
+        b[3] = b[1]
+        idx, gate = oracle_mod.topk_from_scores(s, b, K)
+        key = _keys(s, b)
+        for t in range(T):
+            order = sorted(range(E), key=lambda i: (-float(key[t, i]), i))
+            assert list(idx[t]) == order[:K]
+            # brute force: best K-subset by sorted key tuples, then lowest indices
+            best = max(itertools.combinations(range(E), K),
+                       key=lambda c: (sorted((float(key[t, i]) for i in c), reverse=True),
+                                      [-i for i in sorted(c)]))
+            assert set(best) == set(idx[t])
+
+
+def test_topk_lexsort_and_dominance(oracle_mod):
+    rng = np.random.default_rng(13)
+    T, E, K = 300, 64, 8
+    s = rng.uniform(0, 1, (T, E)).astype(np.float32)
+    s[:, 10:20] = s[:, 0:10]   # duplicated scores -> ties broken by index
+    b = np.zeros(E, np.float32)
+    idx, gate = oracle_mod.topk_from_scores(s, b, K)
+    key = _keys(s, b)
+    for t in range(T):
+        order = np.lexsort((np.arange(E), -key[t].astype(np.float64)))
+        np.testing.assert_array_equal(idx[t], order[:K])
+        chosen = set(idx[t].tolist())
+        kmin = min((float(key[t, i]), -i) for i in chosen)
+        for j in range(E):
+            if j not in chosen:
+                assert (float(key[t, j]), -j) < kmin
+
+
+def test_topk_exactly_k_distinct_and_gates_sum_to_one(oracle_mod):
+    rng = np.random.default_rng(14)
+    T, E, K = 500, 256, 8
+    s = oracle_mod.sigmoid_spec_array(rng.standard_normal((T, E)).astype(np.float32))
+    b = rng.uniform(-0.05, 0.05, E).astype(np.float32)
+    idx, gate = oracle_mod.topk_from_scores(s, b, K)
+    for t in range(T):
+        assert len(set(idx[t].tolist())) == K
+    assert np.all((idx >= 0) & (idx < E))
+    assert np.max(np.abs(gate.astype(np.float64).sum(1) - 1.0)) <= K * 2.0 ** -23
+    # gates are the raw scores normalised over the chosen experts (no bias)
+    raw = np.take_along_axis(s, idx, 1).astype(np.float64)
+    np.testing.assert_allclose(gate, raw / raw.sum(1, keepdims=True), rtol=3e-7)
+
+
+def test_bias_changes_choice_not_gates(oracle_mod):
+    """Shifting the bias of the already-chosen experts up keeps the set and,
+    per expert, the gate values; a large bias on an unchosen expert pulls it
+    in, and its gate is its raw score over the new chosen sum."""
+    rng = np.random.default_rng(15)
+    T, E, K = 200, 32, 4
+    s = oracle_mod.sigmoid_spec_array(rng.standard_normal((T, E)).astype(np.float32))
+    b = np.zeros(E, np.float32)
+    idx0, g0 = oracle_mod.topk_from_scores(s, b, K)
+    # uniform shift of every bias by a power of two keeps every key order
+    idx1, g1 = oracle_mod.topk_from_scores(s, b + np.float32(4.0), K)
+    same_order = np.all(idx0 == idx1, axis=1)
+    np.testing.assert_array_equal(g0[same_order], g1[same_order])
+    for t in range(T):
+        d0 = dict(zip(idx0[t].tolist(), g0[t].tolist()))
+        d1 = dict(zip(idx1[t].tolist(), g1[t].tolist()))
+        assert d0.keys() == d1.keys()
+        for k in d0:
+            assert abs(d0[k] - d1[k]) <= 2 * 2.0 ** -24
+    # a huge bias forces expert 5 into every token's choice, first slot
+    b2 = b.copy()
+    b2[5] = 10.0
+    idx2, g2 = oracle_mod.topk_from_scores(s, b2, K)
+    assert np.all(idx2[:, 0] == 5)
+    raw = np.take_along_axis(s, idx2, 1).astype(np.float64)
+    np.testing.assert_allclose(g2, raw / raw.sum(1, keepdims=True), rtol=3e-7)
+
+
+def test_topk_k_equals_e_ignores_bias_for_selection(oracle_mod):
+    rng = np.random.default_rng(16)
+    T, E = 50, 12
+    s = rng.uniform(0, 1, (T, E)).astype(np.float32)
+    for b in (np.zeros(E, np.float32), rng.uniform(-1, 1, E).astype(np.float32)):
+        idx, gate = oracle_mod.topk_from_scores(s, b, E)
+        assert all(sorted(r) == list(range(E)) for r in idx.tolist())
+
+
+def test_topk_degenerate_all_zero_scores(oracle_mod):
+    s = np.zeros((3, 6), np.float32)
+    b = np.array([0, 0.1, 0, 0.2, 0, 0], np.float32)
+    idx, gate = oracle_mod.topk_from_scores(s, b, 3)
+    np.testing.assert_array_equal(idx[0], [3, 1, 0])
+    assert np.all(gate == 0)
+
+
+# ------------------------------------------------------------------ dispatch
+def _random_idx(rng, T, E, K):
+    return np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("shared", [True, False])
+def test_dispatch_against_numpy(oracle_mod, shared):
+    rng = np.random.default_rng(17)
+    for T, E, K in [(1, 4, 2), (37, 16, 4), (300, 256, 8), (64, 8, 8)]:
+        idx = _random_idx(rng, T, E, K)
+        count, go, row_token, slot_row = oracle_mod.dispatch(idx, E, shared)
+        np.testing.assert_array_equal(count, np.bincount(idx.ravel(), minlength=E))
+        exp_go = np.concatenate([[0], np.cumsum(count)])
+        if shared:
+            exp_go = np.concatenate([exp_go, [T * K + T]])
+        np.testing.assert_array_equal(go, exp_go)
+        tok = np.repeat(np.arange(T), K)
+        order = np.lexsort((tok, idx.ravel()))      # by expert, then token
+        np.testing.assert_array_equal(row_token[:T * K], tok[order])
+        if shared:
+            np.testing.assert_array_equal(row_token[T * K:], np.arange(T))
+        assert row_token.shape[0] == T * K + (T if shared else 0)
+        # slot_row is the inverse permutation
+        inv = np.empty(T * K, np.int64)
+        inv[order] = np.arange(T * K)
+        np.testing.assert_array_equal(slot_row.ravel(), inv)
+        # conservation: every token appears K (+1 shared) times, no drop
+        np.testing.assert_array_equal(np.bincount(row_token, minlength=T), np.full(T, K + (1 if shared else 0)))
+        # each row lies in its expert's group
+        for t in range(T):
+            for k in range(K):
+                r = slot_row[t, k]
+                e = idx[t, k]
+                assert go[e] <= r < go[e + 1] and row_token[r] == t
+
+
+def test_permute_unpermute_identity(oracle_mod):
+    rng = np.random.default_rng(18)
+    T, E, K, d = 50, 16, 4, 8
+    idx = _random_idx(rng, T, E, K)
+    count, go, row_token, slot_row = oracle_mod.dispatch(idx, E, False)
+    x = rng.standard_normal((T, d))
+    xp = x[row_token]
+    back = xp[slot_row]          # [T, K, d]
+    for k in range(K):
+        np.testing.assert_array_equal(back[:, k], x)
+
+
+def test_dispatch_rejects_bad_index(oracle_mod):
+    with pytest.raises(ValueError):
+        oracle_mod.dispatch(np.array([[0, 5]], np.int32), 4, True)
+
+
+# ------------------------------------------------------------------ bias update
+def test_bias_update_sign_table(oracle_mod):
+    """Overloaded (above the batch mean) -> b - gamma, underloaded -> b + gamma,
+    exactly at the mean -> unchanged; gamma = 0 leaves b unchanged."""
+    E, TK = 4, 40            # mean load 10
+    count = np.array([11, 9, 10, 0], np.int32)
+    b = np.array([0.5, -0.25, 0.125, 0.0], np.float32)
+    out = oracle_mod.bias_update(b, count, TK, 0.125)
+    np.testing.assert_array_equal(out, np.array([0.375, -0.125, 0.125, 0.125], np.float32))
+    np.testing.assert_array_equal(oracle_mod.bias_update(b, count, TK, 0.0), b)
+    # FP32 rounding of the update
+    out = oracle_mod.bias_update(np.array([0.01, 0.01, 0, 0], np.float32), count, TK, 1e-3)
+    assert out[0] == np.float32(np.float32(0.01) - np.float32(1e-3))
+    assert out[1] == np.float32(np.float32(0.01) + np.float32(1e-3))
+
+
+def test_bias_update_feedback_balances_load(oracle_mod):
+    """Repeating route -> count -> update on fixed scores drives the most
+    loaded expert's load down (the page's stated purpose of the rule)."""
+    rng = np.random.default_rng(19)
+    T, E, K = 2000, 16, 2
+    base = rng.standard_normal(E) * 0.5
+    s = oracle_mod.sigmoid_spec_array((rng.standard_normal((T, E)) * 0.3 + base).astype(np.float32))
+    b = np.zeros(E, np.float32)
+    idx, _ = oracle_mod.topk_from_scores(s, b, K)
+    c0 = np.bincount(idx.ravel(), minlength=E)
+    for _ in range(200):
+        idx, _ = oracle_mod.topk_from_scores(s, b, K)
+        c = np.bincount(idx.ravel(), minlength=E).astype(np.int32)
+        b = oracle_mod.bias_update(b, c, T * K, 0.01)
+    assert c.max() / c.mean() < 0.5 * c0.max() / c0.mean()
