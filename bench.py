@@ -1,0 +1,350 @@
+"""Benchmark of the DeepSeekMoE layer forward on one MI355X.
+
+One step = one pass of the whole layer over one batch held in HBM:
+router (sigmoid affinity + biased top-K + gates) -> dispatch (histogram, scan,
+permutation) -> 1x128 FP8 quantisation of u -> grouped GEMM1 with SwiGLU and
+1x128 re-quantisation -> grouped GEMM2 -> combine (u + shared + gated routed)
+-> bias update (into the next step's bias).  Expert weights are quantised to
+128x128-block E4M3 once, before timing (an offline step).
+
+Default workload: the prefill-shaped layer, T=16384 tokens, d=7168, 256 routed
+experts top-8 + 1 shared, SwiGLU inter=2048, router bias calibrated for a
+Zipf(1.1)-like expert load (max/mean ~4), u ~ N(0,1) with 0.1% outliers x100.
+Other workloads (--workload): decode (T=256), rdc (router + dispatch + permute
++ combine with identity experts, T=8192), dense (block-scaled FP8 GEMM,
+M=8192, N=7168, K=4096), tiny.
+
+Prints one JSON line: tokens/s for the whole step, the roofline of the
+dominant kernel (its average duration from HIP events on the launch stream
+over the timed steps), and the CPU oracle's rate on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import sigmoid_top_routing_02_amd as moe  # noqa: E402
+import workloads  # noqa: E402
+
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_sha(name):
+    with open(os.path.join(ROOT, "sigmoid_top_routing_02_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(kernel_key, src):
+    """HBM bytes per launch measured with rocprofv3 counters (FETCH_SIZE +
+    WRITE_SIZE, scaled by the copy-kernel calibration), or None if the kernel
+    source changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != source_sha(src):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+class Events:
+    def __init__(self):
+        self.pairs = {}
+
+    def mark(self, name):
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record()
+        return ev
+
+    def add(self, name, a, b):
+        self.pairs.setdefault(name, []).append((a, b))
+
+    def avg_ms(self, name):
+        p = self.pairs.get(name, [])
+        return float(np.mean([a.elapsed_time(b) for a, b in p])) if p else float("nan")
+
+
+# ----------------------------------------------------------------------------- layer workloads
+def pack_weights(sh):
+    G = sh.E + 1
+    packed = torch.empty(moe.moe_packed_weight_bytes(G, sh.d, sh.I), dtype=torch.uint8, device="cuda")
+    for g in range(G):
+        w1, w3, w2 = workloads.expert_weights(sh, g, device="cuda")
+        moe.moe_prepare_expert_weights(w1, w3, w2, g, G, packed)
+        del w1, w3, w2
+    torch.cuda.synchronize()
+    return packed
+
+
+def layer_setup(sh):
+    u = workloads.activations(sh).cuda()
+    e = workloads.centroids(sh).cuda()
+    b = workloads.bias(sh).cuda()
+    packed = pack_weights(sh)
+    T, d, E, K, I = sh.T, sh.d, sh.E, sh.K, sh.I
+    R = T * K + T
+    dev = u.device
+    st = dict(
+        u=u, e=e, b=b, b_next=torch.empty_like(b), packed=packed,
+        views=moe.packed_views(packed, E + 1, d, I),
+        scores=torch.empty(T, E, dtype=torch.float32, device=dev),
+        idx=torch.empty(T, K, dtype=torch.int32, device=dev),
+        gate=torch.empty(T, K, dtype=torch.float32, device=dev),
+        uq=torch.empty(T, d, dtype=torch.uint8, device=dev),
+        us=torch.empty(T, d // 128, dtype=torch.float32, device=dev),
+        hq=torch.empty(R, I, dtype=torch.uint8, device=dev),
+        hs=torch.empty(R, I // 128, dtype=torch.float32, device=dev),
+        y=torch.empty(R, d, dtype=torch.float32, device=dev),
+        out=torch.empty(T, d, dtype=torch.float32, device=dev),
+        dws=torch.empty(max(moe.moe_dispatch_workspace_bytes(T, E), 256), dtype=torch.uint8, device=dev),
+        gws=torch.empty(max(moe.moe_gemm_workspace_bytes(E + 1), 256), dtype=torch.uint8, device=dev),
+    )
+    return st
+
+
+def layer_step(sh, st, ev=None):
+    T, d, E, K, I = sh.T, sh.d, sh.E, sh.K, sh.I
+    R = T * K + T
+    w13q, w2q, w13s, w2s = st["views"]
+    m = [ev.mark("start")] if ev else None
+    moe.moe_router_topk(st["u"], st["e"], st["b"], K, st["scores"], st["idx"], st["gate"])
+    if ev: m.append(ev.mark("router"))
+    count, go, row_token, slot_row = moe.moe_dispatch(st["idx"], E, True, ws=st["dws"])
+    if ev: m.append(ev.mark("dispatch"))
+    moe.fp8_quant_1x128(st["u"], st["uq"], st["us"])
+    if ev: m.append(ev.mark("quant"))
+    moe.grouped_gemm_fp8_blockscaled(st["uq"], st["us"], go, R, w13q, w13s, epi=moe.MOE_EPI_SWIGLU_QUANT,
+                                     a_row_index=row_token, out_q=st["hq"], out_scale=st["hs"], ws=st["gws"])
+    if ev: m.append(ev.mark("gemm1"))
+    moe.grouped_gemm_fp8_blockscaled(st["hq"], st["hs"], go, R, w2q, w2s, epi=moe.MOE_EPI_STORE_F32,
+                                     out=st["y"], ws=st["gws"])
+    if ev: m.append(ev.mark("gemm2"))
+    moe.moe_combine(st["u"], st["y"], st["gate"], slot_row, shared_row0=T * K, out=st["out"])
+    if ev: m.append(ev.mark("combine"))
+    st["b_next"].copy_(st["b"])
+    moe.moe_bias_update(st["b_next"], count, T * K, sh.gamma)
+    if ev:
+        m.append(ev.mark("bias"))
+        names = ["router", "dispatch", "quant", "gemm1", "gemm2", "combine", "bias_update"]
+        for i, n in enumerate(names):
+            ev.add(n, m[i], m[i + 1])
+    st["count"] = count
+
+
+def layer_flops(sh):
+    R = sh.T * (sh.K + 1)
+    g1 = 2.0 * R * (2 * sh.I) * sh.d
+    g2 = 2.0 * R * sh.d * sh.I
+    return g1, g2
+
+
+def gemm1_bytes(sh, count):
+    """Algorithmic HBM bytes of GEMM1: every expert's W13 codes + scales that
+    at least one row uses, the gathered A rows (codes + scales, once per
+    row), and the h codes + scales written."""
+    used = int((count > 0).sum()) + 1
+    w = used * (2 * sh.I * sh.d + (2 * sh.I // 128) * (sh.d // 128) * 4)
+    R = sh.T * (sh.K + 1)
+    a = sh.T * (sh.d + sh.d // 128 * 4)
+    h = R * (sh.I + sh.I // 128 * 4)
+    return w + a + h
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+def cpu_baseline_layer(sh, st, budget_s=12.0):
+    """The oracle (untuned) timed on a bounded sample of the same batch:
+    router for a token slice, then the FFNs (GEMM1 + SwiGLU + h quant + GEMM2)
+    of a few experts' rows with weights the oracle quantised beforehand
+    (untimed, like the GPU's), dispatch, quantisation of u and combine on the
+    slice; the per-token cost is scaled to tokens/s."""
+    import oracle
+    oracle.lib()
+    T, d, E, K, I = sh.T, sh.d, sh.E, sh.K, sh.I
+    nt = min(T, 512 if T >= 512 else T)
+    u_h = st["u"][:nt].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    e_h = st["e"].view(torch.int16).cpu().numpy().view(np.uint16)
+    b_h = st["b"].cpu().numpy()
+    t0 = time.perf_counter()
+    idx, gate, s = oracle.router_topk(u_h, e_h, b_h, K)
+    count, go, rt, sr = oracle.dispatch(idx, E, True)
+    uf = (u_h.astype(np.uint32) << 16).view(np.float32)
+    uq, us = oracle.quant_1x128(uf)
+    t_route = time.perf_counter() - t0
+    # FFN rows of a few experts (the shared expert and the busiest routed ones in the slice)
+    groups = [E] + [int(g) for g in np.argsort(-count)[:3]]
+    wq = {}
+    for g in groups:
+        w1, w3, w2 = (w.cpu().numpy() for w in workloads.expert_weights(sh, g, device="cuda"))
+        wq[g] = (oracle.quant_128x128(w1), oracle.quant_128x128(w3), oracle.quant_128x128(w2))
+    rows_done, t_ffn = 0, 0.0
+    y_rows = {}
+    for g in groups:
+        r0, r1 = int(go[g]), int(go[g + 1])
+        rows = np.arange(r0, min(r1, r0 + 64))
+        (q1, s1), (q3, s3), (q2, s2) = wq[g]
+        t1 = time.perf_counter()
+        zg = oracle.gemm_blockscaled(uq, us, q1, s1, a_rows=rt[rows])
+        zu = oracle.gemm_blockscaled(uq, us, q3, s3, a_rows=rt[rows])
+        h = oracle.swiglu(zg, zu).astype(np.float32)
+        hq, hs = oracle.quant_1x128(h)
+        y = oracle.gemm_blockscaled(hq, hs, q2, s2)
+        t_ffn += time.perf_counter() - t1
+        rows_done += rows.size
+        for i, r in enumerate(rows):
+            y_rows[int(r)] = y[i]
+        if t_route + t_ffn > budget_s:
+            break
+    t2 = time.perf_counter()
+    yfull = np.zeros((nt * (K + 1), d))
+    oracle.combine(u_h, yfull, nt * K, gate, sr)
+    oracle.bias_update(b_h, count, nt * K, sh.gamma)
+    t_comb = time.perf_counter() - t2
+    per_token = (t_route + t_comb) / nt + (K + 1) * t_ffn / rows_done
+    return {
+        "value": 1.0 / per_token, "unit": "tokens/s", "cores": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)),
+        "kind": "oracle",
+        "sample": f"router+dispatch+quant+combine+bias on the first {nt} tokens ({t_route + t_comb:.1f}s); "
+                  f"FFN on {rows_done} rows of experts {groups} ({t_ffn:.1f}s); per-token cost = "
+                  f"slice cost/{nt} + {K + 1} x per-row FFN cost",
+    }
+
+
+# ----------------------------------------------------------------------------- runners
+def run_layer(sh, steps, warmup, with_cpu):
+    log(f"[bench] setup {sh.name}: T={sh.T} d={sh.d} E={sh.E} K={sh.K} I={sh.I}")
+    t = time.time()
+    st = layer_setup(sh)
+    log(f"[bench] inputs + packed weights ready in {time.time() - t:.1f}s")
+    for _ in range(warmup):
+        layer_step(sh, st)
+    torch.cuda.synchronize()
+    log("[bench] warmup done")
+    ev = Events()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        layer_step(sh, st, ev)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = wall * 1e3 / steps
+    count = st["count"].cpu().numpy()
+    stages = {n: round(ev.avg_ms(n), 4) for n in ev.pairs}
+    g1, g2 = layer_flops(sh)
+    g1_ms = ev.avg_ms("gemm1")
+    if sh.T >= 4096:
+        achieved = g1 / (g1_ms * 1e-3) / 1e12
+        roof = {"kernel": "grouped_gemm_fp8_blockscaled (GEMM1, SwiGLU + 1x128 requant epilogue)",
+                "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
+                "traffic": traffic_for(f"gemm1_{sh.name}", "gemm.hip"),
+                "algorithmic_per_launch": g1, "avg_launch_ms": round(g1_ms, 4)}
+    else:
+        nbytes = gemm1_bytes(sh, count)
+        achieved = nbytes / (g1_ms * 1e-3) / 1e9
+        roof = {"kernel": "grouped_gemm_fp8_blockscaled (GEMM1, SwiGLU + 1x128 requant epilogue)",
+                "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": traffic_for(f"gemm1_{sh.name}", "gemm.hip"),
+                "algorithmic_per_launch": nbytes, "avg_launch_ms": round(g1_ms, 4)}
+    log(f"[bench] {ms:.3f} ms/step; stages {stages}")
+    res = {
+        "metric": "MoE-layer tokens/s (d=7168, 256E top-8, FP8) + % of FP8 MFMA / HBM roofline",
+        "value": round(sh.T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate)", "data": "synthetic (seeded; random-init expert weights)",
+        "config": {"workload": f"moe_layer_{sh.name}", "T": sh.T, "d": sh.d, "routed_experts": sh.E,
+                   "top_k": sh.K, "shared_experts": sh.shared, "inter": sh.I,
+                   "load_max_over_mean": round(float(count.max() / count.mean()), 3),
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "stages_ms": stages,
+        "gemm_tflops": {"gemm1": round(g1 / (ev.avg_ms("gemm1") * 1e-3) / 1e12, 1),
+                        "gemm2": round(g2 / (ev.avg_ms("gemm2") * 1e-3) / 1e12, 1)},
+    }
+    if with_cpu:
+        log("[bench] CPU oracle baseline")
+        res["cpu_baseline"] = cpu_baseline_layer(sh, st)
+    return res
+
+
+def run_dense(steps, warmup, K=4096):
+    M, N = workloads.DENSE["M"], workloads.DENSE["N"]
+    log(f"[bench] dense GEMM M={M} N={N} K={K}")
+    a, b = workloads.dense_operands(M, N, K, device="cuda")
+    aq, as_ = moe.fp8_quant_1x128(a)
+    bq, bs = moe.fp8_quant_128x128(b)
+    del a, b
+    go = torch.tensor([0, M], dtype=torch.int32, device="cuda")
+    out = torch.empty(M, N, dtype=torch.float32, device="cuda")
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    bq3, bs3 = bq.view(1, N, K), bs.view(1, N // 128, K // 128)
+    for _ in range(warmup):
+        moe.grouped_gemm_fp8_blockscaled(aq, as_, go, M, bq3, bs3, out=out, ws=ws)
+    ev = Events()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        a0 = ev.mark("s")
+        moe.grouped_gemm_fp8_blockscaled(aq, as_, go, M, bq3, bs3, out=out, ws=ws)
+        ev.add("gemm", a0, ev.mark("e"))
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    flops = 2.0 * M * N * K
+    g_ms = ev.avg_ms("gemm")
+    ach = flops / (g_ms * 1e-3) / 1e12
+    return {
+        "metric": "block-scaled FP8 GEMM TFLOP/s", "value": round(flops / (ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3 (fp32 accumulate)",
+        "data": "synthetic", "config": {"workload": "dense_blockscaled_gemm", "M": M, "N": N, "K": K},
+        "roofline": {"kernel": "grouped_gemm_fp8_blockscaled (1 group)", "bound": "mfma",
+                     "achieved": round(ach, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(ach / PEAK_FP8_TFLOPS, 4), "traffic": traffic_for(f"dense_k{K}", "gemm.hip")},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill", choices=["prefill", "decode", "tiny", "dense", "dense16k"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this layer forward is a single-GPU path "
+              f"(--gpus {args.gpus} is not supported)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    moe.load_library()
+    if args.workload in ("dense", "dense16k"):
+        res = run_dense(args.steps, args.warmup, K=4096 if args.workload == "dense" else 16384)
+    else:
+        res = run_layer(workloads.SHAPES[args.workload], args.steps, args.warmup,
+                        with_cpu=not args.no_cpu_baseline)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,229 @@
+/*
+ * moe_fp8.h -- C ABI of the MI355X (gfx950) DeepSeekMoE layer forward.
+ *
+ * One DeepSeekMoE layer: sigmoid top-K routing with a selection-only bias,
+ * drop-free dispatch, FP8 (OCP E4M3) block-scaled SwiGLU expert FFNs for one
+ * shared and E routed experts, the weighted combine, and the bias update.
+ *
+ * Sources ("the pages"):
+ *   [IFS]     "DeepSeek-V3 Technical Report" notes, learn.ifs.name/d/deepseekv3:
+ *             the MoE-routing paragraph, the bias-balancing paragraph, the FP8
+ *             tiling paragraph and the FP8-accumulation paragraph.
+ *   [LINEAGE] "DeepSeek-V3" summary, nlp-lineage.vercel.app: "The idea"
+ *             (load-balancing and FP8 bullets) and "The notation" (the layer's
+ *             output equation).
+ *
+ * Conventions for every call below
+ *   - Tensor pointers are DEVICE pointers owned by the caller, row-major and
+ *     contiguous, 16-byte aligned (else MOE_ERR_ALIGN).  bf16 data is passed
+ *     as raw 16-bit words, E4M3 data as raw bytes (OCP OFP8 E4M3: bias 7, no
+ *     infinities, max 448).
+ *   - Every call only enqueues work on `stream` (a hipStream_t; NULL is the
+ *     legacy default stream) and returns without synchronising.  The library
+ *     never allocates or frees device memory; scratch space is passed in.
+ *   - Arguments are checked on the host before anything is enqueued; on an
+ *     error nothing is launched and the status says why (moe_last_error()
+ *     gives a thread-local message).  A failed launch returns MOE_ERR_HIP.
+ *     Faults inside kernels surface at the caller's next synchronisation.
+ *   - Results are deterministic: identical inputs give identical bits.
+ *   - T = 0 (no tokens) is valid and enqueues nothing.
+ */
+#ifndef MOE_FP8_H
+#define MOE_FP8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* moe_stream_t; /* the same type as hipStream_t */
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_NULLPTR = -1,     /* a required pointer is NULL */
+    MOE_ERR_SHAPE = -2,       /* sizes inconsistent or not multiples of 128 */
+    MOE_ERR_UNSUPPORTED = -3, /* sizes outside what the kernels handle */
+    MOE_ERR_WORKSPACE = -4,   /* scratch buffer too small */
+    MOE_ERR_ALIGN = -5,       /* a pointer is not 16-byte aligned */
+    MOE_ERR_HIP = -6          /* the HIP runtime reported an error */
+} moe_status;
+
+typedef enum { MOE_BF16 = 0, MOE_F32 = 1 } moe_dtype;
+
+/* What the grouped GEMM writes (grouped_gemm_fp8_blockscaled). */
+typedef enum {
+    MOE_EPI_STORE_F32 = 0,   /* out = C, FP32 [M_total, N] */
+    MOE_EPI_SWIGLU_F32 = 1,  /* out = SiLU(C_gate) * C_up, FP32 [M_total, N/2] */
+    MOE_EPI_SWIGLU_QUANT = 2 /* the same h, quantised per 1x128 tile into
+                                out_q E4M3 [M_total, N/2] + out_scale FP32
+                                [M_total, N/256] */
+} moe_epilogue;
+
+const char* moe_status_string(int status);
+const char* moe_last_error(void);
+/* Library version: major*10000 + minor*100 + patch. */
+int moe_version(void);
+
+/* ------------------------------------------------------------------ router
+ * moe_router_topk -- [IFS] MoE-routing paragraph: each token picks the top K
+ * of E routed experts by sigmoid affinity to the expert's centroid, and the
+ * gates are normalised over the chosen ones; [IFS] bias paragraph and
+ * [LINEAGE] "The notation": a per-expert bias is added to the score for the
+ * choice only, the gate uses the raw score.
+ *
+ *   s[t,i]   = sigmoid(sum_k u[t,k] e[i,k])   FP32, summed in increasing k with
+ *              one FMA per term; the sigmoid is the library's fixed binary32
+ *              algorithm (Cody-Waite reduced exp with a degree-7 Taylor
+ *              polynomial, then 1/(1+exp(-x))), identical bit for bit across runs.
+ *   key      = s[t,i] + bias[i]  (binary32 add)
+ *   topk_idx[t,0..K-1]  = experts ranked by (key descending, index ascending)
+ *   topk_gate[t,k]      = s[t,idx] / D, D = binary32 sum of the chosen s in
+ *                         slot order (all gates 0 if D = 0)
+ *
+ * u_bf16 [T,d], centroids_bf16 [E,d] (bf16 words); bias FP32 [E], read only;
+ * scores FP32 [T,E]: caller-provided scratch that holds s on return;
+ * topk_idx int32 [T,K]; topk_gate FP32 [T,K].
+ * Limits: d % 128 == 0, 1 <= E <= 256, 1 <= K <= min(E, 16).
+ */
+int moe_router_topk(const void* u_bf16, const void* centroids_bf16, const float* bias,
+                    int64_t T, int d, int E, int K, float* scores, int32_t* topk_idx,
+                    float* topk_gate, moe_stream_t stream);
+
+/* ------------------------------------------------------------------ dispatch
+ * moe_dispatch -- turns the routing into GEMM rows.  No token is ever dropped
+ * ([LINEAGE] "The idea", load-balancing bullet): there is no capacity limit.
+ * Rows are ordered by (expert, token); with include_shared the T rows of the
+ * shared expert ([IFS] MoE-routing paragraph: one shared expert every token
+ * uses) follow in token order.  R = T*K + (include_shared ? T : 0).
+ *
+ *   expert_count int32 [E]                  assignments per routed expert
+ *   group_offset int32 [E + 1 + include_shared]
+ *                exclusive scan of expert_count, then T*K (, then T*K + T)
+ *   row_token    int32 [R]                  token of each GEMM row
+ *   slot_row     int32 [T,K]                row holding assignment (t, k)
+ * topk_idx must hold values in [0, E) with distinct experts per token (as
+ * moe_router_topk writes); other input gives unspecified rows but no
+ * out-of-bounds access.  ws: scratch of moe_dispatch_workspace_bytes(T, E).
+ */
+size_t moe_dispatch_workspace_bytes(int64_t T, int E);
+int moe_dispatch(const int32_t* topk_idx, int64_t T, int K, int E, int include_shared,
+                 int32_t* expert_count, int32_t* group_offset, int32_t* row_token,
+                 int32_t* slot_row, void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* moe_permute_rows -- out[r] = x[row_token[r]] for r < rows, rows of d
+ * elements of type dt (the dispatch's data movement, made explicit). */
+int moe_permute_rows(const void* x, int dt, const int32_t* row_token, int64_t rows, int d,
+                     void* out, moe_stream_t stream);
+
+/* ------------------------------------------------------------------ FP8 quantisers
+ * [IFS] FP8-tiling paragraph: activations are scaled per 1x128 tile (one
+ * token, 128 channels) and weights per 128x128 block, so an outlier only
+ * affects its own group.  Scale rule for every tile/block:
+ *   amax = max|x|;  if amax == 0 or 448/amax is not finite: scale = inv = 1,
+ *   else inv = fl32(448/amax), scale = fl32(amax/448);
+ *   q = E4M3(fl32(x * inv)), round to nearest even, finite overflow saturates
+ *   to +-448, NaN -> 0x7F|sign.  The value is decoded as E4M3(q) * scale.
+ *
+ * fp8_quant_1x128: x [rows, cols] (bf16 or FP32) -> q [rows, cols],
+ *                  scale FP32 [rows, cols/128].  cols % 128 == 0.
+ * fp8_quant_128x128: w [rows, cols] FP32 -> q [rows, cols],
+ *                  scale FP32 [rows/128, cols/128].  rows, cols % 128 == 0.
+ */
+int fp8_quant_1x128(const void* x, int in_dt, int64_t rows, int cols, uint8_t* q,
+                    float* scale, moe_stream_t stream);
+int fp8_quant_128x128(const float* w, int64_t rows, int cols, uint8_t* q, float* scale,
+                      moe_stream_t stream);
+
+/* ------------------------------------------------------------------ grouped GEMM
+ * grouped_gemm_fp8_blockscaled -- [IFS] FP8-accumulation paragraph: the inner
+ * dimension is processed in 128-element slices and each slice's partial sum is
+ * promoted to FP32, where the per-group scales are applied:
+ *   C[m,n] = sum_j  a_scale[am,j] * b_scale[g, n/128, j] * P_j[m,n],
+ *   P_j[m,n] = sum_{k in slice j} E4M3(a_q[am,k]) * E4M3(b_q[g,n,k])
+ * with every P_j an FP8 MFMA into a fresh FP32 accumulator and the scaled sum
+ * an FP32 FMA chain over j.  Row m belongs to group g when
+ * group_offset[g] <= m < group_offset[g+1]; am = a_row_index[m] (a gather; NULL
+ * means am = m).
+ *
+ *   a_q  E4M3 [*, K], a_scale FP32 [*, K/128]
+ *   group_offset int32 [G+1] (device), non-decreasing, group_offset[0] = 0,
+ *                group_offset[G] = M_total (the host-known total row count)
+ *   b_q  E4M3 [G, N, K], b_scale FP32 [G, N/128, K/128]
+ *   epi  MOE_EPI_STORE_F32:   out FP32 [M_total, N]
+ *        MOE_EPI_SWIGLU_F32:  out FP32 [M_total, N/2]; B's rows are interleaved
+ *                             in 128-row blocks: rows [256j, 256j+128) are the
+ *                             gate projection's rows [128j, 128j+128) and rows
+ *                             [256j+128, 256j+256) the up projection's;
+ *                             h[m, 128j+c] = SiLU(C[m,256j+c]) * C[m,256j+128+c]
+ *        MOE_EPI_SWIGLU_QUANT: the same h, quantised per 1x128 tile with the
+ *                             rule above into out_q [M_total, N/2] and
+ *                             out_scale [M_total, N/256]; out may be NULL.
+ *   ws   scratch of moe_gemm_workspace_bytes(G).
+ * Limits: K % 128 == 0, N % 256 == 0 for the SwiGLU epilogues, N % 128 == 0
+ * otherwise, G >= 1.
+ */
+size_t moe_gemm_workspace_bytes(int G);
+int grouped_gemm_fp8_blockscaled(const uint8_t* a_q, const float* a_scale,
+                                 const int32_t* a_row_index, const int32_t* group_offset,
+                                 int G, int64_t M_total, const uint8_t* b_q,
+                                 const float* b_scale, int N, int K, int epi, float* out,
+                                 uint8_t* out_q, float* out_scale, void* ws, size_t ws_bytes,
+                                 moe_stream_t stream);
+
+/* ------------------------------------------------------------------ combine
+ * moe_combine -- [LINEAGE] "The notation":
+ *   h'[t] = u[t] + sum_shared FFN(u[t]) + sum_k g[t,k] FFN_{idx[t,k]}(u[t])
+ *   out[t,c] = u[t,c] + y[shared_row0 + t, c] + sum_k gate[t,k] * y[slot_row[t,k], c]
+ * evaluated in FP32 in exactly that order (shared term skipped when
+ * shared_row0 < 0).  u_bf16 [T,d]; y [rows, d] of type y_dt (FP32 or bf16);
+ * gate FP32 [T,K]; slot_row int32 [T,K]; out FP32 [T,d].
+ */
+int moe_combine(const void* u_bf16, const void* y, int y_dt, int64_t shared_row0,
+                const float* topk_gate, const int32_t* slot_row, int64_t T, int K, int d,
+                float* out, moe_stream_t stream);
+
+/* ------------------------------------------------------------------ bias update
+ * moe_bias_update -- [IFS] bias paragraph: after each step the bias of an
+ * overloaded expert is lowered by gamma and that of an underloaded one raised.
+ * Overloaded: expert_count[i]*E > total_assignments; underloaded: <; an expert
+ * exactly at the batch mean keeps its bias.  bias FP32 [E] is updated in place
+ * (binary32 add).  total_assignments = T*K of the batch the counts came from.
+ */
+int moe_bias_update(float* bias, const int32_t* expert_count, int E, int64_t total_assignments,
+                    float gamma, moe_stream_t stream);
+
+/* ------------------------------------------------------------------ weights and the whole layer
+ * Packed expert weights, for G = E + 1 groups (routed experts 0..E-1, then
+ * the shared expert as group E):
+ *   [W13_q  E4M3 G x (2I) x d ]  gate/up rows interleaved per 128-row block
+ *   [W2_q   E4M3 G x d x I    ]
+ *   [W13_s  FP32 G x (2I/128) x (d/128)]
+ *   [W2_s   FP32 G x (d/128) x (I/128)]
+ * moe_prepare_expert_weights quantises one expert's FP32 masters (W1, W3
+ * [I,d], W2 [d,I]; FFN(x) = W2 (SiLU(W1 x) * W3 x)) per 128x128 block into
+ * its slots of `packed`.  The pages name the expert only as FFN_i; the SwiGLU
+ * form is this library's reading.
+ */
+size_t moe_packed_weight_bytes(int n_groups, int d, int I);
+int moe_prepare_expert_weights(const float* w1, const float* w3, const float* w2,
+                               int expert_index, int n_groups, int d, int I, void* packed,
+                               moe_stream_t stream);
+
+/* moe_layer_forward -- the whole layer: router, dispatch, 1x128 quantisation
+ * of u, GEMM1 with fused SwiGLU and 1x128 re-quantisation, GEMM2, combine.
+ * The bias is read only (update it with moe_bias_update).  packed_weights as
+ * above with G = E + 1; out FP32 [T,d]; expert_count_out int32 [E] (may be
+ * NULL); ws of moe_layer_workspace_bytes(T, d, E, K, I).
+ */
+size_t moe_layer_workspace_bytes(int64_t T, int d, int E, int K, int I);
+int moe_layer_forward(const void* u_bf16, const void* centroids_bf16, const float* bias,
+                      const void* packed_weights, int64_t T, int d, int E, int K, int I,
+                      float* out, int32_t* expert_count_out, void* ws, size_t ws_bytes,
+                      moe_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_FP8_H */

@@ -1,0 +1,308 @@
+"""Python binding of libmoefp8.so, the MI355X (gfx950) DeepSeekMoE layer forward.
+
+Thin ctypes marshalling over the C ABI declared in ``include/moe_fp8.h``:
+every function here has the name of a C entry point, checks tensor dtypes,
+devices and shapes, allocates outputs with torch when the caller passes none,
+and hands raw device pointers plus torch's current HIP stream to the library.
+All arithmetic runs in the library's HIP kernels; there is no fallback.  If
+the shared library is missing the calls raise instead of computing anything.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoefp8.so")
+
+MOE_BF16, MOE_F32 = 0, 1
+MOE_EPI_STORE_F32, MOE_EPI_SWIGLU_F32, MOE_EPI_SWIGLU_QUANT = 0, 1, 2
+
+# every symbol the header declares (kept in step with include/moe_fp8.h)
+EXPORTS = (
+    "moe_status_string", "moe_last_error", "moe_version",
+    "moe_router_topk",
+    "moe_dispatch_workspace_bytes", "moe_dispatch", "moe_permute_rows",
+    "fp8_quant_1x128", "fp8_quant_128x128",
+    "moe_gemm_workspace_bytes", "grouped_gemm_fp8_blockscaled",
+    "moe_combine", "moe_bias_update",
+    "moe_packed_weight_bytes", "moe_prepare_expert_weights",
+    "moe_layer_workspace_bytes", "moe_layer_forward",
+)
+
+
+class MoEError(RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libmoefp8.so and declare the C signatures (no GPU needed)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise MoEError(f"{path} is missing: build it with sigmoid_top_routing_02_amd/build.py")
+    L = ctypes.CDLL(path)
+    P, I64, I32, F32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    sig = {
+        "moe_status_string": ([I32], ctypes.c_char_p),
+        "moe_last_error": ([], ctypes.c_char_p),
+        "moe_version": ([], I32),
+        "moe_router_topk": ([P, P, P, I64, I32, I32, I32, P, P, P, P], I32),
+        "moe_dispatch_workspace_bytes": ([I64, I32], SZ),
+        "moe_dispatch": ([P, I64, I32, I32, I32, P, P, P, P, P, SZ, P], I32),
+        "moe_permute_rows": ([P, I32, P, I64, I32, P, P], I32),
+        "fp8_quant_1x128": ([P, I32, I64, I32, P, P, P], I32),
+        "fp8_quant_128x128": ([P, I64, I32, P, P, P], I32),
+        "moe_gemm_workspace_bytes": ([I32], SZ),
+        "grouped_gemm_fp8_blockscaled": ([P, P, P, P, I32, I64, P, P, I32, I32, I32, P, P, P, P, SZ, P], I32),
+        "moe_combine": ([P, P, I32, I64, P, P, I64, I32, I32, P, P], I32),
+        "moe_bias_update": ([P, P, I32, I64, F32, P], I32),
+        "moe_packed_weight_bytes": ([I32, I32, I32], SZ),
+        "moe_prepare_expert_weights": ([P, P, P, I32, I32, I32, I32, P, P], I32),
+        "moe_layer_workspace_bytes": ([I64, I32, I32, I32, I32], SZ),
+        "moe_layer_forward": ([P, P, P, P, I64, I32, I32, I32, I32, P, P, P, SZ, P], I32),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = L
+    return L
+
+
+def _check(status: int, name: str):
+    if status != 0:
+        L = load_library()
+        raise MoEError(f"{name}: {L.moe_status_string(status).decode()} ({status}): "
+                       f"{L.moe_last_error().decode()}")
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise MoEError("tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise MoEError("tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _want(t, dtype, shape, name):
+    if t.dtype != dtype:
+        raise MoEError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise MoEError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _new(shape, dtype, like):
+    return torch.empty(shape, dtype=dtype, device=like.device)
+
+
+# ---------------------------------------------------------------- router
+def moe_router_topk(u, centroids, bias, K, scores=None, topk_idx=None, topk_gate=None):
+    """u bf16 [T,d], centroids bf16 [E,d], bias f32 [E] -> (idx i32 [T,K], gate f32 [T,K], scores f32 [T,E])."""
+    T, d = u.shape
+    E = centroids.shape[0]
+    _want(u, torch.bfloat16, (T, d), "u")
+    _want(centroids, torch.bfloat16, (E, d), "centroids")
+    _want(bias, torch.float32, (E,), "bias")
+    scores = _new((T, E), torch.float32, u) if scores is None else scores
+    topk_idx = _new((T, K), torch.int32, u) if topk_idx is None else topk_idx
+    topk_gate = _new((T, K), torch.float32, u) if topk_gate is None else topk_gate
+    _want(scores, torch.float32, (T, E), "scores")
+    _want(topk_idx, torch.int32, (T, K), "topk_idx")
+    _want(topk_gate, torch.float32, (T, K), "topk_gate")
+    L = load_library()
+    _check(L.moe_router_topk(_ptr(u), _ptr(centroids), _ptr(bias), T, d, E, K, _ptr(scores),
+                             _ptr(topk_idx), _ptr(topk_gate), _stream()), "moe_router_topk")
+    return topk_idx, topk_gate, scores
+
+
+# ---------------------------------------------------------------- dispatch
+def moe_dispatch_workspace_bytes(T, E):
+    return load_library().moe_dispatch_workspace_bytes(T, E)
+
+
+def moe_dispatch(topk_idx, E, include_shared=True, ws=None):
+    """-> (expert_count [E], group_offset [E+1(+1)], row_token [R], slot_row [T,K]), int32."""
+    T, K = topk_idx.shape
+    _want(topk_idx, torch.int32, (T, K), "topk_idx")
+    sh = 1 if include_shared else 0
+    R = T * K + sh * T
+    count = _new((E,), torch.int32, topk_idx)
+    go = _new((E + 1 + sh,), torch.int32, topk_idx)
+    row_token = _new((max(R, 1),), torch.int32, topk_idx)
+    slot_row = _new((T, K), torch.int32, topk_idx)
+    L = load_library()
+    nb = L.moe_dispatch_workspace_bytes(T, E)
+    if ws is None:
+        ws = _new((max(nb, 256),), torch.uint8, topk_idx)
+    _check(L.moe_dispatch(_ptr(topk_idx), T, K, E, sh, _ptr(count), _ptr(go), _ptr(row_token),
+                          _ptr(slot_row), _ptr(ws), ws.numel(), _stream()), "moe_dispatch")
+    return count, go, row_token[:R], slot_row
+
+
+def moe_permute_rows(x, row_token, out=None):
+    rows = row_token.shape[0]
+    T, d = x.shape
+    dt = {torch.bfloat16: MOE_BF16, torch.float32: MOE_F32}[x.dtype]
+    out = _new((rows, d), x.dtype, x) if out is None else out
+    _want(out, x.dtype, (rows, d), "out")
+    L = load_library()
+    _check(L.moe_permute_rows(_ptr(x), dt, _ptr(row_token), rows, d, _ptr(out), _stream()),
+           "moe_permute_rows")
+    return out
+
+
+# ---------------------------------------------------------------- quantisers
+def fp8_quant_1x128(x, q=None, scale=None):
+    """x bf16/f32 [rows, cols] -> (q uint8 [rows, cols], scale f32 [rows, cols/128])."""
+    rows, cols = x.shape
+    dt = {torch.bfloat16: MOE_BF16, torch.float32: MOE_F32}[x.dtype]
+    q = _new((rows, cols), torch.uint8, x) if q is None else q
+    scale = _new((rows, cols // 128), torch.float32, x) if scale is None else scale
+    _want(q, torch.uint8, (rows, cols), "q")
+    _want(scale, torch.float32, (rows, cols // 128), "scale")
+    L = load_library()
+    _check(L.fp8_quant_1x128(_ptr(x), dt, rows, cols, _ptr(q), _ptr(scale), _stream()),
+           "fp8_quant_1x128")
+    return q, scale
+
+
+def fp8_quant_128x128(w, q=None, scale=None):
+    rows, cols = w.shape
+    _want(w, torch.float32, (rows, cols), "w")
+    q = _new((rows, cols), torch.uint8, w) if q is None else q
+    scale = _new((rows // 128, cols // 128), torch.float32, w) if scale is None else scale
+    L = load_library()
+    _check(L.fp8_quant_128x128(_ptr(w), rows, cols, _ptr(q), _ptr(scale), _stream()),
+           "fp8_quant_128x128")
+    return q, scale
+
+
+# ---------------------------------------------------------------- grouped GEMM
+def moe_gemm_workspace_bytes(G):
+    return load_library().moe_gemm_workspace_bytes(G)
+
+
+def grouped_gemm_fp8_blockscaled(a_q, a_scale, group_offset, M_total, b_q, b_scale,
+                                 epi=MOE_EPI_STORE_F32, a_row_index=None, out=None, out_q=None,
+                                 out_scale=None, ws=None):
+    """a_q uint8 [*,K], a_scale f32 [*,K/128], group_offset i32 [G+1] (device),
+    b_q uint8 [G,N,K], b_scale f32 [G,N/128,K/128]."""
+    G, N, K = b_q.shape
+    _want(b_scale, torch.float32, (G, N // 128, K // 128), "b_scale")
+    if a_q.shape[1] != K:
+        raise MoEError("a_q: inner dimension differs from b_q")
+    if group_offset.numel() < G + 1:
+        raise MoEError("group_offset must hold G+1 entries")
+    if epi == MOE_EPI_STORE_F32:
+        out = _new((M_total, N), torch.float32, a_q) if out is None else out
+    elif epi == MOE_EPI_SWIGLU_F32:
+        out = _new((M_total, N // 2), torch.float32, a_q) if out is None else out
+    else:
+        out_q = _new((M_total, N // 2), torch.uint8, a_q) if out_q is None else out_q
+        out_scale = _new((M_total, N // 256), torch.float32, a_q) if out_scale is None else out_scale
+    L = load_library()
+    if ws is None:
+        ws = _new((max(L.moe_gemm_workspace_bytes(G), 256),), torch.uint8, a_q)
+    _check(L.grouped_gemm_fp8_blockscaled(
+        _ptr(a_q), _ptr(a_scale), _ptr(a_row_index), _ptr(group_offset), G, M_total, _ptr(b_q),
+        _ptr(b_scale), N, K, epi, _ptr(out), _ptr(out_q), _ptr(out_scale), _ptr(ws), ws.numel(),
+        _stream()), "grouped_gemm_fp8_blockscaled")
+    if epi == MOE_EPI_SWIGLU_QUANT:
+        return out_q, out_scale
+    return out
+
+
+# ---------------------------------------------------------------- combine / bias
+def moe_combine(u, y, topk_gate, slot_row, shared_row0=-1, out=None):
+    T, d = u.shape
+    K = topk_gate.shape[1]
+    _want(u, torch.bfloat16, (T, d), "u")
+    _want(topk_gate, torch.float32, (T, K), "topk_gate")
+    _want(slot_row, torch.int32, (T, K), "slot_row")
+    dt = {torch.bfloat16: MOE_BF16, torch.float32: MOE_F32}[y.dtype]
+    out = _new((T, d), torch.float32, u) if out is None else out
+    L = load_library()
+    _check(L.moe_combine(_ptr(u), _ptr(y), dt, shared_row0, _ptr(topk_gate), _ptr(slot_row), T, K,
+                         d, _ptr(out), _stream()), "moe_combine")
+    return out
+
+
+def moe_bias_update(bias, expert_count, total_assignments, gamma):
+    """In-place update of bias (f32 [E]) from expert_count (i32 [E])."""
+    E = bias.shape[0]
+    _want(bias, torch.float32, (E,), "bias")
+    _want(expert_count, torch.int32, (E,), "expert_count")
+    L = load_library()
+    _check(L.moe_bias_update(_ptr(bias), _ptr(expert_count), E, total_assignments, gamma, _stream()),
+           "moe_bias_update")
+    return bias
+
+
+# ---------------------------------------------------------------- weights / layer
+def moe_packed_weight_bytes(n_groups, d, I):
+    return load_library().moe_packed_weight_bytes(n_groups, d, I)
+
+
+def moe_prepare_expert_weights(w1, w3, w2, expert_index, n_groups, packed):
+    I, d = w1.shape
+    _want(w1, torch.float32, (I, d), "w1")
+    _want(w3, torch.float32, (I, d), "w3")
+    _want(w2, torch.float32, (d, I), "w2")
+    L = load_library()
+    _check(L.moe_prepare_expert_weights(_ptr(w1), _ptr(w3), _ptr(w2), expert_index, n_groups, d, I,
+                                        _ptr(packed), _stream()), "moe_prepare_expert_weights")
+    return packed
+
+
+def packed_views(packed, n_groups, d, I):
+    """Views of the packed weight buffer: (w13_q [G,2I,d], w2_q [G,d,I],
+    w13_s [G,2I/128,d/128], w2_s [G,d/128,I/128]) -- the layout the header
+    documents (each part starts on a 256-byte boundary)."""
+    def al(x):
+        return (x + 255) // 256 * 256
+    G = n_groups
+    o0 = 0
+    o1 = o0 + al(G * 2 * I * d)
+    o2 = o1 + al(G * d * I)
+    o3 = o2 + al(G * (2 * I // 128) * (d // 128) * 4)
+    w13q = packed[o0:o0 + G * 2 * I * d].view(G, 2 * I, d)
+    w2q = packed[o1:o1 + G * d * I].view(G, d, I)
+    w13s = packed[o2:o2 + G * (2 * I // 128) * (d // 128) * 4].view(torch.float32).view(G, 2 * I // 128, d // 128)
+    w2s = packed[o3:o3 + G * (d // 128) * (I // 128) * 4].view(torch.float32).view(G, d // 128, I // 128)
+    return w13q, w2q, w13s, w2s
+
+
+def moe_layer_workspace_bytes(T, d, E, K, I):
+    return load_library().moe_layer_workspace_bytes(T, d, E, K, I)
+
+
+def moe_layer_forward(u, centroids, bias, packed, K, I, out=None, expert_count=None, ws=None):
+    T, d = u.shape
+    E = centroids.shape[0]
+    _want(u, torch.bfloat16, (T, d), "u")
+    _want(centroids, torch.bfloat16, (E, d), "centroids")
+    _want(bias, torch.float32, (E,), "bias")
+    L = load_library()
+    need = L.moe_packed_weight_bytes(E + 1, d, I)
+    if packed.dtype != torch.uint8 or packed.numel() < need:
+        raise MoEError(f"packed weights: need {need} bytes of uint8")
+    out = _new((T, d), torch.float32, u) if out is None else out
+    if ws is None:
+        ws = _new((max(L.moe_layer_workspace_bytes(T, d, E, K, I), 256),), torch.uint8, u)
+    _check(L.moe_layer_forward(_ptr(u), _ptr(centroids), _ptr(bias), _ptr(packed), T, d, E, K, I,
+                               _ptr(out), _ptr(expert_count), _ptr(ws), ws.numel(), _stream()),
+           "moe_layer_forward")
+    return out

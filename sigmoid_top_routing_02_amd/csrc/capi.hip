@@ -1,0 +1,385 @@
+// C ABI of the library (declared in include/moe_fp8.h).  Every entry point
+// checks its arguments on the host, then enqueues kernels on the caller's
+// stream.  No allocation, no synchronisation, no global state except the
+// thread-local text of the last error.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/moe_fp8.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return MOE_OK;
+    return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define REQUIRE_PTR(p)                                                               \
+    do {                                                                             \
+        if (!(p)) return fail(MOE_ERR_NULLPTR, "%s: %s is NULL", __func__, #p);      \
+        if (!aligned16(p)) return fail(MOE_ERR_ALIGN, "%s: %s is not 16-byte aligned", __func__, #p); \
+    } while (0)
+
+#define REQUIRE(cond, status, ...)                      \
+    do {                                                \
+        if (!(cond)) return fail(status, __VA_ARGS__);  \
+    } while (0)
+
+inline hipStream_t S(moe_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int s) {
+    switch (s) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_NULLPTR: return "null pointer";
+        case MOE_ERR_SHAPE: return "invalid shape";
+        case MOE_ERR_UNSUPPORTED: return "unsupported size";
+        case MOE_ERR_WORKSPACE: return "workspace too small";
+        case MOE_ERR_ALIGN: return "misaligned pointer";
+        case MOE_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+int moe_version(void) { return 10000; }
+
+int moe_router_topk(const void* u_bf16, const void* centroids_bf16, const float* bias, int64_t T,
+                    int d, int E, int K, float* scores, int32_t* topk_idx, float* topk_gate,
+                    moe_stream_t stream) {
+    REQUIRE(T >= 0, MOE_ERR_SHAPE, "moe_router_topk: T < 0");
+    REQUIRE(d > 0 && d % 128 == 0, MOE_ERR_SHAPE, "moe_router_topk: d=%d not a positive multiple of 128", d);
+    REQUIRE(E >= 1 && E <= 256, MOE_ERR_UNSUPPORTED, "moe_router_topk: E=%d outside [1, 256]", E);
+    REQUIRE(K >= 1 && K <= E && K <= 16, MOE_ERR_UNSUPPORTED, "moe_router_topk: K=%d outside [1, min(E,16)]", K);
+    if (T == 0) return MOE_OK;
+    REQUIRE_PTR(u_bf16);
+    REQUIRE_PTR(centroids_bf16);
+    REQUIRE_PTR(bias);
+    REQUIRE_PTR(scores);
+    REQUIRE_PTR(topk_idx);
+    REQUIRE_PTR(topk_gate);
+    hipError_t e = moe::launch_router_scores(static_cast<const uint16_t*>(u_bf16),
+                                             static_cast<const uint16_t*>(centroids_bf16), T, d, E,
+                                             scores, S(stream));
+    if (e != hipSuccess) return hip_status(e, "router scores launch");
+    e = moe::launch_router_topk(scores, bias, T, E, K, topk_idx, topk_gate, S(stream));
+    return hip_status(e, "router top-k launch");
+}
+
+size_t moe_dispatch_workspace_bytes(int64_t T, int E) {
+    if (T <= 0 || E <= 0) return 0;
+    return moe::dispatch_ws_bytes(T, E);
+}
+
+int moe_dispatch(const int32_t* topk_idx, int64_t T, int K, int E, int include_shared,
+                 int32_t* expert_count, int32_t* group_offset, int32_t* row_token,
+                 int32_t* slot_row, void* ws, size_t ws_bytes, moe_stream_t stream) {
+    REQUIRE(T >= 0, MOE_ERR_SHAPE, "moe_dispatch: T < 0");
+    REQUIRE(E >= 1 && E <= 256, MOE_ERR_UNSUPPORTED, "moe_dispatch: E=%d outside [1, 256]", E);
+    REQUIRE(K >= 1 && K <= E && K <= 16, MOE_ERR_UNSUPPORTED, "moe_dispatch: K=%d outside [1, min(E,16)]", K);
+    REQUIRE(include_shared == 0 || include_shared == 1, MOE_ERR_SHAPE, "moe_dispatch: include_shared must be 0 or 1");
+    REQUIRE(T * (K + 1) < (int64_t)1 << 31, MOE_ERR_UNSUPPORTED, "moe_dispatch: T*(K+1) exceeds int32 rows");
+    if (T == 0) return MOE_OK;
+    REQUIRE_PTR(topk_idx);
+    REQUIRE_PTR(expert_count);
+    REQUIRE_PTR(group_offset);
+    REQUIRE_PTR(row_token);
+    REQUIRE_PTR(slot_row);
+    REQUIRE_PTR(ws);
+    REQUIRE(ws_bytes >= moe::dispatch_ws_bytes(T, E), MOE_ERR_WORKSPACE,
+            "moe_dispatch: workspace %zu < %zu bytes", ws_bytes, moe::dispatch_ws_bytes(T, E));
+    return hip_status(moe::launch_dispatch(topk_idx, T, K, E, include_shared, expert_count,
+                                           group_offset, row_token, slot_row, ws, S(stream)),
+                      "dispatch launch");
+}
+
+int moe_permute_rows(const void* x, int dt, const int32_t* row_token, int64_t rows, int d,
+                     void* out, moe_stream_t stream) {
+    REQUIRE(rows >= 0, MOE_ERR_SHAPE, "moe_permute_rows: rows < 0");
+    REQUIRE(dt == MOE_BF16 || dt == MOE_F32, MOE_ERR_UNSUPPORTED, "moe_permute_rows: dtype %d", dt);
+    const size_t eb = dt == MOE_F32 ? 4 : 2;
+    REQUIRE(d > 0 && (d * eb) % 16 == 0, MOE_ERR_SHAPE, "moe_permute_rows: row of %d elements is not a multiple of 16 bytes", d);
+    if (rows == 0) return MOE_OK;
+    REQUIRE_PTR(x);
+    REQUIRE_PTR(row_token);
+    REQUIRE_PTR(out);
+    return hip_status(moe::launch_permute_rows(x, eb, row_token, rows, d, out, S(stream)),
+                      "permute launch");
+}
+
+int fp8_quant_1x128(const void* x, int in_dt, int64_t rows, int cols, uint8_t* q, float* scale,
+                    moe_stream_t stream) {
+    REQUIRE(rows >= 0, MOE_ERR_SHAPE, "fp8_quant_1x128: rows < 0");
+    REQUIRE(cols > 0 && cols % 128 == 0, MOE_ERR_SHAPE, "fp8_quant_1x128: cols=%d not a positive multiple of 128", cols);
+    REQUIRE(in_dt == MOE_BF16 || in_dt == MOE_F32, MOE_ERR_UNSUPPORTED, "fp8_quant_1x128: dtype %d", in_dt);
+    if (rows == 0) return MOE_OK;
+    REQUIRE_PTR(x);
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(scale);
+    return hip_status(moe::launch_quant_1x128(x, in_dt == MOE_F32, rows, cols, q, scale, S(stream)),
+                      "quant 1x128 launch");
+}
+
+int fp8_quant_128x128(const float* w, int64_t rows, int cols, uint8_t* q, float* scale,
+                      moe_stream_t stream) {
+    REQUIRE(rows >= 0 && rows % 128 == 0, MOE_ERR_SHAPE, "fp8_quant_128x128: rows=%lld not a multiple of 128", (long long)rows);
+    REQUIRE(cols > 0 && cols % 128 == 0, MOE_ERR_SHAPE, "fp8_quant_128x128: cols=%d not a positive multiple of 128", cols);
+    REQUIRE(rows / 128 <= 65535, MOE_ERR_UNSUPPORTED, "fp8_quant_128x128: too many rows");
+    if (rows == 0) return MOE_OK;
+    REQUIRE_PTR(w);
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(scale);
+    return hip_status(moe::launch_quant_128x128(w, rows, cols, q, scale, 1, 0, S(stream)),
+                      "quant 128x128 launch");
+}
+
+size_t moe_gemm_workspace_bytes(int G) { return G > 0 ? moe::gemm_ws_bytes(G) : 0; }
+
+int grouped_gemm_fp8_blockscaled(const uint8_t* a_q, const float* a_scale,
+                                 const int32_t* a_row_index, const int32_t* group_offset, int G,
+                                 int64_t M_total, const uint8_t* b_q, const float* b_scale, int N,
+                                 int K, int epi, float* out, uint8_t* out_q, float* out_scale,
+                                 void* ws, size_t ws_bytes, moe_stream_t stream) {
+    REQUIRE(G >= 1 && G <= 65535, MOE_ERR_UNSUPPORTED, "grouped_gemm: G=%d outside [1, 65535]", G);
+    REQUIRE(M_total >= 0 && M_total < ((int64_t)1 << 31), MOE_ERR_UNSUPPORTED, "grouped_gemm: M_total out of range");
+    REQUIRE(K > 0 && K % 128 == 0, MOE_ERR_SHAPE, "grouped_gemm: K=%d not a positive multiple of 128", K);
+    REQUIRE(epi >= MOE_EPI_STORE_F32 && epi <= MOE_EPI_SWIGLU_QUANT, MOE_ERR_UNSUPPORTED, "grouped_gemm: epilogue %d", epi);
+    if (epi == MOE_EPI_STORE_F32)
+        REQUIRE(N > 0 && N % 128 == 0, MOE_ERR_SHAPE, "grouped_gemm: N=%d not a positive multiple of 128", N);
+    else
+        REQUIRE(N > 0 && N % 256 == 0, MOE_ERR_SHAPE, "grouped_gemm: SwiGLU needs N=%d a multiple of 256", N);
+    REQUIRE(M_total / 128 + G < 65535, MOE_ERR_UNSUPPORTED, "grouped_gemm: too many row tiles");
+    if (M_total == 0) return MOE_OK;
+    REQUIRE_PTR(a_q);
+    REQUIRE_PTR(a_scale);
+    REQUIRE_PTR(group_offset);
+    REQUIRE_PTR(b_q);
+    REQUIRE_PTR(b_scale);
+    if (a_row_index) REQUIRE_PTR(a_row_index);
+    if (epi == MOE_EPI_SWIGLU_QUANT) {
+        REQUIRE_PTR(out_q);
+        REQUIRE_PTR(out_scale);
+        if (out) REQUIRE_PTR(out);
+    } else {
+        REQUIRE_PTR(out);
+    }
+    REQUIRE_PTR(ws);
+    REQUIRE(ws_bytes >= moe::gemm_ws_bytes(G), MOE_ERR_WORKSPACE,
+            "grouped_gemm: workspace %zu < %zu bytes", ws_bytes, moe::gemm_ws_bytes(G));
+    return hip_status(moe::launch_grouped_gemm(a_q, a_scale, a_row_index, group_offset, G, M_total,
+                                               b_q, b_scale, N, K, epi, out, out_q, out_scale, ws,
+                                               S(stream)),
+                      "grouped gemm launch");
+}
+
+int moe_combine(const void* u_bf16, const void* y, int y_dt, int64_t shared_row0,
+                const float* topk_gate, const int32_t* slot_row, int64_t T, int K, int d,
+                float* out, moe_stream_t stream) {
+    REQUIRE(T >= 0, MOE_ERR_SHAPE, "moe_combine: T < 0");
+    REQUIRE(K >= 1 && K <= 16, MOE_ERR_UNSUPPORTED, "moe_combine: K=%d outside [1, 16]", K);
+    REQUIRE(d > 0 && d % 8 == 0, MOE_ERR_SHAPE, "moe_combine: d=%d not a positive multiple of 8", d);
+    REQUIRE(y_dt == MOE_BF16 || y_dt == MOE_F32, MOE_ERR_UNSUPPORTED, "moe_combine: dtype %d", y_dt);
+    if (T == 0) return MOE_OK;
+    REQUIRE_PTR(u_bf16);
+    REQUIRE_PTR(y);
+    REQUIRE_PTR(topk_gate);
+    REQUIRE_PTR(slot_row);
+    REQUIRE_PTR(out);
+    return hip_status(moe::launch_combine(static_cast<const uint16_t*>(u_bf16), y, y_dt == MOE_F32,
+                                          shared_row0, topk_gate, slot_row, T, K, d, out,
+                                          S(stream)),
+                      "combine launch");
+}
+
+int moe_bias_update(float* bias, const int32_t* expert_count, int E, int64_t total_assignments,
+                    float gamma, moe_stream_t stream) {
+    REQUIRE(E >= 1 && E <= 65536, MOE_ERR_UNSUPPORTED, "moe_bias_update: E=%d", E);
+    REQUIRE(total_assignments >= 0, MOE_ERR_SHAPE, "moe_bias_update: total < 0");
+    REQUIRE_PTR(bias);
+    REQUIRE_PTR(expert_count);
+    return hip_status(moe::launch_bias_update(bias, expert_count, E, total_assignments, gamma,
+                                              S(stream)),
+                      "bias update launch");
+}
+
+// ---------------------------------------------------------------- packed weights
+namespace {
+struct Packed {
+    uint8_t* w13q;
+    uint8_t* w2q;
+    float* w13s;
+    float* w2s;
+};
+Packed packed_layout(void* base, int G, int d, int I) {
+    char* p = static_cast<char*>(base);
+    Packed k;
+    k.w13q = reinterpret_cast<uint8_t*>(p);
+    p += al256((size_t)G * 2 * I * d);
+    k.w2q = reinterpret_cast<uint8_t*>(p);
+    p += al256((size_t)G * d * I);
+    k.w13s = reinterpret_cast<float*>(p);
+    p += al256((size_t)G * (2 * I / 128) * (d / 128) * sizeof(float));
+    k.w2s = reinterpret_cast<float*>(p);
+    return k;
+}
+}  // namespace
+
+size_t moe_packed_weight_bytes(int n_groups, int d, int I) {
+    if (n_groups <= 0 || d <= 0 || I <= 0) return 0;
+    const size_t G = (size_t)n_groups;
+    return al256(G * 2 * I * d) + al256(G * d * I) +
+           al256(G * (2 * I / 128) * (d / 128) * sizeof(float)) +
+           al256(G * (d / 128) * (I / 128) * sizeof(float));
+}
+
+int moe_prepare_expert_weights(const float* w1, const float* w3, const float* w2, int expert_index,
+                               int n_groups, int d, int I, void* packed, moe_stream_t stream) {
+    REQUIRE(d > 0 && d % 128 == 0 && I > 0 && I % 128 == 0, MOE_ERR_SHAPE,
+            "moe_prepare_expert_weights: d=%d, I=%d must be positive multiples of 128", d, I);
+    REQUIRE(n_groups >= 1 && expert_index >= 0 && expert_index < n_groups, MOE_ERR_SHAPE,
+            "moe_prepare_expert_weights: expert %d of %d", expert_index, n_groups);
+    REQUIRE(I / 128 <= 32767 && d / 128 <= 65535, MOE_ERR_UNSUPPORTED, "moe_prepare_expert_weights: too large");
+    REQUIRE_PTR(w1);
+    REQUIRE_PTR(w3);
+    REQUIRE_PTR(w2);
+    REQUIRE_PTR(packed);
+    Packed pk = packed_layout(packed, n_groups, d, I);
+    const size_t g = (size_t)expert_index;
+    uint8_t* q13 = pk.w13q + g * 2 * I * d;
+    float* s13 = pk.w13s + g * (2 * I / 128) * (d / 128);
+    uint8_t* q2 = pk.w2q + g * d * I;
+    float* s2 = pk.w2s + g * (d / 128) * (I / 128);
+    hipError_t e = moe::launch_quant_128x128(w1, I, d, q13, s13, 2, 0, S(stream));
+    if (e == hipSuccess) e = moe::launch_quant_128x128(w3, I, d, q13, s13, 2, 1, S(stream));
+    if (e == hipSuccess) e = moe::launch_quant_128x128(w2, d, I, q2, s2, 1, 0, S(stream));
+    return hip_status(e, "weight quantisation launch");
+}
+
+// ---------------------------------------------------------------- whole layer
+namespace {
+struct LayerWs {
+    float* scores;
+    int32_t* idx;
+    float* gate;
+    int32_t* count;
+    int32_t* go;
+    int32_t* row_token;
+    int32_t* slot_row;
+    uint8_t* uq;
+    float* us;
+    uint8_t* hq;
+    float* hs;
+    float* y;
+    void* dws;
+    void* gws;
+    size_t total;
+};
+LayerWs layer_ws(void* base, int64_t T, int d, int E, int K, int I) {
+    char* p = static_cast<char*>(base);
+    const size_t R = (size_t)T * (K + 1);
+    LayerWs w{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        char* q = p ? p + off : nullptr;
+        off += al256(bytes);
+        return q;
+    };
+    w.scores = reinterpret_cast<float*>(take((size_t)T * E * 4));
+    w.idx = reinterpret_cast<int32_t*>(take((size_t)T * K * 4));
+    w.gate = reinterpret_cast<float*>(take((size_t)T * K * 4));
+    w.count = reinterpret_cast<int32_t*>(take((size_t)E * 4));
+    w.go = reinterpret_cast<int32_t*>(take((size_t)(E + 2) * 4));
+    w.row_token = reinterpret_cast<int32_t*>(take(R * 4));
+    w.slot_row = reinterpret_cast<int32_t*>(take((size_t)T * K * 4));
+    w.uq = reinterpret_cast<uint8_t*>(take((size_t)T * d));
+    w.us = reinterpret_cast<float*>(take((size_t)T * (d / 128) * 4));
+    w.hq = reinterpret_cast<uint8_t*>(take(R * I));
+    w.hs = reinterpret_cast<float*>(take(R * (I / 128) * 4));
+    w.y = reinterpret_cast<float*>(take(R * d * 4));
+    w.dws = take(moe::dispatch_ws_bytes(T, E));
+    w.gws = take(moe::gemm_ws_bytes(E + 1));
+    w.total = off;
+    return w;
+}
+}  // namespace
+
+size_t moe_layer_workspace_bytes(int64_t T, int d, int E, int K, int I) {
+    if (T <= 0 || d <= 0 || E <= 0 || K <= 0 || I <= 0) return 0;
+    return layer_ws(nullptr, T, d, E, K, I).total;
+}
+
+int moe_layer_forward(const void* u_bf16, const void* centroids_bf16, const float* bias,
+                      const void* packed_weights, int64_t T, int d, int E, int K, int I,
+                      float* out, int32_t* expert_count_out, void* ws, size_t ws_bytes,
+                      moe_stream_t stream) {
+    REQUIRE(T >= 0, MOE_ERR_SHAPE, "moe_layer_forward: T < 0");
+    REQUIRE(d > 0 && d % 128 == 0, MOE_ERR_SHAPE, "moe_layer_forward: d=%d must be a multiple of 128", d);
+    REQUIRE(I > 0 && I % 128 == 0, MOE_ERR_SHAPE, "moe_layer_forward: I=%d must be a multiple of 128", I);
+    REQUIRE(E >= 1 && E <= 256, MOE_ERR_UNSUPPORTED, "moe_layer_forward: E=%d outside [1, 256]", E);
+    REQUIRE(K >= 1 && K <= E && K <= 16, MOE_ERR_UNSUPPORTED, "moe_layer_forward: K=%d", K);
+    REQUIRE(T * (K + 1) < ((int64_t)1 << 31) && T * (K + 1) / 128 + E + 1 < 65535, MOE_ERR_UNSUPPORTED,
+            "moe_layer_forward: T=%lld too large", (long long)T);
+    if (T == 0) return MOE_OK;
+    REQUIRE_PTR(u_bf16);
+    REQUIRE_PTR(centroids_bf16);
+    REQUIRE_PTR(bias);
+    REQUIRE_PTR(packed_weights);
+    REQUIRE_PTR(out);
+    REQUIRE_PTR(ws);
+    if (expert_count_out) REQUIRE_PTR(expert_count_out);
+    LayerWs w = layer_ws(ws, T, d, E, K, I);
+    REQUIRE(ws_bytes >= w.total, MOE_ERR_WORKSPACE, "moe_layer_forward: workspace %zu < %zu bytes",
+            ws_bytes, w.total);
+    const int G = E + 1;
+    Packed pk = packed_layout(const_cast<void*>(packed_weights), G, d, I);
+    const int64_t R = T * (K + 1);
+    hipStream_t st = S(stream);
+    hipError_t e;
+    e = moe::launch_router_scores(static_cast<const uint16_t*>(u_bf16),
+                                  static_cast<const uint16_t*>(centroids_bf16), T, d, E, w.scores, st);
+    if (e != hipSuccess) return hip_status(e, "router scores launch");
+    e = moe::launch_router_topk(w.scores, bias, T, E, K, w.idx, w.gate, st);
+    if (e != hipSuccess) return hip_status(e, "router top-k launch");
+    e = moe::launch_dispatch(w.idx, T, K, E, 1, w.count, w.go, w.row_token, w.slot_row, w.dws, st);
+    if (e != hipSuccess) return hip_status(e, "dispatch launch");
+    e = moe::launch_quant_1x128(u_bf16, 0, T, d, w.uq, w.us, st);
+    if (e != hipSuccess) return hip_status(e, "quant launch");
+    e = moe::launch_grouped_gemm(w.uq, w.us, w.row_token, w.go, G, R, pk.w13q, pk.w13s, 2 * I, d,
+                                 moe::EPI_SWIGLU_QUANT, nullptr, w.hq, w.hs, w.gws, st);
+    if (e != hipSuccess) return hip_status(e, "gemm1 launch");
+    e = moe::launch_grouped_gemm(w.hq, w.hs, nullptr, w.go, G, R, pk.w2q, pk.w2s, d, I,
+                                 moe::EPI_STORE_F32, w.y, nullptr, nullptr, w.gws, st);
+    if (e != hipSuccess) return hip_status(e, "gemm2 launch");
+    e = moe::launch_combine(static_cast<const uint16_t*>(u_bf16), w.y, 1, T * K, w.gate, w.slot_row,
+                            T, K, d, out, st);
+    if (e != hipSuccess) return hip_status(e, "combine launch");
+    if (expert_count_out) {
+        e = hipMemcpyAsync(expert_count_out, w.count, (size_t)E * 4, hipMemcpyDeviceToDevice, st);
+        if (e != hipSuccess) return hip_status(e, "count copy");
+    }
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,168 @@
+// Dispatch: per-expert histogram, exclusive scan and a stable counting-sort
+// permutation of the (token, slot) assignments, with no capacity limit -- no
+// token is ever dropped (nlp-lineage summary, "The idea", load-balancing
+// bullet).  Rows are ordered by (expert, token); the shared expert's rows
+// ("DeepSeek-V3 Technical Report" notes, MoE-routing paragraph: one shared
+// expert every token uses) follow in token order.
+//
+// Deterministic without order-dependent atomics:
+//  1. hist:    per chunk of 64 tokens, a 64-bit token mask per expert (LDS
+//              atomicOr is order-independent), its popcount = chunk count.
+//  2. scan:    per expert, exclusive prefix over chunks; then the exclusive
+//              scan over experts gives group_offset.
+//  3. scatter: row = group_offset[e] + chunk_prefix[c][e]
+//              + popcount(mask[c][e] & lanes-below-t).
+#include "device_math.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int CHUNK = 64;   // tokens per histogram chunk (one 64-bit mask)
+
+struct DispatchWs {
+    uint64_t* mask;     // [nchunk][E]
+    int32_t* cnt;       // [nchunk][E]
+    int32_t* prefix;    // [nchunk][E]
+};
+
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+__host__ __device__ inline DispatchWs carve(void* ws, int64_t nchunk, int E) {
+    char* p = static_cast<char*>(ws);
+    DispatchWs w;
+    w.mask = reinterpret_cast<uint64_t*>(p);
+    p += align256(sizeof(uint64_t) * nchunk * E);
+    w.cnt = reinterpret_cast<int32_t*>(p);
+    p += align256(sizeof(int32_t) * nchunk * E);
+    w.prefix = reinterpret_cast<int32_t*>(p);
+    return w;
+}
+
+__global__ __launch_bounds__(256) void dispatch_hist_kernel(const int32_t* __restrict__ idx,
+                                                            int64_t T, int K, int E,
+                                                            DispatchWs w) {
+    __shared__ unsigned long long m[256];
+    const int c = blockIdx.x;
+    for (int e = threadIdx.x; e < E; e += 256) m[e] = 0ull;
+    __syncthreads();
+    const int64_t t0 = (int64_t)c * CHUNK;
+    const int n = CHUNK * K;
+    for (int j = threadIdx.x; j < n; j += 256) {
+        const int tl = j / K;
+        const int64_t t = t0 + tl;
+        if (t >= T) continue;
+        const int ex = idx[t * K + (j % K)];
+        if (ex >= 0 && ex < E) atomicOr(&m[ex], 1ull << tl);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += 256) {
+        const unsigned long long v = m[e];
+        w.mask[(int64_t)c * E + e] = v;
+        w.cnt[(int64_t)c * E + e] = __popcll(v);
+    }
+}
+
+// One block: expert e is thread e (E <= 256).
+__global__ __launch_bounds__(256) void dispatch_scan_kernel(int64_t nchunk, int64_t T, int K,
+                                                            int E, int include_shared,
+                                                            DispatchWs w, int32_t* count,
+                                                            int32_t* group_offset) {
+    __shared__ int32_t tot[256];
+    const int e = threadIdx.x;
+    int32_t run = 0;
+    if (e < E) {
+        for (int64_t c = 0; c < nchunk; ++c) {
+            w.prefix[c * E + e] = run;
+            run += w.cnt[c * E + e];
+        }
+        count[e] = run;
+    }
+    tot[e] = (e < E) ? run : 0;
+    __syncthreads();
+    // inclusive Hillis-Steele scan over 256 entries
+    for (int off = 1; off < 256; off <<= 1) {
+        const int32_t v = (e >= off) ? tot[e - off] : 0;
+        __syncthreads();
+        tot[e] += v;
+        __syncthreads();
+    }
+    if (e < E) group_offset[e] = tot[e] - run;   // exclusive
+    if (e == 0) {
+        group_offset[E] = tot[255];
+        if (include_shared) group_offset[E + 1] = tot[255] + (int32_t)T;
+    }
+}
+
+__global__ __launch_bounds__(256) void dispatch_scatter_kernel(
+    const int32_t* __restrict__ idx, int64_t T, int K, int E, int include_shared, DispatchWs w,
+    const int32_t* __restrict__ group_offset, int32_t* __restrict__ row_token,
+    int32_t* __restrict__ slot_row) {
+    const int c = blockIdx.x;
+    const int64_t t0 = (int64_t)c * CHUNK;
+    const int n = CHUNK * K;
+    for (int j = threadIdx.x; j < n; j += 256) {
+        const int tl = j / K;
+        const int k = j % K;
+        const int64_t t = t0 + tl;
+        if (t >= T) continue;
+        const int ex = idx[t * K + k];
+        if (ex < 0 || ex >= E) continue;
+        const uint64_t below = (tl == 0) ? 0ull : (w.mask[(int64_t)c * E + ex] & ((1ull << tl) - 1ull));
+        const int32_t row = group_offset[ex] + w.prefix[(int64_t)c * E + ex] + __popcll(below);
+        row_token[row] = (int32_t)t;
+        slot_row[t * K + k] = row;
+    }
+    if (include_shared) {
+        for (int tl = threadIdx.x; tl < CHUNK; tl += 256) {
+            const int64_t t = t0 + tl;
+            if (t < T) row_token[T * K + t] = (int32_t)t;
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void permute_rows_kernel(const uint4* __restrict__ x,
+                                                           const int32_t* __restrict__ row_token,
+                                                           int64_t rows, int row_vecs,
+                                                           uint4* __restrict__ out) {
+    for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+        const int64_t src = row_token[r];
+        const uint4* xs = x + src * row_vecs;
+        uint4* o = out + r * row_vecs;
+        for (int v = threadIdx.x; v < row_vecs; v += 256) o[v] = xs[v];
+    }
+}
+
+}  // namespace
+
+size_t dispatch_ws_bytes(int64_t T, int E) {
+    const int64_t nchunk = (T + CHUNK - 1) / CHUNK;
+    return align256(sizeof(uint64_t) * nchunk * E) + align256(sizeof(int32_t) * nchunk * E) +
+           align256(sizeof(int32_t) * nchunk * E);
+}
+
+hipError_t launch_dispatch(const int32_t* idx, int64_t T, int K, int E, int include_shared,
+                           int32_t* count, int32_t* group_offset, int32_t* row_token,
+                           int32_t* slot_row, void* ws, hipStream_t st) {
+    const int64_t nchunk = (T + CHUNK - 1) / CHUNK;
+    DispatchWs w = carve(ws, nchunk, E);
+    hipLaunchKernelGGL(dispatch_hist_kernel, dim3((unsigned)nchunk), dim3(256), 0, st, idx, T, K,
+                       E, w);
+    hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(256), 0, st, nchunk, T, K, E,
+                       include_shared, w, count, group_offset);
+    hipLaunchKernelGGL(dispatch_scatter_kernel, dim3((unsigned)nchunk), dim3(256), 0, st, idx, T,
+                       K, E, include_shared, w, group_offset, row_token, slot_row);
+    return hipGetLastError();
+}
+
+hipError_t launch_permute_rows(const void* x, size_t elem_bytes, const int32_t* row_token,
+                               int64_t rows, int d, void* out, hipStream_t st) {
+    const int row_vecs = (int)(d * elem_bytes / 16);
+    const unsigned grid = (unsigned)(rows < 65536 ? rows : 65536);
+    hipLaunchKernelGGL(permute_rows_kernel, dim3(grid), dim3(256), 0, st,
+                       static_cast<const uint4*>(x), row_token, rows, row_vecs,
+                       static_cast<uint4*>(out));
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,49 @@
+// Internal launchers: each .hip file enqueues its kernels on a stream and
+// returns the hipError_t of the launch.  Argument checking happens in the
+// C ABI layer (capi.hip) before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// router.hip
+hipError_t launch_router_scores(const uint16_t* u, const uint16_t* e, int64_t T, int d, int E,
+                                float* s, hipStream_t st);
+hipError_t launch_router_topk(const float* s, const float* bias, int64_t T, int E, int K,
+                              int32_t* idx, float* gate, hipStream_t st);
+
+// dispatch.hip
+size_t dispatch_ws_bytes(int64_t T, int E);
+hipError_t launch_dispatch(const int32_t* idx, int64_t T, int K, int E, int include_shared,
+                           int32_t* count, int32_t* group_offset, int32_t* row_token,
+                           int32_t* slot_row, void* ws, hipStream_t st);
+hipError_t launch_permute_rows(const void* x, size_t elem_bytes, const int32_t* row_token,
+                               int64_t rows, int d, void* out, hipStream_t st);
+
+// quant.hip
+hipError_t launch_quant_1x128(const void* x, int in_is_f32, int64_t rows, int cols, uint8_t* q,
+                              float* scale, hipStream_t st);
+// Block-row br of the source lands in block-row br*row_mul + row_add of the destination.
+hipError_t launch_quant_128x128(const float* w, int64_t rows, int cols, uint8_t* q, float* scale,
+                                int row_mul, int row_add, hipStream_t st);
+
+// gemm.hip
+enum { EPI_STORE_F32 = 0, EPI_SWIGLU_F32 = 1, EPI_SWIGLU_QUANT = 2 };
+size_t gemm_ws_bytes(int G);
+hipError_t launch_grouped_gemm(const uint8_t* a_q, const float* a_s, const int32_t* a_rows,
+                               const int32_t* group_offset, int G, int64_t M_total,
+                               const uint8_t* b_q, const float* b_s, int N, int K, int epi,
+                               float* out, uint8_t* out_q, float* out_s, void* ws,
+                               hipStream_t st);
+
+// combine.hip
+hipError_t launch_combine(const uint16_t* u, const void* y, int y_is_f32, int64_t shared_row0,
+                          const float* gate, const int32_t* slot_row, int64_t T, int K, int d,
+                          float* out, hipStream_t st);
+hipError_t launch_bias_update(float* bias, const int32_t* count, int E, int64_t total,
+                              float gamma, hipStream_t st);
+
+}  // namespace moe

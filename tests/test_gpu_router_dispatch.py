@@ -1,0 +1,151 @@
+"""GPU parity: router (affinity, biased top-K, gates), dispatch, permute,
+bias update against the CPU oracle.  All of these are bit-exact: the router's
+scores follow the same binary32 FMA chain and sigmoid on both sides, and the
+dispatch is integer work."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sigmoid_top_routing_02_amd as moe
+import workloads
+from helpers import dev, np_, say, u16
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(T, d, E, seed, std_e=None, ties=False):
+    g = torch.Generator().manual_seed(seed)
+    u = torch.randn(T, d, generator=g).to(torch.bfloat16)
+    e = (torch.randn(E, d, generator=g) * (std_e if std_e else d ** -0.5)).to(torch.bfloat16)
+    if ties and E >= 4:
+        e[3] = e[1]            # identical centroids -> identical scores -> index tie-break
+    b = (torch.rand(E, generator=g) - 0.5) * 0.1
+    if ties and E >= 4:
+        b[3] = b[1]
+    return u, e, b
+
+
+ROUTER_CASES = [
+    # (T, d, E, K)
+    (128, 512, 16, 4),        # tiny workload shape
+    (37, 256, 16, 4),         # ragged T
+    (300, 1024, 256, 8),      # full expert count, ragged T
+    (1000, 384, 40, 6),       # E not a multiple of 64
+    (1, 128, 8, 8),           # one token, K = E
+    (4096, 512, 256, 8),      # the mid-size tile
+    (16384, 256, 256, 8),     # the large tile
+]
+
+
+@pytest.mark.parametrize("T,d,E,K", ROUTER_CASES)
+def test_router_bit_exact(T, d, E, K):
+    say(f"router T={T} d={d} E={E} K={K}")
+    u, e, b = _inputs(T, d, E, seed=T * 7 + E, ties=True)
+    idx, gate, s = moe.moe_router_topk(u.to(dev()), e.to(dev()), b.to(dev()), K)
+    torch.cuda.synchronize()
+    s_ref = oracle.router_scores(u16(u), u16(e))
+    np.testing.assert_array_equal(np_(s).view(np.uint32), s_ref.view(np.uint32))
+    idx_ref, gate_ref = oracle.topk_from_scores(s_ref, b.numpy(), K)
+    np.testing.assert_array_equal(np_(idx), idx_ref)
+    np.testing.assert_array_equal(np_(gate).view(np.uint32), gate_ref.view(np.uint32))
+
+
+def test_router_tiny_workload_and_determinism():
+    sh = workloads.SHAPES["tiny"]
+    u, e, b = workloads.activations(sh), workloads.centroids(sh), workloads.bias(sh)
+    say("router tiny workload x2")
+    r1 = moe.moe_router_topk(u.to(dev()), e.to(dev()), b.to(dev()), sh.K)
+    r2 = moe.moe_router_topk(u.to(dev()), e.to(dev()), b.to(dev()), sh.K)
+    torch.cuda.synchronize()
+    idx_ref, gate_ref, s_ref = oracle.router_topk(u16(u), u16(e), b.numpy(), sh.K)
+    for r in (r1, r2):
+        np.testing.assert_array_equal(np_(r[0]), idx_ref)
+        np.testing.assert_array_equal(np_(r[1]).view(np.uint32), gate_ref.view(np.uint32))
+
+
+def test_router_rdc_workload_slice():
+    """The router+dispatch+combine workload's shapes (d=7168, 256 experts,
+    top-8) on its first 512 tokens (the oracle's cost is per token)."""
+    sh = workloads.SHAPES["rdc"]
+    u = workloads.activations(sh)[:512].contiguous()
+    e, b = workloads.centroids(sh), workloads.bias(sh)
+    say("router rdc slice 512 tokens")
+    idx, gate, s = moe.moe_router_topk(u.to(dev()), e.to(dev()), b.to(dev()), sh.K)
+    torch.cuda.synchronize()
+    idx_ref, gate_ref, s_ref = oracle.router_topk(u16(u), u16(e), b.numpy(), sh.K)
+    np.testing.assert_array_equal(np_(s).view(np.uint32), s_ref.view(np.uint32))
+    np.testing.assert_array_equal(np_(idx), idx_ref)
+    np.testing.assert_array_equal(np_(gate).view(np.uint32), gate_ref.view(np.uint32))
+
+
+def _rand_idx(T, E, K, seed, skew=False):
+    rng = np.random.default_rng(seed)
+    p = None
+    if skew:
+        p = 1.0 / np.arange(1, E + 1) ** 1.1
+        p /= p.sum()
+    return np.stack([rng.choice(E, K, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+
+
+DISPATCH_CASES = [(1, 4, 2), (63, 16, 4), (64, 16, 4), (65, 16, 4), (1000, 256, 8), (4097, 256, 8),
+                  (300, 8, 8), (2000, 200, 16)]
+
+
+@pytest.mark.parametrize("T,E,K", DISPATCH_CASES)
+@pytest.mark.parametrize("shared", [True, False])
+def test_dispatch_bit_exact(T, E, K, shared):
+    say(f"dispatch T={T} E={E} K={K} shared={shared}")
+    idx = _rand_idx(T, E, K, seed=T + E, skew=(T % 2 == 0))
+    count, go, row_token, slot_row = moe.moe_dispatch(torch.from_numpy(idx).to(dev()), E, shared)
+    torch.cuda.synchronize()
+    c_ref, go_ref, rt_ref, sr_ref = oracle.dispatch(idx, E, shared)
+    np.testing.assert_array_equal(np_(count), c_ref)
+    np.testing.assert_array_equal(np_(go), go_ref)
+    np.testing.assert_array_equal(np_(row_token), rt_ref)
+    np.testing.assert_array_equal(np_(slot_row), sr_ref)
+
+
+def test_dispatch_all_tokens_one_expert():
+    """Degenerate routing: every token picks the same K experts."""
+    T, E, K = 777, 64, 4
+    idx = np.tile(np.array([5, 0, 63, 7], np.int32), (T, 1))
+    say("dispatch degenerate")
+    count, go, row_token, slot_row = moe.moe_dispatch(torch.from_numpy(idx).to(dev()), E, True)
+    torch.cuda.synchronize()
+    c_ref, go_ref, rt_ref, sr_ref = oracle.dispatch(idx, E, True)
+    np.testing.assert_array_equal(np_(count), c_ref)
+    np.testing.assert_array_equal(np_(row_token), rt_ref)
+    np.testing.assert_array_equal(np_(slot_row), sr_ref)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_permute_rows_and_unpermute(dtype):
+    T, E, K, d = 333, 32, 4, 384
+    idx = _rand_idx(T, E, K, seed=5)
+    x = torch.randn(T, d).to(dtype)
+    say(f"permute {dtype}")
+    count, go, row_token, slot_row = moe.moe_dispatch(torch.from_numpy(idx).to(dev()), E, False)
+    xp = moe.moe_permute_rows(x.to(dev()), row_token)
+    torch.cuda.synchronize()
+    _, _, rt_ref, sr_ref = oracle.dispatch(idx, E, False)
+    np.testing.assert_array_equal(np_(xp.view(torch.int16) if dtype == torch.bfloat16 else xp),
+                                  np_(x.view(torch.int16) if dtype == torch.bfloat16 else x)[rt_ref])
+    back = xp[slot_row.long()]            # [T, K, d]: every slot returns the token's own row
+    for k in range(K):
+        assert torch.equal(back[:, k].cpu(), x)
+
+
+def test_bias_update_bit_exact():
+    E, T, K = 256, 8192, 8
+    rng = np.random.default_rng(9)
+    count = rng.multinomial(T * K, np.ones(E) / E).astype(np.int32)
+    count[:4] = T * K // E          # exactly at the mean
+    b = rng.uniform(-0.05, 0.05, E).astype(np.float32)
+    say("bias update")
+    bd = torch.from_numpy(b).to(dev())
+    moe.moe_bias_update(bd, torch.from_numpy(count).to(dev()), T * K, 1e-3)
+    torch.cuda.synchronize()
+    ref = oracle.bias_update(b, count, T * K, 1e-3)
+    np.testing.assert_array_equal(np_(bd).view(np.uint32), ref.view(np.uint32))
+    np.testing.assert_array_equal(np_(bd)[:4], b[:4])

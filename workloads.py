@@ -18,11 +18,12 @@ learn.ifs.name, MoE-routing and FP8 paragraphs, and the nlp-lineage summary,
   dense     M=8192, N=7168, K in {4096, 16384}: block-scaled FP8 GEMM alone
 
 Seeding: every tensor gets its own 63-bit seed from
-numpy SeedSequence([BASE_SEED, workload_id, tensor_id, expert_id]) and is drawn
-with a ``torch.Generator`` of that seed.  Activations, centroids and biases are
-always drawn on the CPU (identical bytes on every machine).  Expert weights are
-drawn per expert on the device that will hold them; tests copy the FP32 masters
-of the experts they check back to the host for the oracle.
+numpy SeedSequence([BASE_SEED, workload_id, tensor_id, expert_id]).  On the CPU
+it is drawn with numpy's PCG64 generator of that seed (activations, centroids
+and biases are always drawn there: identical bytes on every machine); expert
+weights that live on the GPU are drawn per expert with a torch CUDA generator
+of the same seed, and tests copy the FP32 masters of the experts they check
+back to the host for the oracle.
 """
 from __future__ import annotations
 
@@ -81,10 +82,36 @@ def _gen(device, seed: int) -> torch.Generator:
     return g
 
 
+_CHUNK = 1 << 20
+
+
+def _cpu_normal(shape, seed: int) -> np.ndarray:
+    """Standard normals in fixed chunks of 2^20 values, chunk c drawn from
+    PCG64(SeedSequence([seed, c])); the chunks are filled by a thread pool, so
+    the bytes do not depend on the number of threads."""
+    from concurrent.futures import ThreadPoolExecutor
+    n = int(np.prod(shape))
+    out = np.empty(n, np.float32)
+    nchunk = (n + _CHUNK - 1) // _CHUNK
+
+    def fill(c):
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, c])))
+        lo, hi = c * _CHUNK, min(n, (c + 1) * _CHUNK)
+        rng.standard_normal(hi - lo, dtype=np.float32, out=out[lo:hi])
+
+    with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        list(ex.map(fill, range(nchunk)))
+    return out.reshape(shape)
+
+
 def normal(shape, std: float, seed: int, device="cpu") -> torch.Tensor:
-    """FP32 N(0, std^2) drawn with a generator of the given seed."""
-    g = _gen(device, seed)
-    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    """FP32 N(0, std^2) drawn from a generator of the given seed (numpy PCG64
+    on the CPU, torch's generator on a GPU)."""
+    if torch.device(device).type == "cpu":
+        x = torch.from_numpy(_cpu_normal(shape, seed))
+    else:
+        g = _gen(device, seed)
+        x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
     if std != 1.0:
         x.mul_(std)
     return x
@@ -92,13 +119,14 @@ def normal(shape, std: float, seed: int, device="cpu") -> torch.Tensor:
 
 def add_outliers(x: torch.Tensor, seed: int, frac: float = 1e-3, factor: float = 100.0) -> torch.Tensor:
     """Scale exactly round(frac * numel) entries, chosen uniformly without
-    replacement, by ``factor`` (in place, before any rounding to bf16)."""
+    replacement (numpy PCG64 of the given seed), by ``factor`` (in place,
+    before any rounding to bf16)."""
     n = x.numel()
     cnt = int(round(frac * n))
     if cnt == 0:
         return x
-    g = _gen(x.device, seed)
-    pos = torch.randperm(n, generator=g, device=x.device)[:cnt]
+    rng = np.random.Generator(np.random.PCG64(seed))
+    pos = torch.from_numpy(rng.choice(n, size=cnt, replace=False).astype(np.int64)).to(x.device)
     x.view(-1)[pos] *= factor
     return x
 
@@ -121,8 +149,8 @@ def centroids(shape: MoEShape, workload: str | None = None) -> torch.Tensor:
 def uniform_bias(shape: MoEShape, workload: str | None = None) -> torch.Tensor:
     """b: FP32 [E] on the CPU, U(-0.05, 0.05)."""
     wl = workload or shape.name
-    g = _gen("cpu", seed_for(wl, "bias"))
-    return (torch.rand(shape.E, generator=g, dtype=torch.float32) - 0.5) * 0.1
+    rng = np.random.Generator(np.random.PCG64(seed_for(wl, "bias")))
+    return torch.from_numpy((rng.random(shape.E, dtype=np.float32) - np.float32(0.5)) * np.float32(0.1))
 
 
 def load_prefill_bias() -> torch.Tensor:
@@ -164,8 +192,8 @@ def zipf_target_profile(E: int, s: float = 1.1, q: float = 31.334190744039795) -
 
 def rank_permutation(E: int, workload: str = "prefill") -> np.ndarray:
     """Seeded map rank -> expert index for the skewed load profile."""
-    g = _gen("cpu", seed_for(workload, "rank_perm"))
-    return torch.randperm(E, generator=g).numpy()
+    rng = np.random.Generator(np.random.PCG64(seed_for(workload, "rank_perm")))
+    return rng.permutation(E)
 
 
 def dense_operands(M: int, N: int, K: int, device="cpu"):
