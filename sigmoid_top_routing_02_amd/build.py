@@ -25,6 +25,7 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",
     "-Wno-unused-command-line-argument",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",   # MFMA results in VGPRs: the VALU consumes every slice
 ]
 
 

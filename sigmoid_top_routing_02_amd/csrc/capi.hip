@@ -170,7 +170,9 @@ int grouped_gemm_fp8_blockscaled(const uint8_t* a_q, const float* a_scale,
         REQUIRE(N > 0 && N % 128 == 0, MOE_ERR_SHAPE, "grouped_gemm: N=%d not a positive multiple of 128", N);
     else
         REQUIRE(N > 0 && N % 256 == 0, MOE_ERR_SHAPE, "grouped_gemm: SwiGLU needs N=%d a multiple of 256", N);
-    REQUIRE(M_total / 128 + G < 65535, MOE_ERR_UNSUPPORTED, "grouped_gemm: too many row tiles");
+    REQUIRE(((M_total + 127) / 128 + G) * ((N + 255) / 256) < ((int64_t)1 << 31), MOE_ERR_UNSUPPORTED,
+            "grouped_gemm: too many tiles");
+    REQUIRE((int64_t)N * K < ((int64_t)1 << 32), MOE_ERR_UNSUPPORTED, "grouped_gemm: one group's B exceeds 4 GiB");
     if (M_total == 0) return MOE_OK;
     REQUIRE_PTR(a_q);
     REQUIRE_PTR(a_scale);
@@ -339,7 +341,7 @@ int moe_layer_forward(const void* u_bf16, const void* centroids_bf16, const floa
     REQUIRE(I > 0 && I % 128 == 0, MOE_ERR_SHAPE, "moe_layer_forward: I=%d must be a multiple of 128", I);
     REQUIRE(E >= 1 && E <= 256, MOE_ERR_UNSUPPORTED, "moe_layer_forward: E=%d outside [1, 256]", E);
     REQUIRE(K >= 1 && K <= E && K <= 16, MOE_ERR_UNSUPPORTED, "moe_layer_forward: K=%d", K);
-    REQUIRE(T * (K + 1) < ((int64_t)1 << 31) && T * (K + 1) / 128 + E + 1 < 65535, MOE_ERR_UNSUPPORTED,
+    REQUIRE(T * (K + 1) < ((int64_t)1 << 31) && T * (int64_t)d < ((int64_t)1 << 32), MOE_ERR_UNSUPPORTED,
             "moe_layer_forward: T=%lld too large", (long long)T);
     if (T == 0) return MOE_OK;
     REQUIRE_PTR(u_bf16);

@@ -8,26 +8,30 @@
 // 128-wide slice, so every slice is one MFMA into a fresh FP32 accumulator and
 // the scaled sum over slices is an FP32 FMA chain on the VALU:
 //     acc = fma(P_j, a_scale[m,j] * b_scale[n/128,j], acc)
-// (FP8 tiling paragraph: A is scaled per 1x128 tile, B per 128x128 block.)
+// (FP8-tiling paragraph: A is scaled per 1x128 tile, B per 128x128 block.)
 //
-// Tiling (CDNA4): 256 threads = 4 wave64s in a 2x2 grid, block tile
-// 128 (M) x 256 (N), wave tile 64 x 128 = 4 x 8 MFMA tiles of 16x16, one
-// 128-byte K slice per stage.  A rows are gathered through a_row_index
-// (the dispatch permutation), so the activations are never materialised in
-// expert order.  Both operands go global -> LDS with global_load_lds_dwordx4
-// (no VGPR staging) into a 2-stage ring; LDS rows are 128 bytes with the
-// 16-byte chunk index XOR-swizzled by (row & 7) so the MFMA fragment reads are
-// bank-conflict free.  The A scales of the slice ride along as one more
-// LDS DMA (4 bytes per row); B scales are wave-uniform scalar loads.
+// Tiling (CDNA4): block tile 128 (M) x 256 (N), one 128-byte K slice per
+// pipeline stage, 8 wave64s in a 2 x 4 grid with a 64 x 64 wave tile (4 x 4
+// MFMA tiles of 16x16).  Two waves share each SIMD, so one wave's MFMAs run
+// while the other's VALU applies the slice scales: the MFMA -> scale-FMA
+// dependency of a single wave is hidden without extra registers.
 //
-// Grouping: a device-side tile map (exclusive scan of ceil(rows_g / 128))
-// turns blockIdx.y into (group, m-tile); the grid is sized from the host-known
-// total row count plus one partial tile per group, and surplus blocks exit.
+// Data movement: A rows are gathered through a_row_index (the dispatch
+// permutation), so activations are never materialised in expert order.  A, B
+// and the A scales of each slice go global -> LDS by buffer_load ... lds (no
+// VGPR staging) into a 3-stage ring; LDS rows are 128 bytes with the 16-byte
+// chunk c of row r in slot c ^ ((r >> 1) & 7), which keeps the fragment reads
+// bank-conflict free.  The B scales of the tile are staged in LDS once.
+//
+// Schedule: persistent, one block per CU, tiles walked XCD by XCD in groups
+// of GROUP_M row tiles (see the kernel).  Grouping: a device-side tile map
+// (exclusive scan of ceil(rows_g / 128)) turns a row-tile index into (group,
+// tile); the host only needs the total row count.
 //
 // Epilogues: FP32 store; SwiGLU (B rows interleaved gate/up per 128-row
 // block, so one N tile holds the gate and up columns of the same 128 h
 // columns); SwiGLU + 1x128 E4M3 re-quantisation of h, whose row maximum over
-// the 128 h columns of the tile is reduced across the two N-waves in LDS.
+// the tile's 128 h columns is reduced across the N-waves in LDS.
 #include "device_math.h"
 #include "kernels.h"
 
@@ -37,13 +41,22 @@ namespace {
 constexpr int BM = 128;
 constexpr int BN = 256;
 constexpr int BK = 128;                       // one scale slice
-constexpr int NT = 256;
+constexpr int WAVES_M = 2;
+constexpr int WAVES_N = 4;
+constexpr int NWAVES = WAVES_M * WAVES_N;
+constexpr int NT = 64 * NWAVES;
+constexpr int WN_COLS = BN / WAVES_N;         // 64 columns per wave
+constexpr int NI = WN_COLS / 16;              // MFMA column tiles per wave
+constexpr int MI = 4;                         // 64 rows per wave
+constexpr int GROUP_M = 8;                    // row tiles per L2-sharing group
 constexpr int A_BYTES = BM * BK;              // 16 KiB
 constexpr int B_BYTES = BN * BK;              // 32 KiB
-constexpr int SA_BYTES = BM * 4;              // 512 B
-constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES;
-constexpr int NSTAGE = 2;
-constexpr int LDS_BYTES = STAGE * NSTAGE;     // 99,328 B
+constexpr int A_DMA = A_BYTES / 1024 / NWAVES;  // 1 KiB DMA instructions per wave
+constexpr int B_DMA = B_BYTES / 1024 / NWAVES;
+constexpr int DMA_PER_STAGE = A_DMA + B_DMA + 1;  // + one A-scale DMA
+constexpr int MAX_SLICES = 128;               // K <= 16384
+static_assert(DMA_PER_STAGE == 7, "stage barrier below waits for vmcnt(7)");
+static_assert(B_DMA % 2 == 0, "B DMA offsets come in swizzle-parity pairs");
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -65,18 +78,73 @@ struct GemmArgs {
     float* out_s;
 };
 
-__device__ __forceinline__ void lds_dma16(const void* g, char* lds) {
-    __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
+// The three pipeline stages are separate LDS objects and every access names
+// its stage at compile time, so the compiler can see that reading one stage
+// does not alias the DMA still filling another (it would otherwise wait for
+// every outstanding DMA before each LDS read).
+__shared__ __attribute__((aligned(1024))) char g_a0[A_BYTES];
+__shared__ __attribute__((aligned(1024))) char g_a1[A_BYTES];
+__shared__ __attribute__((aligned(1024))) char g_a2[A_BYTES];
+__shared__ __attribute__((aligned(1024))) char g_b0[B_BYTES];
+__shared__ __attribute__((aligned(1024))) char g_b1[B_BYTES];
+__shared__ __attribute__((aligned(1024))) char g_b2[B_BYTES];
+// A scales of a slice: every wave DMAs 64 rows (wave & 1 picks the half) into
+// its own 256-byte copy, so all waves issue the same DMA count with no
+// lane-dependent branch; rows 0..127 are the copies of waves 0 and 1.
+__shared__ __attribute__((aligned(16))) float g_sa0[64 * NWAVES];
+__shared__ __attribute__((aligned(16))) float g_sa1[64 * NWAVES];
+__shared__ __attribute__((aligned(16))) float g_sa2[64 * NWAVES];
+__shared__ __attribute__((aligned(16))) float g_bscale[2 * MAX_SLICES];
+
+template <int ST>
+__device__ __forceinline__ char* a_buf() {
+    if constexpr (ST == 0) return g_a0;
+    else if constexpr (ST == 1) return g_a1;
+    else return g_a2;
 }
-__device__ __forceinline__ void lds_dma4(const void* g, char* lds) {
-    __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 4, 0, 0);
+template <int ST>
+__device__ __forceinline__ char* b_buf() {
+    if constexpr (ST == 0) return g_b0;
+    else if constexpr (ST == 1) return g_b1;
+    else return g_b2;
+}
+template <int ST>
+__device__ __forceinline__ float* sa_buf() {
+    if constexpr (ST == 0) return g_sa0;
+    else if constexpr (ST == 1) return g_sa1;
+    else return g_sa2;
 }
 
-// 32 K-bytes of row r for lanes of k-block kb (= lane / 16) from a swizzled tile.
-__device__ __forceinline__ v8i frag(const char* tile, int r, int kb) {
-    const int sw = r & 7;
-    const uint4 x = *reinterpret_cast<const uint4*>(tile + r * 128 + (((2 * kb) ^ sw) << 4));
-    const uint4 y = *reinterpret_cast<const uint4*>(tile + r * 128 + (((2 * kb + 1) ^ sw) << 4));
+template <int V>
+struct IC { static constexpr int value = V; };
+
+// Buffer resource (gfx9 family descriptor word 3); out-of-range offsets read 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+// global -> LDS DMA: lane l's `size` bytes land at lds + l*size (lds is wave-uniform).
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, char* lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, char* lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, voff, soff, 0, 0);
+}
+
+// LDS tiles hold 128-byte rows; the 16-byte chunk c of row r sits in slot
+// c ^ ((r >> 1) & 7).  A 16-lane group of a fragment read covers 16
+// consecutive rows: rows of equal parity land 32 banks apart and the swizzle
+// spreads the 8 rows of each parity over 8 distinct 4-bank groups, so the
+// reads are conflict free on the 64-bank LDS.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+
+// 32 K-bytes of one MFMA fragment from a swizzled tile.  off0/off1 are the
+// lane's byte offsets of its two 16-byte chunks inside a 16-row band
+// (row lane%16, chunks 2*kb and 2*kb+1 swizzled); every band starts at a
+// multiple of 16 rows, so the swizzle (a function of r mod 16) never changes
+// between bands and `band` is a compile-time byte offset.
+__device__ __forceinline__ v8i frag(const char* tile, int band, uint32_t off0, uint32_t off1) {
+    const uint4 x = *reinterpret_cast<const uint4*>(tile + band + off0);
+    const uint4 y = *reinterpret_cast<const uint4*>(tile + band + off1);
     v8i f;
     f[0] = (int)x.x; f[1] = (int)x.y; f[2] = (int)x.z; f[3] = (int)x.w;
     f[4] = (int)y.x; f[5] = (int)y.y; f[6] = (int)y.z; f[7] = (int)y.w;
@@ -86,23 +154,53 @@ __device__ __forceinline__ v8i frag(const char* tile, int r, int kb) {
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
 // Column offset (inside the 256-wide N tile) of MFMA column-tile ni of wave wn.
+// SwiGLU waves take WN_COLS/2 gate columns and the matching up columns.
 template <int EPI>
 __device__ __forceinline__ int ncol(int wn, int ni) {
     if constexpr (EPI == EPI_STORE_F32) {
-        return wn * 128 + ni * 16;
+        return wn * WN_COLS + ni * 16;
     } else {
-        return (ni < 4) ? (wn * 64 + ni * 16) : (128 + wn * 64 + (ni - 4) * 16);
+        constexpr int HALF = NI / 2;
+        return (ni < HALF) ? (wn * (WN_COLS / 2) + ni * 16)
+                           : (128 + wn * (WN_COLS / 2) + (ni - HALF) * 16);
     }
 }
 
 template <int EPI>
 __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
-    __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
+    char* const smem = g_b0;       // epilogue scratch (after the K loop)
+    const int K = p.K;
+    const int ns = K / BK;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    const int kb = lane >> 4;
+    const int lr = lane & 15;
 
-    // ---- which tile is this block?
-    const int mt_lin = blockIdx.y;
+    // ---- persistent schedule.  Workgroups go to the 8 XCDs round-robin
+    // (block b runs on XCD b % 8) and the grid holds one block per CU.  Each
+    // XCD owns one contiguous share of the tile sequence, ordered in groups of
+    // GROUP_M row tiles x all column tiles (row tile fastest), and its blocks
+    // take consecutive tiles of that share round by round, so the blocks of an
+    // XCD work on neighbouring tiles at the same time and share A and B
+    // slices in the XCD's L2.
     const int total_tiles = p.tile_start[p.G];
-    if (mt_lin >= total_tiles) return;
+    const int n_tiles = (p.N + BN - 1) / BN;
+    const int xcd = blockIdx.x & 7;
+    const int slot = blockIdx.x >> 3;
+    const int xcd_blocks = gridDim.x >> 3;
+    const int total = total_tiles * n_tiles;
+    const int share = (total + 7) >> 3;
+    for (int tl = slot; tl < share; tl += xcd_blocks) {
+    const int t = xcd * share + tl;
+    if (t >= total) break;
+    const int grp = t / (GROUP_M * n_tiles);
+    const int first_m = grp * GROUP_M;
+    const int gm = min(GROUP_M, total_tiles - first_m);
+    const int t_in = t - grp * GROUP_M * n_tiles;
+    const int mt_lin = first_m + t_in % gm;
+    const int n_tile = t_in / gm;
     int lo = 0, hi = p.G - 1;                 // largest g with tile_start[g] <= mt_lin
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -111,99 +209,121 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
     const int g = lo;
     const int m0 = p.group_offset[g] + (mt_lin - p.tile_start[g]) * BM;
     const int rows = min(BM, p.group_offset[g + 1] - m0);
-    const int n0 = blockIdx.x * BN;
-    const int K = p.K;
-    const int ns = K / BK;
+    const int n0 = n_tile * BN;
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-
-    // ---- per-lane global sources for the LDS DMA (loop-invariant)
-    const uint8_t* a_src[4];
+    // ---- per-lane DMA sources (loop-invariant byte offsets; the slice moves soffset)
+    const auto a_rsrc = make_rsrc(p.a_q, 0xFFFFFFFFu);
+    uint32_t a_off[A_DMA];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = (wave * 4 + i) * 8 + (lane >> 3);
-        const int c = (lane & 7) ^ (r & 7);
+    for (int i = 0; i < A_DMA; ++i) {
+        const int r = (wave * A_DMA + i) * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ swz(r);
         const int m = m0 + min(r, rows - 1);
-        const int64_t am = p.a_rows ? (int64_t)p.a_rows[m] : (int64_t)m;
-        a_src[i] = p.a_q + am * K + c * 16;
+        const uint32_t am = p.a_rows ? (uint32_t)p.a_rows[m] : (uint32_t)m;
+        a_off[i] = am * (uint32_t)K + c * 16;
     }
-    const uint8_t* b_src[8];
-    const uint8_t* bgrp = p.b_q + (int64_t)g * p.N * K;
+    const auto b_rsrc = make_rsrc(p.b_q + (int64_t)g * p.N * K, (uint32_t)p.N * (uint32_t)K);
+    // B rows of DMA i are r0 + 8i; the swizzle of r0 + 8i only depends on i & 1
+    uint32_t b_off[2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int r = (wave * 8 + i) * 8 + (lane >> 3);
-        const int c = (lane & 7) ^ (r & 7);
-        const int n = min(n0 + r, p.N - 1);
-        b_src[i] = bgrp + (int64_t)n * K + c * 16;
+    for (int par = 0; par < 2; ++par) {
+        const int r = (wave * B_DMA + par) * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ swz(r);
+        b_off[par] = (uint32_t)(n0 + r) * (uint32_t)K + c * 16;   // rows past N read as 0
     }
-    const float* sa_src[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int r = i * 64 + lane;
+    const auto sa_rsrc = make_rsrc(p.a_s, 0xFFFFFFFFu);
+    uint32_t sa_off;
+    {
+        const int r = (wave & 1) * 64 + lane;
         const int m = m0 + min(r, rows - 1);
-        const int64_t am = p.a_rows ? (int64_t)p.a_rows[m] : (int64_t)m;
-        sa_src[i] = p.a_s + am * ns;
+        const uint32_t am = p.a_rows ? (uint32_t)p.a_rows[m] : (uint32_t)m;
+        sa_off = am * (uint32_t)ns * 4u;
     }
 
-    auto issue = [&](int slice, int stage) {
-        char* base = smem + stage * STAGE;
-        const int koff = slice * BK;
+    // A descriptor with no records: every access is out of range, so no memory
+    // is touched (the target stage is a spare one).  Past the last slice the
+    // pipeline still issues its DMAs through this descriptor, which keeps the
+    // instruction stream (and the compiler's wait-count model) identical on
+    // every step: no step needs a conservative full drain.
+    const auto null_rsrc = make_rsrc(p.a_q, 0u);
+    auto issue = [&](auto stc, int slice) {
+        constexpr int ST = decltype(stc)::value;
+        const bool live = slice < ns;
+        const uint32_t koff = live ? (uint32_t)slice * BK : 0u;
+        const auto ar = live ? a_rsrc : null_rsrc;
+        const auto br = live ? b_rsrc : null_rsrc;
+        const auto sr = live ? sa_rsrc : null_rsrc;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) lds_dma16(a_src[i] + koff, base + (wave * 4 + i) * 1024);
+        for (int i = 0; i < A_DMA; ++i)
+            lds_dma16(ar, a_off[i], koff, a_buf<ST>() + (wave * A_DMA + i) * 1024);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            lds_dma16(b_src[i] + koff, base + A_BYTES + (wave * 8 + i) * 1024);
-        if (wave == 0) {
-#pragma unroll
-            for (int i = 0; i < 2; ++i) lds_dma4(sa_src[i] + slice, base + A_BYTES + B_BYTES + i * 256);
-        }
+        for (int i = 0; i < B_DMA; ++i)
+            lds_dma16(br, b_off[i & 1] + (uint32_t)((i & ~1) * 8) * (uint32_t)K, koff,
+                      b_buf<ST>() + (wave * B_DMA + i) * 1024);
+        lds_dma4(sr, sa_off, live ? (uint32_t)slice * 4u : 0u,
+                 reinterpret_cast<char*>(sa_buf<ST>()) + wave * 256);
     };
 
-    // ---- B scales: wave-uniform rows of b_scale for this wave's columns
+    // ---- B scales of the tile's two 128-row blocks, all slices, into LDS once
     const int nblk_per_g = p.N / 128;
     const float* bs_g = p.b_s + (int64_t)g * nblk_per_g * ns;
-    int bblk0, bblk1;
+    float* sbs = g_bscale;                                              // [2][MAX_SLICES]
+    for (int i = tid; i < 2 * ns; i += NT) {
+        const int blk = min(n0 / 128 + i / ns, nblk_per_g - 1);
+        sbs[(i / ns) * MAX_SLICES + (i % ns)] = bs_g[(int64_t)blk * ns + (i % ns)];
+    }
+    int sbrow0, sbrow1;   // which of the two blocks scales this wave's column tiles
     if constexpr (EPI == EPI_STORE_F32) {
-        bblk0 = min((n0 + wn * 128) / 128, nblk_per_g - 1);
-        bblk1 = bblk0;
+        sbrow0 = (wn * WN_COLS) / 128;
+        sbrow1 = sbrow0;
     } else {
-        bblk0 = n0 / 128;
-        bblk1 = n0 / 128 + 1;
+        sbrow0 = 0;
+        sbrow1 = 1;
     }
 
-    v4f acc[4][8];
+    v4f acc[MI][NI];
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 8; ++ni) acc[mi][ni] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    const int kb = lane >> 4;
-    const int lr = lane & 15;
+    // lane offsets of the fragment chunks; the wave's row/column base is folded in
+    const uint32_t sw0 = (uint32_t)(((2 * kb) ^ swz(lr)) << 4);
+    const uint32_t sw1 = (uint32_t)(((2 * kb + 1) ^ swz(lr)) << 4);
+    const uint32_t a_lo0 = (uint32_t)(wm * 64 + lr) * 128 + sw0;
+    const uint32_t a_lo1 = (uint32_t)(wm * 64 + lr) * 128 + sw1;
+    const uint32_t bcol = (uint32_t)(ncol<EPI>(wn, 0) - ncol<EPI>(0, 0) + lr);
+    const uint32_t b_lo0 = bcol * 128 + sw0;
+    const uint32_t b_lo1 = bcol * 128 + sw1;
+    const int sa_lane = wm * 64 + kb * 4;
 
-    issue(0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    // Stage barriers: wait for this wave's DMA of the next slice (the one after
+    // may stay in flight) and for its own LDS reads, then s_barrier.  A plain
+    // __syncthreads() would also drain every outstanding DMA (vmcnt(0)) and
+    // serialise the pipeline.  The "memory" clobber keeps the compiler from
+    // moving LDS accesses across it.
+#define MOE_STAGE_BARRIER(N) asm volatile("s_waitcnt vmcnt(" #N ") lgkmcnt(0)\n\ts_barrier" ::: "memory")
+    issue(IC<0>{}, 0);
+    issue(IC<1>{}, 1);
+    MOE_STAGE_BARRIER(7);      // slice 0 landed; also publishes the B scales
 
-    for (int s = 0; s < ns; ++s) {
-        const int stage = s & 1;
-        if (s + 1 < ns) issue(s + 1, stage ^ 1);
-        const char* At = smem + stage * STAGE;
-        const char* Bt = At + A_BYTES;
-        const float* SAt = reinterpret_cast<const float*>(At + A_BYTES + B_BYTES);
+    // one K slice on stage ST; the DMA for slice s+2 goes to stage (ST+2)%3
+    auto slice_step = [&](auto stc, int s) {
+        constexpr int ST = decltype(stc)::value;
+        issue(IC<(ST + 2) % 3>{}, s + 2);
+        const char* At = a_buf<ST>();
+        const char* Bt = b_buf<ST>();
+        const float* SAt = sa_buf<ST>();
 
-        const float sb0 = bs_g[(int64_t)bblk0 * ns + s];
-        const float sb1 = bs_g[(int64_t)bblk1 * ns + s];
+        const float sb0 = sbs[sbrow0 * MAX_SLICES + s];
+        const float sb1 = sbs[sbrow1 * MAX_SLICES + s];
 
-        v8i af[4];
-        float c0[4][4], c1[4][4];
+        v8i af[MI];
+        float c0[MI][4], c1[MI][4];
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-            const int r = wm * 64 + mi * 16;
-            af[mi] = frag(At, r + lr, kb);
-            const float4 sa = *reinterpret_cast<const float4*>(SAt + r + kb * 4);
+        for (int mi = 0; mi < MI; ++mi) {
+            af[mi] = frag(At, mi * 16 * 128, a_lo0, a_lo1);
+            const float4 sa = *reinterpret_cast<const float4*>(SAt + sa_lane + mi * 16);
             const float sv[4] = {sa.x, sa.y, sa.z, sa.w};
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -211,71 +331,101 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
                 c1[mi][j] = sv[j] * sb1;
             }
         }
+        // Software pipeline over the column tiles: the MFMAs of tile ni are
+        // issued before the scale FMAs of tile ni-1 consume their partials, and
+        // the B fragment of tile ni+1 is read from LDS meanwhile, so a wave
+        // always has independent MFMA, VALU and LDS work in flight.
+        auto scale_into = [&](const v4f (&part)[MI], int ni) {
+            const bool second = (EPI != EPI_STORE_F32) && ni >= NI / 2;
 #pragma unroll
-        for (int ni = 0; ni < 8; ++ni) {
-            const v8i bf = frag(Bt, ncol<EPI>(wn, ni) + lr, kb);
-            const bool second = (EPI != EPI_STORE_F32) && ni >= 4;
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi) {
-                const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    af[mi], bf, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+            for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    acc[mi][ni][j] = __builtin_fmaf(part[j], second ? c1[mi][j] : c0[mi][j],
+                    acc[mi][ni][j] = __builtin_fmaf(part[mi][j], second ? c1[mi][j] : c0[mi][j],
                                                     acc[mi][ni][j]);
-            }
+        };
+        v8i bnext = frag(Bt, ncol<EPI>(0, 0) * 128, b_lo0, b_lo1);
+        v4f prev[MI];
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+            const v8i bf = bnext;
+            if (ni + 1 < NI) bnext = frag(Bt, ncol<EPI>(0, ni + 1) * 128, b_lo0, b_lo1);
+            v4f cur[MI];
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi)
+                cur[mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    af[mi], bf, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+            if (ni > 0) scale_into(prev, ni - 1);
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi) prev[mi] = cur[mi];
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
+        scale_into(prev, NI - 1);
+        // slice s+1 must have landed (slice s+2 may still be in flight)
+        MOE_STAGE_BARRIER(7);
+    };
+
+    // whole rounds of three stages, then the remaining one or two slices
+    int s = 0;
+    for (; s + 3 <= ns; s += 3) {
+        slice_step(IC<0>{}, s);
+        slice_step(IC<1>{}, s + 1);
+        slice_step(IC<2>{}, s + 2);
     }
+    if (s < ns) slice_step(IC<0>{}, s);
+    if (s + 1 < ns) slice_step(IC<1>{}, s + 1);
+    MOE_STAGE_BARRIER(0);      // drain the spare-stage DMAs before LDS is reused
+#undef MOE_STAGE_BARRIER
 
     // ---- epilogues.  Lane holds C[row = base + 4*kb + j][col = base + lr].
     if constexpr (EPI == EPI_STORE_F32) {
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
+        for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = wm * 64 + mi * 16 + kb * 4 + j;
                 if (r >= rows) continue;
                 float* orow = p.out + (int64_t)(m0 + r) * p.N;
 #pragma unroll
-                for (int ni = 0; ni < 8; ++ni) {
+                for (int ni = 0; ni < NI; ++ni) {
                     const int n = n0 + ncol<EPI>(wn, ni) + lr;
                     if (n < p.N) orow[n] = acc[mi][ni][j];
                 }
             }
     } else {
+        constexpr int HALF = NI / 2;
+        constexpr int HC = WN_COLS / 2;    // h columns per wave
         const int I = p.N / 2;
         const int h0 = n0 / 2;             // first h column of this tile
-        float h[4][4][4];
+        float h[MI][HALF][4];
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
+        for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
+            for (int ni = 0; ni < HALF; ++ni)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) h[mi][ni][j] = silu(acc[mi][ni][j]) * acc[mi][ni + 4][j];
+                for (int j = 0; j < 4; ++j)
+                    h[mi][ni][j] = silu(acc[mi][ni][j]) * acc[mi][ni + HALF][j];
         if constexpr (EPI == EPI_SWIGLU_F32) {
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
+            for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int r = wm * 64 + mi * 16 + kb * 4 + j;
                     if (r >= rows) continue;
-                    float* orow = p.out + (int64_t)(m0 + r) * I + h0 + wn * 64;
+                    float* orow = p.out + (int64_t)(m0 + r) * I + h0 + wn * HC;
 #pragma unroll
-                    for (int ni = 0; ni < 4; ++ni) orow[ni * 16 + lr] = h[mi][ni][j];
+                    for (int ni = 0; ni < HALF; ++ni) orow[ni * 16 + lr] = h[mi][ni][j];
                 }
         } else {
-            // row maximum over this wave's 64 h columns, then across wn in LDS
-            float* amax_s = reinterpret_cast<float*>(smem);           // [2][128]
-            char* qtile = smem + 1024;                                  // [128][128] codes
+            // row maximum over this wave's HC h columns, then across the N-waves in LDS
+            float* amax_s = reinterpret_cast<float*>(smem);           // [WAVES_N][128]
+            char* qtile = smem + 4096;                                  // [128][128] codes
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
+            for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     float m = 0.0f;
 #pragma unroll
-                    for (int ni = 0; ni < 4; ++ni) {
+                    for (int ni = 0; ni < HALF; ++ni) {
                         const float a = __builtin_fabsf(h[mi][ni][j]);
                         m = a > m ? a : m;
                     }
@@ -288,25 +438,28 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
                 }
             __syncthreads();
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
+            for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int r = wm * 64 + mi * 16 + kb * 4 + j;
-                    const float a0 = amax_s[r], a1 = amax_s[128 + r];
-                    const float amax = a1 > a0 ? a1 : a0;
+                    float amax = amax_s[r];
+#pragma unroll
+                    for (int w = 1; w < WAVES_N; ++w) {
+                        const float a = amax_s[w * 128 + r];
+                        amax = a > amax ? a : amax;
+                    }
                     float inv, sc;
                     tile_scale(amax, inv, sc);
 #pragma unroll
-                    for (int ni = 0; ni < 4; ++ni)
-                        qtile[r * 128 + wn * 64 + ni * 16 + lr] =
-                            (char)e4m3_encode(h[mi][ni][j] * inv);
+                    for (int ni = 0; ni < HALF; ++ni)
+                        qtile[r * 128 + wn * HC + ni * 16 + lr] = (char)e4m3_encode(h[mi][ni][j] * inv);
                     if (wn == 0 && lr == 0 && r < rows)
                         p.out_s[(int64_t)(m0 + r) * (I / 128) + h0 / 128] = sc;
                 }
             __syncthreads();
             // 128 rows x 128 bytes, 16-byte stores
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < (BM * 128 / 16) / NT; ++i) {
                 const int c = tid + i * NT;
                 const int r = c >> 3, part = c & 7;
                 if (r < rows)
@@ -315,18 +468,20 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
             }
             if (p.out) {
 #pragma unroll
-                for (int mi = 0; mi < 4; ++mi)
+                for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int r = wm * 64 + mi * 16 + kb * 4 + j;
                         if (r >= rows) continue;
-                        float* orow = p.out + (int64_t)(m0 + r) * I + h0 + wn * 64;
+                        float* orow = p.out + (int64_t)(m0 + r) * I + h0 + wn * HC;
 #pragma unroll
-                        for (int ni = 0; ni < 4; ++ni) orow[ni * 16 + lr] = h[mi][ni][j];
+                        for (int ni = 0; ni < HALF; ++ni) orow[ni * 16 + lr] = h[mi][ni][j];
                     }
             }
         }
     }
+    __syncthreads();   // the next tile's DMAs overwrite the stages and the scratch
+    }  // persistent tile loop
 }
 
 // tile_start[g] = sum_{g' < g} ceil(rows_g' / BM), for g = 0..G.
@@ -355,6 +510,18 @@ __global__ __launch_bounds__(256) void gemm_tile_map_kernel(const int32_t* __res
     if (threadIdx.x == 0) ts[G] = carry;
 }
 
+int cu_count_for_current_device() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        cached[dev] = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) ==
+                           hipSuccess && n > 0) ? n : 256;
+    }
+    return cached[dev];
+}
+
 }  // namespace
 
 size_t gemm_ws_bytes(int G) { return (size_t)(G + 1) * sizeof(int32_t); }
@@ -368,7 +535,11 @@ hipError_t launch_grouped_gemm(const uint8_t* a_q, const float* a_s, const int32
     hipLaunchKernelGGL(gemm_tile_map_kernel, dim3(1), dim3(256), 0, st, group_offset, G, ts);
     GemmArgs p{a_q, a_s, a_rows, group_offset, ts, G, b_q, b_s, N, K, out, out_q, out_s};
     const int64_t mt_bound = (M_total + BM - 1) / BM + G;
-    dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)mt_bound);
+    const int64_t blocks = mt_bound * ((N + BN - 1) / BN);
+    // one block per CU (its ~150 KB of LDS admit one), a multiple of the 8 XCDs
+    const int64_t persistent = ((int64_t)cu_count_for_current_device() + 7) / 8 * 8;
+    const int64_t needed = (blocks + 7) / 8 * 8;
+    dim3 grid((unsigned)(needed < persistent ? needed : persistent));
     switch (epi) {
         case EPI_STORE_F32:
             hipLaunchKernelGGL(grouped_gemm_kernel<EPI_STORE_F32>, grid, dim3(NT), 0, st, p);
