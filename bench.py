@@ -168,7 +168,7 @@ def gemm1_bytes(sh, count):
 
 
 # ----------------------------------------------------------------------------- CPU baseline
-def cpu_baseline_layer(sh, st, budget_s=12.0):
+def cpu_baseline_layer(sh, st, budget_s=15.0):
     """The oracle (untuned) timed on a bounded sample of the same batch:
     router for a token slice, then the FFNs (GEMM1 + SwiGLU + h quant + GEMM2)
     of a few experts' rows with weights the oracle quantised beforehand
@@ -177,7 +177,7 @@ def cpu_baseline_layer(sh, st, budget_s=12.0):
     import oracle
     oracle.lib()
     T, d, E, K, I = sh.T, sh.d, sh.E, sh.K, sh.I
-    nt = min(T, 512 if T >= 512 else T)
+    nt = min(T, 4096)
     u_h = st["u"][:nt].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
     e_h = st["e"].view(torch.int16).cpu().numpy().view(np.uint16)
     b_h = st["b"].cpu().numpy()
@@ -188,7 +188,7 @@ def cpu_baseline_layer(sh, st, budget_s=12.0):
     uq, us = oracle.quant_1x128(uf)
     t_route = time.perf_counter() - t0
     # FFN rows of a few experts (the shared expert and the busiest routed ones in the slice)
-    groups = [E] + [int(g) for g in np.argsort(-count)[:3]]
+    groups = [E] + [int(g) for g in np.argsort(-count)[:7]]
     wq = {}
     for g in groups:
         w1, w3, w2 = (w.cpu().numpy() for w in workloads.expert_weights(sh, g, device="cuda"))
@@ -197,7 +197,7 @@ def cpu_baseline_layer(sh, st, budget_s=12.0):
     y_rows = {}
     for g in groups:
         r0, r1 = int(go[g]), int(go[g + 1])
-        rows = np.arange(r0, min(r1, r0 + 64))
+        rows = np.arange(r0, min(r1, r0 + 256))
         (q1, s1), (q3, s3), (q2, s2) = wq[g]
         t1 = time.perf_counter()
         zg = oracle.gemm_blockscaled(uq, us, q1, s1, a_rows=rt[rows])
@@ -218,7 +218,7 @@ def cpu_baseline_layer(sh, st, budget_s=12.0):
     t_comb = time.perf_counter() - t2
     per_token = (t_route + t_comb) / nt + (K + 1) * t_ffn / rows_done
     return {
-        "value": 1.0 / per_token, "unit": "tokens/s", "cores": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)),
+        "value": round(1.0 / per_token, 2), "unit": "tokens/s", "cores": _cores(),
         "kind": "oracle",
         "sample": f"router+dispatch+quant+combine+bias on the first {nt} tokens ({t_route + t_comb:.1f}s); "
                   f"FFN on {rows_done} rows of experts {groups} ({t_ffn:.1f}s); per-token cost = "
@@ -286,6 +286,110 @@ def run_layer(sh, steps, warmup, with_cpu):
     return res
 
 
+def run_rdc(steps, warmup, with_cpu):
+    """Router + dispatch + permute + combine with identity experts (Y = the
+    permuted bf16 rows, no shared expert) + bias update, T=8192, d=7168,
+    256 experts top-8: the bandwidth-bound part of the layer."""
+    sh = workloads.SHAPES["rdc"]
+    T, d, E, K = sh.T, sh.d, sh.E, sh.K
+    log(f"[bench] setup rdc: T={T} d={d} E={E} K={K}")
+    u = workloads.activations(sh).cuda()
+    e = workloads.centroids(sh).cuda()
+    b = workloads.bias(sh).cuda()
+    st = dict(scores=torch.empty(T, E, device="cuda"), idx=torch.empty(T, K, dtype=torch.int32, device="cuda"),
+              gate=torch.empty(T, K, device="cuda"), xp=torch.empty(T * K, d, dtype=torch.bfloat16, device="cuda"),
+              out=torch.empty(T, d, device="cuda"), b_next=torch.empty_like(b),
+              dws=torch.empty(max(moe.moe_dispatch_workspace_bytes(T, E), 256), dtype=torch.uint8, device="cuda"))
+
+    def step(ev=None):
+        m = [ev.mark("s")] if ev else None
+        moe.moe_router_topk(u, e, b, K, st["scores"], st["idx"], st["gate"])
+        if ev: m.append(ev.mark("router"))
+        count, go, row_token, slot_row = moe.moe_dispatch(st["idx"], E, False, ws=st["dws"])
+        if ev: m.append(ev.mark("dispatch"))
+        moe.moe_permute_rows(u, row_token, out=st["xp"])
+        if ev: m.append(ev.mark("permute"))
+        moe.moe_combine(u, st["xp"], st["gate"], slot_row, shared_row0=-1, out=st["out"])
+        if ev: m.append(ev.mark("combine"))
+        st["b_next"].copy_(b)
+        moe.moe_bias_update(st["b_next"], count, T * K, sh.gamma)
+        if ev:
+            m.append(ev.mark("bias"))
+            for i, n in enumerate(["router", "dispatch", "permute", "combine", "bias_update"]):
+                ev.add(n, m[i], m[i + 1])
+
+    for _ in range(warmup):
+        step()
+    ev = Events()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(ev)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    stages = {n: round(ev.avg_ms(n), 4) for n in ev.pairs}
+    # algorithmic bytes of the combine: K bf16 rows of X_perm + u read, FP32 h' written, gates and slots
+    comb_bytes = T * K * d * 2 + T * d * 2 + T * d * 4 + T * K * 8
+    comb_ms = ev.avg_ms("combine")
+    ach = comb_bytes / (comb_ms * 1e-3) / 1e9
+    perm_bytes = T * K * d * 2 * 2 + T * K * 4
+    res = {
+        "metric": "router+dispatch+combine tokens/s (d=7168, 256E top-8) + % of HBM roofline",
+        "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 in, fp32 router/combine", "data": "synthetic (seeded)",
+        "config": {"workload": "router_dispatch_combine", "T": T, "d": d, "routed_experts": E, "top_k": K,
+                   "parallelism": "single GPU"},
+        "roofline": {"kernel": "moe_combine", "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                     "traffic": traffic_for("combine_rdc", "combine.hip"),
+                     "algorithmic_per_launch": comb_bytes, "avg_launch_ms": round(comb_ms, 4)},
+        "stages_ms": stages,
+        "permute_gbs": round(perm_bytes / (ev.avg_ms("permute") * 1e-3) / 1e9, 1),
+        "router_tflops": round(2.0 * T * E * d / (ev.avg_ms("router") * 1e-3) / 1e12, 2),
+    }
+    if with_cpu:
+        import oracle
+        oracle.lib()
+        nt = 2048
+        u_h = u[:nt].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        e_h = e.view(torch.int16).cpu().numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        idx, gate, s = oracle.router_topk(u_h, e_h, b.cpu().numpy(), K)
+        cnt, go, rt, sr = oracle.dispatch(idx, E, False)
+        uf = (u_h.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        y = uf[rt]
+        oracle.combine(u_h, y, -1, gate, sr)
+        oracle.bias_update(b.cpu().numpy(), cnt, nt * K, sh.gamma)
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(nt / dt, 1), "unit": "tokens/s", "cores": _cores(), "kind": "oracle",
+                               "sample": f"the whole rdc pass on the first {nt} tokens ({dt:.1f}s)"}
+    return res
+
+
+COPY_ROWS, COPY_D = 32768, 65536     # 32768 rows x 65536 bf16 = 4 GiB
+
+
+def copy_calibration():
+    """A plain copy kernel of known size: 4 GiB read, 4 GiB written.  The
+    source is 16x the 256 MB Infinity Cache, so nearly all of it comes from
+    HBM."""
+    src = torch.ones(COPY_ROWS, COPY_D, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    ident = torch.arange(COPY_ROWS, dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        moe.moe_permute_rows(src, ident, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def _cores():
+    try:
+        return len(os.sched_getaffinity(0)) if not os.environ.get("OMP_NUM_THREADS") else int(os.environ["OMP_NUM_THREADS"])
+    except Exception:
+        return os.cpu_count() or 1
+
+
 def run_dense(steps, warmup, K=4096):
     M, N = workloads.DENSE["M"], workloads.DENSE["N"]
     log(f"[bench] dense GEMM M={M} N={N} K={K}")
@@ -327,8 +431,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="prefill", choices=["prefill", "decode", "tiny", "dense", "dense16k"])
+    ap.add_argument("--workload", default="prefill",
+                    choices=["prefill", "decode", "tiny", "rdc", "dense", "dense16k"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--with-copy", action="store_true",
+                    help="first run a plain 4 GiB copy kernel (moe_permute_rows with the identity "
+                         "permutation) so a counter profile can calibrate FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this layer forward is a single-GPU path "
@@ -338,7 +446,11 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     moe.load_library()
-    if args.workload in ("dense", "dense16k"):
+    if args.with_copy:
+        copy_calibration()
+    if args.workload == "rdc":
+        res = run_rdc(args.steps, args.warmup, with_cpu=not args.no_cpu_baseline)
+    elif args.workload in ("dense", "dense16k"):
         res = run_dense(args.steps, args.warmup, K=4096 if args.workload == "dense" else 16384)
     else:
         res = run_layer(workloads.SHAPES[args.workload], args.steps, args.warmup,

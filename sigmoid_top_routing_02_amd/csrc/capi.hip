@@ -170,7 +170,7 @@ int grouped_gemm_fp8_blockscaled(const uint8_t* a_q, const float* a_scale,
         REQUIRE(N > 0 && N % 128 == 0, MOE_ERR_SHAPE, "grouped_gemm: N=%d not a positive multiple of 128", N);
     else
         REQUIRE(N > 0 && N % 256 == 0, MOE_ERR_SHAPE, "grouped_gemm: SwiGLU needs N=%d a multiple of 256", N);
-    REQUIRE(((M_total + 127) / 128 + G) * ((N + 255) / 256) < ((int64_t)1 << 31), MOE_ERR_UNSUPPORTED,
+    REQUIRE(((M_total + 31) / 32 + G) * ((N + 255) / 256) < ((int64_t)1 << 31), MOE_ERR_UNSUPPORTED,
             "grouped_gemm: too many tiles");
     REQUIRE((int64_t)N * K < ((int64_t)1 << 32), MOE_ERR_UNSUPPORTED, "grouped_gemm: one group's B exceeds 4 GiB");
     if (M_total == 0) return MOE_OK;

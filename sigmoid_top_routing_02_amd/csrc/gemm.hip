@@ -38,25 +38,36 @@
 namespace moe {
 namespace {
 
-constexpr int BM = 128;
 constexpr int BN = 256;
 constexpr int BK = 128;                       // one scale slice
-constexpr int WAVES_M = 2;
-constexpr int WAVES_N = 4;
-constexpr int NWAVES = WAVES_M * WAVES_N;
+constexpr int NWAVES = 8;
 constexpr int NT = 64 * NWAVES;
-constexpr int WN_COLS = BN / WAVES_N;         // 64 columns per wave
-constexpr int NI = WN_COLS / 16;              // MFMA column tiles per wave
-constexpr int MI = 4;                         // 64 rows per wave
 constexpr int GROUP_M = 8;                    // row tiles per L2-sharing group
-constexpr int A_BYTES = BM * BK;              // 16 KiB
 constexpr int B_BYTES = BN * BK;              // 32 KiB
-constexpr int A_DMA = A_BYTES / 1024 / NWAVES;  // 1 KiB DMA instructions per wave
-constexpr int B_DMA = B_BYTES / 1024 / NWAVES;
-constexpr int DMA_PER_STAGE = A_DMA + B_DMA + 1;  // + one A-scale DMA
+constexpr int A_MAX_BYTES = 128 * BK;         // A stage buffer (largest row tile)
 constexpr int MAX_SLICES = 128;               // K <= 16384
-static_assert(DMA_PER_STAGE == 7, "stage barrier below waits for vmcnt(7)");
-static_assert(B_DMA % 2 == 0, "B DMA offsets come in swizzle-parity pairs");
+
+// Row-tile variants: 128 rows (2 x 4 waves of 64 x 64) for well-filled groups,
+// 32 rows (1 x 8 waves of 32 x 32) for groups of a few rows (decode), where a
+// 128-row tile would spend most MFMA work on padding.
+template <int BM_>
+struct Cfg {
+    static constexpr int BM = BM_;
+    static constexpr int WAVES_M = BM_ >= 64 ? BM_ / 64 : 1;
+    static constexpr int WAVES_N = NWAVES / WAVES_M;
+    static constexpr int WROWS = BM_ / WAVES_M;           // rows per wave
+    static constexpr int MI = WROWS / 16;                  // MFMA row tiles per wave
+    static constexpr int WN_COLS = BN / WAVES_N;           // columns per wave
+    static constexpr int NI = WN_COLS / 16;                // MFMA column tiles per wave
+    static constexpr int A_INSTR = BM_ * BK / 1024;        // 1 KiB DMAs per A copy
+    static constexpr int A_COPIES = A_INSTR >= NWAVES ? 1 : NWAVES / A_INSTR;
+    static constexpr int A_DMA = A_INSTR * A_COPIES / NWAVES;
+    static constexpr int B_DMA = B_BYTES / 1024 / NWAVES;
+    static constexpr int DMA_PER_STAGE = A_DMA + B_DMA + 1;   // + one A-scale DMA
+    static_assert(A_INSTR * A_COPIES * 1024 <= A_MAX_BYTES, "A stage too small");
+    static_assert(B_DMA % 2 == 0, "B DMA offsets come in swizzle-parity pairs");
+    static_assert(DMA_PER_STAGE == 6 || DMA_PER_STAGE == 7, "stage barrier waits for vmcnt(6|7)");
+};
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -82,15 +93,15 @@ struct GemmArgs {
 // its stage at compile time, so the compiler can see that reading one stage
 // does not alias the DMA still filling another (it would otherwise wait for
 // every outstanding DMA before each LDS read).
-__shared__ __attribute__((aligned(1024))) char g_a0[A_BYTES];
-__shared__ __attribute__((aligned(1024))) char g_a1[A_BYTES];
-__shared__ __attribute__((aligned(1024))) char g_a2[A_BYTES];
+__shared__ __attribute__((aligned(1024))) char g_a0[A_MAX_BYTES];
+__shared__ __attribute__((aligned(1024))) char g_a1[A_MAX_BYTES];
+__shared__ __attribute__((aligned(1024))) char g_a2[A_MAX_BYTES];
 __shared__ __attribute__((aligned(1024))) char g_b0[B_BYTES];
 __shared__ __attribute__((aligned(1024))) char g_b1[B_BYTES];
 __shared__ __attribute__((aligned(1024))) char g_b2[B_BYTES];
-// A scales of a slice: every wave DMAs 64 rows (wave & 1 picks the half) into
-// its own 256-byte copy, so all waves issue the same DMA count with no
-// lane-dependent branch; rows 0..127 are the copies of waves 0 and 1.
+// A scales of a slice: wave w DMAs rows (64w + lane) mod BM into its own
+// 256-byte copy, so all waves issue the same DMA count with no lane-dependent
+// branch; row r < BM is then at float index r.
 __shared__ __attribute__((aligned(16))) float g_sa0[64 * NWAVES];
 __shared__ __attribute__((aligned(16))) float g_sa1[64 * NWAVES];
 __shared__ __attribute__((aligned(16))) float g_sa2[64 * NWAVES];
@@ -155,26 +166,29 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z));
 
 // Column offset (inside the 256-wide N tile) of MFMA column-tile ni of wave wn.
 // SwiGLU waves take WN_COLS/2 gate columns and the matching up columns.
-template <int EPI>
+template <int EPI, typename C>
 __device__ __forceinline__ int ncol(int wn, int ni) {
     if constexpr (EPI == EPI_STORE_F32) {
-        return wn * WN_COLS + ni * 16;
+        return wn * C::WN_COLS + ni * 16;
     } else {
-        constexpr int HALF = NI / 2;
-        return (ni < HALF) ? (wn * (WN_COLS / 2) + ni * 16)
-                           : (128 + wn * (WN_COLS / 2) + (ni - HALF) * 16);
+        constexpr int HALF = C::NI / 2;
+        return (ni < HALF) ? (wn * (C::WN_COLS / 2) + ni * 16)
+                           : (128 + wn * (C::WN_COLS / 2) + (ni - HALF) * 16);
     }
 }
 
-template <int EPI>
+template <int EPI, int BM_>
 __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
+    using C = Cfg<BM_>;
+    constexpr int BM = C::BM, MI = C::MI, NI = C::NI, WAVES_N = C::WAVES_N;
+    constexpr int WN_COLS = C::WN_COLS, WROWS = C::WROWS, A_DMA = C::A_DMA, B_DMA = C::B_DMA;
     char* const smem = g_b0;       // epilogue scratch (after the K loop)
     const int K = p.K;
     const int ns = K / BK;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;   // wave row / column in the block
     const int kb = lane >> 4;
     const int lr = lane & 15;
 
@@ -216,7 +230,8 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
     uint32_t a_off[A_DMA];
 #pragma unroll
     for (int i = 0; i < A_DMA; ++i) {
-        const int r = (wave * A_DMA + i) * 8 + (lane >> 3);
+        // DMA li = wave*A_DMA + i fills LDS bytes [li*1 KiB, +1 KiB): copy li / A_INSTR
+        const int r = ((wave * A_DMA + i) % C::A_INSTR) * 8 + (lane >> 3);
         const int c = (lane & 7) ^ swz(r);
         const int m = m0 + min(r, rows - 1);
         const uint32_t am = p.a_rows ? (uint32_t)p.a_rows[m] : (uint32_t)m;
@@ -234,7 +249,7 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
     const auto sa_rsrc = make_rsrc(p.a_s, 0xFFFFFFFFu);
     uint32_t sa_off;
     {
-        const int r = (wave & 1) * 64 + lane;
+        const int r = (wave * 64 + lane) % BM;
         const int m = m0 + min(r, rows - 1);
         const uint32_t am = p.a_rows ? (uint32_t)p.a_rows[m] : (uint32_t)m;
         sa_off = am * (uint32_t)ns * 4u;
@@ -290,12 +305,12 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
     // lane offsets of the fragment chunks; the wave's row/column base is folded in
     const uint32_t sw0 = (uint32_t)(((2 * kb) ^ swz(lr)) << 4);
     const uint32_t sw1 = (uint32_t)(((2 * kb + 1) ^ swz(lr)) << 4);
-    const uint32_t a_lo0 = (uint32_t)(wm * 64 + lr) * 128 + sw0;
-    const uint32_t a_lo1 = (uint32_t)(wm * 64 + lr) * 128 + sw1;
-    const uint32_t bcol = (uint32_t)(ncol<EPI>(wn, 0) - ncol<EPI>(0, 0) + lr);
+    const uint32_t a_lo0 = (uint32_t)(wm * WROWS + lr) * 128 + sw0;
+    const uint32_t a_lo1 = (uint32_t)(wm * WROWS + lr) * 128 + sw1;
+    const uint32_t bcol = (uint32_t)(ncol<EPI, C>(wn, 0) - ncol<EPI, C>(0, 0) + lr);
     const uint32_t b_lo0 = bcol * 128 + sw0;
     const uint32_t b_lo1 = bcol * 128 + sw1;
-    const int sa_lane = wm * 64 + kb * 4;
+    const int sa_lane = wm * WROWS + kb * 4;
 
     // Stage barriers: wait for this wave's DMA of the next slice (the one after
     // may stay in flight) and for its own LDS reads, then s_barrier.  A plain
@@ -303,9 +318,14 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
     // serialise the pipeline.  The "memory" clobber keeps the compiler from
     // moving LDS accesses across it.
 #define MOE_STAGE_BARRIER(N) asm volatile("s_waitcnt vmcnt(" #N ") lgkmcnt(0)\n\ts_barrier" ::: "memory")
+    // waits until only the newest stage's DMAs (DMA_PER_STAGE per wave) may be in flight
+    auto stage_barrier = [&]() {
+        if constexpr (C::DMA_PER_STAGE == 7) MOE_STAGE_BARRIER(7);
+        else MOE_STAGE_BARRIER(6);
+    };
     issue(IC<0>{}, 0);
     issue(IC<1>{}, 1);
-    MOE_STAGE_BARRIER(7);      // slice 0 landed; also publishes the B scales
+    stage_barrier();           // slice 0 landed; also publishes the B scales
 
     // one K slice on stage ST; the DMA for slice s+2 goes to stage (ST+2)%3
     auto slice_step = [&](auto stc, int s) {
@@ -344,12 +364,12 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
                     acc[mi][ni][j] = __builtin_fmaf(part[mi][j], second ? c1[mi][j] : c0[mi][j],
                                                     acc[mi][ni][j]);
         };
-        v8i bnext = frag(Bt, ncol<EPI>(0, 0) * 128, b_lo0, b_lo1);
+        v8i bnext = frag(Bt, ncol<EPI, C>(0, 0) * 128, b_lo0, b_lo1);
         v4f prev[MI];
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) {
             const v8i bf = bnext;
-            if (ni + 1 < NI) bnext = frag(Bt, ncol<EPI>(0, ni + 1) * 128, b_lo0, b_lo1);
+            if (ni + 1 < NI) bnext = frag(Bt, ncol<EPI, C>(0, ni + 1) * 128, b_lo0, b_lo1);
             v4f cur[MI];
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi)
@@ -361,7 +381,7 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
         }
         scale_into(prev, NI - 1);
         // slice s+1 must have landed (slice s+2 may still be in flight)
-        MOE_STAGE_BARRIER(7);
+        stage_barrier();
     };
 
     // whole rounds of three stages, then the remaining one or two slices
@@ -382,12 +402,12 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
         for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int r = wm * 64 + mi * 16 + kb * 4 + j;
+                const int r = wm * WROWS + mi * 16 + kb * 4 + j;
                 if (r >= rows) continue;
                 float* orow = p.out + (int64_t)(m0 + r) * p.N;
 #pragma unroll
                 for (int ni = 0; ni < NI; ++ni) {
-                    const int n = n0 + ncol<EPI>(wn, ni) + lr;
+                    const int n = n0 + ncol<EPI, C>(wn, ni) + lr;
                     if (n < p.N) orow[n] = acc[mi][ni][j];
                 }
             }
@@ -409,7 +429,7 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
             for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int r = wm * 64 + mi * 16 + kb * 4 + j;
+                    const int r = wm * WROWS + mi * 16 + kb * 4 + j;
                     if (r >= rows) continue;
                     float* orow = p.out + (int64_t)(m0 + r) * I + h0 + wn * HC;
 #pragma unroll
@@ -417,8 +437,8 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
                 }
         } else {
             // row maximum over this wave's HC h columns, then across the N-waves in LDS
-            float* amax_s = reinterpret_cast<float*>(smem);           // [WAVES_N][128]
-            char* qtile = smem + 4096;                                  // [128][128] codes
+            float* amax_s = reinterpret_cast<float*>(smem);           // [WAVES_N][BM]
+            char* qtile = smem + 4096;                                  // [BM][128] codes
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
@@ -434,18 +454,18 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
                         const float other = __shfl_xor(m, o, 64);
                         m = other > m ? other : m;
                     }
-                    if (lr == 0) amax_s[wn * 128 + wm * 64 + mi * 16 + kb * 4 + j] = m;
+                    if (lr == 0) amax_s[wn * BM + wm * WROWS + mi * 16 + kb * 4 + j] = m;
                 }
             __syncthreads();
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int r = wm * 64 + mi * 16 + kb * 4 + j;
+                    const int r = wm * WROWS + mi * 16 + kb * 4 + j;
                     float amax = amax_s[r];
 #pragma unroll
                     for (int w = 1; w < WAVES_N; ++w) {
-                        const float a = amax_s[w * 128 + r];
+                        const float a = amax_s[w * BM + r];
                         amax = a > amax ? a : amax;
                     }
                     float inv, sc;
@@ -458,9 +478,7 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
                 }
             __syncthreads();
             // 128 rows x 128 bytes, 16-byte stores
-#pragma unroll
-            for (int i = 0; i < (BM * 128 / 16) / NT; ++i) {
-                const int c = tid + i * NT;
+            for (int c = tid; c < BM * 8; c += NT) {
                 const int r = c >> 3, part = c & 7;
                 if (r < rows)
                     *reinterpret_cast<uint4*>(p.out_q + (int64_t)(m0 + r) * I + h0 + part * 16) =
@@ -471,7 +489,7 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
                 for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        const int r = wm * 64 + mi * 16 + kb * 4 + j;
+                        const int r = wm * WROWS + mi * 16 + kb * 4 + j;
                         if (r >= rows) continue;
                         float* orow = p.out + (int64_t)(m0 + r) * I + h0 + wn * HC;
 #pragma unroll
@@ -486,7 +504,7 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
 
 // tile_start[g] = sum_{g' < g} ceil(rows_g' / BM), for g = 0..G.
 __global__ __launch_bounds__(256) void gemm_tile_map_kernel(const int32_t* __restrict__ go,
-                                                            int G, int32_t* __restrict__ ts) {
+                                                            int G, int BM, int32_t* __restrict__ ts) {
     __shared__ int32_t buf[256];
     __shared__ int32_t carry;
     if (threadIdx.x == 0) carry = 0;
@@ -532,25 +550,31 @@ hipError_t launch_grouped_gemm(const uint8_t* a_q, const float* a_s, const int32
                                float* out, uint8_t* out_q, float* out_s, void* ws,
                                hipStream_t st) {
     int32_t* ts = static_cast<int32_t*>(ws);
-    hipLaunchKernelGGL(gemm_tile_map_kernel, dim3(1), dim3(256), 0, st, group_offset, G, ts);
+    // 32-row tiles when the groups average at most 64 rows (few tokens per expert)
+    const int bm = (M_total <= (int64_t)64 * G) ? 32 : 128;
+    hipLaunchKernelGGL(gemm_tile_map_kernel, dim3(1), dim3(256), 0, st, group_offset, G, bm, ts);
     GemmArgs p{a_q, a_s, a_rows, group_offset, ts, G, b_q, b_s, N, K, out, out_q, out_s};
-    const int64_t mt_bound = (M_total + BM - 1) / BM + G;
+    const int64_t mt_bound = (M_total + bm - 1) / bm + G;
     const int64_t blocks = mt_bound * ((N + BN - 1) / BN);
     // one block per CU (its ~150 KB of LDS admit one), a multiple of the 8 XCDs
     const int64_t persistent = ((int64_t)cu_count_for_current_device() + 7) / 8 * 8;
     const int64_t needed = (blocks + 7) / 8 * 8;
     dim3 grid((unsigned)(needed < persistent ? needed : persistent));
-    switch (epi) {
-        case EPI_STORE_F32:
-            hipLaunchKernelGGL(grouped_gemm_kernel<EPI_STORE_F32>, grid, dim3(NT), 0, st, p);
-            break;
-        case EPI_SWIGLU_F32:
-            hipLaunchKernelGGL(grouped_gemm_kernel<EPI_SWIGLU_F32>, grid, dim3(NT), 0, st, p);
-            break;
-        default:
-            hipLaunchKernelGGL(grouped_gemm_kernel<EPI_SWIGLU_QUANT>, grid, dim3(NT), 0, st, p);
-            break;
+#define MOE_LAUNCH(E, B) hipLaunchKernelGGL((grouped_gemm_kernel<E, B>), grid, dim3(NT), 0, st, p)
+    if (bm == 32) {
+        switch (epi) {
+            case EPI_STORE_F32: MOE_LAUNCH(EPI_STORE_F32, 32); break;
+            case EPI_SWIGLU_F32: MOE_LAUNCH(EPI_SWIGLU_F32, 32); break;
+            default: MOE_LAUNCH(EPI_SWIGLU_QUANT, 32); break;
+        }
+    } else {
+        switch (epi) {
+            case EPI_STORE_F32: MOE_LAUNCH(EPI_STORE_F32, 128); break;
+            case EPI_SWIGLU_F32: MOE_LAUNCH(EPI_SWIGLU_F32, 128); break;
+            default: MOE_LAUNCH(EPI_SWIGLU_QUANT, 128); break;
+        }
     }
+#undef MOE_LAUNCH
     return hipGetLastError();
 }
 

@@ -81,11 +81,15 @@ def _int_operands(M, N, K, G, seed):
     return va, vb, qa, qb
 
 
+# The library takes 128-row tiles when the groups average more than 64 rows
+# and 32-row tiles otherwise; the cases below cover both.
 @pytest.mark.parametrize("sizes,N,K", [
-    ([128], 256, 128),                 # one tile
-    ([1], 256, 256),                   # one row
-    ([200, 0, 57, 128, 1], 512, 384),  # ragged groups incl. an empty one
-    ([300], 384, 256),                 # N % 256 == 128 (masked half tile)
+    ([128], 256, 128),                 # one tile (128-row tiles)
+    ([1], 256, 256),                   # one row (32-row tiles)
+    ([200, 0, 57, 128, 1], 512, 384),  # ragged groups incl. an empty one (128)
+    ([300], 384, 256),                 # N % 256 == 128, masked half tile (128)
+    ([5, 40, 0, 33, 9, 64], 512, 384), # ragged groups, 32-row tiles
+    ([7, 31, 70], 384, 256),           # N % 256 == 128 with 32-row tiles
 ])
 def test_gemm_integer_exact(sizes, N, K):
     """Exact integer results pin the MFMA operand/accumulator layouts, the
@@ -124,7 +128,8 @@ def _scaled_operands(M, N, K, G, seed, outliers=True):
     return qa, sa, qb, sb
 
 
-@pytest.mark.parametrize("sizes,N,K", [([129, 3, 0, 250], 256, 512), ([1000], 768, 1024)])
+@pytest.mark.parametrize("sizes,N,K", [([129, 3, 0, 250], 256, 512), ([1000], 768, 1024),
+                                       ([20, 3, 0, 45, 9], 256, 512)])
 def test_gemm_store_f32_vs_oracle(sizes, N, K):
     G = len(sizes)
     go = _groups(sizes)
@@ -154,7 +159,8 @@ def _interleave(w1, w3):
     return out
 
 
-@pytest.mark.parametrize("sizes,I,d", [([130, 0, 77, 256], 256, 512), ([64], 512, 256)])
+@pytest.mark.parametrize("sizes,I,d", [([130, 0, 77, 256], 256, 512), ([64], 512, 256),
+                                       ([9, 0, 33, 12, 50], 256, 512)])
 def test_gemm_swiglu_epilogues(sizes, I, d):
     """SwiGLU FP32 h against the oracle's FP64 h; the fused quantising
     epilogue equals SwiGLU_F32 followed by fp8_quant_1x128 bit for bit; its
