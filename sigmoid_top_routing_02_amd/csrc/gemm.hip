@@ -20,8 +20,8 @@
 // permutation), so activations are never materialised in expert order.  A, B
 // and the A scales of each slice go global -> LDS by buffer_load ... lds (no
 // VGPR staging) into a 3-stage ring; LDS rows are 128 bytes with the 16-byte
-// chunk c of row r in slot c ^ ((r >> 1) & 7), which keeps the fragment reads
-// bank-conflict free.  The B scales of the tile are staged in LDS once.
+// chunks of each row permuted (see swz) so that fragment reads are free of
+// bank conflicts.  The B scales of the tile are staged in LDS once.
 //
 // Schedule: persistent, one block per CU, tiles walked XCD by XCD in groups
 // of GROUP_M row tiles (see the kernel).  Grouping: a device-side tile map
@@ -49,7 +49,9 @@ constexpr int MAX_SLICES = 128;               // K <= 16384
 
 // Row-tile variants: 128 rows (2 x 4 waves of 64 x 64) for well-filled groups,
 // 32 rows (1 x 8 waves of 32 x 32) for groups of a few rows (decode), where a
-// 128-row tile would spend most MFMA work on padding.
+// 128-row tile would spend most MFMA work on padding.  (A 256-row tile would
+// halve the B traffic per flop, but 8 waves of 128 x 64 need more than the
+// 256 VGPRs a wave can address once the per-slice FP32 partials are counted.)
 template <int BM_>
 struct Cfg {
     static constexpr int BM = BM_;
@@ -64,6 +66,7 @@ struct Cfg {
     static constexpr int A_DMA = A_INSTR * A_COPIES / NWAVES;
     static constexpr int B_DMA = B_BYTES / 1024 / NWAVES;
     static constexpr int DMA_PER_STAGE = A_DMA + B_DMA + 1;   // + one A-scale DMA
+    static constexpr int NSTAGES = 3;
     static_assert(A_INSTR * A_COPIES * 1024 <= A_MAX_BYTES, "A stage too small");
     static_assert(B_DMA % 2 == 0, "B DMA offsets come in swizzle-parity pairs");
     static_assert(DMA_PER_STAGE == 6 || DMA_PER_STAGE == 7, "stage barrier waits for vmcnt(6|7)");
@@ -79,6 +82,7 @@ struct GemmArgs {
     const int32_t* a_rows;
     const int32_t* group_offset;
     const int32_t* tile_start;
+    int32_t* counters;            // [8] next tile of each XCD's share, zeroed by the tile map
     int G;
     const uint8_t* b_q;
     const float* b_s;
@@ -107,7 +111,7 @@ __shared__ __attribute__((aligned(16))) float g_sa1[64 * NWAVES];
 __shared__ __attribute__((aligned(16))) float g_sa2[64 * NWAVES];
 __shared__ __attribute__((aligned(16))) float g_bscale[2 * MAX_SLICES];
 
-template <int ST>
+template <int ST, int BM_>
 __device__ __forceinline__ char* a_buf() {
     if constexpr (ST == 0) return g_a0;
     else if constexpr (ST == 1) return g_a1;
@@ -142,11 +146,13 @@ __device__ __forceinline__ void lds_dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff
 }
 
 // LDS tiles hold 128-byte rows; the 16-byte chunk c of row r sits in slot
-// c ^ ((r >> 1) & 7).  A 16-lane group of a fragment read covers 16
-// consecutive rows: rows of equal parity land 32 banks apart and the swizzle
-// spreads the 8 rows of each parity over 8 distinct 4-bank groups, so the
-// reads are conflict free on the 64-bank LDS.
-__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+// c ^ (r & 7) ^ ((r >> 3) & 1).  A fragment read (ds_read_b128) has the 16
+// lanes of a group on 16 consecutive rows at one chunk index.  Measured on
+// gfx950, such a read runs at full LDS rate only if every 8 consecutive lanes
+// hit 8 distinct slots and the 16 lanes cover each (row parity, slot) pair
+// once; this swizzle meets both, while c ^ (r & 7) or c ^ ((r >> 1) & 7)
+// alone meet one and halve the read rate.
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 // 32 K-bytes of one MFMA fragment from a swizzled tile.  off0/off1 are the
 // lane's byte offsets of its two 16-byte chunks inside a 16-row band
@@ -182,7 +188,7 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
     using C = Cfg<BM_>;
     constexpr int BM = C::BM, MI = C::MI, NI = C::NI, WAVES_N = C::WAVES_N;
     constexpr int WN_COLS = C::WN_COLS, WROWS = C::WROWS, A_DMA = C::A_DMA, B_DMA = C::B_DMA;
-    char* const smem = g_b0;       // epilogue scratch (after the K loop)
+    constexpr int NS = C::NSTAGES;
     const int K = p.K;
     const int ns = K / BK;
     const int tid = threadIdx.x;
@@ -194,34 +200,39 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
 
     // ---- persistent schedule.  Workgroups go to the 8 XCDs round-robin
     // (block b runs on XCD b % 8) and the grid holds one block per CU.  Each
-    // XCD owns one contiguous share of the tile sequence, ordered in groups of
-    // GROUP_M row tiles x all column tiles (row tile fastest), and its blocks
-    // take consecutive tiles of that share round by round, so the blocks of an
-    // XCD work on neighbouring tiles at the same time and share A and B
-    // slices in the XCD's L2.
+    // XCD owns one contiguous share of the tile sequence and its blocks take
+    // the next tile of that share from a per-XCD counter, so the tiles in
+    // flight on an XCD are always neighbours in the sequence.  The sequence
+    // walks the groups in order; inside a group it takes chunks of up to
+    // GROUP_M row tiles, and inside a chunk the column tile is the slow
+    // index: the blocks of an XCD then share the A rows of the chunk and the B
+    // columns of one group in the XCD's L2, and never mix two groups' B unless
+    // the window straddles a group boundary.
     const int total_tiles = p.tile_start[p.G];
     const int n_tiles = (p.N + BN - 1) / BN;
     const int xcd = blockIdx.x & 7;
-    const int slot = blockIdx.x >> 3;
-    const int xcd_blocks = gridDim.x >> 3;
     const int total = total_tiles * n_tiles;
     const int share = (total + 7) >> 3;
-    for (int tl = slot; tl < share; tl += xcd_blocks) {
+    __shared__ int s_next;
+    if (tid == 0) s_next = atomicAdd(p.counters + xcd, 1);
+    __syncthreads();
+    for (int tl = s_next; tl < share; ) {
     const int t = xcd * share + tl;
     if (t >= total) break;
-    const int grp = t / (GROUP_M * n_tiles);
-    const int first_m = grp * GROUP_M;
-    const int gm = min(GROUP_M, total_tiles - first_m);
-    const int t_in = t - grp * GROUP_M * n_tiles;
-    const int mt_lin = first_m + t_in % gm;
-    const int n_tile = t_in / gm;
-    int lo = 0, hi = p.G - 1;                 // largest g with tile_start[g] <= mt_lin
+    const int q = t / n_tiles;               // tile_start[g] <= q < tile_start[g+1]
+    int lo = 0, hi = p.G - 1;                 // largest g with tile_start[g] <= q
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (p.tile_start[mid] <= mt_lin) lo = mid; else hi = mid - 1;
+        if (p.tile_start[mid] <= q) lo = mid; else hi = mid - 1;
     }
     const int g = lo;
-    const int m0 = p.group_offset[g] + (mt_lin - p.tile_start[g]) * BM;
+    const int mt_g = p.tile_start[g + 1] - p.tile_start[g];
+    const int local = t - p.tile_start[g] * n_tiles;
+    const int chunk = local / (GROUP_M * n_tiles);
+    const int chunk_rows = min(GROUP_M, mt_g - chunk * GROUP_M);
+    const int in_chunk = local - chunk * GROUP_M * n_tiles;
+    const int n_tile = in_chunk / chunk_rows;
+    const int m0 = p.group_offset[g] + (chunk * GROUP_M + in_chunk % chunk_rows) * BM;
     const int rows = min(BM, p.group_offset[g + 1] - m0);
     const int n0 = n_tile * BN;
 
@@ -261,22 +272,25 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
     // instruction stream (and the compiler's wait-count model) identical on
     // every step: no step needs a conservative full drain.
     const auto null_rsrc = make_rsrc(p.a_q, 0u);
-    auto issue = [&](auto stc, int slice) {
+    // DMA k (0 <= k < DMA_PER_STAGE) of one stage: A chunks, then B chunks, then the A scales
+    auto issue_one = [&](auto stc, int slice, int k) {
         constexpr int ST = decltype(stc)::value;
         const bool live = slice < ns;
         const uint32_t koff = live ? (uint32_t)slice * BK : 0u;
-        const auto ar = live ? a_rsrc : null_rsrc;
-        const auto br = live ? b_rsrc : null_rsrc;
-        const auto sr = live ? sa_rsrc : null_rsrc;
-#pragma unroll
-        for (int i = 0; i < A_DMA; ++i)
-            lds_dma16(ar, a_off[i], koff, a_buf<ST>() + (wave * A_DMA + i) * 1024);
-#pragma unroll
-        for (int i = 0; i < B_DMA; ++i)
-            lds_dma16(br, b_off[i & 1] + (uint32_t)((i & ~1) * 8) * (uint32_t)K, koff,
+        if (k < A_DMA) {
+            lds_dma16(live ? a_rsrc : null_rsrc, a_off[k], koff, a_buf<ST, BM>() + (wave * A_DMA + k) * 1024);
+        } else if (k < A_DMA + B_DMA) {
+            const int i = k - A_DMA;
+            lds_dma16(live ? b_rsrc : null_rsrc, b_off[i & 1] + (uint32_t)((i & ~1) * 8) * (uint32_t)K, koff,
                       b_buf<ST>() + (wave * B_DMA + i) * 1024);
-        lds_dma4(sr, sa_off, live ? (uint32_t)slice * 4u : 0u,
-                 reinterpret_cast<char*>(sa_buf<ST>()) + wave * 256);
+        } else {
+            lds_dma4(live ? sa_rsrc : null_rsrc, sa_off, live ? (uint32_t)slice * 4u : 0u,
+                     reinterpret_cast<char*>(sa_buf<ST>()) + wave * 256);
+        }
+    };
+    auto issue = [&](auto stc, int slice) {
+#pragma unroll
+        for (int k = 0; k < C::DMA_PER_STAGE; ++k) issue_one(stc, slice, k);
     };
 
     // ---- B scales of the tile's two 128-row blocks, all slices, into LDS once
@@ -327,59 +341,74 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
     issue(IC<1>{}, 1);
     stage_barrier();           // slice 0 landed; also publishes the B scales
 
-    // one K slice on stage ST; the DMA for slice s+2 goes to stage (ST+2)%3
+    // One K slice on stage ST; the DMAs for slice s+2 go to the stage that
+    // slice s-1 used (every wave has passed the barrier after reading it).
     auto slice_step = [&](auto stc, int s) {
         constexpr int ST = decltype(stc)::value;
-        issue(IC<(ST + 2) % 3>{}, s + 2);
-        const char* At = a_buf<ST>();
+        constexpr int NEXT = (ST + NS - 1) % NS;     // stage that slice s-1 used
+        const char* At = a_buf<ST, BM>();
         const char* Bt = b_buf<ST>();
         const float* SAt = sa_buf<ST>();
 
         const float sb0 = sbs[sbrow0 * MAX_SLICES + s];
         const float sb1 = sbs[sbrow1 * MAX_SLICES + s];
 
-        v8i af[MI];
-        float c0[MI][4], c1[MI][4];
+        // The wave's B fragments stay in registers for the slice and the row
+        // tiles are walked in a software pipeline.  The order is pinned (a
+        // scheduling barrier after each MFMA): MFMA (mi, ni), then the four
+        // scale FMAs of (mi-1, ni), whose partial finished four MFMAs earlier;
+        // the A fragment and scales of row tile mi+1 are read after the first
+        // MFMA of row tile mi.  The DMAs of slice s+2 are spread evenly
+        // over the MFMAs: issued back to back they stall the wave until
+        // the memory pipeline accepts them, keeping it off the matrix core.
+        v8i bfr[NI];
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi) {
-            af[mi] = frag(At, mi * 16 * 128, a_lo0, a_lo1);
-            const float4 sa = *reinterpret_cast<const float4*>(SAt + sa_lane + mi * 16);
-            const float sv[4] = {sa.x, sa.y, sa.z, sa.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                c0[mi][j] = sv[j] * sb0;
-                c1[mi][j] = sv[j] * sb1;
-            }
-        }
-        // Software pipeline over the column tiles: the MFMAs of tile ni are
-        // issued before the scale FMAs of tile ni-1 consume their partials, and
-        // the B fragment of tile ni+1 is read from LDS meanwhile, so a wave
-        // always has independent MFMA, VALU and LDS work in flight.
-        auto scale_into = [&](const v4f (&part)[MI], int ni) {
+        for (int ni = 0; ni < NI; ++ni) bfr[ni] = frag(Bt, ncol<EPI, C>(0, ni) * 128, b_lo0, b_lo1);
+        auto fma4 = [&](const v4f& part, int mi, int ni, const float (&c0)[4], const float (&c1)[4]) {
             const bool second = (EPI != EPI_STORE_F32) && ni >= NI / 2;
 #pragma unroll
-            for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[mi][ni][j] = __builtin_fmaf(part[mi][j], second ? c1[mi][j] : c0[mi][j],
-                                                    acc[mi][ni][j]);
+            for (int j = 0; j < 4; ++j)
+                acc[mi][ni][j] = __builtin_fmaf(part[j], second ? c1[j] : c0[j], acc[mi][ni][j]);
         };
-        v8i bnext = frag(Bt, ncol<EPI, C>(0, 0) * 128, b_lo0, b_lo1);
-        v4f prev[MI];
+        v8i anext = frag(At, 0, a_lo0, a_lo1);
+        float4 sanext = *reinterpret_cast<const float4*>(SAt + sa_lane);
+        v4f prev[NI];
+        float p0[4], p1[4];
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni) {
-            const v8i bf = bnext;
-            if (ni + 1 < NI) bnext = frag(Bt, ncol<EPI, C>(0, ni + 1) * 128, b_lo0, b_lo1);
-            v4f cur[MI];
+        for (int mi = 0; mi < MI; ++mi) {
+            const v8i af = anext;
+            const float4 sa = sanext;
+            float q0[4], q1[4];
+            v4f cur[NI];
 #pragma unroll
-            for (int mi = 0; mi < MI; ++mi)
-                cur[mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    af[mi], bf, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-            if (ni > 0) scale_into(prev, ni - 1);
+            for (int ni = 0; ni < NI; ++ni) {
+                cur[ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    af, bfr[ni], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+                {
+                    constexpr int Q = MI * NI, D = C::DMA_PER_STAGE;
+                    const int q = mi * NI + ni;
 #pragma unroll
-            for (int mi = 0; mi < MI; ++mi) prev[mi] = cur[mi];
+                    for (int k = 0; k < D; ++k)
+                        if ((k * Q) / D == q) issue_one(IC<NEXT>{}, s + NS - 1, k);
+                }
+                if (ni == 0 && mi + 1 < MI) {
+                    anext = frag(At, (mi + 1) * 16 * 128, a_lo0, a_lo1);
+                    sanext = *reinterpret_cast<const float4*>(SAt + sa_lane + (mi + 1) * 16);
+                }
+                if (mi > 0) fma4(prev[ni], mi - 1, ni, p0, p1);
+                if (ni == NI - 1) {
+                    q0[0] = sa.x * sb0; q0[1] = sa.y * sb0; q0[2] = sa.z * sb0; q0[3] = sa.w * sb0;
+                    q1[0] = sa.x * sb1; q1[1] = sa.y * sb1; q1[2] = sa.z * sb1; q1[3] = sa.w * sb1;
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni) prev[ni] = cur[ni];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) { p0[j] = q0[j]; p1[j] = q1[j]; }
         }
-        scale_into(prev, NI - 1);
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) fma4(prev[ni], MI - 1, ni, p0, p1);
         // slice s+1 must have landed (slice s+2 may still be in flight)
         stage_barrier();
     };
@@ -437,8 +466,8 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
                 }
         } else {
             // row maximum over this wave's HC h columns, then across the N-waves in LDS
-            float* amax_s = reinterpret_cast<float*>(smem);           // [WAVES_N][BM]
-            char* qtile = smem + 4096;                                  // [BM][128] codes
+            float* amax_s = reinterpret_cast<float*>(g_b0);           // [WAVES_N][BM]
+            char* qtile = a_buf<0, BM>();                               // [BM][128] codes
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
@@ -498,13 +527,17 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
             }
         }
     }
+    if (tid == 0) s_next = atomicAdd(p.counters + xcd, 1);
     __syncthreads();   // the next tile's DMAs overwrite the stages and the scratch
+    tl = s_next;
     }  // persistent tile loop
 }
 
-// tile_start[g] = sum_{g' < g} ceil(rows_g' / BM), for g = 0..G.
+// tile_start[g] = sum_{g' < g} ceil(rows_g' / BM), for g = 0..G; zeroes the
+// 8 per-XCD tile counters that follow it.
 __global__ __launch_bounds__(256) void gemm_tile_map_kernel(const int32_t* __restrict__ go,
                                                             int G, int BM, int32_t* __restrict__ ts) {
+    if (threadIdx.x < 8) ts[G + 1 + threadIdx.x] = 0;
     __shared__ int32_t buf[256];
     __shared__ int32_t carry;
     if (threadIdx.x == 0) carry = 0;
@@ -542,7 +575,7 @@ int cu_count_for_current_device() {
 
 }  // namespace
 
-size_t gemm_ws_bytes(int G) { return (size_t)(G + 1) * sizeof(int32_t); }
+size_t gemm_ws_bytes(int G) { return (size_t)(G + 1 + 8) * sizeof(int32_t); }
 
 hipError_t launch_grouped_gemm(const uint8_t* a_q, const float* a_s, const int32_t* a_rows,
                                const int32_t* group_offset, int G, int64_t M_total,
@@ -553,7 +586,7 @@ hipError_t launch_grouped_gemm(const uint8_t* a_q, const float* a_s, const int32
     // 32-row tiles when the groups average at most 64 rows (few tokens per expert)
     const int bm = (M_total <= (int64_t)64 * G) ? 32 : 128;
     hipLaunchKernelGGL(gemm_tile_map_kernel, dim3(1), dim3(256), 0, st, group_offset, G, bm, ts);
-    GemmArgs p{a_q, a_s, a_rows, group_offset, ts, G, b_q, b_s, N, K, out, out_q, out_s};
+    GemmArgs p{a_q, a_s, a_rows, group_offset, ts, ts + G + 1, G, b_q, b_s, N, K, out, out_q, out_s};
     const int64_t mt_bound = (M_total + bm - 1) / bm + G;
     const int64_t blocks = mt_bound * ((N + BN - 1) / BN);
     // one block per CU (its ~150 KB of LDS admit one), a multiple of the 8 XCDs
