@@ -9,7 +9,7 @@ import torch
 import oracle
 import sigmoid_top_routing_02_amd as moe
 import workloads
-from helpers import dev, np_, say, u16
+from helpers import TOL, dev, np_, rowinf_rel, say, u16
 
 pytestmark = pytest.mark.gpu
 
@@ -149,3 +149,24 @@ def test_bias_update_bit_exact():
     ref = oracle.bias_update(b, count, T * K, 1e-3)
     np.testing.assert_array_equal(np_(bd).view(np.uint32), ref.view(np.uint32))
     np.testing.assert_array_equal(np_(bd)[:4], b[:4])
+
+
+@pytest.mark.parametrize("T,d,E,K", [(300, 512, 16, 4), (1000, 7168, 256, 8)])
+def test_combine_identity_experts_bf16(T, d, E, K):
+    """The router-dispatch-combine path with identity experts: Y is the
+    permuted bf16 input, no shared term; h' against the oracle's FP64 combine
+    (per-row relative error <= 2e-3), and the conservation h' ~ 2u (sum g = 1)."""
+    u, e, b = _inputs(T, d, E, seed=T + d)
+    say(f"combine identity experts T={T} d={d} E={E} K={K}")
+    idx, gate, _ = moe.moe_router_topk(u.to(dev()), e.to(dev()), b.to(dev()), K)
+    count, go, row_token, slot_row = moe.moe_dispatch(idx, E, False)
+    xp = moe.moe_permute_rows(u.to(dev()), row_token)
+    out = moe.moe_combine(u.to(dev()), xp, gate, slot_row, shared_row0=-1)
+    torch.cuda.synchronize()
+    y = (u16(xp).astype(np.uint32) << 16).view(np.float32)
+    ref = oracle.combine(u16(u), y, -1, np_(gate), np_(slot_row))
+    err = rowinf_rel(np_(out), ref)
+    say(f"  per-row rel err {err:.3e}")
+    assert err <= TOL
+    uf = (u16(u).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert rowinf_rel(np_(out), 2 * uf) <= 1e-5
