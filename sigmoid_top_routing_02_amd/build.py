@@ -26,6 +26,9 @@ FLAGS = [
     "-Wall",
     "-Wno-unused-command-line-argument",
     "-mllvm", "-amdgpu-mfma-vgpr-form",   # MFMA results in VGPRs: the VALU consumes every slice
+    # no wave-level rewriting of atomics: the GEMM's next-tile request must not
+    # be waited for (with every DMA in flight) right where it is issued
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
 ]
 
 

@@ -110,6 +110,9 @@ __shared__ __attribute__((aligned(16))) float g_sa0[64 * NWAVES];
 __shared__ __attribute__((aligned(16))) float g_sa1[64 * NWAVES];
 __shared__ __attribute__((aligned(16))) float g_sa2[64 * NWAVES];
 __shared__ __attribute__((aligned(16))) float g_bscale[2 * MAX_SLICES];
+// tile_start[0..G] of the launch, for the tile-to-group search (G < MAX_LDS_GROUPS)
+constexpr int MAX_LDS_GROUPS = 1024;
+__shared__ int32_t g_tstart[MAX_LDS_GROUPS];
 
 template <int ST, int BM_>
 __device__ __forceinline__ char* a_buf() {
@@ -168,7 +171,9 @@ __device__ __forceinline__ v8i frag(const char* tile, int band, uint32_t off0, u
     return f;
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+// SiLU(z) = z * sigmoid(z), with the hardware exp and reciprocal (not bit-exact
+// with any reference; the SwiGLU output is checked against a tolerance).
+__device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // Column offset (inside the 256-wide N tile) of MFMA column-tile ni of wave wn.
 // SwiGLU waves take WN_COLS/2 gate columns and the matching up columns.
@@ -189,6 +194,13 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
     constexpr int BM = C::BM, MI = C::MI, NI = C::NI, WAVES_N = C::WAVES_N;
     constexpr int WN_COLS = C::WN_COLS, WROWS = C::WROWS, A_DMA = C::A_DMA, B_DMA = C::B_DMA;
     constexpr int NS = C::NSTAGES;
+    constexpr int D = C::DMA_PER_STAGE;
+    // MFMA operand order.  SwiGLU tiles put B first, so a lane's four results
+    // share one output row and one scale (one multiply per row tile instead
+    // of four).  FP32-store tiles keep A first: a lane's results are then four
+    // rows of one column, and its stores cover 16 consecutive columns per row,
+    // which measured faster for the large FP32 output than 4-column pieces.
+    constexpr bool TR = (EPI != EPI_STORE_F32);
     const int K = p.K;
     const int ns = K / BK;
     const int tid = threadIdx.x;
@@ -207,72 +219,97 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
     // GROUP_M row tiles, and inside a chunk the column tile is the slow
     // index: the blocks of an XCD then share the A rows of the chunk and the B
     // columns of one group in the XCD's L2, and never mix two groups' B unless
-    // the window straddles a group boundary.
+    // the window straddles a group boundary.  A block asks for its next tile
+    // when it starts the current one.
     const int total_tiles = p.tile_start[p.G];
     const int n_tiles = (p.N + BN - 1) / BN;
     const int xcd = blockIdx.x & 7;
     const int total = total_tiles * n_tiles;
     const int share = (total + 7) >> 3;
     __shared__ int s_next;
-    if (tid == 0) s_next = atomicAdd(p.counters + xcd, 1);
-    __syncthreads();
-    for (int tl = s_next; tl < share; ) {
-    const int t = xcd * share + tl;
-    if (t >= total) break;
-    const int q = t / n_tiles;               // tile_start[g] <= q < tile_start[g+1]
-    int lo = 0, hi = p.G - 1;                 // largest g with tile_start[g] <= q
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (p.tile_start[mid] <= q) lo = mid; else hi = mid - 1;
-    }
-    const int g = lo;
-    const int mt_g = p.tile_start[g + 1] - p.tile_start[g];
-    const int local = t - p.tile_start[g] * n_tiles;
-    const int chunk = local / (GROUP_M * n_tiles);
-    const int chunk_rows = min(GROUP_M, mt_g - chunk * GROUP_M);
-    const int in_chunk = local - chunk * GROUP_M * n_tiles;
-    const int n_tile = in_chunk / chunk_rows;
-    const int m0 = p.group_offset[g] + (chunk * GROUP_M + in_chunk % chunk_rows) * BM;
-    const int rows = min(BM, p.group_offset[g + 1] - m0);
-    const int n0 = n_tile * BN;
+    // the group search reads tile_start from LDS (one global load chain per
+    // step of the search would otherwise sit between two tiles)
+    const bool ts_lds = p.G < MAX_LDS_GROUPS;
+    if (ts_lds)
+        for (int i = tid; i <= p.G; i += NT) g_tstart[i] = p.tile_start[i];
+    struct Tile { int g, m0, rows, n0; };
+    auto tile_at = [&](int t) {
+        const int q = t / n_tiles;               // tile_start[g] <= q < tile_start[g+1]
+        int lo = 0, hi = p.G - 1;                 // largest g with tile_start[g] <= q
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            const int v = ts_lds ? g_tstart[mid] : p.tile_start[mid];
+            if (v <= q) lo = mid; else hi = mid - 1;
+        }
+        Tile T;
+        lo = __builtin_amdgcn_readfirstlane(lo);      // block-uniform (the search read LDS)
+        T.g = lo;
+        const int mt_g = p.tile_start[lo + 1] - p.tile_start[lo];
+        const int local = t - p.tile_start[lo] * n_tiles;
+        const int chunk = local / (GROUP_M * n_tiles);
+        const int chunk_rows = min(GROUP_M, mt_g - chunk * GROUP_M);
+        const int in_chunk = local - chunk * GROUP_M * n_tiles;
+        T.m0 = p.group_offset[lo] + (chunk * GROUP_M + in_chunk % chunk_rows) * BM;
+        T.rows = min(BM, p.group_offset[lo + 1] - T.m0);
+        T.n0 = (in_chunk / chunk_rows) * BN;
+        T.m0 = __builtin_amdgcn_readfirstlane(T.m0);
+        T.rows = __builtin_amdgcn_readfirstlane(T.rows);
+        T.n0 = __builtin_amdgcn_readfirstlane(T.n0);
+        return T;
+    };
+    // the global index of this XCD's tile number tl (-1: none left)
+    auto global_tile = [&](int tl) {
+        const int t = xcd * share + tl;
+        return (tl < share && t < total) ? t : -1;
+    };
 
-    // ---- per-lane DMA sources (loop-invariant byte offsets; the slice moves soffset)
+    // ---- per-tile DMA sources (byte offsets; the slice moves soffset)
     const auto a_rsrc = make_rsrc(p.a_q, 0xFFFFFFFFu);
-    uint32_t a_off[A_DMA];
-#pragma unroll
-    for (int i = 0; i < A_DMA; ++i) {
-        // DMA li = wave*A_DMA + i fills LDS bytes [li*1 KiB, +1 KiB): copy li / A_INSTR
-        const int r = ((wave * A_DMA + i) % C::A_INSTR) * 8 + (lane >> 3);
-        const int c = (lane & 7) ^ swz(r);
-        const int m = m0 + min(r, rows - 1);
-        const uint32_t am = p.a_rows ? (uint32_t)p.a_rows[m] : (uint32_t)m;
-        a_off[i] = am * (uint32_t)K + c * 16;
-    }
-    const auto b_rsrc = make_rsrc(p.b_q + (int64_t)g * p.N * K, (uint32_t)p.N * (uint32_t)K);
-    // B rows of DMA i are r0 + 8i; the swizzle of r0 + 8i only depends on i & 1
-    uint32_t b_off[2];
-#pragma unroll
-    for (int par = 0; par < 2; ++par) {
-        const int r = (wave * B_DMA + par) * 8 + (lane >> 3);
-        const int c = (lane & 7) ^ swz(r);
-        b_off[par] = (uint32_t)(n0 + r) * (uint32_t)K + c * 16;   // rows past N read as 0
-    }
     const auto sa_rsrc = make_rsrc(p.a_s, 0xFFFFFFFFu);
-    uint32_t sa_off;
-    {
-        const int r = (wave * 64 + lane) % BM;
-        const int m = m0 + min(r, rows - 1);
-        const uint32_t am = p.a_rows ? (uint32_t)p.a_rows[m] : (uint32_t)m;
-        sa_off = am * (uint32_t)ns * 4u;
-    }
-
     // A descriptor with no records: every access is out of range, so no memory
     // is touched (the target stage is a spare one).  Past the last slice the
     // pipeline still issues its DMAs through this descriptor, which keeps the
     // instruction stream (and the compiler's wait-count model) identical on
     // every step: no step needs a conservative full drain.
     const auto null_rsrc = make_rsrc(p.a_q, 0u);
-    // DMA k (0 <= k < DMA_PER_STAGE) of one stage: A chunks, then B chunks, then the A scales
+    const int nblk_per_g = p.N / 128;
+    uint32_t a_off[A_DMA], b_off[2], sa_off = 0;
+    uint32_t am_pre[A_DMA + 1];                  // gathered A rows of the next tile's DMA lanes
+    __amdgpu_buffer_rsrc_t b_rsrc = null_rsrc;
+    // A-row indices of this lane's A DMAs and of its A-scale DMA (the gather)
+    auto load_rows = [&](const Tile& T) {
+#pragma unroll
+        for (int i = 0; i <= A_DMA; ++i) {
+            // A DMA li = wave*A_DMA + i fills LDS bytes [li*1 KiB, +1 KiB): copy li / A_INSTR;
+            // the A-scale DMA of wave w covers rows (64w + lane) mod BM
+            const int r = (i < A_DMA) ? ((wave * A_DMA + i) % C::A_INSTR) * 8 + (lane >> 3)
+                                      : (wave * 64 + lane) % BM;
+            const int m = T.m0 + min(r, T.rows - 1);
+            am_pre[i] = p.a_rows ? (uint32_t)p.a_rows[m] : (uint32_t)m;
+        }
+    };
+    auto setup = [&](const Tile& T) {
+#pragma unroll
+        for (int i = 0; i < A_DMA; ++i) {
+            const int r = ((wave * A_DMA + i) % C::A_INSTR) * 8 + (lane >> 3);
+            a_off[i] = am_pre[i] * (uint32_t)K + ((lane & 7) ^ swz(r)) * 16;
+        }
+        sa_off = am_pre[A_DMA] * (uint32_t)ns * 4u;
+        b_rsrc = make_rsrc(p.b_q + (int64_t)T.g * p.N * K, (uint32_t)p.N * (uint32_t)K);
+        // B rows of DMA i are r0 + 8i; the swizzle of r0 + 8i only depends on i & 1
+#pragma unroll
+        for (int par = 0; par < 2; ++par) {
+            const int r = (wave * B_DMA + par) * 8 + (lane >> 3);
+            b_off[par] = (uint32_t)(T.n0 + r) * (uint32_t)K + ((lane & 7) ^ swz(r)) * 16;  // rows past N read 0
+        }
+        // B scales of the tile's two 128-row blocks, all slices, into LDS
+        const float* bs_g = p.b_s + (int64_t)T.g * nblk_per_g * ns;
+        for (int i = tid; i < 2 * ns; i += NT) {
+            const int blk = min(T.n0 / 128 + i / ns, nblk_per_g - 1);
+            g_bscale[(i / ns) * MAX_SLICES + (i % ns)] = bs_g[(int64_t)blk * ns + (i % ns)];
+        }
+    };
+    // DMA k (0 <= k < D) of one stage: A chunks, then B chunks, then the A scales
     auto issue_one = [&](auto stc, int slice, int k) {
         constexpr int ST = decltype(stc)::value;
         const bool live = slice < ns;
@@ -290,18 +327,10 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
     };
     auto issue = [&](auto stc, int slice) {
 #pragma unroll
-        for (int k = 0; k < C::DMA_PER_STAGE; ++k) issue_one(stc, slice, k);
+        for (int k = 0; k < D; ++k) issue_one(stc, slice, k);
     };
 
-    // ---- B scales of the tile's two 128-row blocks, all slices, into LDS once
-    const int nblk_per_g = p.N / 128;
-    const float* bs_g = p.b_s + (int64_t)g * nblk_per_g * ns;
-    float* sbs = g_bscale;                                              // [2][MAX_SLICES]
-    for (int i = tid; i < 2 * ns; i += NT) {
-        const int blk = min(n0 / 128 + i / ns, nblk_per_g - 1);
-        sbs[(i / ns) * MAX_SLICES + (i % ns)] = bs_g[(int64_t)blk * ns + (i % ns)];
-    }
-    int sbrow0, sbrow1;   // which of the two blocks scales this wave's column tiles
+    int sbrow0, sbrow1;   // which of the two B blocks scales this wave's column tiles
     if constexpr (EPI == EPI_STORE_F32) {
         sbrow0 = (wn * WN_COLS) / 128;
         sbrow1 = sbrow0;
@@ -309,13 +338,6 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
         sbrow0 = 0;
         sbrow1 = 1;
     }
-
-    v4f acc[MI][NI];
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = v4f{0.f, 0.f, 0.f, 0.f};
-
     // lane offsets of the fragment chunks; the wave's row/column base is folded in
     const uint32_t sw0 = (uint32_t)(((2 * kb) ^ swz(lr)) << 4);
     const uint32_t sw1 = (uint32_t)(((2 * kb + 1) ^ swz(lr)) << 4);
@@ -324,22 +346,20 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
     const uint32_t bcol = (uint32_t)(ncol<EPI, C>(wn, 0) - ncol<EPI, C>(0, 0) + lr);
     const uint32_t b_lo0 = bcol * 128 + sw0;
     const uint32_t b_lo1 = bcol * 128 + sw1;
-    const int sa_lane = wm * WROWS + kb * 4;
+    const int sa_row = wm * WROWS + lr;      // this lane's output row inside the tile (+ mi * 16)
 
-    // Stage barriers: wait for this wave's DMA of the next slice (the one after
+    v4f acc[MI][NI];
+
+    // Stage barriers: wait for this wave's DMAs of the next slice (newer ones
     // may stay in flight) and for its own LDS reads, then s_barrier.  A plain
     // __syncthreads() would also drain every outstanding DMA (vmcnt(0)) and
     // serialise the pipeline.  The "memory" clobber keeps the compiler from
     // moving LDS accesses across it.
 #define MOE_STAGE_BARRIER(N) asm volatile("s_waitcnt vmcnt(" #N ") lgkmcnt(0)\n\ts_barrier" ::: "memory")
-    // waits until only the newest stage's DMAs (DMA_PER_STAGE per wave) may be in flight
     auto stage_barrier = [&]() {
-        if constexpr (C::DMA_PER_STAGE == 7) MOE_STAGE_BARRIER(7);
+        if constexpr (D == 7) MOE_STAGE_BARRIER(7);
         else MOE_STAGE_BARRIER(6);
     };
-    issue(IC<0>{}, 0);
-    issue(IC<1>{}, 1);
-    stage_barrier();           // slice 0 landed; also publishes the B scales
 
     // One K slice on stage ST; the DMAs for slice s+2 go to the stage that
     // slice s-1 used (every wave has passed the barrier after reading it).
@@ -350,42 +370,63 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
         const char* Bt = b_buf<ST>();
         const float* SAt = sa_buf<ST>();
 
-        const float sb0 = sbs[sbrow0 * MAX_SLICES + s];
-        const float sb1 = sbs[sbrow1 * MAX_SLICES + s];
+        const float sb0 = g_bscale[sbrow0 * MAX_SLICES + s];
+        const float sb1 = g_bscale[sbrow1 * MAX_SLICES + s];
 
         // The wave's B fragments stay in registers for the slice and the row
         // tiles are walked in a software pipeline.  The order is pinned (a
         // scheduling barrier after each MFMA): MFMA (mi, ni), then the four
         // scale FMAs of (mi-1, ni), whose partial finished four MFMAs earlier;
-        // the A fragment and scales of row tile mi+1 are read after the first
-        // MFMA of row tile mi.  The DMAs of slice s+2 are spread evenly
-        // over the MFMAs: issued back to back they stall the wave until
-        // the memory pipeline accepts them, keeping it off the matrix core.
+        // the A fragment and scale of row tile mi+1 are read after the first
+        // MFMA of row tile mi.  The DMAs of slice s+2 are spread evenly over
+        // the MFMAs: issued back to back they stall the wave until the memory
+        // pipeline accepts them, keeping it off the matrix core.
         v8i bfr[NI];
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) bfr[ni] = frag(Bt, ncol<EPI, C>(0, ni) * 128, b_lo0, b_lo1);
-        auto fma4 = [&](const v4f& part, int mi, int ni, const float (&c0)[4], const float (&c1)[4]) {
+        // Scales: with B first a lane's four results share one row (lr) and
+        // one scale; with A first they are rows 4*kb + j of one column.
+        constexpr int NC = TR ? 1 : 4;
+        auto fma4 = [&](const v4f& part, int mi, int ni, const float (&c0)[NC], const float (&c1)[NC]) {
             const bool second = (EPI != EPI_STORE_F32) && ni >= NI / 2;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[mi][ni][j] = __builtin_fmaf(part[j], second ? c1[j] : c0[j], acc[mi][ni][j]);
+            for (int j = 0; j < 4; ++j) {
+                const float c = second ? c1[TR ? 0 : j] : c0[TR ? 0 : j];
+                acc[mi][ni][j] = __builtin_fmaf(part[j], c, acc[mi][ni][j]);
+            }
+        };
+        // this lane's A scales of row tile mi: one row (B first) or four (A first)
+        auto read_sa = [&](int mi, float (&v)[NC]) {
+            if constexpr (TR) {
+                v[0] = SAt[sa_row + mi * 16];
+            } else {
+                const float4 t = *reinterpret_cast<const float4*>(SAt + wm * WROWS + 4 * kb + mi * 16);
+                v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+            }
         };
         v8i anext = frag(At, 0, a_lo0, a_lo1);
-        float4 sanext = *reinterpret_cast<const float4*>(SAt + sa_lane);
+        float sanext[NC];
+        read_sa(0, sanext);
         v4f prev[NI];
-        float p0[4], p1[4];
+        float p0[NC], p1[NC];
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi) {
             const v8i af = anext;
-            const float4 sa = sanext;
-            float q0[4], q1[4];
+            float sa[NC];
+#pragma unroll
+            for (int j = 0; j < NC; ++j) sa[j] = sanext[j];
+            float q0[NC], q1[NC];
             v4f cur[NI];
 #pragma unroll
             for (int ni = 0; ni < NI; ++ni) {
-                cur[ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    af, bfr[ni], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+                if constexpr (TR)
+                    cur[ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        bfr[ni], af, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+                else
+                    cur[ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        af, bfr[ni], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
                 {
-                    constexpr int Q = MI * NI, D = C::DMA_PER_STAGE;
+                    constexpr int Q = MI * NI;
                     const int q = mi * NI + ni;
 #pragma unroll
                     for (int k = 0; k < D; ++k)
@@ -393,19 +434,22 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
                 }
                 if (ni == 0 && mi + 1 < MI) {
                     anext = frag(At, (mi + 1) * 16 * 128, a_lo0, a_lo1);
-                    sanext = *reinterpret_cast<const float4*>(SAt + sa_lane + (mi + 1) * 16);
+                    read_sa(mi + 1, sanext);
                 }
                 if (mi > 0) fma4(prev[ni], mi - 1, ni, p0, p1);
                 if (ni == NI - 1) {
-                    q0[0] = sa.x * sb0; q0[1] = sa.y * sb0; q0[2] = sa.z * sb0; q0[3] = sa.w * sb0;
-                    q1[0] = sa.x * sb1; q1[1] = sa.y * sb1; q1[2] = sa.z * sb1; q1[3] = sa.w * sb1;
+#pragma unroll
+                    for (int j = 0; j < NC; ++j) {
+                        q0[j] = sa[j] * sb0;
+                        q1[j] = (EPI != EPI_STORE_F32) ? sa[j] * sb1 : 0.f;
+                    }
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
             for (int ni = 0; ni < NI; ++ni) prev[ni] = cur[ni];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) { p0[j] = q0[j]; p1[j] = q1[j]; }
+            for (int j = 0; j < NC; ++j) { p0[j] = q0[j]; p1[j] = q1[j]; }
         }
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) fma4(prev[ni], MI - 1, ni, p0, p1);
@@ -413,84 +457,67 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
         stage_barrier();
     };
 
-    // whole rounds of three stages, then the remaining one or two slices
-    int s = 0;
-    for (; s + 3 <= ns; s += 3) {
-        slice_step(IC<0>{}, s);
-        slice_step(IC<1>{}, s + 1);
-        slice_step(IC<2>{}, s + 2);
-    }
-    if (s < ns) slice_step(IC<0>{}, s);
-    if (s + 1 < ns) slice_step(IC<1>{}, s + 1);
-    MOE_STAGE_BARRIER(0);      // drain the spare-stage DMAs before LDS is reused
-#undef MOE_STAGE_BARRIER
-
-    // ---- epilogues.  Lane holds C[row = base + 4*kb + j][col = base + lr].
-    if constexpr (EPI == EPI_STORE_F32) {
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = wm * WROWS + mi * 16 + kb * 4 + j;
-                if (r >= rows) continue;
-                float* orow = p.out + (int64_t)(m0 + r) * p.N;
-#pragma unroll
-                for (int ni = 0; ni < NI; ++ni) {
-                    const int n = n0 + ncol<EPI, C>(wn, ni) + lr;
-                    if (n < p.N) orow[n] = acc[mi][ni][j];
-                }
-            }
-    } else {
-        constexpr int HALF = NI / 2;
-        constexpr int HC = WN_COLS / 2;    // h columns per wave
-        const int I = p.N / 2;
-        const int h0 = n0 / 2;             // first h column of this tile
-        float h[MI][HALF][4];
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-            for (int ni = 0; ni < HALF; ++ni)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    h[mi][ni][j] = silu(acc[mi][ni][j]) * acc[mi][ni + HALF][j];
-        if constexpr (EPI == EPI_SWIGLU_F32) {
+    // FP32-store epilogue (A-first layout: lane holds rows 4*kb + j of column lr)
+    auto store_f32 = [&](const Tile& T) {
+        if constexpr (EPI == EPI_STORE_F32) {
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int r = wm * WROWS + mi * 16 + kb * 4 + j;
-                    if (r >= rows) continue;
-                    float* orow = p.out + (int64_t)(m0 + r) * I + h0 + wn * HC;
+                    if (r >= T.rows) continue;
+                    float* orow = p.out + (int64_t)(T.m0 + r) * p.N;
 #pragma unroll
-                    for (int ni = 0; ni < HALF; ++ni) orow[ni * 16 + lr] = h[mi][ni][j];
+                    for (int ni = 0; ni < NI; ++ni) {
+                        const int n = T.n0 + ncol<EPI, C>(wn, ni) + lr;
+                        if (n < p.N) orow[n] = acc[mi][ni][j];
+                    }
                 }
-        } else {
-            // row maximum over this wave's HC h columns, then across the N-waves in LDS
-            float* amax_s = reinterpret_cast<float*>(g_b0);           // [WAVES_N][BM]
-            char* qtile = a_buf<0, BM>();                               // [BM][128] codes
+        }
+    };
+
+    // SwiGLU epilogues, in two parts around the next tile's first DMAs: the
+    // arithmetic (scratch in stage 2, which the next tile's first two slices
+    // leave alone), then the global stores.
+    constexpr int HALF = NI / 2;
+    constexpr int HC = WN_COLS / 2;          // h columns per wave
+    float h[EPI == EPI_STORE_F32 ? 1 : MI][HALF > 0 ? HALF : 1][4];   // row sa_row + mi*16, h column wn*HC + ni*16 + 4*kb + j
+    float* const amax_s = reinterpret_cast<float*>(g_b2);               // [WAVES_N][BM] row maxima
+    float* const scale_s = amax_s + WAVES_N * BM;                        // [BM] row scales
+    char* const qtile = a_buf<2, BM>();                                  // [BM][128] codes
+    auto swiglu_compute = [&]() {
+        if constexpr (EPI != EPI_STORE_F32) {
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
+                for (int ni = 0; ni < HALF; ++ni)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        h[mi][ni][j] = silu(acc[mi][ni][j]) * acc[mi][ni + HALF][j];
+            if constexpr (EPI == EPI_SWIGLU_QUANT) {
+                // row maximum over this wave's HC h columns (lanes lr, lr+16, lr+32
+                // and lr+48 hold one row), then across the N-waves in LDS
+#pragma unroll
+                for (int mi = 0; mi < MI; ++mi) {
                     float m = 0.0f;
 #pragma unroll
-                    for (int ni = 0; ni < HALF; ++ni) {
-                        const float a = __builtin_fabsf(h[mi][ni][j]);
-                        m = a > m ? a : m;
-                    }
+                    for (int ni = 0; ni < HALF; ++ni)
 #pragma unroll
-                    for (int o = 1; o < 16; o <<= 1) {
+                        for (int j = 0; j < 4; ++j) {
+                            const float a = __builtin_fabsf(h[mi][ni][j]);
+                            m = a > m ? a : m;
+                        }
+#pragma unroll
+                    for (int o = 16; o < 64; o <<= 1) {
                         const float other = __shfl_xor(m, o, 64);
                         m = other > m ? other : m;
                     }
-                    if (lr == 0) amax_s[wn * BM + wm * WROWS + mi * 16 + kb * 4 + j] = m;
+                    if (kb == 0) amax_s[wn * BM + sa_row + mi * 16] = m;
                 }
-            __syncthreads();
+                __syncthreads();
 #pragma unroll
-            for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int r = wm * WROWS + mi * 16 + kb * 4 + j;
+                for (int mi = 0; mi < MI; ++mi) {
+                    const int r = sa_row + mi * 16;
                     float amax = amax_s[r];
 #pragma unroll
                     for (int w = 1; w < WAVES_N; ++w) {
@@ -500,37 +527,104 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
                     float inv, sc;
                     tile_scale(amax, inv, sc);
 #pragma unroll
-                    for (int ni = 0; ni < HALF; ++ni)
-                        qtile[r * 128 + wn * HC + ni * 16 + lr] = (char)e4m3_encode(h[mi][ni][j] * inv);
-                    if (wn == 0 && lr == 0 && r < rows)
-                        p.out_s[(int64_t)(m0 + r) * (I / 128) + h0 / 128] = sc;
-                }
-            __syncthreads();
-            // 128 rows x 128 bytes, 16-byte stores
-            for (int c = tid; c < BM * 8; c += NT) {
-                const int r = c >> 3, part = c & 7;
-                if (r < rows)
-                    *reinterpret_cast<uint4*>(p.out_q + (int64_t)(m0 + r) * I + h0 + part * 16) =
-                        *reinterpret_cast<const uint4*>(qtile + r * 128 + part * 16);
-            }
-            if (p.out) {
+                    for (int ni = 0; ni < HALF; ++ni) {
+                        uint32_t w4 = 0;
 #pragma unroll
-                for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int r = wm * WROWS + mi * 16 + kb * 4 + j;
-                        if (r >= rows) continue;
-                        float* orow = p.out + (int64_t)(m0 + r) * I + h0 + wn * HC;
-#pragma unroll
-                        for (int ni = 0; ni < HALF; ++ni) orow[ni * 16 + lr] = h[mi][ni][j];
+                        for (int j = 0; j < 4; ++j)
+                            w4 |= (uint32_t)e4m3_encode(h[mi][ni][j] * inv) << (8 * j);
+                        *reinterpret_cast<uint32_t*>(qtile + r * 128 + wn * HC + ni * 16 + 4 * kb) = w4;
                     }
+                    if (wn == 0 && kb == 0) scale_s[r] = sc;
+                }
+                __syncthreads();
             }
         }
-    }
+    };
+    auto swiglu_store = [&](const Tile& T) {
+        if constexpr (EPI != EPI_STORE_F32) {
+            const int I = p.N / 2;
+            const int h0 = T.n0 / 2;         // first h column of this tile
+            if constexpr (EPI == EPI_SWIGLU_QUANT) {
+                // BM rows x 128 bytes, 16-byte stores, and one scale per row
+                for (int c = tid; c < BM * 8; c += NT) {
+                    const int r = c >> 3, part = c & 7;
+                    if (r < T.rows)
+                        *reinterpret_cast<uint4*>(p.out_q + (int64_t)(T.m0 + r) * I + h0 + part * 16) =
+                            *reinterpret_cast<const uint4*>(qtile + r * 128 + part * 16);
+                }
+                if (tid < BM && tid < T.rows) p.out_s[(int64_t)(T.m0 + tid) * (I / 128) + h0 / 128] = scale_s[tid];
+            }
+            if (EPI == EPI_SWIGLU_F32 || p.out) {
+#pragma unroll
+                for (int mi = 0; mi < MI; ++mi) {
+                    const int r = sa_row + mi * 16;
+                    if (r >= T.rows) continue;
+                    float* orow = p.out + (int64_t)(T.m0 + r) * I + h0 + wn * HC + 4 * kb;
+#pragma unroll
+                    for (int ni = 0; ni < HALF; ++ni)
+                        *reinterpret_cast<float4*>(orow + ni * 16) =
+                            make_float4(h[mi][ni][0], h[mi][ni][1], h[mi][ni][2], h[mi][ni][3]);
+                }
+            }
+        }
+    };
+
+    // ---- the tile loop
     if (tid == 0) s_next = atomicAdd(p.counters + xcd, 1);
-    __syncthreads();   // the next tile's DMAs overwrite the stages and the scratch
-    tl = s_next;
-    }  // persistent tile loop
+    __syncthreads();
+    int t_cur = global_tile(__builtin_amdgcn_readfirstlane(s_next));
+    if (t_cur < 0) return;
+    Tile cur = tile_at(t_cur);
+    load_rows(cur);
+    setup(cur);
+    issue(IC<0>{}, 0);
+    issue(IC<1>{}, 1);
+    // The tile after this one.  Its result is only needed after the K loop;
+    // the library is built without the compiler's atomic optimizer, which
+    // would otherwise consume it (and drain every DMA in flight) right here.
+    int nxt_raw = 0;
+    if (tid == 0) nxt_raw = atomicAdd(p.counters + xcd, 1);
+    for (;;) {
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = v4f{0.f, 0.f, 0.f, 0.f};
+        stage_barrier();               // slice 0 landed; also publishes the B scales
+
+        // whole rounds of three stages, then the remaining one or two slices
+        int s = 0;
+        for (; s + 3 <= ns; s += 3) {
+            slice_step(IC<0>{}, s);
+            slice_step(IC<1>{}, s + 1);
+            slice_step(IC<2>{}, s + 2);
+        }
+        if (s < ns) slice_step(IC<0>{}, s);
+        if (s + 1 < ns) slice_step(IC<1>{}, s + 1);
+        MOE_STAGE_BARRIER(0);      // drain the spare-stage DMAs before LDS is reused
+
+        // next tile: its index was requested when this tile started
+        if (tid == 0) s_next = nxt_raw;
+        __syncthreads();
+        const int t_nxt = global_tile(__builtin_amdgcn_readfirstlane(s_next));
+        Tile nxt = cur;
+        if (t_nxt >= 0) {
+            nxt = tile_at(t_nxt);
+            load_rows(nxt);
+        }
+        swiglu_compute();
+        if (t_nxt >= 0) {
+            setup(nxt);
+            issue(IC<0>{}, 0);
+            issue(IC<1>{}, 1);
+            if (tid == 0) nxt_raw = atomicAdd(p.counters + xcd, 1);
+        }
+        store_f32(cur);
+        swiglu_store(cur);
+        if (t_nxt < 0) break;
+        __syncthreads();   // stage-2 scratch and the tile's LDS reads are done before slice 2 lands
+        cur = nxt;
+    }
+#undef MOE_STAGE_BARRIER
 }
 
 // tile_start[g] = sum_{g' < g} ceil(rows_g' / BM), for g = 0..G; zeroes the
