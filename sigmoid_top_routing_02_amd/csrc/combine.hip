@@ -4,9 +4,8 @@
 // input plus the shared experts plus the chosen routed experts weighted by
 // their gates,
 //     h'[t] = u[t] + y[shared_row0 + t] + sum_k g[t,k] * y[slot_row[t,k]]
-// evaluated per element in FP32 in that order (one FMA per routed term).  One
-// block per token row; 16-byte loads of the K+1 expert rows and of u, 16-byte
-// FP32 stores; bandwidth bound.
+// evaluated per element in FP32 in that order (one FMA per routed term);
+// bandwidth bound.
 //
 // Bias update -- "DeepSeek-V3 Technical Report" notes, bias paragraph: after
 // each step an overloaded expert's bias is lowered by gamma and an
@@ -28,7 +27,11 @@ __device__ __forceinline__ float4 load_y4(const void* y, int64_t row, int d, int
     }
 }
 
-template <bool Y_F32>
+// One block per token row (grid-strided); each thread owns one or two 4-column
+// chunks.  All K + 2 row loads of a chunk are issued before the first
+// arithmetic, so a wave keeps up to 2 * (K + 2) loads in flight instead of waiting
+// for them one by one; the arithmetic then runs in the fixed order above.
+template <bool Y_F32, int KMAX>
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ u,
                                                       const void* __restrict__ y,
                                                       int64_t shared_row0,
@@ -36,29 +39,47 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
                                                       const int32_t* __restrict__ slot_row,
                                                       int64_t T, int K, int d,
                                                       float* __restrict__ out) {
+    constexpr int CH = KMAX > 8 ? 1 : 2;        // 4-column chunks per thread per pass
     const int d4 = d / 4;
     for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
-        float g[16];
-        int64_t r[16];
-        for (int k = 0; k < K; ++k) {
-            g[k] = gate[t * K + k];
-            r[k] = slot_row[t * K + k];
+        float g[KMAX];
+        int64_t r[KMAX];
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            g[k] = k < K ? gate[t * K + k] : 0.0f;
+            r[k] = k < K ? slot_row[t * K + k] : 0;
         }
-        for (int c4 = threadIdx.x; c4 < d4; c4 += 256) {
-            const uint2 uw = reinterpret_cast<const uint2*>(u + t * d)[c4];
-            float4 v = make_float4(bf16_lo(uw.x), bf16_hi(uw.x), bf16_lo(uw.y), bf16_hi(uw.y));
-            if (shared_row0 >= 0) {
-                const float4 s = load_y4<Y_F32>(y, shared_row0 + t, d, c4);
-                v.x = v.x + s.x; v.y = v.y + s.y; v.z = v.z + s.z; v.w = v.w + s.w;
+        for (int base = threadIdx.x; base < d4; base += 256 * CH) {
+            float4 v[CH], sh[CH], yk[CH][KMAX];
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                const int c4 = base + c * 256;
+                if (c4 >= d4) continue;
+                const uint2 uw = reinterpret_cast<const uint2*>(u + t * d)[c4];
+                v[c] = make_float4(bf16_lo(uw.x), bf16_hi(uw.x), bf16_lo(uw.y), bf16_hi(uw.y));
+                if (shared_row0 >= 0) sh[c] = load_y4<Y_F32>(y, shared_row0 + t, d, c4);
+#pragma unroll
+                for (int k = 0; k < KMAX; ++k)
+                    if (k < K) yk[c][k] = load_y4<Y_F32>(y, r[k], d, c4);
             }
-            for (int k = 0; k < K; ++k) {
-                const float4 yk = load_y4<Y_F32>(y, r[k], d, c4);
-                v.x = __builtin_fmaf(g[k], yk.x, v.x);
-                v.y = __builtin_fmaf(g[k], yk.y, v.y);
-                v.z = __builtin_fmaf(g[k], yk.z, v.z);
-                v.w = __builtin_fmaf(g[k], yk.w, v.w);
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                const int c4 = base + c * 256;
+                if (c4 >= d4) continue;
+                float4 a = v[c];
+                if (shared_row0 >= 0) {
+                    a.x = a.x + sh[c].x; a.y = a.y + sh[c].y; a.z = a.z + sh[c].z; a.w = a.w + sh[c].w;
+                }
+#pragma unroll
+                for (int k = 0; k < KMAX; ++k) {
+                    if (k >= K) break;
+                    a.x = __builtin_fmaf(g[k], yk[c][k].x, a.x);
+                    a.y = __builtin_fmaf(g[k], yk[c][k].y, a.y);
+                    a.z = __builtin_fmaf(g[k], yk[c][k].z, a.z);
+                    a.w = __builtin_fmaf(g[k], yk[c][k].w, a.w);
+                }
+                reinterpret_cast<float4*>(out + t * d)[c4] = a;
             }
-            reinterpret_cast<float4*>(out + t * d)[c4] = v;
         }
     }
 }
@@ -78,12 +99,18 @@ hipError_t launch_combine(const uint16_t* u, const void* y, int y_is_f32, int64_
                           const float* gate, const int32_t* slot_row, int64_t T, int K, int d,
                           float* out, hipStream_t st) {
     const unsigned grid = (unsigned)(T < 65536 ? T : 65536);
-    if (y_is_f32)
-        hipLaunchKernelGGL(combine_kernel<true>, dim3(grid), dim3(256), 0, st, u, y, shared_row0,
-                           gate, slot_row, T, K, d, out);
-    else
-        hipLaunchKernelGGL(combine_kernel<false>, dim3(grid), dim3(256), 0, st, u, y, shared_row0,
-                           gate, slot_row, T, K, d, out);
+#define MOE_COMBINE(F, KM) hipLaunchKernelGGL((combine_kernel<F, KM>), dim3(grid), dim3(256), 0, st, u, y, \
+                                              shared_row0, gate, slot_row, T, K, d, out)
+    if (y_is_f32) {
+        if (K <= 4) MOE_COMBINE(true, 4);
+        else if (K <= 8) MOE_COMBINE(true, 8);
+        else MOE_COMBINE(true, 16);
+    } else {
+        if (K <= 4) MOE_COMBINE(false, 4);
+        else if (K <= 8) MOE_COMBINE(false, 8);
+        else MOE_COMBINE(false, 16);
+    }
+#undef MOE_COMBINE
     return hipGetLastError();
 }
 

@@ -32,6 +32,8 @@
 // block, so one N tile holds the gate and up columns of the same 128 h
 // columns); SwiGLU + 1x128 E4M3 re-quantisation of h, whose row maximum over
 // the tile's 128 h columns is reduced across the N-waves in LDS.
+#include <type_traits>
+
 #include "device_math.h"
 #include "kernels.h"
 
@@ -83,6 +85,7 @@ struct GemmArgs {
     const int32_t* group_offset;
     const int32_t* tile_start;
     int32_t* counters;            // [8] next tile of each XCD's share, zeroed by the tile map
+    const int4* tiles;            // per tile of the sequence: {group, first row, rows, first column}
     int G;
     const uint8_t* b_q;
     const float* b_s;
@@ -110,9 +113,7 @@ __shared__ __attribute__((aligned(16))) float g_sa0[64 * NWAVES];
 __shared__ __attribute__((aligned(16))) float g_sa1[64 * NWAVES];
 __shared__ __attribute__((aligned(16))) float g_sa2[64 * NWAVES];
 __shared__ __attribute__((aligned(16))) float g_bscale[2 * MAX_SLICES];
-// tile_start[0..G] of the launch, for the tile-to-group search (G < MAX_LDS_GROUPS)
-constexpr int MAX_LDS_GROUPS = 1024;
-__shared__ int32_t g_tstart[MAX_LDS_GROUPS];
+
 
 template <int ST, int BM_>
 __device__ __forceinline__ char* a_buf() {
@@ -227,34 +228,14 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
     const int total = total_tiles * n_tiles;
     const int share = (total + 7) >> 3;
     __shared__ int s_next;
-    // the group search reads tile_start from LDS (one global load chain per
-    // step of the search would otherwise sit between two tiles)
-    const bool ts_lds = p.G < MAX_LDS_GROUPS;
-    if (ts_lds)
-        for (int i = tid; i <= p.G; i += NT) g_tstart[i] = p.tile_start[i];
     struct Tile { int g, m0, rows, n0; };
-    auto tile_at = [&](int t) {
-        const int q = t / n_tiles;               // tile_start[g] <= q < tile_start[g+1]
-        int lo = 0, hi = p.G - 1;                 // largest g with tile_start[g] <= q
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            const int v = ts_lds ? g_tstart[mid] : p.tile_start[mid];
-            if (v <= q) lo = mid; else hi = mid - 1;
-        }
-        Tile T;
-        lo = __builtin_amdgcn_readfirstlane(lo);      // block-uniform (the search read LDS)
-        T.g = lo;
-        const int mt_g = p.tile_start[lo + 1] - p.tile_start[lo];
-        const int local = t - p.tile_start[lo] * n_tiles;
-        const int chunk = local / (GROUP_M * n_tiles);
-        const int chunk_rows = min(GROUP_M, mt_g - chunk * GROUP_M);
-        const int in_chunk = local - chunk * GROUP_M * n_tiles;
-        T.m0 = p.group_offset[lo] + (chunk * GROUP_M + in_chunk % chunk_rows) * BM;
-        T.rows = min(BM, p.group_offset[lo + 1] - T.m0);
-        T.n0 = (in_chunk / chunk_rows) * BN;
-        T.m0 = __builtin_amdgcn_readfirstlane(T.m0);
-        T.rows = __builtin_amdgcn_readfirstlane(T.rows);
-        T.n0 = __builtin_amdgcn_readfirstlane(T.n0);
+    auto tile_at = [&](int t) {               // from the list the tile-map kernels built
+        const int4 v = p.tiles[t];
+        Tile T;                                   // block-uniform: keep it in SGPRs
+        T.g = __builtin_amdgcn_readfirstlane(v.x);
+        T.m0 = __builtin_amdgcn_readfirstlane(v.y);
+        T.rows = __builtin_amdgcn_readfirstlane(v.z);
+        T.n0 = __builtin_amdgcn_readfirstlane(v.w);
         return T;
     };
     // the global index of this XCD's tile number tl (-1: none left)
@@ -363,8 +344,11 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
 
     // One K slice on stage ST; the DMAs for slice s+2 go to the stage that
     // slice s-1 used (every wave has passed the barrier after reading it).
-    auto slice_step = [&](auto stc, int s) {
+    auto slice_step = [&](auto stc, int s, auto firstc) {
         constexpr int ST = decltype(stc)::value;
+        // a tile's first step also issues slice 1 (the tile prologue issues
+        // slice 0 only, so the DMAs of a tile switch are spread over MFMAs)
+        constexpr bool FIRST = decltype(firstc)::value;
         constexpr int NEXT = (ST + NS - 1) % NS;     // stage that slice s-1 used
         const char* At = a_buf<ST, BM>();
         const char* Bt = b_buf<ST>();
@@ -427,10 +411,14 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
                         af, bfr[ni], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
                 {
                     constexpr int Q = MI * NI;
+                    constexpr int DD = FIRST ? 2 * D : D;
                     const int q = mi * NI + ni;
 #pragma unroll
-                    for (int k = 0; k < D; ++k)
-                        if ((k * Q) / D == q) issue_one(IC<NEXT>{}, s + NS - 1, k);
+                    for (int k = 0; k < DD; ++k)
+                        if ((k * Q) / DD == q) {
+                            if (FIRST && k < D) issue_one(IC<(ST + 1) % 3>{}, s + 1, k);
+                            else issue_one(IC<NEXT>{}, s + NS - 1, FIRST ? k - D : k);
+                        }
                 }
                 if (ni == 0 && mi + 1 < MI) {
                     anext = frag(At, (mi + 1) * 16 * 128, a_lo0, a_lo1);
@@ -578,7 +566,6 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
     load_rows(cur);
     setup(cur);
     issue(IC<0>{}, 0);
-    issue(IC<1>{}, 1);
     // The tile after this one.  Its result is only needed after the K loop;
     // the library is built without the compiler's atomic optimizer, which
     // would otherwise consume it (and drain every DMA in flight) right here.
@@ -589,17 +576,28 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
         for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
             for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = v4f{0.f, 0.f, 0.f, 0.f};
-        stage_barrier();               // slice 0 landed; also publishes the B scales
+        // slice 0 landed (it and the previous tile's stores are all that is in
+        // flight: a full wait); also publishes the B scales
+        MOE_STAGE_BARRIER(0);
 
         // whole rounds of three stages, then the remaining one or two slices
-        int s = 0;
-        for (; s + 3 <= ns; s += 3) {
-            slice_step(IC<0>{}, s);
-            slice_step(IC<1>{}, s + 1);
-            slice_step(IC<2>{}, s + 2);
+        using First = std::true_type;
+        using Later = std::false_type;
+        slice_step(IC<0>{}, 0, First{});
+        int s = 1;
+        if (ns >= 3) {
+            slice_step(IC<1>{}, 1, Later{});
+            slice_step(IC<2>{}, 2, Later{});
+            for (s = 3; s + 3 <= ns; s += 3) {
+                slice_step(IC<0>{}, s, Later{});
+                slice_step(IC<1>{}, s + 1, Later{});
+                slice_step(IC<2>{}, s + 2, Later{});
+            }
+            if (s < ns) slice_step(IC<0>{}, s, Later{});
+            if (s + 1 < ns) slice_step(IC<1>{}, s + 1, Later{});
+        } else if (ns == 2) {
+            slice_step(IC<1>{}, 1, Later{});
         }
-        if (s < ns) slice_step(IC<0>{}, s);
-        if (s + 1 < ns) slice_step(IC<1>{}, s + 1);
         MOE_STAGE_BARRIER(0);      // drain the spare-stage DMAs before LDS is reused
 
         // next tile: its index was requested when this tile started
@@ -615,7 +613,6 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
         if (t_nxt >= 0) {
             setup(nxt);
             issue(IC<0>{}, 0);
-            issue(IC<1>{}, 1);
             if (tid == 0) nxt_raw = atomicAdd(p.counters + xcd, 1);
         }
         store_f32(cur);
@@ -655,6 +652,31 @@ __global__ __launch_bounds__(256) void gemm_tile_map_kernel(const int32_t* __res
     if (threadIdx.x == 0) ts[G] = carry;
 }
 
+// The tile sequence: tile t = (row tile q, column tile) with q = t / n_tiles in
+// group g (tile_start[g] <= q < tile_start[g+1]); inside a group, chunks of
+// up to GROUP_M row tiles, the column tile slow inside a chunk.
+__global__ __launch_bounds__(256) void gemm_tile_list_kernel(const int32_t* __restrict__ go,
+                                                             const int32_t* __restrict__ ts, int G,
+                                                             int BM, int N, int4* __restrict__ tiles) {
+    const int n_tiles = (N + BN - 1) / BN;
+    const int total = ts[G] * n_tiles;
+    const int t = blockIdx.x * 256 + threadIdx.x;
+    if (t >= total) return;
+    const int q = t / n_tiles;
+    int lo = 0, hi = G - 1;                       // largest g with ts[g] <= q
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (ts[mid] <= q) lo = mid; else hi = mid - 1;
+    }
+    const int mt_g = ts[lo + 1] - ts[lo];
+    const int local = t - ts[lo] * n_tiles;
+    const int chunk = local / (GROUP_M * n_tiles);
+    const int chunk_rows = min(GROUP_M, mt_g - chunk * GROUP_M);
+    const int in_chunk = local - chunk * GROUP_M * n_tiles;
+    const int m0 = go[lo] + (chunk * GROUP_M + in_chunk % chunk_rows) * BM;
+    tiles[t] = make_int4(lo, m0, min(BM, go[lo + 1] - m0), (in_chunk / chunk_rows) * BN);
+}
+
 int cu_count_for_current_device() {
     static int cached[64] = {0};
     int dev = 0;
@@ -669,7 +691,15 @@ int cu_count_for_current_device() {
 
 }  // namespace
 
-size_t gemm_ws_bytes(int G) { return (size_t)(G + 1 + 8) * sizeof(int32_t); }
+// [tile_start: G+1][counters: 8] (16-byte aligned) [tile list: int4 per tile, bound for 32-row tiles]
+static int64_t tile_list_offset(int G) { return ((int64_t)(G + 1 + 8) * 4 + 15) / 16 * 16; }
+static int64_t tile_bound(int G, int64_t M_total, int N) {
+    return ((M_total + 31) / 32 + G) * (int64_t)((N + BN - 1) / BN);
+}
+
+size_t gemm_ws_bytes(int G, int64_t M_total, int N) {
+    return (size_t)(tile_list_offset(G) + tile_bound(G, M_total, N) * 16);
+}
 
 hipError_t launch_grouped_gemm(const uint8_t* a_q, const float* a_s, const int32_t* a_rows,
                                const int32_t* group_offset, int G, int64_t M_total,
@@ -677,12 +707,15 @@ hipError_t launch_grouped_gemm(const uint8_t* a_q, const float* a_s, const int32
                                float* out, uint8_t* out_q, float* out_s, void* ws,
                                hipStream_t st) {
     int32_t* ts = static_cast<int32_t*>(ws);
+    int4* tiles = reinterpret_cast<int4*>(static_cast<char*>(ws) + tile_list_offset(G));
     // 32-row tiles when the groups average at most 64 rows (few tokens per expert)
     const int bm = (M_total <= (int64_t)64 * G) ? 32 : 128;
     hipLaunchKernelGGL(gemm_tile_map_kernel, dim3(1), dim3(256), 0, st, group_offset, G, bm, ts);
-    GemmArgs p{a_q, a_s, a_rows, group_offset, ts, ts + G + 1, G, b_q, b_s, N, K, out, out_q, out_s};
-    const int64_t mt_bound = (M_total + bm - 1) / bm + G;
-    const int64_t blocks = mt_bound * ((N + BN - 1) / BN);
+    const int64_t list_bound = ((M_total + bm - 1) / bm + G) * (int64_t)((N + BN - 1) / BN);
+    hipLaunchKernelGGL(gemm_tile_list_kernel, dim3((unsigned)((list_bound + 255) / 256)), dim3(256), 0, st,
+                       group_offset, ts, G, bm, N, tiles);
+    GemmArgs p{a_q, a_s, a_rows, group_offset, ts, ts + G + 1, tiles, G, b_q, b_s, N, K, out, out_q, out_s};
+    const int64_t blocks = list_bound;
     // one block per CU (its ~150 KB of LDS admit one), a multiple of the 8 XCDs
     const int64_t persistent = ((int64_t)cu_count_for_current_device() + 7) / 8 * 8;
     const int64_t needed = (blocks + 7) / 8 * 8;
