@@ -159,6 +159,61 @@ __global__ __launch_bounds__(NTHREADS) void router_scores_kernel(
     }
 }
 
+// Few tokens (decode): one block per (token, 256 experts), one output per
+// lane.  Every logit is still a single FMA chain in increasing k, so with few
+// outputs the chains' length, not the arithmetic, sets the time; this layout
+// runs T * E chains at once across the chip instead of giving each thread
+// several.  The token's u row is staged once in LDS (every lane then reads the
+// same address: a broadcast); each lane streams its own centroid row with
+// RING groups of 32 bf16 in flight ahead of its FMAs.
+constexpr int ROWS_MAX_D = 16384;                // LDS for the u row: 2*d bytes
+
+__global__ __launch_bounds__(256) void router_scores_rows_kernel(
+    const uint16_t* __restrict__ u, const uint16_t* __restrict__ e, int64_t T, int d, int E,
+    float* __restrict__ s) {
+    __shared__ uint4 us[ROWS_MAX_D / 8];
+    const int eblocks = (E + 255) / 256;
+    const int64_t t = blockIdx.x / eblocks;
+    const int ex = (blockIdx.x % eblocks) * 256 + threadIdx.x;
+    const bool live = ex < E;
+    const uint4* ur = reinterpret_cast<const uint4*>(u + t * d);
+    const uint4* er = reinterpret_cast<const uint4*>(e + (int64_t)(live ? ex : 0) * d);
+    const int nchunk = d / 8;
+    for (int c = threadIdx.x; c < nchunk; c += 256) us[c] = ur[c];
+
+    constexpr int G4 = 4, RING = 4;
+    const int ng = d / (8 * G4);                 // d is a multiple of 128: ng % RING == 0
+    uint4 ring[RING][G4];
+#pragma unroll
+    for (int r = 0; r < RING; ++r)
+#pragma unroll
+        for (int i = 0; i < G4; ++i) ring[r][i] = er[r * G4 + i];
+    __syncthreads();
+
+    float acc = 0.0f;
+    for (int g0 = 0; g0 < ng; g0 += RING) {
+#pragma unroll
+        for (int r = 0; r < RING; ++r) {
+#pragma unroll
+            for (int i = 0; i < G4; ++i) {
+                const uint4 uv = us[(g0 + r) * G4 + i];
+                const uint32_t ea[4] = {ring[r][i].x, ring[r][i].y, ring[r][i].z, ring[r][i].w};
+                const uint32_t ua[4] = {uv.x, uv.y, uv.z, uv.w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    acc = __builtin_fmaf(bf16_lo(ua[q]), bf16_lo(ea[q]), acc);
+                    acc = __builtin_fmaf(bf16_hi(ua[q]), bf16_hi(ea[q]), acc);
+                }
+            }
+            // refill this slot with the group RING ahead (the tail re-reads the last group)
+            const int gn = min(g0 + r + RING, ng - 1);
+#pragma unroll
+            for (int i = 0; i < G4; ++i) ring[r][i] = er[gn * G4 + i];
+        }
+    }
+    if (live) s[t * E + ex] = sigmoid_fixed(acc);
+}
+
 // One wavefront per token.  Lane l holds experts l, l+64, l+128, l+192.
 __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ s,
                                                           const float* __restrict__ bias,
@@ -227,8 +282,10 @@ hipError_t launch_router_scores(const uint16_t* u, const uint16_t* e, int64_t T,
     if (E > 64) {
         if (T >= 16384) return launch_scores<32, 256, 4, 8>(u, e, T, d, E, s, st);
         if (T >= 4096) return launch_scores<16, 256, 2, 8>(u, e, T, d, E, s, st);
-        if (T >= 1024) return launch_scores<16, 128, 2, 4>(u, e, T, d, E, s, st);
-        return launch_scores<4, 64, 1, 1>(u, e, T, d, E, s, st);
+        if (T >= 1024 || d > ROWS_MAX_D) return launch_scores<16, 128, 2, 4>(u, e, T, d, E, s, st);
+        const unsigned grid = (unsigned)(T * ((E + 255) / 256));
+        hipLaunchKernelGGL(router_scores_rows_kernel, dim3(grid), dim3(256), 0, st, u, e, T, d, E, s);
+        return hipGetLastError();
     }
     if (T >= 4096) return launch_scores<64, 64, 4, 4>(u, e, T, d, E, s, st);
     return launch_scores<16, 16, 1, 1>(u, e, T, d, E, s, st);

@@ -35,6 +35,9 @@ ROUTER_CASES = [
     (1, 128, 8, 8),           # one token, K = E
     (4096, 512, 256, 8),      # the mid-size tile
     (16384, 256, 256, 8),     # the large tile
+    (256, 7168, 256, 8),      # decode: one block per token, one logit per lane
+    (50, 256, 200, 6),        # decode layout with idle lanes (E < 256)
+    (3, 16512, 72, 4),        # u row too long for the decode layout's LDS stage
 ]
 
 
