@@ -114,7 +114,7 @@ def layer_setup(sh):
         y=torch.empty(R, d, dtype=torch.float32, device=dev),
         out=torch.empty(T, d, dtype=torch.float32, device=dev),
         dws=torch.empty(max(moe.moe_dispatch_workspace_bytes(T, E), 256), dtype=torch.uint8, device=dev),
-        gws=torch.empty(max(moe.moe_gemm_workspace_bytes(E + 1, R, max(2 * I, d)), 256), dtype=torch.uint8, device=dev),
+        gws=torch.empty(max(moe.moe_gemm_workspace_bytes(E + 1, R, max(2 * I, d), max(I, d)), 256), dtype=torch.uint8, device=dev),
     )
     return st
 

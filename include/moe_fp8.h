@@ -160,14 +160,15 @@ int fp8_quant_128x128(const float* w, int64_t rows, int cols, uint8_t* q, float*
  *        MOE_EPI_SWIGLU_QUANT: the same h, quantised per 1x128 tile with the
  *                             rule above into out_q [M_total, N/2] and
  *                             out_scale [M_total, N/256]; out may be NULL.
- *   ws   scratch of moe_gemm_workspace_bytes(G, M_total, N) bytes (the
- *        device-built tile map and tile list; its contents need no setup).
+ *   ws   scratch of moe_gemm_workspace_bytes(G, M_total, N, K) bytes (the
+ *        device-built tile map and tile list, and the A scales gathered into
+ *        GEMM row order, slice-major; its contents need no setup).
  * Limits: K % 128 == 0, N % 256 == 0 for the SwiGLU epilogues, N % 128 == 0
- * otherwise, G >= 1.
+ * otherwise, G >= 1, (M_total + 128) * K / 32 < 2^32 (the gathered A scales).
  */
-/* Scratch bytes for a grouped GEMM with G groups, M_total rows and N columns
- * (0 for G < 1, M_total < 0 or N < 1). */
-size_t moe_gemm_workspace_bytes(int G, int64_t M_total, int N);
+/* Scratch bytes for a grouped GEMM with G groups, M_total rows, N columns and
+ * inner dimension K (0 for G < 1, M_total < 0, N < 1 or K < 1). */
+size_t moe_gemm_workspace_bytes(int G, int64_t M_total, int N, int K);
 int grouped_gemm_fp8_blockscaled(const uint8_t* a_q, const float* a_scale,
                                  const int32_t* a_row_index, const int32_t* group_offset,
                                  int G, int64_t M_total, const uint8_t* b_q,

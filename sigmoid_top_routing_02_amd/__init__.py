@@ -59,7 +59,7 @@ def load_library(path: str = LIB_PATH):
         "moe_permute_rows": ([P, I32, P, I64, I32, P, P], I32),
         "fp8_quant_1x128": ([P, I32, I64, I32, P, P, P], I32),
         "fp8_quant_128x128": ([P, I64, I32, P, P, P], I32),
-        "moe_gemm_workspace_bytes": ([I32, I64, I32], SZ),
+        "moe_gemm_workspace_bytes": ([I32, I64, I32, I32], SZ),
         "grouped_gemm_fp8_blockscaled": ([P, P, P, P, I32, I64, P, P, I32, I32, I32, P, P, P, P, SZ, P], I32),
         "moe_combine": ([P, P, I32, I64, P, P, I64, I32, I32, P, P], I32),
         "moe_bias_update": ([P, P, I32, I64, F32, P], I32),
@@ -191,8 +191,8 @@ def fp8_quant_128x128(w, q=None, scale=None):
 
 
 # ---------------------------------------------------------------- grouped GEMM
-def moe_gemm_workspace_bytes(G, M_total, N):
-    return load_library().moe_gemm_workspace_bytes(G, M_total, N)
+def moe_gemm_workspace_bytes(G, M_total, N, K):
+    return load_library().moe_gemm_workspace_bytes(G, M_total, N, K)
 
 
 def grouped_gemm_fp8_blockscaled(a_q, a_scale, group_offset, M_total, b_q, b_scale,
@@ -215,7 +215,7 @@ def grouped_gemm_fp8_blockscaled(a_q, a_scale, group_offset, M_total, b_q, b_sca
         out_scale = _new((M_total, N // 256), torch.float32, a_q) if out_scale is None else out_scale
     L = load_library()
     if ws is None:
-        ws = _new((max(L.moe_gemm_workspace_bytes(G, M_total, N), 256),), torch.uint8, a_q)
+        ws = _new((max(L.moe_gemm_workspace_bytes(G, M_total, N, K), 256),), torch.uint8, a_q)
     _check(L.grouped_gemm_fp8_blockscaled(
         _ptr(a_q), _ptr(a_scale), _ptr(a_row_index), _ptr(group_offset), G, M_total, _ptr(b_q),
         _ptr(b_scale), N, K, epi, _ptr(out), _ptr(out_q), _ptr(out_scale), _ptr(ws), ws.numel(),

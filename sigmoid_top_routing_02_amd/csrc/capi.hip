@@ -155,8 +155,8 @@ int fp8_quant_128x128(const float* w, int64_t rows, int cols, uint8_t* q, float*
                       "quant 128x128 launch");
 }
 
-size_t moe_gemm_workspace_bytes(int G, int64_t M_total, int N) {
-    return (G > 0 && M_total >= 0 && N > 0) ? moe::gemm_ws_bytes(G, M_total, N) : 0;
+size_t moe_gemm_workspace_bytes(int G, int64_t M_total, int N, int K) {
+    return (G > 0 && M_total >= 0 && N > 0 && K > 0) ? moe::gemm_ws_bytes(G, M_total, N, K) : 0;
 }
 
 int grouped_gemm_fp8_blockscaled(const uint8_t* a_q, const float* a_scale,
@@ -175,6 +175,8 @@ int grouped_gemm_fp8_blockscaled(const uint8_t* a_q, const float* a_scale,
     REQUIRE(((M_total + 31) / 32 + G) * ((N + 255) / 256) < ((int64_t)1 << 31), MOE_ERR_UNSUPPORTED,
             "grouped_gemm: too many tiles");
     REQUIRE((int64_t)N * K < ((int64_t)1 << 32), MOE_ERR_UNSUPPORTED, "grouped_gemm: one group's B exceeds 4 GiB");
+    REQUIRE((M_total + 128) * (K / 128) * 4 < ((int64_t)1 << 32), MOE_ERR_UNSUPPORTED,
+            "grouped_gemm: the A scales of M_total=%lld rows exceed 4 GiB", (long long)M_total);
     if (M_total == 0) return MOE_OK;
     REQUIRE_PTR(a_q);
     REQUIRE_PTR(a_scale);
@@ -190,8 +192,8 @@ int grouped_gemm_fp8_blockscaled(const uint8_t* a_q, const float* a_scale,
         REQUIRE_PTR(out);
     }
     REQUIRE_PTR(ws);
-    REQUIRE(ws_bytes >= moe::gemm_ws_bytes(G, M_total, N), MOE_ERR_WORKSPACE,
-            "grouped_gemm: workspace %zu < %zu bytes", ws_bytes, moe::gemm_ws_bytes(G, M_total, N));
+    REQUIRE(ws_bytes >= moe::gemm_ws_bytes(G, M_total, N, K), MOE_ERR_WORKSPACE,
+            "grouped_gemm: workspace %zu < %zu bytes", ws_bytes, moe::gemm_ws_bytes(G, M_total, N, K));
     return hip_status(moe::launch_grouped_gemm(a_q, a_scale, a_row_index, group_offset, G, M_total,
                                                b_q, b_scale, N, K, epi, out, out_q, out_scale, ws,
                                                S(stream)),
@@ -323,7 +325,7 @@ LayerWs layer_ws(void* base, int64_t T, int d, int E, int K, int I) {
     w.hs = reinterpret_cast<float*>(take(R * (I / 128) * 4));
     w.y = reinterpret_cast<float*>(take(R * d * 4));
     w.dws = take(moe::dispatch_ws_bytes(T, E));
-    w.gws = take(moe::gemm_ws_bytes(E + 1, R, 2 * I > d ? 2 * I : d));   // shared by both GEMMs
+    w.gws = take(moe::gemm_ws_bytes(E + 1, R, 2 * I > d ? 2 * I : d, I > d ? I : d));   // shared by both GEMMs
     w.total = off;
     return w;
 }

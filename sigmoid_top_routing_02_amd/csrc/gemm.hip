@@ -80,7 +80,8 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 struct GemmArgs {
     const uint8_t* a_q;
-    const float* a_s;
+    const float* a_sT;            // A scales slice-major: [K/128][M_total], in GEMM row order
+    uint32_t sa_stride;           // M_total * 4: bytes from one slice's scales to the next
     const int32_t* a_rows;
     const int32_t* group_offset;
     const int32_t* tile_start;
@@ -106,9 +107,9 @@ __shared__ __attribute__((aligned(1024))) char g_a2[A_MAX_BYTES];
 __shared__ __attribute__((aligned(1024))) char g_b0[B_BYTES];
 __shared__ __attribute__((aligned(1024))) char g_b1[B_BYTES];
 __shared__ __attribute__((aligned(1024))) char g_b2[B_BYTES];
-// A scales of a slice: wave w DMAs rows (64w + lane) mod BM into its own
-// 256-byte copy, so all waves issue the same DMA count with no lane-dependent
-// branch; row r < BM is then at float index r.
+// A scales of a slice: wave w DMAs rows 64w .. 64w+63 of the tile into floats
+// 64w .. 64w+63 (the waves past the tile's rows issue a DMA that touches no
+// memory, so every wave issues the same count); row r < BM is at float r.
 __shared__ __attribute__((aligned(16))) float g_sa0[64 * NWAVES];
 __shared__ __attribute__((aligned(16))) float g_sa1[64 * NWAVES];
 __shared__ __attribute__((aligned(16))) float g_sa2[64 * NWAVES];
@@ -246,7 +247,8 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
 
     // ---- per-tile DMA sources (byte offsets; the slice moves soffset)
     const auto a_rsrc = make_rsrc(p.a_q, 0xFFFFFFFFu);
-    const auto sa_rsrc = make_rsrc(p.a_s, 0xFFFFFFFFu);
+    // every row past M_total (the padding of the last tile) reads scale 0
+    const auto sa_rsrc = make_rsrc(p.a_sT, p.sa_stride * (uint32_t)ns);
     // A descriptor with no records: every access is out of range, so no memory
     // is touched (the target stage is a spare one).  Past the last slice the
     // pipeline still issues its DMAs through this descriptor, which keeps the
@@ -255,16 +257,14 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
     const auto null_rsrc = make_rsrc(p.a_q, 0u);
     const int nblk_per_g = p.N / 128;
     uint32_t a_off[A_DMA], b_off[2], sa_off = 0;
-    uint32_t am_pre[A_DMA + 1];                  // gathered A rows of the next tile's DMA lanes
+    uint32_t am_pre[A_DMA];                      // gathered A rows of the next tile's DMA lanes
     __amdgpu_buffer_rsrc_t b_rsrc = null_rsrc;
-    // A-row indices of this lane's A DMAs and of its A-scale DMA (the gather)
+    // A-row indices of this lane's A DMAs (the gather)
     auto load_rows = [&](const Tile& T) {
 #pragma unroll
-        for (int i = 0; i <= A_DMA; ++i) {
-            // A DMA li = wave*A_DMA + i fills LDS bytes [li*1 KiB, +1 KiB): copy li / A_INSTR;
-            // the A-scale DMA of wave w covers rows (64w + lane) mod BM
-            const int r = (i < A_DMA) ? ((wave * A_DMA + i) % C::A_INSTR) * 8 + (lane >> 3)
-                                      : (wave * 64 + lane) % BM;
+        for (int i = 0; i < A_DMA; ++i) {
+            // A DMA li = wave*A_DMA + i fills LDS bytes [li*1 KiB, +1 KiB): copy li / A_INSTR
+            const int r = ((wave * A_DMA + i) % C::A_INSTR) * 8 + (lane >> 3);
             const int m = T.m0 + min(r, T.rows - 1);
             am_pre[i] = p.a_rows ? (uint32_t)p.a_rows[m] : (uint32_t)m;
         }
@@ -275,7 +275,9 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
             const int r = ((wave * A_DMA + i) % C::A_INSTR) * 8 + (lane >> 3);
             a_off[i] = am_pre[i] * (uint32_t)K + ((lane & 7) ^ swz(r)) * 16;
         }
-        sa_off = am_pre[A_DMA] * (uint32_t)ns * 4u;
+        // A scales: the tile's rows are contiguous in the slice-major copy; wave w
+        // moves rows 64w .. 64w+63 (waves past the tile's rows move nothing)
+        sa_off = (uint32_t)(T.m0 + wave * 64 + lane) * 4u;
         b_rsrc = make_rsrc(p.b_q + (int64_t)T.g * p.N * K, (uint32_t)p.N * (uint32_t)K);
         // B rows of DMA i are r0 + 8i; the swizzle of r0 + 8i only depends on i & 1
 #pragma unroll
@@ -302,7 +304,8 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
             lds_dma16(live ? b_rsrc : null_rsrc, b_off[i & 1] + (uint32_t)((i & ~1) * 8) * (uint32_t)K, koff,
                       b_buf<ST>() + (wave * B_DMA + i) * 1024);
         } else {
-            lds_dma4(live ? sa_rsrc : null_rsrc, sa_off, live ? (uint32_t)slice * 4u : 0u,
+            lds_dma4((live && wave * 64 < BM) ? sa_rsrc : null_rsrc, sa_off,
+                     live ? (uint32_t)slice * p.sa_stride : 0u,
                      reinterpret_cast<char*>(sa_buf<ST>()) + wave * 256);
         }
     };
@@ -331,46 +334,97 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
 
     v4f acc[MI][NI];
 
-    // Stage barriers: wait for this wave's DMAs of the next slice (newer ones
-    // may stay in flight) and for its own LDS reads, then s_barrier.  A plain
-    // __syncthreads() would also drain every outstanding DMA (vmcnt(0)) and
-    // serialise the pipeline.  The "memory" clobber keeps the compiler from
-    // moving LDS accesses across it.
+    // Ping-pong schedule.  The waves form two groups, waves 0-3 and 4-7, one
+    // wave of each on every SIMD.  Every wave works a slice in two phases: a
+    // memory phase (read the slice's A and B fragments and scales from LDS
+    // into registers, issue the DMAs of slice s+2) and a matrix phase (the 16
+    // MFMAs and the scale FMAs, registers only), with a workgroup barrier
+    // before each phase.  Both groups run the same instruction stream, but
+    // group 1 passes one extra barrier when a tile starts (and group 0 one
+    // when it ends), so group 1 is one phase behind:
+    //     phase 2s:   group 0 memory(s),  group 1 matrix(s-1)
+    //     phase 2s+1: group 0 matrix(s),  group 1 memory(s)
+    // and on each SIMD one wave feeds the matrix core while the other loads.
+    // Stage reuse: the DMAs of slice s+2 (issued in phases 2s and 2s+1) go to
+    // the stage of slice s-1, whose last reader (group 1, phase 2s-1) finished
+    // before the barrier that opens phase 2s.  Data: the barrier that opens
+    // phase 2s must see every wave's DMAs of slice s complete.  For group 0
+    // it precedes memory(s), and its newer DMAs are those of slice s+1; for
+    // group 1 it precedes matrix(s-1), and its newer DMAs are again those of
+    // slice s+1: both wait for vmcnt(D).  The barrier before group 0's matrix
+    // phase has no data to wait for (slices s+1 and s+2 may be in flight:
+    // vmcnt(2D)).  The "memory" clobber keeps the compiler from moving LDS
+    // accesses across a barrier, the scheduling barriers keep it from moving
+    // MFMAs across.
 #define MOE_STAGE_BARRIER(N) asm volatile("s_waitcnt vmcnt(" #N ") lgkmcnt(0)\n\ts_barrier" ::: "memory")
-    auto stage_barrier = [&]() {
+    const bool lead = wave < NWAVES / 2;           // group 0
+    auto barrier_mem = [&]() {                     // opens a memory phase
+        __builtin_amdgcn_sched_barrier(0);
         if constexpr (D == 7) MOE_STAGE_BARRIER(7);
         else MOE_STAGE_BARRIER(6);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // opens a matrix phase.  The wait count depends on the group; it is chosen
+    // inside one asm block (every lane of a wave gives the same comparison, so
+    // vcc is all ones or all zeros) so that the K loop has no branch the
+    // compiler can see: a visible one costs registers and lets it move the
+    // scale FMAs across barriers.
+    auto barrier_mat = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (D == 7)
+            asm volatile("v_cmp_gt_u32 vcc, %0, %1\n\ts_cbranch_vccz 1f\n\ts_waitcnt vmcnt(14)\n\ts_branch 2f\n"
+                         "1:\n\ts_waitcnt vmcnt(7)\n2:\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier"
+                         :: "n"(NT / 2), "v"(tid) : "memory", "vcc");
+        else
+            asm volatile("v_cmp_gt_u32 vcc, %0, %1\n\ts_cbranch_vccz 1f\n\ts_waitcnt vmcnt(12)\n\ts_branch 2f\n"
+                         "1:\n\ts_waitcnt vmcnt(6)\n2:\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier"
+                         :: "n"(NT / 2), "v"(tid) : "memory", "vcc");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto plain_barrier = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
     };
 
-    // One K slice on stage ST; the DMAs for slice s+2 go to the stage that
-    // slice s-1 used (every wave has passed the barrier after reading it).
-    auto slice_step = [&](auto stc, int s, auto firstc) {
+    // The slice a wave is working on, as its memory phase left it.
+    constexpr int NC = TR ? 1 : 4;
+    v8i bfr[NI], afr[MI];
+    float sav[MI][NC];
+    float sb0 = 0.f, sb1 = 0.f;
+
+    // Memory phase of slice s on stage ST.  A tile's first slice also issues
+    // slice 1 (the tile prologue issues slice 0 only).
+    auto mem_phase = [&](auto stc, int s, auto firstc) {
         constexpr int ST = decltype(stc)::value;
-        // a tile's first step also issues slice 1 (the tile prologue issues
-        // slice 0 only, so the DMAs of a tile switch are spread over MFMAs)
         constexpr bool FIRST = decltype(firstc)::value;
-        constexpr int NEXT = (ST + NS - 1) % NS;     // stage that slice s-1 used
         const char* At = a_buf<ST, BM>();
         const char* Bt = b_buf<ST>();
         const float* SAt = sa_buf<ST>();
-
-        const float sb0 = g_bscale[sbrow0 * MAX_SLICES + s];
-        const float sb1 = g_bscale[sbrow1 * MAX_SLICES + s];
-
-        // The wave's B fragments stay in registers for the slice and the row
-        // tiles are walked in a software pipeline.  The order is pinned (a
-        // scheduling barrier after each MFMA): MFMA (mi, ni), then the four
-        // scale FMAs of (mi-1, ni), whose partial finished four MFMAs earlier;
-        // the A fragment and scale of row tile mi+1 are read after the first
-        // MFMA of row tile mi.  The DMAs of slice s+2 are spread evenly over
-        // the MFMAs: issued back to back they stall the wave until the memory
-        // pipeline accepts them, keeping it off the matrix core.
-        v8i bfr[NI];
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) bfr[ni] = frag(Bt, ncol<EPI, C>(0, ni) * 128, b_lo0, b_lo1);
-        // Scales: with B first a lane's four results share one row (lr) and
-        // one scale; with A first they are rows 4*kb + j of one column.
-        constexpr int NC = TR ? 1 : 4;
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) {
+            afr[mi] = frag(At, mi * 16 * 128, a_lo0, a_lo1);
+            // scales: with B first a lane's four results share one row (lr) and
+            // one scale; with A first they are rows 4*kb + j of one column
+            if constexpr (TR) {
+                sav[mi][0] = SAt[sa_row + mi * 16];
+            } else {
+                const float4 t = *reinterpret_cast<const float4*>(SAt + wm * WROWS + 4 * kb + mi * 16);
+                sav[mi][0] = t.x; sav[mi][1] = t.y; sav[mi][2] = t.z; sav[mi][3] = t.w;
+            }
+        }
+        sb0 = g_bscale[sbrow0 * MAX_SLICES + s];
+        sb1 = g_bscale[sbrow1 * MAX_SLICES + s];
+        if constexpr (FIRST) issue(IC<(ST + 1) % NS>{}, s + 1);
+        issue(IC<(ST + 2) % NS>{}, s + 2);
+    };
+
+    // Matrix phase: MFMA (mi, ni), then the four scale FMAs of (mi-1, ni),
+    // whose partial finished four MFMAs earlier (the order is pinned by a
+    // scheduling barrier after each MFMA).
+    auto mat_phase = [&]() {
         auto fma4 = [&](const v4f& part, int mi, int ni, const float (&c0)[NC], const float (&c1)[NC]) {
             const bool second = (EPI != EPI_STORE_F32) && ni >= NI / 2;
 #pragma unroll
@@ -379,57 +433,26 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
                 acc[mi][ni][j] = __builtin_fmaf(part[j], c, acc[mi][ni][j]);
             }
         };
-        // this lane's A scales of row tile mi: one row (B first) or four (A first)
-        auto read_sa = [&](int mi, float (&v)[NC]) {
-            if constexpr (TR) {
-                v[0] = SAt[sa_row + mi * 16];
-            } else {
-                const float4 t = *reinterpret_cast<const float4*>(SAt + wm * WROWS + 4 * kb + mi * 16);
-                v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
-            }
-        };
-        v8i anext = frag(At, 0, a_lo0, a_lo1);
-        float sanext[NC];
-        read_sa(0, sanext);
         v4f prev[NI];
         float p0[NC], p1[NC];
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi) {
-            const v8i af = anext;
-            float sa[NC];
-#pragma unroll
-            for (int j = 0; j < NC; ++j) sa[j] = sanext[j];
             float q0[NC], q1[NC];
             v4f cur[NI];
 #pragma unroll
             for (int ni = 0; ni < NI; ++ni) {
                 if constexpr (TR)
                     cur[ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        bfr[ni], af, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+                        bfr[ni], afr[mi], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
                 else
                     cur[ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        af, bfr[ni], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-                {
-                    constexpr int Q = MI * NI;
-                    constexpr int DD = FIRST ? 2 * D : D;
-                    const int q = mi * NI + ni;
-#pragma unroll
-                    for (int k = 0; k < DD; ++k)
-                        if ((k * Q) / DD == q) {
-                            if (FIRST && k < D) issue_one(IC<(ST + 1) % 3>{}, s + 1, k);
-                            else issue_one(IC<NEXT>{}, s + NS - 1, FIRST ? k - D : k);
-                        }
-                }
-                if (ni == 0 && mi + 1 < MI) {
-                    anext = frag(At, (mi + 1) * 16 * 128, a_lo0, a_lo1);
-                    read_sa(mi + 1, sanext);
-                }
+                        afr[mi], bfr[ni], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
                 if (mi > 0) fma4(prev[ni], mi - 1, ni, p0, p1);
                 if (ni == NI - 1) {
 #pragma unroll
                     for (int j = 0; j < NC; ++j) {
-                        q0[j] = sa[j] * sb0;
-                        q1[j] = (EPI != EPI_STORE_F32) ? sa[j] * sb1 : 0.f;
+                        q0[j] = sav[mi][j] * sb0;
+                        q1[j] = (EPI != EPI_STORE_F32) ? sav[mi][j] * sb1 : 0.f;
                     }
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -441,8 +464,14 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
         }
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) fma4(prev[ni], MI - 1, ni, p0, p1);
-        // slice s+1 must have landed (slice s+2 may still be in flight)
-        stage_barrier();
+    };
+
+    // memory and matrix phase of a slice s >= 1 on stage ST
+    auto slice_pair = [&](auto stc, int s) {
+        barrier_mem();
+        mem_phase(stc, s, std::false_type{});
+        barrier_mat();
+        mat_phase();
     };
 
     // FP32-store epilogue (A-first layout: lane holds rows 4*kb + j of column lr)
@@ -579,25 +608,22 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
         // slice 0 landed (it and the previous tile's stores are all that is in
         // flight: a full wait); also publishes the B scales
         MOE_STAGE_BARRIER(0);
+        __builtin_amdgcn_sched_barrier(0);
 
+        if (!lead) plain_barrier();                // group 1: one phase behind
+        mem_phase(IC<0>{}, 0, std::true_type{});
+        barrier_mat();
+        mat_phase();
         // whole rounds of three stages, then the remaining one or two slices
-        using First = std::true_type;
-        using Later = std::false_type;
-        slice_step(IC<0>{}, 0, First{});
         int s = 1;
-        if (ns >= 3) {
-            slice_step(IC<1>{}, 1, Later{});
-            slice_step(IC<2>{}, 2, Later{});
-            for (s = 3; s + 3 <= ns; s += 3) {
-                slice_step(IC<0>{}, s, Later{});
-                slice_step(IC<1>{}, s + 1, Later{});
-                slice_step(IC<2>{}, s + 2, Later{});
-            }
-            if (s < ns) slice_step(IC<0>{}, s, Later{});
-            if (s + 1 < ns) slice_step(IC<1>{}, s + 1, Later{});
-        } else if (ns == 2) {
-            slice_step(IC<1>{}, 1, Later{});
+        for (; s + 3 <= ns; s += 3) {
+            slice_pair(IC<1>{}, s);
+            slice_pair(IC<2>{}, s + 1);
+            slice_pair(IC<0>{}, s + 2);
         }
+        if (s < ns) slice_pair(IC<1>{}, s);
+        if (s + 1 < ns) slice_pair(IC<2>{}, s + 1);
+        if (lead) plain_barrier();                 // group 0: catch up
         MOE_STAGE_BARRIER(0);      // drain the spare-stage DMAs before LDS is reused
 
         // next tile: its index was requested when this tile started
@@ -677,6 +703,28 @@ __global__ __launch_bounds__(256) void gemm_tile_list_kernel(const int32_t* __re
     tiles[t] = make_int4(lo, m0, min(BM, go[lo + 1] - m0), (in_chunk / chunk_rows) * BN);
 }
 
+// a_sT[j][m] = a_s[am][j] with am = a_rows[m] (or m): the A scales gathered
+// into GEMM row order and made slice-major, so that the scales of one slice
+// for a tile's rows are contiguous.  One block per 64 rows, through LDS.
+__global__ __launch_bounds__(256) void gemm_scale_gather_kernel(const float* __restrict__ a_s,
+                                                                const int32_t* __restrict__ a_rows,
+                                                                int64_t M_total, int ns,
+                                                                float* __restrict__ a_sT) {
+    __shared__ float t[64][MAX_SLICES + 1];
+    const int64_t m0 = (int64_t)blockIdx.x * 64;
+    for (int i = threadIdx.x; i < 64 * ns; i += 256) {
+        const int r = i / ns, j = i - r * ns;
+        const int64_t m = m0 + r;
+        if (m < M_total) t[r][j] = a_s[(a_rows ? (int64_t)a_rows[m] : m) * ns + j];
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < 64 * ns; i += 256) {
+        const int j = i >> 6, r = i & 63;
+        const int64_t m = m0 + r;
+        if (m < M_total) a_sT[j * M_total + m] = t[r][j];
+    }
+}
+
 int cu_count_for_current_device() {
     static int cached[64] = {0};
     int dev = 0;
@@ -691,14 +739,18 @@ int cu_count_for_current_device() {
 
 }  // namespace
 
-// [tile_start: G+1][counters: 8] (16-byte aligned) [tile list: int4 per tile, bound for 32-row tiles]
+// [tile_start: G+1][counters: 8] (16-byte aligned) [tile list: int4 per tile, bound for
+// 32-row tiles] (256-byte aligned) [A scales, slice-major: K/128 x M_total FP32]
 static int64_t tile_list_offset(int G) { return ((int64_t)(G + 1 + 8) * 4 + 15) / 16 * 16; }
 static int64_t tile_bound(int G, int64_t M_total, int N) {
     return ((M_total + 31) / 32 + G) * (int64_t)((N + BN - 1) / BN);
 }
+static int64_t scale_copy_offset(int G, int64_t M_total, int N) {
+    return (tile_list_offset(G) + tile_bound(G, M_total, N) * 16 + 255) / 256 * 256;
+}
 
-size_t gemm_ws_bytes(int G, int64_t M_total, int N) {
-    return (size_t)(tile_list_offset(G) + tile_bound(G, M_total, N) * 16);
+size_t gemm_ws_bytes(int G, int64_t M_total, int N, int K) {
+    return (size_t)(scale_copy_offset(G, M_total, N) + (int64_t)(K / BK) * M_total * 4);
 }
 
 hipError_t launch_grouped_gemm(const uint8_t* a_q, const float* a_s, const int32_t* a_rows,
@@ -708,13 +760,18 @@ hipError_t launch_grouped_gemm(const uint8_t* a_q, const float* a_s, const int32
                                hipStream_t st) {
     int32_t* ts = static_cast<int32_t*>(ws);
     int4* tiles = reinterpret_cast<int4*>(static_cast<char*>(ws) + tile_list_offset(G));
+    float* a_sT = reinterpret_cast<float*>(static_cast<char*>(ws) + scale_copy_offset(G, M_total, N));
+    const int ns = K / BK;
+    hipLaunchKernelGGL(gemm_scale_gather_kernel, dim3((unsigned)((M_total + 63) / 64)), dim3(256), 0, st,
+                       a_s, a_rows, M_total, ns, a_sT);
     // 32-row tiles when the groups average at most 64 rows (few tokens per expert)
     const int bm = (M_total <= (int64_t)64 * G) ? 32 : 128;
     hipLaunchKernelGGL(gemm_tile_map_kernel, dim3(1), dim3(256), 0, st, group_offset, G, bm, ts);
     const int64_t list_bound = ((M_total + bm - 1) / bm + G) * (int64_t)((N + BN - 1) / BN);
     hipLaunchKernelGGL(gemm_tile_list_kernel, dim3((unsigned)((list_bound + 255) / 256)), dim3(256), 0, st,
                        group_offset, ts, G, bm, N, tiles);
-    GemmArgs p{a_q, a_s, a_rows, group_offset, ts, ts + G + 1, tiles, G, b_q, b_s, N, K, out, out_q, out_s};
+    GemmArgs p{a_q, a_sT, (uint32_t)(M_total * 4), a_rows, group_offset, ts, ts + G + 1, tiles, G, b_q, b_s, N, K,
+               out, out_q, out_s};
     const int64_t blocks = list_bound;
     // one block per CU (its ~150 KB of LDS admit one), a multiple of the 8 XCDs
     const int64_t persistent = ((int64_t)cu_count_for_current_device() + 7) / 8 * 8;

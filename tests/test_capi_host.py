@@ -72,10 +72,14 @@ def test_quant_and_gemm_argument_errors(L):
     assert L.fp8_quant_1x128(FAKE, 0, 4, 100, FAKE, FAKE, None) == -2
     assert L.fp8_quant_1x128(FAKE, 7, 4, 128, FAKE, FAKE, None) == -3
     assert L.fp8_quant_128x128(FAKE, 100, 128, FAKE, FAKE, None) == -2
-    gw = L.moe_gemm_workspace_bytes(3, 10, 256)
+    gw = L.moe_gemm_workspace_bytes(3, 10, 256, 128)
     assert gw >= 16
-    assert L.moe_gemm_workspace_bytes(3, 10_000, 7168) > L.moe_gemm_workspace_bytes(3, 10, 7168)
-    assert L.moe_gemm_workspace_bytes(0, 10, 256) == 0
+    assert L.moe_gemm_workspace_bytes(3, 10_000, 7168, 128) > L.moe_gemm_workspace_bytes(3, 10, 7168, 128)
+    # the gathered A scales: 4 bytes per row and 128-wide slice
+    assert (L.moe_gemm_workspace_bytes(3, 10_000, 7168, 1024) - L.moe_gemm_workspace_bytes(3, 10_000, 7168, 128)
+            == 10_000 * 7 * 4)
+    assert L.moe_gemm_workspace_bytes(0, 10, 256, 128) == 0
+    assert L.moe_gemm_workspace_bytes(3, 10, 256, 0) == 0
     # K not a multiple of 128
     assert L.grouped_gemm_fp8_blockscaled(FAKE, FAKE, None, FAKE, 3, 10, FAKE, FAKE, 256, 100, 0,
                                           FAKE, None, None, FAKE, gw, None) == -2
