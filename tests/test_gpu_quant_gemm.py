@@ -84,6 +84,10 @@ def _int_operands(M, N, K, G, seed):
 # The library takes 128-row tiles when the groups average more than 64 rows
 # and 32-row tiles otherwise; the cases below cover both.
 @pytest.mark.parametrize("sizes,N,K", [
+    ([600, 0, 900], 512, 384),         # large ragged groups incl. an empty one (128-row tiles)
+    ([513], 384, 256),                 # N % 256 == 128, one row in the last tile (128)
+    ([1024], 256, 128),                # a single K slice (128)
+    ([768, 400], 256, 640),            # five slices: the three-stage remainder (128)
     ([128], 256, 128),                 # one tile (128-row tiles)
     ([1], 256, 256),                   # one row (32-row tiles)
     ([200, 0, 57, 128, 1], 512, 384),  # ragged groups incl. an empty one (128)
@@ -159,7 +163,7 @@ def _interleave(w1, w3):
     return out
 
 
-@pytest.mark.parametrize("sizes,I,d", [([130, 0, 77, 256], 256, 512), ([64], 512, 256),
+@pytest.mark.parametrize("sizes,I,d", [([130, 0, 77, 256], 256, 512), ([64], 512, 256), ([700, 300], 256, 640),
                                        ([9, 0, 33, 12, 50], 256, 512)])
 def test_gemm_swiglu_epilogues(sizes, I, d):
     """SwiGLU FP32 h against the oracle's FP64 h; the fused quantising
