@@ -399,7 +399,7 @@ def run_dense(steps, warmup, K=4096):
     del a, b
     go = torch.tensor([0, M], dtype=torch.int32, device="cuda")
     out = torch.empty(M, N, dtype=torch.float32, device="cuda")
-    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    ws = torch.empty(max(moe.moe_gemm_workspace_bytes(1, M, N, K), 256), dtype=torch.uint8, device="cuda")
     bq3, bs3 = bq.view(1, N, K), bs.view(1, N // 128, K // 128)
     for _ in range(warmup):
         moe.grouped_gemm_fp8_blockscaled(aq, as_, go, M, bq3, bs3, out=out, ws=ws)
