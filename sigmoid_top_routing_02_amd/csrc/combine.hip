@@ -17,20 +17,11 @@
 namespace moe {
 namespace {
 
-template <bool Y_F32>
-__device__ __forceinline__ float4 load_y4(const void* y, int64_t row, int d, int c4) {
-    if constexpr (Y_F32) {
-        return reinterpret_cast<const float4*>(static_cast<const float*>(y) + row * d)[c4];
-    } else {
-        const uint2 w = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(y) + row * d)[c4];
-        return make_float4(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y));
-    }
-}
-
-// One block per token row (grid-strided); each thread owns one or two 4-column
-// chunks.  All K + 2 row loads of a chunk are issued before the first
-// arithmetic, so a wave keeps up to 2 * (K + 2) loads in flight instead of waiting
-// for them one by one; the arithmetic then runs in the fixed order above.
+// One block per token row (grid-strided); each thread owns one or two chunks of
+// VEC columns (4 for FP32 Y, 8 for bf16 Y: every Y load is 16 bytes).  All
+// K + 2 row loads of a chunk are issued before the first arithmetic, so a wave
+// keeps up to 2 * (K + 2) loads in flight instead of waiting for them one by
+// one; the arithmetic then runs in the fixed order above.
 template <bool Y_F32, int KMAX>
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ u,
                                                       const void* __restrict__ y,
@@ -39,8 +30,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
                                                       const int32_t* __restrict__ slot_row,
                                                       int64_t T, int K, int d,
                                                       float* __restrict__ out) {
-    constexpr int CH = KMAX > 8 ? 1 : 2;        // 4-column chunks per thread per pass
-    const int d4 = d / 4;
+    constexpr int CH = KMAX > 8 ? 1 : 2;        // chunks per thread per pass
+    constexpr int VEC = Y_F32 ? 4 : 8;          // columns per chunk
+    constexpr int UW = VEC / 4;                 // uint2 words of u per chunk
+    const int dv = d / VEC;
+    const uint4* yv = static_cast<const uint4*>(y);
+    const int64_t yrow = (int64_t)d / (Y_F32 ? 4 : 8);   // uint4 per Y row
     for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
         float g[KMAX];
         int64_t r[KMAX];
@@ -49,36 +44,63 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
             g[k] = k < K ? gate[t * K + k] : 0.0f;
             r[k] = k < K ? slot_row[t * K + k] : 0;
         }
-        for (int base = threadIdx.x; base < d4; base += 256 * CH) {
-            float4 v[CH], sh[CH], yk[CH][KMAX];
+        for (int base = threadIdx.x; base < dv; base += 256 * CH) {
+            uint2 uw[CH][UW];
+            uint4 sh[CH], yk[CH][KMAX];
 #pragma unroll
             for (int c = 0; c < CH; ++c) {
-                const int c4 = base + c * 256;
-                if (c4 >= d4) continue;
-                const uint2 uw = reinterpret_cast<const uint2*>(u + t * d)[c4];
-                v[c] = make_float4(bf16_lo(uw.x), bf16_hi(uw.x), bf16_lo(uw.y), bf16_hi(uw.y));
-                if (shared_row0 >= 0) sh[c] = load_y4<Y_F32>(y, shared_row0 + t, d, c4);
+                const int cv = base + c * 256;
+                if (cv >= dv) continue;
+#pragma unroll
+                for (int w = 0; w < UW; ++w) uw[c][w] = reinterpret_cast<const uint2*>(u + t * d)[cv * UW + w];
+                if (shared_row0 >= 0) sh[c] = yv[(shared_row0 + t) * yrow + cv];
 #pragma unroll
                 for (int k = 0; k < KMAX; ++k)
-                    if (k < K) yk[c][k] = load_y4<Y_F32>(y, r[k], d, c4);
+                    if (k < K) yk[c][k] = yv[r[k] * yrow + cv];
             }
 #pragma unroll
             for (int c = 0; c < CH; ++c) {
-                const int c4 = base + c * 256;
-                if (c4 >= d4) continue;
-                float4 a = v[c];
+                const int cv = base + c * 256;
+                if (cv >= dv) continue;
+                float a[VEC];
+#pragma unroll
+                for (int w = 0; w < UW; ++w) {
+                    a[4 * w + 0] = bf16_lo(uw[c][w].x);
+                    a[4 * w + 1] = bf16_hi(uw[c][w].x);
+                    a[4 * w + 2] = bf16_lo(uw[c][w].y);
+                    a[4 * w + 3] = bf16_hi(uw[c][w].y);
+                }
+                // the four 32-bit words of a 16-byte Y load, as VEC floats
+                auto expand = [&](const uint4& v, float (&f)[VEC]) {
+                    const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+                    if constexpr (Y_F32) {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) f[q] = __uint_as_float(wd[q]);
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            f[2 * q] = bf16_lo(wd[q]);
+                            f[2 * q + 1] = bf16_hi(wd[q]);
+                        }
+                    }
+                };
                 if (shared_row0 >= 0) {
-                    a.x = a.x + sh[c].x; a.y = a.y + sh[c].y; a.z = a.z + sh[c].z; a.w = a.w + sh[c].w;
+                    float f[VEC];
+                    expand(sh[c], f);
+#pragma unroll
+                    for (int q = 0; q < VEC; ++q) a[q] = a[q] + f[q];
                 }
 #pragma unroll
                 for (int k = 0; k < KMAX; ++k) {
                     if (k >= K) break;
-                    a.x = __builtin_fmaf(g[k], yk[c][k].x, a.x);
-                    a.y = __builtin_fmaf(g[k], yk[c][k].y, a.y);
-                    a.z = __builtin_fmaf(g[k], yk[c][k].z, a.z);
-                    a.w = __builtin_fmaf(g[k], yk[c][k].w, a.w);
+                    float f[VEC];
+                    expand(yk[c][k], f);
+#pragma unroll
+                    for (int q = 0; q < VEC; ++q) a[q] = __builtin_fmaf(g[k], f[q], a[q]);
                 }
-                reinterpret_cast<float4*>(out + t * d)[c4] = a;
+                float4* o = reinterpret_cast<float4*>(out + t * d) + cv * (VEC / 4);
+#pragma unroll
+                for (int w = 0; w < VEC / 4; ++w) o[w] = make_float4(a[4 * w], a[4 * w + 1], a[4 * w + 2], a[4 * w + 3]);
             }
         }
     }
