@@ -33,8 +33,9 @@ ROUTER_CASES = [
     (300, 1024, 256, 8),      # full expert count, ragged T
     (1000, 384, 40, 6),       # E not a multiple of 64
     (1, 128, 8, 8),           # one token, K = E
-    (4096, 512, 256, 8),      # the mid-size tile
-    (16384, 256, 256, 8),     # the large tile
+    (4096, 512, 256, 8),      # the 32 x 128 tile, fewest tokens
+    (16384, 256, 256, 8),     # the 32 x 128 tile, many blocks
+    (8200, 128, 256, 8),      # the 32 x 128 tile with a ragged last block
     (256, 7168, 256, 8),      # decode: one block per token, one logit per lane
     (50, 256, 200, 6),        # decode layout with idle lanes (E < 256)
     (3, 16512, 72, 4),        # u row too long for the decode layout's LDS stage
