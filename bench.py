@@ -396,6 +396,10 @@ def run_dense(steps, warmup, K=4096):
     a, b = workloads.dense_operands(M, N, K, device="cuda")
     aq, as_ = moe.fp8_quant_1x128(a)
     bq, bs = moe.fp8_quant_128x128(b)
+    # rows checked after timing: first, last and six seeded others
+    rows = sorted({0, M - 1} | set(np.random.default_rng(11).integers(0, M, 6).tolist()))
+    a_rows = a[rows].double().cpu()
+    b_host = b.cpu()
     del a, b
     go = torch.tensor([0, M], dtype=torch.int32, device="cuda")
     out = torch.empty(M, N, dtype=torch.float32, device="cuda")
@@ -415,6 +419,8 @@ def run_dense(steps, warmup, K=4096):
     flops = 2.0 * M * N * K
     g_ms = ev.avg_ms("gemm")
     ach = flops / (g_ms * 1e-3) / 1e12
+    err = dense_errors(out, aq, as_, bq, bs, rows, a_rows, b_host)
+    del b_host
     return {
         "metric": "block-scaled FP8 GEMM TFLOP/s", "value": round(flops / (ms * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 4),
@@ -423,7 +429,30 @@ def run_dense(steps, warmup, K=4096):
         "roofline": {"kernel": "grouped_gemm_fp8_blockscaled (1 group)", "bound": "mfma",
                      "achieved": round(ach, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(ach / PEAK_FP8_TFLOPS, 4), "traffic": traffic_for(f"dense_k{K}", "gemm.hip")},
+        "error": err,
     }
+
+
+def dense_errors(out, aq, as_, bq, bs, rows, a_rows, b_host):
+    """Per-row infinity-norm relative error of sampled output rows against the
+    FP64 product of the dequantised operands (the GEMM's own contract) and
+    against the FP64 product of the unquantised operands (the quantisation
+    error), computed with plain torch on the host."""
+    def deq(q, sc, rep_rows):
+        v = q.view(torch.float8_e4m3fn).cpu().double()
+        s = sc.cpu().double().repeat_interleave(128, dim=1)
+        if rep_rows:
+            s = s.repeat_interleave(128, dim=0)
+        return v * s[: v.shape[0], : v.shape[1]]
+    da = deq(aq[rows], as_[rows], False)
+    db = deq(bq, bs, True)
+    got = out[rows].double().cpu()
+    ref_q = da @ db.T
+    ref_u = a_rows @ b_host.double().T
+    rel = lambda x, r: float(((x - r).abs().amax(dim=1) / r.abs().amax(dim=1)).max())
+    return {"rows": len(rows), "norm": "per-row inf-norm relative, max over rows",
+            "vs_fp64_of_dequantised": round(rel(got, ref_q), 8),
+            "vs_unquantised": round(rel(got, ref_u), 6)}
 
 
 def main():
