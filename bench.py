@@ -227,6 +227,37 @@ def cpu_baseline_layer(sh, st, budget_s=15.0):
 
 
 # ----------------------------------------------------------------------------- runners
+def layer_quant_error(sh, st, n_tok=4):
+    """Quantisation error of the FP8 layer, reported beside the parity tests: the
+    last step's output on sampled tokens (first, last and seeded others) against
+    the same layer evaluated in FP64 with the unquantised FP32 master weights,
+    the same bf16 input and the same routing (idx, gates): per-row inf-norm
+    relative error, max over the tokens.  Plain torch on the GPU in FP64."""
+    T, E = sh.T, sh.E
+    toks = sorted({0, T - 1} | set(np.random.default_rng(5).integers(0, T, n_tok - 2).tolist()))
+    u = st["u"][toks].double()
+    idx = st["idx"][toks].cpu().numpy()
+    gate = st["gate"][toks].double()
+    ref = u.clone()
+    for ex in sorted(set(idx.ravel().tolist()) | {E}):
+        w1, w3, w2 = (w.double() for w in workloads.expert_weights(sh, ex, device="cuda"))
+        for i in range(len(toks)):
+            if ex == E:
+                wgt = 1.0
+            else:
+                hit = np.nonzero(idx[i] == ex)[0]
+                if hit.size == 0:
+                    continue
+                wgt = gate[i, int(hit[0])]
+            z1, z3 = w1 @ u[i], w3 @ u[i]
+            ref[i] += wgt * (w2 @ (z1 * torch.sigmoid(z1) * z3))
+        del w1, w3, w2
+    got = st["out"][toks].double()
+    rel = float(((got - ref).abs().amax(dim=1) / ref.abs().amax(dim=1)).max())
+    return {"tokens": len(toks), "norm": "per-row inf-norm relative, max over tokens",
+            "vs_unquantised_fp64": round(rel, 6)}
+
+
 def run_layer(sh, steps, warmup, with_cpu):
     log(f"[bench] setup {sh.name}: T={sh.T} d={sh.d} E={sh.E} K={sh.K} I={sh.I}")
     t = time.time()
@@ -264,6 +295,8 @@ def run_layer(sh, steps, warmup, with_cpu):
                 "traffic": traffic_for(f"gemm1_{sh.name}", "gemm.hip"),
                 "algorithmic_per_launch": nbytes, "avg_launch_ms": round(g1_ms, 4)}
     log(f"[bench] {ms:.3f} ms/step; stages {stages}")
+    qerr = layer_quant_error(sh, st)
+    log(f"[bench] quantisation error vs the unquantised layer: {qerr}")
     res = {
         "metric": "MoE-layer tokens/s (d=7168, 256E top-8, FP8) + % of FP8 MFMA / HBM roofline",
         "value": round(sh.T / (ms * 1e-3), 1),
@@ -283,6 +316,7 @@ def run_layer(sh, steps, warmup, with_cpu):
     if with_cpu:
         log("[bench] CPU oracle baseline")
         res["cpu_baseline"] = cpu_baseline_layer(sh, st)
+    res["quant_error"] = qerr
     return res
 
 
