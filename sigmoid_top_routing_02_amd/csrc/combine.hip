@@ -17,13 +17,14 @@
 namespace moe {
 namespace {
 
-// One block per token row (grid-strided); each thread owns one or two chunks of
-// VEC columns (4 for FP32 Y, 8 for bf16 Y: every Y load is 16 bytes).  All
+// One block per token row (grid-strided), sized so that one pass covers the
+// row; each thread owns one or two chunks of VEC columns (4 for FP32 Y, 8 for
+// bf16 Y: every Y load is 16 bytes).  All
 // K + 2 row loads of a chunk are issued before the first arithmetic, so a wave
 // keeps up to 2 * (K + 2) loads in flight instead of waiting for them one by
 // one; the arithmetic then runs in the fixed order above.
 template <bool Y_F32, int KMAX>
-__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ u,
+__global__ __launch_bounds__(1024) void combine_kernel(const uint16_t* __restrict__ u,
                                                       const void* __restrict__ y,
                                                       int64_t shared_row0,
                                                       const float* __restrict__ gate,
@@ -44,12 +45,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
             g[k] = k < K ? gate[t * K + k] : 0.0f;
             r[k] = k < K ? slot_row[t * K + k] : 0;
         }
-        for (int base = threadIdx.x; base < dv; base += 256 * CH) {
+        const int nthr = blockDim.x;
+        for (int base = threadIdx.x; base < dv; base += nthr * CH) {
             uint2 uw[CH][UW];
             uint4 sh[CH], yk[CH][KMAX];
 #pragma unroll
             for (int c = 0; c < CH; ++c) {
-                const int cv = base + c * 256;
+                const int cv = base + c * nthr;
                 if (cv >= dv) continue;
 #pragma unroll
                 for (int w = 0; w < UW; ++w) uw[c][w] = reinterpret_cast<const uint2*>(u + t * d)[cv * UW + w];
@@ -60,7 +62,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
             }
 #pragma unroll
             for (int c = 0; c < CH; ++c) {
-                const int cv = base + c * 256;
+                const int cv = base + c * nthr;
                 if (cv >= dv) continue;
                 float a[VEC];
 #pragma unroll
@@ -121,7 +123,12 @@ hipError_t launch_combine(const uint16_t* u, const void* y, int y_is_f32, int64_
                           const float* gate, const int32_t* slot_row, int64_t T, int K, int d,
                           float* out, hipStream_t st) {
     const unsigned grid = (unsigned)(T < 65536 ? T : 65536);
-#define MOE_COMBINE(F, KM) hipLaunchKernelGGL((combine_kernel<F, KM>), dim3(grid), dim3(256), 0, st, u, y, \
+    // threads per block: whole waves covering one row in one pass (two chunks
+    // per thread; one chunk for K > 8), at most 1024
+    const int vec = y_is_f32 ? 4 : 8, ch = K > 8 ? 1 : 2;
+    const int per_row = (d / vec + ch - 1) / ch;
+    const int nthr = per_row >= 1024 ? 1024 : (per_row + 63) / 64 * 64;
+#define MOE_COMBINE(F, KM) hipLaunchKernelGGL((combine_kernel<F, KM>), dim3(grid), dim3(nthr), 0, st, u, y, \
                                               shared_row0, gate, slot_row, T, K, d, out)
     if (y_is_f32) {
         if (K <= 4) MOE_COMBINE(true, 4);
