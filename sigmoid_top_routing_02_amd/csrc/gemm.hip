@@ -10,23 +10,26 @@
 //     acc = fma(P_j, a_scale[m,j] * b_scale[n/128,j], acc)
 // (FP8-tiling paragraph: A is scaled per 1x128 tile, B per 128x128 block.)
 //
-// Tiling (CDNA4): block tile 128 (M) x 256 (N), one 128-byte K slice per
-// pipeline stage, 8 wave64s in a 2 x 4 grid with a 64 x 64 wave tile (4 x 4
-// MFMA tiles of 16x16).  Two waves share each SIMD, so one wave's MFMAs run
-// while the other's VALU applies the slice scales: the MFMA -> scale-FMA
-// dependency of a single wave is hidden without extra registers.
+// Tiling (CDNA4): block tile 128 (M) x 256 (N) (32 x 256 for groups of a few
+// rows), one 128-byte K slice per pipeline stage, 8 wave64s in a 2 x 4 grid
+// with a 64 x 64 wave tile (4 x 4 MFMA tiles of 16x16), two waves per SIMD.
+// Inside a tile the two halves of the workgroup run a phase apart (see the
+// kernel): on each SIMD one wave multiplies from registers while the other
+// reads the next fragments from LDS and issues DMAs.
 //
 // Data movement: A rows are gathered through a_row_index (the dispatch
 // permutation), so activations are never materialised in expert order.  A, B
 // and the A scales of each slice go global -> LDS by buffer_load ... lds (no
 // VGPR staging) into a 3-stage ring; LDS rows are 128 bytes with the 16-byte
 // chunks of each row permuted (see swz) so that fragment reads are free of
-// bank conflicts.  The B scales of the tile are staged in LDS once.
+// bank conflicts.  The A scales are first gathered into GEMM row order and
+// made slice-major in the workspace (one slice of a tile's scales is one
+// contiguous 512-byte run); the B scales of the tile are staged in LDS once.
 //
-// Schedule: persistent, one block per CU, tiles walked XCD by XCD in groups
-// of GROUP_M row tiles (see the kernel).  Grouping: a device-side tile map
-// (exclusive scan of ceil(rows_g / 128)) turns a row-tile index into (group,
-// tile); the host only needs the total row count.
+// Schedule: persistent, one block per CU.  A device-built tile list (exclusive
+// scan of ceil(rows_g / BM) per group, then one record per tile) fixes the
+// order; each XCD takes its share of the list through an atomic counter.  The
+// host only needs the total row count.
 //
 // Epilogues: FP32 store; SwiGLU (B rows interleaved gate/up per 128-row
 // block, so one N tile holds the gate and up columns of the same 128 h
