@@ -159,59 +159,89 @@ __global__ __launch_bounds__(NTHREADS) void router_scores_kernel(
     }
 }
 
-// Few tokens (decode): one block per (token, 256 experts), one output per
-// lane.  Every logit is still a single FMA chain in increasing k, so with few
-// outputs the chains' length, not the arithmetic, sets the time; this layout
-// runs T * E chains at once across the chip instead of giving each thread
-// several.  The token's u row is staged once in LDS (every lane then reads the
-// same address: a broadcast); each lane streams its own centroid row with
-// RING groups of 32 bf16 in flight ahead of its FMAs.
-constexpr int ROWS_MAX_D = 16384;                // LDS for the u row: 2*d bytes
+// Few tokens, centroids shared: one block per (4 tokens, 64 experts), one
+// logit per lane (wave w = token, lane = expert).  Chunks of SM_KC k-values of
+// the block's 64 centroid rows are loaded with coalesced 16-byte loads into
+// LDS (double-buffered through registers) and read by all four waves, so each
+// centroid crosses from L2 once per 4 tokens instead of once per token; the
+// tokens' u chunk is widened to FP32 in LDS and read as a broadcast.  Every
+// logit is still one FMA chain in increasing k.
+constexpr int SM_TOK = 4, SM_EXP = 64;
 
-__global__ __launch_bounds__(256) void router_scores_rows_kernel(
+template <int SM_KC>      // k-values per chunk; divides every d that is a multiple of 128
+                          // (measured: 64 beats 128 and 256, whose unrolled chunk
+                          // the compiler holds in registers)
+__global__ __launch_bounds__(256) void router_scores_small_kernel(
     const uint16_t* __restrict__ u, const uint16_t* __restrict__ e, int64_t T, int d, int E,
     float* __restrict__ s) {
-    __shared__ uint4 us[ROWS_MAX_D / 8];
-    const int eblocks = (E + 255) / 256;
-    const int64_t t = blockIdx.x / eblocks;
-    const int ex = (blockIdx.x % eblocks) * 256 + threadIdx.x;
-    const bool live = ex < E;
-    const uint4* ur = reinterpret_cast<const uint4*>(u + t * d);
-    const uint4* er = reinterpret_cast<const uint4*>(e + (int64_t)(live ? ex : 0) * d);
-    const int nchunk = d / 8;
-    for (int c = threadIdx.x; c < nchunk; c += 256) us[c] = ur[c];
-
-    constexpr int G4 = 4, RING = 4;
-    const int ng = d / (8 * G4);                 // d is a multiple of 128: ng % RING == 0
-    uint4 ring[RING][G4];
-#pragma unroll
-    for (int r = 0; r < RING; ++r)
-#pragma unroll
-        for (int i = 0; i < G4; ++i) ring[r][i] = er[r * G4 + i];
+    // centroid chunk: 64 rows of SM_KC bf16 plus one 16-byte pad per row so
+    // that the 64 lanes' row reads spread over the banks
+    __shared__ uint4 es[2][SM_EXP][SM_KC / 8 + 1];
+    __shared__ float us[2][SM_TOK][SM_KC];
+    const int egroups = (E + SM_EXP - 1) / SM_EXP;
+    const int64_t t0 = (int64_t)(blockIdx.x / egroups) * SM_TOK;
+    const int e0 = (blockIdx.x % egroups) * SM_EXP;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    // loader roles: the chunk's 8 16-byte pieces per centroid row are moved
+    // two per thread (piece p = tid and tid + 256: row p / 8, part p % 8);
+    // threads 0 .. 31 move one piece of the u chunk (token tid / 8, part tid % 8)
+    constexpr int PARTS = SM_KC / 8, UT = SM_TOK * PARTS;
+    static_assert(SM_EXP * PARTS == 512 && UT <= 256, "loader roles assume 64-wide chunks");
+    const int p0 = tid, p1 = tid + 256;
+    const uint4* eg0 = reinterpret_cast<const uint4*>(e + (int64_t)min(e0 + p0 / PARTS, E - 1) * d) + p0 % PARTS;
+    const uint4* eg1 = reinterpret_cast<const uint4*>(e + (int64_t)min(e0 + p1 / PARTS, E - 1) * d) + p1 % PARTS;
+    const int64_t ut = min(t0 + tid / PARTS, T - 1);
+    const uint4* ug = reinterpret_cast<const uint4*>(u + ut * d) + tid % PARTS;
+    const int nch = d / SM_KC;
+    uint4 r0 = eg0[0], r1 = eg1[0], ru = tid < UT ? ug[0] : uint4{0, 0, 0, 0};
+    float* const udst0 = &us[0][tid / PARTS % SM_TOK][(tid % PARTS) * 8];
+    const int ustride = SM_TOK * SM_KC;          // floats from us[0] to us[1]
+#define MOE_SMALL_PUT(B)                                                      \
+    do {                                                                      \
+        es[B][p0 / PARTS][p0 % PARTS] = r0;                                   \
+        es[B][p1 / PARTS][p1 % PARTS] = r1;                                   \
+        if (tid < UT) {                                                       \
+            float* dst = udst0 + (B) * ustride;                               \
+            dst[0] = bf16_lo(ru.x); dst[1] = bf16_hi(ru.x);                   \
+            dst[2] = bf16_lo(ru.y); dst[3] = bf16_hi(ru.y);                   \
+            dst[4] = bf16_lo(ru.z); dst[5] = bf16_hi(ru.z);                   \
+            dst[6] = bf16_lo(ru.w); dst[7] = bf16_hi(ru.w);                   \
+        }                                                                     \
+    } while (0)
+    MOE_SMALL_PUT(0);
     __syncthreads();
-
     float acc = 0.0f;
-    for (int g0 = 0; g0 < ng; g0 += RING) {
+    for (int c = 0; c < nch; ++c) {
+        const int b = c & 1;
+        // next chunk into registers (the last step re-reads the last chunk into
+        // the spare buffer: the loop body has no branch around the loads)
+        const int off = min(c + 1, nch - 1) * PARTS;
+        r0 = eg0[off];
+        r1 = eg1[off];
+        if (tid < UT) ru = ug[off];
 #pragma unroll
-        for (int r = 0; r < RING; ++r) {
+        for (int j = 0; j < PARTS; ++j) {
+            const uint4 ev = es[b][lane][j];
+            const uint32_t wd[4] = {ev.x, ev.y, ev.z, ev.w};
+            const float* uv = &us[b][w][j * 8];
 #pragma unroll
-            for (int i = 0; i < G4; ++i) {
-                const uint4 uv = us[(g0 + r) * G4 + i];
-                const uint32_t ea[4] = {ring[r][i].x, ring[r][i].y, ring[r][i].z, ring[r][i].w};
-                const uint32_t ua[4] = {uv.x, uv.y, uv.z, uv.w};
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    acc = __builtin_fmaf(bf16_lo(ua[q]), bf16_lo(ea[q]), acc);
-                    acc = __builtin_fmaf(bf16_hi(ua[q]), bf16_hi(ea[q]), acc);
-                }
+            for (int q = 0; q < 4; ++q) {
+                acc = __builtin_fmaf(uv[2 * q], bf16_lo(wd[q]), acc);
+                acc = __builtin_fmaf(uv[2 * q + 1], bf16_hi(wd[q]), acc);
             }
-            // refill this slot with the group RING ahead (the tail re-reads the last group)
-            const int gn = min(g0 + r + RING, ng - 1);
-#pragma unroll
-            for (int i = 0; i < G4; ++i) ring[r][i] = er[gn * G4 + i];
         }
+        // the chunk's FMAs stay before the barrier (the compiler would otherwise
+        // sink them below the next chunk's LDS writes, whose wait for the
+        // global loads would then hide nothing)
+        asm volatile("" :: "v"(acc));
+        __syncthreads();                         // every wave is done with buffer b ^ 1's last use
+        MOE_SMALL_PUT(b ^ 1);
+        __syncthreads();
     }
-    if (live) s[t * E + ex] = sigmoid_fixed(acc);
+#undef MOE_SMALL_PUT
+    const int64_t t = t0 + w;
+    const int ex = e0 + lane;
+    if (t < T && ex < E) s[t * E + ex] = sigmoid_fixed(acc);
 }
 
 // One wavefront per token.  Lane l holds experts l, l+64, l+128, l+192.
@@ -284,9 +314,9 @@ hipError_t launch_router_scores(const uint16_t* u, const uint16_t* e, int64_t T,
     // 32 x 256 (4 x 8, too few blocks below 16384 tokens) and 64 x 128 (8 x 4).
     if (E > 64) {
         if (T >= 4096) return launch_scores<32, 128, 4, 4>(u, e, T, d, E, s, st);
-        if (T >= 1024 || d > ROWS_MAX_D) return launch_scores<16, 128, 2, 4>(u, e, T, d, E, s, st);
-        const unsigned grid = (unsigned)(T * ((E + 255) / 256));
-        hipLaunchKernelGGL(router_scores_rows_kernel, dim3(grid), dim3(256), 0, st, u, e, T, d, E, s);
+        if (T >= 1024) return launch_scores<16, 128, 2, 4>(u, e, T, d, E, s, st);
+        const unsigned grid = (unsigned)((T + SM_TOK - 1) / SM_TOK * ((E + SM_EXP - 1) / SM_EXP));
+        hipLaunchKernelGGL(router_scores_small_kernel<64>, dim3(grid), dim3(256), 0, st, u, e, T, d, E, s);
         return hipGetLastError();
     }
     if (T >= 4096) return launch_scores<64, 64, 4, 4>(u, e, T, d, E, s, st);

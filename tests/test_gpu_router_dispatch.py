@@ -36,9 +36,9 @@ ROUTER_CASES = [
     (4096, 512, 256, 8),      # the 32 x 128 tile, fewest tokens
     (16384, 256, 256, 8),     # the 32 x 128 tile, many blocks
     (8200, 128, 256, 8),      # the 32 x 128 tile with a ragged last block
-    (256, 7168, 256, 8),      # decode: one block per token, one logit per lane
-    (50, 256, 200, 6),        # decode layout with idle lanes (E < 256)
-    (3, 16512, 72, 4),        # u row too long for the decode layout's LDS stage
+    (256, 7168, 256, 8),      # decode: blocks of 4 tokens x 64 experts, one logit per lane
+    (50, 256, 200, 6),        # decode layout with idle lanes (E not a multiple of 64, T of 4)
+    (3, 16512, 72, 4),        # decode layout, long rows, one token block
 ]
 
 
