@@ -548,10 +548,8 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
                     tile_scale(amax, inv, sc);
 #pragma unroll
                     for (int ni = 0; ni < HALF; ++ni) {
-                        uint32_t w4 = 0;
-#pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            w4 |= (uint32_t)e4m3_encode(h[mi][ni][j] * inv) << (8 * j);
+                        const uint32_t w4 = e4m3_encode4(h[mi][ni][0] * inv, h[mi][ni][1] * inv,
+                                                         h[mi][ni][2] * inv, h[mi][ni][3] * inv);
                         *reinterpret_cast<uint32_t*>(qtile + r * 128 + wn * HC + ni * 16 + 4 * kb) = w4;
                     }
                     if (wn == 0 && kb == 0) scale_s[r] = sc;

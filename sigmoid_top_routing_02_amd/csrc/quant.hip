@@ -63,11 +63,8 @@ __global__ __launch_bounds__(256) void quant_1x128_kernel(const void* __restrict
         float inv, sc;
         tile_scale(amax, inv, sc);
         if (live) {
-            uint32_t lo = 0, hi = 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) lo |= e4m3_encode(v[i] * inv) << (8 * i);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) hi |= e4m3_encode(v[4 + i] * inv) << (8 * i);
+            const uint32_t lo = e4m3_encode4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+            const uint32_t hi = e4m3_encode4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
             *reinterpret_cast<uint2*>(q + off) = make_uint2(lo, hi);
             if (part == 0) scale[row * ntile + tc] = sc;
         }
@@ -116,11 +113,8 @@ __global__ __launch_bounds__(256) void quant_128x128_kernel(const float* __restr
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int64_t r = dbr * 128 + rbase + 16 * i;
-        uint32_t lo = 0, hi = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) lo |= e4m3_encode(v[i][j] * inv) << (8 * j);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) hi |= e4m3_encode(v[i][4 + j] * inv) << (8 * j);
+        const uint32_t lo = e4m3_encode4(v[i][0] * inv, v[i][1] * inv, v[i][2] * inv, v[i][3] * inv);
+        const uint32_t hi = e4m3_encode4(v[i][4] * inv, v[i][5] * inv, v[i][6] * inv, v[i][7] * inv);
         *reinterpret_cast<uint2*>(q + r * cols + (int64_t)bc * 128 + cpart * 8) = make_uint2(lo, hi);
     }
     if (tid == 0) scale[dbr * (cols / 128) + bc] = sc;
