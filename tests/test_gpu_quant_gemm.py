@@ -50,6 +50,34 @@ def test_quant_1x128_bit_exact(rows, cols, dtype):
     np.testing.assert_array_equal(np_(q), q_ref)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_quant_1x128_nan_and_inf(dtype):
+    """Non-finite inputs through the E4M3 encoder: a NaN input keeps its sign
+    (code 0x7F / 0xFF) and does not enter the tile maximum; a tile holding
+    +-inf has amax = inf, so inv = 448/inf = 0 and scale = inf (the scale rule
+    as written), and inf * 0 is a NaN generated inside the quantiser, whose
+    sign IEEE leaves to the platform: there the codes must be NaN codes
+    (low seven bits 0x7F), elsewhere they are bit-exact."""
+    say(f"quant 1x128 nan/inf {dtype}")
+    x = np.ones((4, 256), np.float32) * np.linspace(-3, 3, 256, dtype=np.float32)
+    x[0, 3], x[0, 4], x[0, 200] = np.nan, -np.nan, np.nan      # NaNs of both signs
+    x[1, 5], x[1, 6], x[1, 130] = np.inf, -np.inf, 1e30         # tiles with +-inf
+    x[2, :] = 0.0
+    x[2, 7] = -np.nan
+    x[3, 129] = np.inf
+    xt = torch.from_numpy(x).to(dtype)
+    q, sc = moe.fp8_quant_1x128(xt.to(dev()))
+    torch.cuda.synchronize()
+    q_ref, sc_ref = oracle.quant_1x128(xt.float().numpy())
+    np.testing.assert_array_equal(np_(sc).view(np.uint32), sc_ref.view(np.uint32))
+    qg = np_(q)
+    generated = np.zeros_like(qg, dtype=bool)          # inf * 0 inside a tile with amax = inf
+    tile_inf = np.isinf(xt.float().numpy()).reshape(4, 2, 128).any(axis=2)
+    generated |= (np.repeat(tile_inf, 128, axis=1) & np.isinf(xt.float().numpy()))
+    np.testing.assert_array_equal(qg[~generated], q_ref[~generated])
+    assert np.all((qg[generated] & 0x7F) == 0x7F) and np.all((q_ref[generated] & 0x7F) == 0x7F)
+
+
 @pytest.mark.parametrize("rows,cols", [(128, 128), (256, 640), (2048, 7168)])
 def test_quant_128x128_bit_exact(rows, cols):
     say(f"quant 128x128 {rows}x{cols}")
