@@ -726,6 +726,94 @@ __global__ __launch_bounds__(256) void gemm_scale_gather_kernel(const float* __r
     }
 }
 
+// The three preparation steps above in one launch, for G <= PREP_MAX_G (the
+// kernels are short, and each launch of its own costs several microseconds):
+// blocks [0, nl) build the tile list, each from its own LDS copy of the tile
+// starts (block 0 also writes them to the workspace and zeroes the per-XCD
+// counters); blocks [nl, nl + ceil(M_total / 64)) gather the A scales.
+constexpr int PREP_MAX_G = 4096;
+
+__global__ __launch_bounds__(256) void gemm_prep_kernel(const int32_t* __restrict__ go, int G, int BM,
+                                                        int N, int nl, int32_t* __restrict__ ts,
+                                                        int4* __restrict__ tiles,
+                                                        const float* __restrict__ a_s,
+                                                        const int32_t* __restrict__ a_rows,
+                                                        int64_t M_total, int ns,
+                                                        float* __restrict__ a_sT) {
+    __shared__ int32_t lts[PREP_MAX_G + 1];
+    __shared__ int32_t part[256];
+    __shared__ float t[64][MAX_SLICES + 1];
+    if ((int)blockIdx.x >= nl) {
+        // every load of the thread is issued before the first LDS store (the
+        // gathered scales are a latency-bound handful per thread)
+        constexpr int PER_T = 64 * MAX_SLICES / 256;
+        const int64_t m0 = (int64_t)(blockIdx.x - nl) * 64;
+        float v[PER_T];
+#pragma unroll
+        for (int k = 0; k < PER_T; ++k) {
+            const int i = threadIdx.x + k * 256;
+            const int r = i / ns, j = i - r * ns;
+            const int64_t m = m0 + r;
+            v[k] = (i < 64 * ns && m < M_total) ? a_s[(a_rows ? (int64_t)a_rows[m] : m) * ns + j] : 0.0f;
+        }
+#pragma unroll
+        for (int k = 0; k < PER_T; ++k) {
+            const int i = threadIdx.x + k * 256;
+            const int r = i / ns, j = i - r * ns;
+            if (i < 64 * ns) t[r][j] = v[k];
+        }
+        __syncthreads();
+        for (int i = threadIdx.x; i < 64 * ns; i += 256) {
+            const int j = i >> 6, r = i & 63;
+            const int64_t m = m0 + r;
+            if (m < M_total) a_sT[j * M_total + m] = t[r][j];
+        }
+        return;
+    }
+    // exclusive scan of ceil(rows_g / BM): thread i owns groups [i*c, i*c + c)
+    const int c = (G + 255) / 256;
+    const int g0 = threadIdx.x * c;
+    int32_t sum = 0;
+    for (int g = g0; g < g0 + c && g < G; ++g) sum += (go[g + 1] - go[g] + BM - 1) / BM;
+    part[threadIdx.x] = sum;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+        const int32_t x = (threadIdx.x >= (unsigned)off) ? part[threadIdx.x - off] : 0;
+        __syncthreads();
+        part[threadIdx.x] += x;
+        __syncthreads();
+    }
+    int32_t run = part[threadIdx.x] - sum;
+    for (int g = g0; g < g0 + c && g < G; ++g) {
+        lts[g] = run;
+        run += (go[g + 1] - go[g] + BM - 1) / BM;
+    }
+    if (threadIdx.x == 255) lts[G] = part[255];
+    __syncthreads();
+    if (blockIdx.x == 0) {
+        for (int g = threadIdx.x; g <= G; g += 256) ts[g] = lts[g];
+        if (threadIdx.x < 8) ts[G + 1 + threadIdx.x] = 0;
+    }
+    // this block's part of the tile list (as gemm_tile_list_kernel)
+    const int n_tiles = (N + BN - 1) / BN;
+    const int total = lts[G] * n_tiles;
+    const int tt = blockIdx.x * 256 + threadIdx.x;
+    if (tt >= total) return;
+    const int q = tt / n_tiles;
+    int lo = 0, hi = G - 1;                       // largest g with lts[g] <= q
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (lts[mid] <= q) lo = mid; else hi = mid - 1;
+    }
+    const int mt_g = lts[lo + 1] - lts[lo];
+    const int local = tt - lts[lo] * n_tiles;
+    const int chunk = local / (GROUP_M * n_tiles);
+    const int chunk_rows = min(GROUP_M, mt_g - chunk * GROUP_M);
+    const int in_chunk = local - chunk * GROUP_M * n_tiles;
+    const int m0 = go[lo] + (chunk * GROUP_M + in_chunk % chunk_rows) * BM;
+    tiles[tt] = make_int4(lo, m0, min(BM, go[lo + 1] - m0), (in_chunk / chunk_rows) * BN);
+}
+
 int cu_count_for_current_device() {
     static int cached[64] = {0};
     int dev = 0;
@@ -763,14 +851,20 @@ hipError_t launch_grouped_gemm(const uint8_t* a_q, const float* a_s, const int32
     int4* tiles = reinterpret_cast<int4*>(static_cast<char*>(ws) + tile_list_offset(G));
     float* a_sT = reinterpret_cast<float*>(static_cast<char*>(ws) + scale_copy_offset(G, M_total, N));
     const int ns = K / BK;
-    hipLaunchKernelGGL(gemm_scale_gather_kernel, dim3((unsigned)((M_total + 63) / 64)), dim3(256), 0, st,
-                       a_s, a_rows, M_total, ns, a_sT);
     // 32-row tiles when the groups average at most 64 rows (few tokens per expert)
     const int bm = (M_total <= (int64_t)64 * G) ? 32 : 128;
-    hipLaunchKernelGGL(gemm_tile_map_kernel, dim3(1), dim3(256), 0, st, group_offset, G, bm, ts);
     const int64_t list_bound = ((M_total + bm - 1) / bm + G) * (int64_t)((N + BN - 1) / BN);
-    hipLaunchKernelGGL(gemm_tile_list_kernel, dim3((unsigned)((list_bound + 255) / 256)), dim3(256), 0, st,
-                       group_offset, ts, G, bm, N, tiles);
+    const int64_t nl = (list_bound + 255) / 256, ng = (M_total + 63) / 64;
+    if (G <= PREP_MAX_G) {
+        hipLaunchKernelGGL(gemm_prep_kernel, dim3((unsigned)(nl + ng)), dim3(256), 0, st, group_offset, G, bm, N,
+                           (int)nl, ts, tiles, a_s, a_rows, M_total, ns, a_sT);
+    } else {
+        hipLaunchKernelGGL(gemm_scale_gather_kernel, dim3((unsigned)ng), dim3(256), 0, st,
+                           a_s, a_rows, M_total, ns, a_sT);
+        hipLaunchKernelGGL(gemm_tile_map_kernel, dim3(1), dim3(256), 0, st, group_offset, G, bm, ts);
+        hipLaunchKernelGGL(gemm_tile_list_kernel, dim3((unsigned)nl), dim3(256), 0, st,
+                           group_offset, ts, G, bm, N, tiles);
+    }
     GemmArgs p{a_q, a_sT, (uint32_t)(M_total * 4), a_rows, group_offset, ts, ts + G + 1, tiles, G, b_q, b_s, N, K,
                out, out_q, out_s};
     const int64_t blocks = list_bound;

@@ -145,6 +145,33 @@ def test_gemm_integer_exact(sizes, N, K):
     np.testing.assert_array_equal(np_(out), ref.astype(np.float32))
 
 
+@pytest.mark.parametrize("G", [4096, 4100])
+def test_gemm_integer_exact_many_groups(G):
+    """The tile map for many groups: up to 4096 groups the map, the tile list
+    and the scale gather run as one launch that scans the groups in each list
+    block; beyond, as three launches.  Two non-empty groups (one of them the
+    last), every other group empty; B is only filled where it is read."""
+    N, K = 256, 256
+    sizes = np.zeros(G, np.int64)
+    sizes[17], sizes[G - 1] = 200, 77
+    go = _groups(sizes)
+    M = int(go[-1])
+    say(f"gemm integer G={G} M={M} N={N} K={K}")
+    va, vb2, qa, qb2 = _int_operands(M, N, K, 2, seed=G)
+    qb = torch.zeros(G, N, K, dtype=torch.uint8, device=dev())
+    qb[17] = torch.from_numpy(qb2[0]).to(dev())
+    qb[G - 1] = torch.from_numpy(qb2[1]).to(dev())
+    out = moe.grouped_gemm_fp8_blockscaled(
+        torch.from_numpy(qa).to(dev()), torch.ones(M, K // 128, device=dev()),
+        torch.from_numpy(go).to(dev()), M, qb,
+        torch.ones(G, N // 128, K // 128, device=dev()), epi=moe.MOE_EPI_STORE_F32)
+    torch.cuda.synchronize()
+    ref = np.zeros((M, N))
+    ref[:200] = va[:200].astype(np.int64) @ vb2[0].astype(np.int64).T
+    ref[200:] = va[200:].astype(np.int64) @ vb2[1].astype(np.int64).T
+    np.testing.assert_array_equal(np_(out), ref.astype(np.float32))
+
+
 def _scaled_operands(M, N, K, G, seed, outliers=True):
     g = torch.Generator().manual_seed(seed)
     a = torch.randn(M, K, generator=g)
