@@ -17,27 +17,35 @@
 namespace moe {
 namespace {
 
-// One block per token row (grid-strided), sized so that one pass covers the
-// row; each thread owns one or two chunks of VEC columns (4 for FP32 Y, 8 for
-// bf16 Y: every Y load is 16 bytes).  All
-// K + 2 row loads of a chunk are issued before the first arithmetic, so a wave
-// keeps up to 2 * (K + 2) loads in flight instead of waiting for them one by
-// one; the arithmetic then runs in the fixed order above.
+typedef uint32_t comb_v4u __attribute__((ext_vector_type(4)));
+typedef float comb_v4f __attribute__((ext_vector_type(4)));
+
+// Each block covers COLS_PER_BLOCK columns of one token row (grid.x: column
+// blocks, grid.y: tokens, strided); each thread owns one chunk of VEC columns
+// (4 for FP32 Y, 8 for bf16 Y: every Y load is 16 bytes).  All K + 2 row loads
+// of a chunk are issued before the first arithmetic; the arithmetic then runs
+// in the fixed order above.  Y is read once and h' written once, so both go
+// through non-temporal loads and stores (they would otherwise evict lines that
+// are still useful and, measured on gfx950, run about 17% slower); u keeps
+// ordinary loads, which measured faster.
+constexpr int COMBINE_COLS_PER_BLOCK = 512;
+
 template <bool Y_F32, int KMAX>
-__global__ __launch_bounds__(1024) void combine_kernel(const uint16_t* __restrict__ u,
-                                                      const void* __restrict__ y,
-                                                      int64_t shared_row0,
-                                                      const float* __restrict__ gate,
-                                                      const int32_t* __restrict__ slot_row,
-                                                      int64_t T, int K, int d,
-                                                      float* __restrict__ out) {
-    constexpr int CH = KMAX > 8 ? 1 : 2;        // chunks per thread per pass
+__global__ __launch_bounds__(128) void combine_kernel(const uint16_t* __restrict__ u,
+                                                     const void* __restrict__ y,
+                                                     int64_t shared_row0,
+                                                     const float* __restrict__ gate,
+                                                     const int32_t* __restrict__ slot_row,
+                                                     int64_t T, int K, int d,
+                                                     float* __restrict__ out) {
     constexpr int VEC = Y_F32 ? 4 : 8;          // columns per chunk
     constexpr int UW = VEC / 4;                 // uint2 words of u per chunk
     const int dv = d / VEC;
-    const uint4* yv = static_cast<const uint4*>(y);
-    const int64_t yrow = (int64_t)d / (Y_F32 ? 4 : 8);   // uint4 per Y row
-    for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+    const comb_v4u* yv = static_cast<const comb_v4u*>(y);
+    const int64_t yrow = (int64_t)d / VEC;      // 16-byte words per Y row
+    const int cv = blockIdx.x * blockDim.x + threadIdx.x;
+    if (cv >= dv) return;
+    for (int64_t t = blockIdx.y; t < T; t += gridDim.y) {
         float g[KMAX];
         int64_t r[KMAX];
 #pragma unroll
@@ -45,65 +53,54 @@ __global__ __launch_bounds__(1024) void combine_kernel(const uint16_t* __restric
             g[k] = k < K ? gate[t * K + k] : 0.0f;
             r[k] = k < K ? slot_row[t * K + k] : 0;
         }
-        const int nthr = blockDim.x;
-        for (int base = threadIdx.x; base < dv; base += nthr * CH) {
-            uint2 uw[CH][UW];
-            uint4 sh[CH], yk[CH][KMAX];
+        uint2 uw[UW];
+        comb_v4u sh = {0u, 0u, 0u, 0u}, yk[KMAX];
 #pragma unroll
-            for (int c = 0; c < CH; ++c) {
-                const int cv = base + c * nthr;
-                if (cv >= dv) continue;
+        for (int w = 0; w < UW; ++w) uw[w] = reinterpret_cast<const uint2*>(u + t * d)[cv * UW + w];
+        if (shared_row0 >= 0) sh = __builtin_nontemporal_load(yv + (shared_row0 + t) * yrow + cv);
 #pragma unroll
-                for (int w = 0; w < UW; ++w) uw[c][w] = reinterpret_cast<const uint2*>(u + t * d)[cv * UW + w];
-                if (shared_row0 >= 0) sh[c] = yv[(shared_row0 + t) * yrow + cv];
+        for (int k = 0; k < KMAX; ++k)
+            if (k < K) yk[k] = __builtin_nontemporal_load(yv + r[k] * yrow + cv);
+        float a[VEC];
 #pragma unroll
-                for (int k = 0; k < KMAX; ++k)
-                    if (k < K) yk[c][k] = yv[r[k] * yrow + cv];
+        for (int w = 0; w < UW; ++w) {
+            a[4 * w + 0] = bf16_lo(uw[w].x);
+            a[4 * w + 1] = bf16_hi(uw[w].x);
+            a[4 * w + 2] = bf16_lo(uw[w].y);
+            a[4 * w + 3] = bf16_hi(uw[w].y);
+        }
+        // the four 32-bit words of a 16-byte Y load, as VEC floats
+        auto expand = [&](const comb_v4u& v, float (&f)[VEC]) {
+            if constexpr (Y_F32) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) f[q] = __uint_as_float(v[q]);
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    f[2 * q] = bf16_lo(v[q]);
+                    f[2 * q + 1] = bf16_hi(v[q]);
+                }
             }
+        };
+        if (shared_row0 >= 0) {
+            float f[VEC];
+            expand(sh, f);
 #pragma unroll
-            for (int c = 0; c < CH; ++c) {
-                const int cv = base + c * nthr;
-                if (cv >= dv) continue;
-                float a[VEC];
+            for (int q = 0; q < VEC; ++q) a[q] = a[q] + f[q];
+        }
 #pragma unroll
-                for (int w = 0; w < UW; ++w) {
-                    a[4 * w + 0] = bf16_lo(uw[c][w].x);
-                    a[4 * w + 1] = bf16_hi(uw[c][w].x);
-                    a[4 * w + 2] = bf16_lo(uw[c][w].y);
-                    a[4 * w + 3] = bf16_hi(uw[c][w].y);
-                }
-                // the four 32-bit words of a 16-byte Y load, as VEC floats
-                auto expand = [&](const uint4& v, float (&f)[VEC]) {
-                    const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
-                    if constexpr (Y_F32) {
+        for (int k = 0; k < KMAX; ++k) {
+            if (k >= K) break;
+            float f[VEC];
+            expand(yk[k], f);
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) f[q] = __uint_as_float(wd[q]);
-                    } else {
+            for (int q = 0; q < VEC; ++q) a[q] = __builtin_fmaf(g[k], f[q], a[q]);
+        }
+        comb_v4f* o = reinterpret_cast<comb_v4f*>(out + t * d) + cv * (VEC / 4);
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            f[2 * q] = bf16_lo(wd[q]);
-                            f[2 * q + 1] = bf16_hi(wd[q]);
-                        }
-                    }
-                };
-                if (shared_row0 >= 0) {
-                    float f[VEC];
-                    expand(sh[c], f);
-#pragma unroll
-                    for (int q = 0; q < VEC; ++q) a[q] = a[q] + f[q];
-                }
-#pragma unroll
-                for (int k = 0; k < KMAX; ++k) {
-                    if (k >= K) break;
-                    float f[VEC];
-                    expand(yk[c][k], f);
-#pragma unroll
-                    for (int q = 0; q < VEC; ++q) a[q] = __builtin_fmaf(g[k], f[q], a[q]);
-                }
-                float4* o = reinterpret_cast<float4*>(out + t * d) + cv * (VEC / 4);
-#pragma unroll
-                for (int w = 0; w < VEC / 4; ++w) o[w] = make_float4(a[4 * w], a[4 * w + 1], a[4 * w + 2], a[4 * w + 3]);
-            }
+        for (int w = 0; w < VEC / 4; ++w) {
+            const comb_v4f v = {a[4 * w], a[4 * w + 1], a[4 * w + 2], a[4 * w + 3]};
+            __builtin_nontemporal_store(v, o + w);
         }
     }
 }
@@ -122,12 +119,10 @@ __global__ void bias_update_kernel(float* __restrict__ bias, const int32_t* __re
 hipError_t launch_combine(const uint16_t* u, const void* y, int y_is_f32, int64_t shared_row0,
                           const float* gate, const int32_t* slot_row, int64_t T, int K, int d,
                           float* out, hipStream_t st) {
-    const unsigned grid = (unsigned)(T < 65536 ? T : 65536);
-    // threads per block: whole waves covering one row in one pass (two chunks
-    // per thread; one chunk for K > 8), at most 1024
-    const int vec = y_is_f32 ? 4 : 8, ch = K > 8 ? 1 : 2;
-    const int per_row = (d / vec + ch - 1) / ch;
-    const int nthr = per_row >= 1024 ? 1024 : (per_row + 63) / 64 * 64;
+    const int vec = y_is_f32 ? 4 : 8;
+    const int nthr = COMBINE_COLS_PER_BLOCK / vec;                 // 128 or 64
+    const int dv = d / vec;
+    const dim3 grid((unsigned)((dv + nthr - 1) / nthr), (unsigned)(T < 65535 ? T : 65535));
 #define MOE_COMBINE(F, KM) hipLaunchKernelGGL((combine_kernel<F, KM>), dim3(grid), dim3(nthr), 0, st, u, y, \
                                               shared_row0, gate, slot_row, T, K, d, out)
     if (y_is_f32) {
