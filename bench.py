@@ -492,7 +492,8 @@ def dense_errors(out, aq, as_, bq, bs, rows, a_rows, b_host):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 20; 200 for the dense GEMM, whose step is ~0.3 ms)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill",
                     choices=["prefill", "decode", "tiny", "rdc", "dense", "dense16k"])
@@ -508,6 +509,8 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.steps is None:
+        args.steps = 200 if args.workload in ("dense", "dense16k") else 20
     moe.load_library()
     if args.with_copy:
         copy_calibration()
