@@ -455,6 +455,7 @@ def run_dense(steps, warmup, K=4096):
     ach = flops / (g_ms * 1e-3) / 1e12
     err = dense_errors(out, aq, as_, bq, bs, rows, a_rows, b_host)
     del b_host
+    acc = accumulation_probe(aq, bq, K)
     return {
         "metric": "block-scaled FP8 GEMM TFLOP/s", "value": round(flops / (ms * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 4),
@@ -464,7 +465,37 @@ def run_dense(steps, warmup, K=4096):
                      "achieved": round(ach, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(ach / PEAK_FP8_TFLOPS, 4), "traffic": traffic_for(f"dense_k{K}", "gemm.hip")},
         "error": err,
+        "accumulation": acc,
     }
+
+
+def accumulation_probe(aq, bq, K, n=256):
+    """FP8 MFMA accumulation with unit scales on the first n rows of A and B:
+    one FP32 accumulator carried through every slice's MFMA (chained) against
+    a fresh MFMA per 128-wide slice plus FP32 adds (promoted, the GEMM's path),
+    both against the FP64 sum of the decoded codes."""
+    a, b = aq[:n].contiguous(), bq[:n].contiguous()
+    cha = moe.moe_fp8_mfma_accumulation_probe(a, b, chained=True)
+    pro = moe.moe_fp8_mfma_accumulation_probe(a, b, chained=False)
+    torch.cuda.synchronize()
+    tab = torch.tensor([oracle_free_e4m3(c) for c in range(256)], dtype=torch.float64)
+    exact = (tab[a.cpu().long()] @ tab[b.cpu().long()].T).numpy()
+    def rel(x):
+        x = x.double().cpu().numpy()
+        den = np.maximum(np.abs(exact).max(axis=1), 1e-300)
+        return float((np.abs(x - exact).max(axis=1) / den).max())
+    return {"rows": n, "cols": n, "K": K, "scales": "unit (codes as quantised)",
+            "norm": "per-row inf-norm relative vs FP64, max over rows",
+            "chained": rel(cha), "promoted_per_128": rel(pro)}
+
+
+def oracle_free_e4m3(code):
+    """Value of an OCP E4M3 code (bias 7, no infinities, S.1111.111 = NaN)."""
+    sgn = -1.0 if code & 0x80 else 1.0
+    e, m = (code >> 3) & 0xF, code & 7
+    if e == 15 and m == 7:
+        return float("nan")
+    return sgn * (m / 8.0 * 2.0 ** -6 if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 7))
 
 
 def dense_errors(out, aq, as_, bq, bs, rows, a_rows, b_host):

@@ -176,6 +176,21 @@ int grouped_gemm_fp8_blockscaled(const uint8_t* a_q, const float* a_scale,
                                  uint8_t* out_q, float* out_scale, void* ws, size_t ws_bytes,
                                  moe_stream_t stream);
 
+/* moe_fp8_mfma_accumulation_probe -- a measurement beside the GEMM, not a
+ * step of the layer.  [IFS] FP8-accumulation paragraph: FP8 products summed
+ * inside a matrix core with limited accumulation precision lose accuracy over
+ * a long inner dimension, which is why the GEMM above promotes every
+ * 128-element slice to FP32.  With every scale equal to 1 this computes
+ *   out[m,n] = sum_k E4M3(a_q[m,k]) * E4M3(b_q[n,k])
+ * either chained (chained = 1: one FP32 accumulator carried through the FP8
+ * MFMA of every 128-wide slice) or promoted (chained = 0: each slice's MFMA
+ * into a fresh accumulator, then an FP32 add, i.e. the GEMM's path).
+ * a_q E4M3 [M, K], b_q E4M3 [N, K], out FP32 [M, N].
+ * Limits: M % 16 == 0 (M <= 1048560), N % 16 == 0, K % 128 == 0, K > 0.
+ */
+int moe_fp8_mfma_accumulation_probe(const uint8_t* a_q, const uint8_t* b_q, int M, int N, int K,
+                                    int chained, float* out, moe_stream_t stream);
+
 /* ------------------------------------------------------------------ combine
  * moe_combine -- [LINEAGE] "The notation":
  *   h'[t] = u[t] + sum_shared FFN(u[t]) + sum_k g[t,k] FFN_{idx[t,k]}(u[t])

@@ -27,7 +27,7 @@ EXPORTS = (
     "moe_dispatch_workspace_bytes", "moe_dispatch", "moe_permute_rows",
     "fp8_quant_1x128", "fp8_quant_128x128",
     "moe_gemm_workspace_bytes", "grouped_gemm_fp8_blockscaled",
-    "moe_combine", "moe_bias_update",
+    "moe_fp8_mfma_accumulation_probe", "moe_combine", "moe_bias_update",
     "moe_packed_weight_bytes", "moe_prepare_expert_weights",
     "moe_layer_workspace_bytes", "moe_layer_forward",
 )
@@ -61,6 +61,7 @@ def load_library(path: str = LIB_PATH):
         "fp8_quant_128x128": ([P, I64, I32, P, P, P], I32),
         "moe_gemm_workspace_bytes": ([I32, I64, I32, I32], SZ),
         "grouped_gemm_fp8_blockscaled": ([P, P, P, P, I32, I64, P, P, I32, I32, I32, P, P, P, P, SZ, P], I32),
+        "moe_fp8_mfma_accumulation_probe": ([P, P, I32, I32, I32, I32, P, P], I32),
         "moe_combine": ([P, P, I32, I64, P, P, I64, I32, I32, P, P], I32),
         "moe_bias_update": ([P, P, I32, I64, F32, P], I32),
         "moe_packed_weight_bytes": ([I32, I32, I32], SZ),
@@ -222,6 +223,21 @@ def grouped_gemm_fp8_blockscaled(a_q, a_scale, group_offset, M_total, b_q, b_sca
         _stream()), "grouped_gemm_fp8_blockscaled")
     if epi == MOE_EPI_SWIGLU_QUANT:
         return out_q, out_scale
+    return out
+
+
+def moe_fp8_mfma_accumulation_probe(a_q, b_q, chained):
+    """sum_k E4M3(a_q[m,k]) * E4M3(b_q[n,k]) with unit scales, FP32 [M, N]:
+    chained=True carries one accumulator through the FP8 MFMA of every slice,
+    chained=False adds each slice's MFMA result in FP32 (the GEMM's path)."""
+    M, K = a_q.shape
+    N = b_q.shape[0]
+    _want(a_q, torch.uint8, (M, K), "a_q")
+    _want(b_q, torch.uint8, (N, K), "b_q")
+    out = _new((M, N), torch.float32, a_q)
+    L = load_library()
+    _check(L.moe_fp8_mfma_accumulation_probe(_ptr(a_q), _ptr(b_q), M, N, K, int(bool(chained)),
+                                             _ptr(out), _stream()), "moe_fp8_mfma_accumulation_probe")
     return out
 
 

@@ -200,6 +200,21 @@ int grouped_gemm_fp8_blockscaled(const uint8_t* a_q, const float* a_scale,
                       "grouped gemm launch");
 }
 
+int moe_fp8_mfma_accumulation_probe(const uint8_t* a_q, const uint8_t* b_q, int M, int N, int K,
+                                    int chained, float* out, moe_stream_t stream) {
+    REQUIRE(M >= 0 && M % 16 == 0 && M / 16 <= 65535, MOE_ERR_SHAPE,
+            "moe_fp8_mfma_accumulation_probe: M=%d not a multiple of 16 in [0, 1048560]", M);
+    REQUIRE(N >= 0 && N % 16 == 0, MOE_ERR_SHAPE, "moe_fp8_mfma_accumulation_probe: N=%d not a multiple of 16", N);
+    REQUIRE(K > 0 && K % 128 == 0, MOE_ERR_SHAPE, "moe_fp8_mfma_accumulation_probe: K=%d not a positive multiple of 128", K);
+    REQUIRE(chained == 0 || chained == 1, MOE_ERR_UNSUPPORTED, "moe_fp8_mfma_accumulation_probe: chained=%d", chained);
+    if (M == 0 || N == 0) return MOE_OK;
+    REQUIRE_PTR(a_q);
+    REQUIRE_PTR(b_q);
+    REQUIRE_PTR(out);
+    return hip_status(moe::launch_accum_probe(a_q, b_q, M, N, K, chained, out, S(stream)),
+                      "accumulation probe launch");
+}
+
 int moe_combine(const void* u_bf16, const void* y, int y_dt, int64_t shared_row0,
                 const float* topk_gate, const int32_t* slot_row, int64_t T, int K, int d,
                 float* out, moe_stream_t stream) {

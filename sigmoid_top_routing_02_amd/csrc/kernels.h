@@ -39,6 +39,10 @@ hipError_t launch_grouped_gemm(const uint8_t* a_q, const float* a_s, const int32
                                float* out, uint8_t* out_q, float* out_s, void* ws,
                                hipStream_t st);
 
+// accum_probe.hip
+hipError_t launch_accum_probe(const uint8_t* a_q, const uint8_t* b_q, int M, int N, int K,
+                              int chained, float* out, hipStream_t st);
+
 // combine.hip
 hipError_t launch_combine(const uint16_t* u, const void* y, int y_is_f32, int64_t shared_row0,
                           const float* gate, const int32_t* slot_row, int64_t T, int K, int d,

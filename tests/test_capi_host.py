@@ -95,6 +95,17 @@ def test_quant_and_gemm_argument_errors(L):
                                           FAKE, None, None, FAKE, gw, None) == -3
 
 
+def test_accumulation_probe_argument_errors(L):
+    f = L.moe_fp8_mfma_accumulation_probe
+    assert f(FAKE, FAKE, 20, 16, 128, 0, FAKE, None) == -2          # M % 16
+    assert f(FAKE, FAKE, 16, 24, 128, 0, FAKE, None) == -2          # N % 16
+    assert f(FAKE, FAKE, 16, 16, 100, 0, FAKE, None) == -2          # K % 128
+    assert f(FAKE, FAKE, 16, 16, 128, 2, FAKE, None) == -3          # chained not 0/1
+    assert f(FAKE, None, 16, 16, 128, 1, FAKE, None) == -1
+    assert f(FAKE, FAKE, 16, 16, 128, 1, MISALIGNED, None) == -5
+    assert f(None, None, 0, 16, 128, 1, None, None) == 0           # nothing to do
+
+
 def test_combine_bias_layer_argument_errors(L):
     assert L.moe_combine(FAKE, FAKE, 1, -1, FAKE, FAKE, 4, 17, 128, FAKE, None) == -3
     assert L.moe_combine(FAKE, FAKE, 5, -1, FAKE, FAKE, 4, 4, 128, FAKE, None) == -3

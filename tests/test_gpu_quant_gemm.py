@@ -302,3 +302,36 @@ def check_codes_close(q, s, q_ref, s_ref, x_ref, x_gpu):
     bad = np.abs(deq - xr) > bound
     assert not bad.any(), f"{int(bad.sum())} E4M3 codes further from the exact value than allowed"
     return int((table[q] != table[q_ref]).sum())
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 16, 128), (32, 64, 1024), (64, 48, 4096)])
+def test_mfma_accumulation_probe(M, N, K):
+    """The accumulation probe (unit scales).  Integer operands: the promoted
+    path (one MFMA per slice, FP32 adds) is exact; with a single slice the
+    chained and promoted paths are the same computation, bit for bit.  Random
+    E4M3 operands: the promoted path within the FP tolerance of the FP64 sum;
+    the chained path's error is what the probe measures, so it is only
+    reported (and bounded loosely, which still catches a wrong layout)."""
+    say(f"accumulation probe M={M} N={N} K={K}")
+    va, vb, qa, qb = _int_operands(M, N, K, 1, seed=K + M)
+    a, b = torch.from_numpy(qa).to(dev()), torch.from_numpy(qb[0]).to(dev())
+    pro = moe.moe_fp8_mfma_accumulation_probe(a, b, chained=False)
+    cha = moe.moe_fp8_mfma_accumulation_probe(a, b, chained=True)
+    torch.cuda.synchronize()
+    ref = va.astype(np.int64) @ vb[0].astype(np.int64).T
+    np.testing.assert_array_equal(np_(pro), ref.astype(np.float32))
+    if K == 128:
+        np.testing.assert_array_equal(np_(cha), np_(pro))
+    rng = np.random.default_rng(K)
+    qa2 = oracle.e4m3_encode_array(rng.standard_normal((M, K)).astype(np.float32) * 16)
+    qb2 = oracle.e4m3_encode_array(rng.standard_normal((N, K)).astype(np.float32) * 16)
+    tab = oracle.e4m3_table()
+    exact = tab[qa2] @ tab[qb2].T
+    a, b = torch.from_numpy(qa2).to(dev()), torch.from_numpy(qb2).to(dev())
+    pro = moe.moe_fp8_mfma_accumulation_probe(a, b, chained=False)
+    cha = moe.moe_fp8_mfma_accumulation_probe(a, b, chained=True)
+    torch.cuda.synchronize()
+    errp, errc = rowinf_rel(np_(pro), exact), rowinf_rel(np_(cha), exact)
+    say(f"  per-row rel err: promoted {errp:.3e}, chained {errc:.3e}")
+    assert errp <= TOL
+    assert errc <= 0.1

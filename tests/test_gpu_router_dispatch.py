@@ -174,3 +174,31 @@ def test_combine_identity_experts_bf16(T, d, E, K):
     assert err <= TOL
     uf = (u16(u).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     assert rowinf_rel(np_(out), 2 * uf) <= 1e-5
+
+
+@pytest.mark.parametrize("ydt", [torch.bfloat16, torch.float32])
+def test_permute_combine_past_grid_rows(ydt):
+    """More token rows than the 65,535 grid rows of the permute and combine
+    launches (the rows wrap round the grid), with a row that does not fill
+    the last column block (d = 136: 17 words of bf16, 34 of FP32).  Permute is
+    bit-exact; combine (with a shared row block) within the FP tolerance."""
+    T, K, d, E = 70003, 2, 136, 8
+    rng = np.random.default_rng(21)
+    idx = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+    g = torch.Generator().manual_seed(22)
+    u = torch.randn(T, d, generator=g).to(torch.bfloat16)
+    say(f"permute + combine past the grid rows, Y {ydt}")
+    count, go, row_token, slot_row = moe.moe_dispatch(torch.from_numpy(idx).to(dev()), E, True)
+    xp = moe.moe_permute_rows(u.to(dev()), row_token)                     # R = T*K + T rows
+    torch.cuda.synchronize()
+    _, _, rt_ref, _ = oracle.dispatch(idx, E, True)
+    np.testing.assert_array_equal(u16(xp), u16(u)[rt_ref])
+    y = xp.to(ydt)
+    gate = torch.rand(T, K, generator=g).to(dev())
+    out = moe.moe_combine(u.to(dev()), y, gate, slot_row, shared_row0=T * K)
+    torch.cuda.synchronize()
+    yf = np_(y.float()).astype(np.float64)
+    ref = oracle.combine(u16(u), yf, T * K, np_(gate), np_(slot_row))
+    err = rowinf_rel(np_(out), ref)
+    say(f"  per-row rel err {err:.3e}")
+    assert err <= TOL
