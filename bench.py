@@ -317,6 +317,7 @@ def run_layer(sh, steps, warmup, with_cpu):
         log("[bench] CPU oracle baseline")
         res["cpu_baseline"] = cpu_baseline_layer(sh, st)
     res["quant_error"] = qerr
+    res["copy_ceiling_gbs"] = copy_ceiling_gbs()
     return res
 
 
@@ -362,6 +363,7 @@ def run_rdc(steps, warmup, with_cpu):
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
     stages = {n: round(ev.avg_ms(n), 4) for n in ev.pairs}
+    grouped = grouped_router_timing(u, e, b, K, st, steps)
     # algorithmic bytes of the combine: K bf16 rows of X_perm + u read, FP32 h' written, gates and slots
     comb_bytes = T * K * d * 2 + T * d * 2 + T * d * 4 + T * K * 8
     comb_ms = ev.avg_ms("combine")
@@ -380,6 +382,7 @@ def run_rdc(steps, warmup, with_cpu):
                      "algorithmic_per_launch": comb_bytes, "avg_launch_ms": round(comb_ms, 4)},
         "stages_ms": stages,
         "permute_gbs": round(perm_bytes / (ev.avg_ms("permute") * 1e-3) / 1e9, 1),
+        "grouped_router": grouped,
         "router_tflops": round(2.0 * T * E * d / (ev.avg_ms("router") * 1e-3) / 1e12, 2),
     }
     if with_cpu:
@@ -398,6 +401,7 @@ def run_rdc(steps, warmup, with_cpu):
         dt = time.perf_counter() - t0
         res["cpu_baseline"] = {"value": round(nt / dt, 1), "unit": "tokens/s", "cores": _cores(), "kind": "oracle",
                                "sample": f"the whole rdc pass on the first {nt} tokens ({dt:.1f}s)"}
+    res["copy_ceiling_gbs"] = copy_ceiling_gbs()
     return res
 
 
@@ -415,6 +419,48 @@ def copy_calibration():
         moe.moe_permute_rows(src, ident, out=dst)
     torch.cuda.synchronize()
     del src, dst
+
+
+def grouped_router_timing(u, e, b, K, st, steps, n_groups=8, topk_groups=4):
+    """The group-limited router (8 groups of 32 experts, at most 4 groups per
+    token, as the pages' 4-node limit) beside the plain one on the same batch:
+    both calls run the score kernel and a top-K kernel; the difference is the
+    group stage.  Also checks that no token's experts span more than 4 groups."""
+    E = e.shape[0]
+    ev = Events()
+    for grouped in (False, True):
+        kw = dict(n_groups=n_groups, topk_groups=topk_groups) if grouped else {}
+        moe.moe_router_topk(u, e, b, K, st["scores"], st["idx"], st["gate"], **kw)
+        for _ in range(steps):
+            a0 = ev.mark("s")
+            moe.moe_router_topk(u, e, b, K, st["scores"], st["idx"], st["gate"], **kw)
+            ev.add("grouped" if grouped else "plain", a0, ev.mark("e"))
+    torch.cuda.synchronize()
+    groups = (st["idx"] // (E // n_groups)).cpu().numpy()
+    span = max(len(set(r.tolist())) for r in groups)
+    return {"n_groups": n_groups, "topk_groups": topk_groups, "router_ms": round(ev.avg_ms("plain"), 4),
+            "grouped_router_ms": round(ev.avg_ms("grouped"), 4), "max_groups_per_token": span}
+
+
+def copy_ceiling_gbs(reps=10):
+    """The practical HBM ceiling: a plain 1 GiB bf16 copy (the library's row
+    copy with the identity permutation; the source is 4x the 256 MB Infinity
+    Cache), read + written bytes over the median of `reps` timed copies."""
+    rows, d = 1 << 16, 8192
+    src = torch.ones(rows, d, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    ident = torch.arange(rows, dtype=torch.int32, device="cuda")
+    moe.moe_permute_rows(src, ident, out=dst)
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        moe.moe_permute_rows(src, ident, out=dst)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    del src, dst
+    return round(2.0 * rows * d * 2 / (float(np.median(ts)) * 1e-3) / 1e9, 1)
 
 
 def _cores():

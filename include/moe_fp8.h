@@ -91,6 +91,23 @@ int moe_router_topk(const void* u_bf16, const void* centroids_bf16, const float*
                     int64_t T, int d, int E, int K, float* scores, int32_t* topk_idx,
                     float* topk_gate, moe_stream_t stream);
 
+/* moe_router_topk_grouped -- the group-limited variant of moe_router_topk
+ * ("DeepSeek-V3 Technical Report" notes, MoE-routing paragraph: each token is
+ * sent to at most 4 nodes).  The pages give no rule for choosing the groups;
+ * this library's reading: the E experts form n_groups groups of E/n_groups
+ * consecutive indices (one group per node), a group's score is the largest
+ * key = s + bias among its experts, the topk_groups groups with the largest
+ * scores are kept (ties to the lower group index), and the K experts are the
+ * top K of the kept groups' experts by (key descending, index ascending).
+ * Gates as in moe_router_topk.  n_groups = 1 is moe_router_topk.
+ * Limits: as moe_router_topk, plus 1 <= n_groups <= 64 dividing E,
+ * 1 <= topk_groups <= n_groups, K <= topk_groups * E / n_groups.
+ */
+int moe_router_topk_grouped(const void* u_bf16, const void* centroids_bf16, const float* bias,
+                            int64_t T, int d, int E, int K, int n_groups, int topk_groups,
+                            float* scores, int32_t* topk_idx, float* topk_gate,
+                            moe_stream_t stream);
+
 /* ------------------------------------------------------------------ dispatch
  * moe_dispatch -- turns the routing into GEMM rows.  No token is ever dropped
  * ([LINEAGE] "The idea", load-balancing bullet): there is no capacity limit.

@@ -56,6 +56,7 @@ def lib():
         L.oracle_e4m3_encode_n.argtypes = [P, i64, P]
         L.oracle_router_scores.argtypes = [P, P, i64, i32, i32, P]
         L.oracle_topk_from_scores.argtypes = [P, P, i64, i32, i32, P, P]
+        L.oracle_topk_grouped_from_scores.argtypes = [P, P, i64, i32, i32, i32, i32, P, P]
         L.oracle_dispatch.argtypes = [P, i64, i32, i32, i32, P, P, P, P]
         L.oracle_dispatch.restype = i32
         L.oracle_quant_1x128.argtypes = [P, i64, i32, P, P]
@@ -136,6 +137,26 @@ def topk_from_scores(s: np.ndarray, bias: np.ndarray, K: int):
     gate = np.empty((T, K), np.float32)
     lib().oracle_topk_from_scores(_p(s), _p(b), T, E, K, _p(idx), _p(gate))
     return idx, gate
+
+
+def topk_grouped_from_scores(s: np.ndarray, bias: np.ndarray, K: int, n_groups: int, topk_groups: int):
+    """Group-limited top-K (see moe_oracle.c): n_groups groups of consecutive
+    experts, the topk_groups groups with the largest best key are kept."""
+    s = _c(s, np.float32)
+    b = _c(bias, np.float32)
+    T, E = s.shape
+    if E % n_groups or not (1 <= topk_groups <= n_groups) or K > topk_groups * (E // n_groups):
+        raise ValueError("invalid grouping")
+    idx = np.empty((T, K), np.int32)
+    gate = np.empty((T, K), np.float32)
+    lib().oracle_topk_grouped_from_scores(_p(s), _p(b), T, E, K, n_groups, topk_groups, _p(idx), _p(gate))
+    return idx, gate
+
+
+def router_topk_grouped(u_bf16, e_bf16, bias, K: int, n_groups: int, topk_groups: int):
+    s = router_scores(u_bf16, e_bf16)
+    idx, gate = topk_grouped_from_scores(s, bias, K, n_groups, topk_groups)
+    return idx, gate, s
 
 
 def router_topk(u_bf16, e_bf16, bias, K: int):

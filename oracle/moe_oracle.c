@@ -199,6 +199,52 @@ void oracle_topk_from_scores(const float* s, const float* bias, int64_t T, int E
 }
 
 /* ------------------------------------------------------------------------ */
+/* A2, group-limited variant.  [IFS] MoE-routing paragraph: each token is    */
+/* sent to at most 4 nodes.  The pages give no rule for picking the nodes.   */
+/* READING: the E experts form n_groups groups of E/n_groups consecutive     */
+/* indices; a group's score is the largest key (as above) of its experts;    */
+/* the topk_groups groups ranked first by (score descending, group index     */
+/* ascending) are kept; the K experts are the first K of the kept groups'    */
+/* experts ranked by (key descending, index ascending).  Gates as above.     */
+/* ------------------------------------------------------------------------ */
+void oracle_topk_grouped_from_scores(const float* s, const float* bias, int64_t T, int E, int K,
+                                     int n_groups, int topk_groups, int32_t* idx, float* gate) {
+    const int gs = E / n_groups;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        float* key = (float*)malloc(sizeof(float) * (size_t)E);
+        ranked_t* grp = (ranked_t*)malloc(sizeof(ranked_t) * (size_t)n_groups);
+        ranked_t* r = (ranked_t*)malloc(sizeof(ranked_t) * (size_t)E);
+        for (int i = 0; i < E; ++i) key[i] = canonical_key(s[t * E + i] + bias[i]);
+        for (int g = 0; g < n_groups; ++g) {
+            float best = key[g * gs];
+            for (int i = g * gs + 1; i < (g + 1) * gs; ++i)
+                if (key[i] > best) best = key[i];
+            grp[g].key = best;
+            grp[g].idx = g;
+        }
+        qsort(grp, (size_t)n_groups, sizeof(ranked_t), cmp_ranked);
+        int n = 0;
+        for (int q = 0; q < topk_groups; ++q)
+            for (int i = grp[q].idx * gs; i < (grp[q].idx + 1) * gs; ++i) {
+                r[n].key = key[i];
+                r[n].idx = i;
+                ++n;
+            }
+        qsort(r, (size_t)n, sizeof(ranked_t), cmp_ranked);
+        float D = 0.0f;
+        for (int k = 0; k < K; ++k) D = D + s[t * E + r[k].idx];
+        for (int k = 0; k < K; ++k) {
+            idx[t * K + k] = r[k].idx;
+            gate[t * K + k] = (D == 0.0f) ? 0.0f : s[t * E + r[k].idx] / D;
+        }
+        free(key);
+        free(grp);
+        free(r);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* A3: dispatch.  Every (token, slot) assignment becomes one GEMM row; no     */
 /* token is dropped ([LINEAGE] "The idea", load-balancing bullet).  READING: */
 /* rows sorted by (expert, token); the shared expert's T rows follow the     */

@@ -23,7 +23,7 @@ MOE_EPI_STORE_F32, MOE_EPI_SWIGLU_F32, MOE_EPI_SWIGLU_QUANT = 0, 1, 2
 # every symbol the header declares (kept in step with include/moe_fp8.h)
 EXPORTS = (
     "moe_status_string", "moe_last_error", "moe_version",
-    "moe_router_topk",
+    "moe_router_topk", "moe_router_topk_grouped",
     "moe_dispatch_workspace_bytes", "moe_dispatch", "moe_permute_rows",
     "fp8_quant_1x128", "fp8_quant_128x128",
     "moe_gemm_workspace_bytes", "grouped_gemm_fp8_blockscaled",
@@ -54,6 +54,7 @@ def load_library(path: str = LIB_PATH):
         "moe_last_error": ([], ctypes.c_char_p),
         "moe_version": ([], I32),
         "moe_router_topk": ([P, P, P, I64, I32, I32, I32, P, P, P, P], I32),
+        "moe_router_topk_grouped": ([P, P, P, I64, I32, I32, I32, I32, I32, P, P, P, P], I32),
         "moe_dispatch_workspace_bytes": ([I64, I32], SZ),
         "moe_dispatch": ([P, I64, I32, I32, I32, P, P, P, P, P, SZ, P], I32),
         "moe_permute_rows": ([P, I32, P, I64, I32, P, P], I32),
@@ -110,8 +111,10 @@ def _new(shape, dtype, like):
 
 
 # ---------------------------------------------------------------- router
-def moe_router_topk(u, centroids, bias, K, scores=None, topk_idx=None, topk_gate=None):
-    """u bf16 [T,d], centroids bf16 [E,d], bias f32 [E] -> (idx i32 [T,K], gate f32 [T,K], scores f32 [T,E])."""
+def moe_router_topk(u, centroids, bias, K, scores=None, topk_idx=None, topk_gate=None,
+                    n_groups=1, topk_groups=1):
+    """u bf16 [T,d], centroids bf16 [E,d], bias f32 [E] -> (idx i32 [T,K], gate f32 [T,K], scores f32 [T,E]).
+    n_groups > 1 calls the group-limited variant (moe_router_topk_grouped)."""
     T, d = u.shape
     E = centroids.shape[0]
     _want(u, torch.bfloat16, (T, d), "u")
@@ -124,8 +127,13 @@ def moe_router_topk(u, centroids, bias, K, scores=None, topk_idx=None, topk_gate
     _want(topk_idx, torch.int32, (T, K), "topk_idx")
     _want(topk_gate, torch.float32, (T, K), "topk_gate")
     L = load_library()
-    _check(L.moe_router_topk(_ptr(u), _ptr(centroids), _ptr(bias), T, d, E, K, _ptr(scores),
-                             _ptr(topk_idx), _ptr(topk_gate), _stream()), "moe_router_topk")
+    if n_groups == 1:
+        _check(L.moe_router_topk(_ptr(u), _ptr(centroids), _ptr(bias), T, d, E, K, _ptr(scores),
+                                 _ptr(topk_idx), _ptr(topk_gate), _stream()), "moe_router_topk")
+    else:
+        _check(L.moe_router_topk_grouped(_ptr(u), _ptr(centroids), _ptr(bias), T, d, E, K, n_groups,
+                                         topk_groups, _ptr(scores), _ptr(topk_idx), _ptr(topk_gate),
+                                         _stream()), "moe_router_topk_grouped")
     return topk_idx, topk_gate, scores
 
 

@@ -69,10 +69,25 @@ int moe_version(void) { return 10000; }
 int moe_router_topk(const void* u_bf16, const void* centroids_bf16, const float* bias, int64_t T,
                     int d, int E, int K, float* scores, int32_t* topk_idx, float* topk_gate,
                     moe_stream_t stream) {
+    return moe_router_topk_grouped(u_bf16, centroids_bf16, bias, T, d, E, K, 1, 1, scores,
+                                   topk_idx, topk_gate, stream);
+}
+
+int moe_router_topk_grouped(const void* u_bf16, const void* centroids_bf16, const float* bias,
+                            int64_t T, int d, int E, int K, int n_groups, int topk_groups,
+                            float* scores, int32_t* topk_idx, float* topk_gate,
+                            moe_stream_t stream) {
     REQUIRE(T >= 0, MOE_ERR_SHAPE, "moe_router_topk: T < 0");
     REQUIRE(d > 0 && d % 128 == 0, MOE_ERR_SHAPE, "moe_router_topk: d=%d not a positive multiple of 128", d);
     REQUIRE(E >= 1 && E <= 256, MOE_ERR_UNSUPPORTED, "moe_router_topk: E=%d outside [1, 256]", E);
     REQUIRE(K >= 1 && K <= E && K <= 16, MOE_ERR_UNSUPPORTED, "moe_router_topk: K=%d outside [1, min(E,16)]", K);
+    REQUIRE(n_groups >= 1 && n_groups <= 64 && E % n_groups == 0, MOE_ERR_SHAPE,
+            "moe_router_topk: n_groups=%d must divide E=%d and lie in [1, 64]", n_groups, E);
+    REQUIRE(topk_groups >= 1 && topk_groups <= n_groups, MOE_ERR_SHAPE,
+            "moe_router_topk: topk_groups=%d outside [1, n_groups=%d]", topk_groups, n_groups);
+    REQUIRE(K <= topk_groups * (E / n_groups), MOE_ERR_SHAPE,
+            "moe_router_topk: K=%d exceeds the %d experts of %d kept groups", K,
+            topk_groups * (E / n_groups), topk_groups);
     if (T == 0) return MOE_OK;
     REQUIRE_PTR(u_bf16);
     REQUIRE_PTR(centroids_bf16);
@@ -84,7 +99,8 @@ int moe_router_topk(const void* u_bf16, const void* centroids_bf16, const float*
                                              static_cast<const uint16_t*>(centroids_bf16), T, d, E,
                                              scores, S(stream));
     if (e != hipSuccess) return hip_status(e, "router scores launch");
-    e = moe::launch_router_topk(scores, bias, T, E, K, topk_idx, topk_gate, S(stream));
+    e = moe::launch_router_topk(scores, bias, T, E, K, n_groups, topk_groups, topk_idx, topk_gate,
+                                S(stream));
     return hip_status(e, "router top-k launch");
 }
 
@@ -381,7 +397,7 @@ int moe_layer_forward(const void* u_bf16, const void* centroids_bf16, const floa
     e = moe::launch_router_scores(static_cast<const uint16_t*>(u_bf16),
                                   static_cast<const uint16_t*>(centroids_bf16), T, d, E, w.scores, st);
     if (e != hipSuccess) return hip_status(e, "router scores launch");
-    e = moe::launch_router_topk(w.scores, bias, T, E, K, w.idx, w.gate, st);
+    e = moe::launch_router_topk(w.scores, bias, T, E, K, 1, 1, w.idx, w.gate, st);
     if (e != hipSuccess) return hip_status(e, "router top-k launch");
     e = moe::launch_dispatch(w.idx, T, K, E, 1, w.count, w.go, w.row_token, w.slot_row, w.dws, st);
     if (e != hipSuccess) return hip_status(e, "dispatch launch");

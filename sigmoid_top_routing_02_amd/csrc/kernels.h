@@ -12,8 +12,10 @@ namespace moe {
 // router.hip
 hipError_t launch_router_scores(const uint16_t* u, const uint16_t* e, int64_t T, int d, int E,
                                 float* s, hipStream_t st);
+// n_groups = 1: plain top-K; otherwise group-limited (see router_topk_kernel)
 hipError_t launch_router_topk(const float* s, const float* bias, int64_t T, int E, int K,
-                              int32_t* idx, float* gate, hipStream_t st);
+                              int n_groups, int topk_groups, int32_t* idx, float* gate,
+                              hipStream_t st);
 
 // dispatch.hip
 size_t dispatch_ws_bytes(int64_t T, int E);

@@ -244,10 +244,31 @@ __global__ __launch_bounds__(256) void router_scores_small_kernel(
     if (t < T && ex < E) s[t * E + ex] = sigmoid_fixed(acc);
 }
 
+// wave-wide maximum of a 64-bit key
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const uint32_t lo = __shfl_xor((uint32_t)v, off, 64);
+        const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, 64);
+        const uint64_t o = ((uint64_t)hi << 32) | lo;
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
 // One wavefront per token.  Lane l holds experts l, l+64, l+128, l+192.
+// Each expert's 64-bit key is (orderable(s + b) << 32) | (~index), so the
+// largest key is the largest biased score with ties to the lower index, and 0
+// marks an expert that is taken or not eligible.
+// Group-limited selection (n_groups > 1): the experts form n_groups groups of
+// E / n_groups consecutive indices; a group's score is the largest key of its
+// experts, the topk_groups best groups are kept (ties to the lower group,
+// which the index part of the key gives), and the K experts are chosen among
+// the kept groups' experts only.
 __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ s,
                                                           const float* __restrict__ bias,
                                                           int64_t T, int E, int K,
+                                                          int n_groups, int topk_groups,
                                                           int32_t* __restrict__ idx,
                                                           float* __restrict__ gate) {
     const int lane = threadIdx.x & 63;
@@ -265,18 +286,41 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
             key[j] = ((uint64_t)orderable_key(kv) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)ex);
         }
     }
+    if (n_groups > 1) {
+        const int gs = E / n_groups;
+        // lane g < n_groups ends up holding group g's score
+        uint64_t gscore = 0;
+        for (int g = 0; g < n_groups; ++g) {
+            uint64_t m = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int ex = lane + 64 * j;
+                if (ex < E && ex / gs == g) m = key[j] > m ? key[j] : m;
+            }
+            m = wave_max_u64(m);
+            if (lane == g) gscore = m;
+        }
+        uint64_t kept = 0;                       // bit g: group g is kept
+        for (int r = 0; r < topk_groups; ++r) {
+            const uint64_t best = wave_max_u64(gscore);
+            const uint64_t win = __ballot(gscore == best && best != 0);
+            if (win == 0) break;
+            const int g = __builtin_ctzll(win);
+            kept |= 1ull << g;
+            if (lane == g) gscore = 0;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int ex = lane + 64 * j;
+            if (ex < E && !((kept >> (ex / gs)) & 1ull)) key[j] = 0;
+        }
+    }
     int chosen[16];
     for (int k = 0; k < K; ++k) {
         uint64_t best = key[0];
 #pragma unroll
         for (int j = 1; j < 4; ++j) best = key[j] > best ? key[j] : best;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const uint32_t lo = __shfl_xor((uint32_t)best, off, 64);
-            const uint32_t hi = __shfl_xor((uint32_t)(best >> 32), off, 64);
-            const uint64_t o = ((uint64_t)hi << 32) | lo;
-            best = o > best ? o : best;
-        }
+        best = wave_max_u64(best);
         const int ex = (int)(0xFFFFFFFFu - (uint32_t)best);
         chosen[k] = ex;
 #pragma unroll
@@ -324,9 +368,11 @@ hipError_t launch_router_scores(const uint16_t* u, const uint16_t* e, int64_t T,
 }
 
 hipError_t launch_router_topk(const float* s, const float* bias, int64_t T, int E, int K,
-                              int32_t* idx, float* gate, hipStream_t st) {
+                              int n_groups, int topk_groups, int32_t* idx, float* gate,
+                              hipStream_t st) {
     dim3 grid((unsigned)((T + 3) / 4));
-    hipLaunchKernelGGL(router_topk_kernel, grid, dim3(256), 0, st, s, bias, T, E, K, idx, gate);
+    hipLaunchKernelGGL(router_topk_kernel, grid, dim3(256), 0, st, s, bias, T, E, K, n_groups,
+                       topk_groups, idx, gate);
     return hipGetLastError();
 }
 

@@ -57,6 +57,12 @@ def test_router_argument_errors(L):
     assert L.moe_router_topk(None, FAKE, FAKE, 8, 128, 16, 4, FAKE, FAKE, FAKE, None) == -1
     assert L.moe_router_topk(MISALIGNED, FAKE, FAKE, 8, 128, 16, 4, FAKE, FAKE, FAKE, None) == -5
     assert L.moe_router_topk(None, None, None, 0, 128, 16, 4, None, None, None, None) == 0  # T = 0
+    g = L.moe_router_topk_grouped
+    assert g(FAKE, FAKE, FAKE, 8, 128, 256, 8, 7, 2, FAKE, FAKE, FAKE, None) == -2    # 7 does not divide 256
+    assert g(FAKE, FAKE, FAKE, 8, 128, 256, 8, 8, 9, FAKE, FAKE, FAKE, None) == -2    # keep > groups
+    assert g(FAKE, FAKE, FAKE, 8, 128, 256, 8, 128, 2, FAKE, FAKE, FAKE, None) == -2  # > 64 groups
+    assert g(FAKE, FAKE, FAKE, 8, 128, 256, 9, 64, 2, FAKE, FAKE, FAKE, None) == -2   # K > 2 * 4 kept experts
+    assert g(None, FAKE, FAKE, 8, 128, 256, 8, 8, 4, FAKE, FAKE, FAKE, None) == -1
 
 
 def test_dispatch_argument_errors(L):

@@ -55,6 +55,33 @@ def test_router_bit_exact(T, d, E, K):
     np.testing.assert_array_equal(np_(gate).view(np.uint32), gate_ref.view(np.uint32))
 
 
+GROUPED_CASES = [
+    # (T, d, E, K, n_groups, topk_groups)
+    (300, 512, 256, 8, 8, 4),      # the pages' shape: 8 groups of 32, at most 4 per token
+    (1000, 256, 64, 6, 8, 3),      # groups of 8
+    (37, 128, 16, 4, 4, 2),        # ragged T, groups of 4, with score ties
+    (256, 7168, 256, 8, 8, 4),     # decode-layout scores
+    (8200, 128, 256, 8, 64, 2),    # 64 groups of 4: K equals the kept experts
+    (50, 256, 200, 6, 8, 3),       # groups of 25 straddle the lanes' expert slots
+    (64, 128, 96, 5, 1, 1),        # one group: plain top-K
+]
+
+
+@pytest.mark.parametrize("T,d,E,K,ng,m", GROUPED_CASES)
+def test_router_grouped_bit_exact(T, d, E, K, ng, m):
+    say(f"grouped router T={T} d={d} E={E} K={K} groups={ng} keep={m}")
+    u, e, b = _inputs(T, d, E, seed=T * 11 + E + ng, ties=True)
+    idx, gate, s = moe.moe_router_topk(u.to(dev()), e.to(dev()), b.to(dev()), K, n_groups=ng,
+                                       topk_groups=m)
+    torch.cuda.synchronize()
+    s_ref = oracle.router_scores(u16(u), u16(e))
+    np.testing.assert_array_equal(np_(s).view(np.uint32), s_ref.view(np.uint32))
+    idx_ref, gate_ref = oracle.topk_grouped_from_scores(s_ref, b.numpy(), K, ng, m)
+    np.testing.assert_array_equal(np_(idx), idx_ref)
+    np.testing.assert_array_equal(np_(gate).view(np.uint32), gate_ref.view(np.uint32))
+    assert max(len(set(r.tolist())) for r in np_(idx) // (E // ng)) <= m
+
+
 def test_router_tiny_workload_and_determinism():
     sh = workloads.SHAPES["tiny"]
     u, e, b = workloads.activations(sh), workloads.centroids(sh), workloads.bias(sh)

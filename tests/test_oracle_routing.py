@@ -245,3 +245,83 @@ def test_bias_update_feedback_balances_load(oracle_mod):
         c = np.bincount(idx.ravel(), minlength=E).astype(np.int32)
         b = oracle_mod.bias_update(b, c, T * K, 0.01)
     assert c.max() / c.mean() < 0.5 * c0.max() / c0.mean()
+
+
+# ---------------------------------------------------------------- group-limited routing
+# "DeepSeek-V3 Technical Report" notes, MoE-routing paragraph: each token is
+# sent to at most 4 nodes.  The group rule (a group's score is its best key;
+# the topk_groups best groups are kept) is this build's reading, so these pins
+# fix the reading's consequences: its reductions to plain top-K, brute force
+# over all group subsets, a worked example, and the "at most M groups" fact.
+
+def test_grouped_topk_reduces_to_plain_topk(oracle_mod):
+    rng = np.random.default_rng(30)
+    T, E, K = 200, 64, 6
+    s = rng.uniform(0, 1, (T, E)).astype(np.float32)
+    b = rng.uniform(-0.05, 0.05, E).astype(np.float32)
+    idx0, g0 = oracle_mod.topk_from_scores(s, b, K)
+    for ng, m in [(1, 1), (8, 8), (64, 64), (16, 16)]:
+        idx, g = oracle_mod.topk_grouped_from_scores(s, b, K, ng, m)
+        np.testing.assert_array_equal(idx, idx0)
+        np.testing.assert_array_equal(g.view(np.uint32), g0.view(np.uint32))
+
+
+def test_grouped_topk_brute_force_over_group_subsets(oracle_mod):
+    """The kept groups are the M-subset whose scores, sorted descending, are
+    largest (ties to lower group indices); the experts are then the top K of
+    that subset's experts (itself brute-forced over K-subsets)."""
+    rng = np.random.default_rng(31)
+    for E, ng, m, K in [(8, 4, 2, 3), (12, 4, 2, 4), (12, 6, 3, 2), (16, 8, 2, 4), (16, 4, 1, 4)]:
+        gs = E // ng
+        T = 30
+        s = rng.uniform(0, 1, (T, E)).astype(np.float32)
+        s[:, gs] = s[:, 0]              # equal best keys in groups 0 and 1 for some tokens
+        b = np.zeros(E, np.float32)
+        idx, gate = oracle_mod.topk_grouped_from_scores(s, b, K, ng, m)
+        key = _keys(s, b)
+        for t in range(T):
+            score = [max(float(key[t, i]) for i in range(g * gs, (g + 1) * gs)) for g in range(ng)]
+            kept = max(itertools.combinations(range(ng), m),
+                       key=lambda c: (sorted((score[g] for g in c), reverse=True), [-g for g in sorted(c)]))
+            cand = [i for g in kept for i in range(g * gs, (g + 1) * gs)]
+            best = max(itertools.combinations(cand, K),
+                       key=lambda c: (sorted((float(key[t, i]) for i in c), reverse=True),
+                                      [-i for i in sorted(c)]))
+            assert set(best) == set(idx[t].tolist())
+            # slot order: key descending, index ascending
+            assert list(idx[t]) == sorted(best, key=lambda i: (-float(key[t, i]), i))
+
+
+def test_grouped_topk_worked_example(oracle_mod):
+    """8 experts in 4 groups of 2, keep 2 groups, K = 3.  Keys by expert:
+    0.9 0.1 | 0.8 0.7 | 0.85 0.2 | 0.3 0.3.  Group scores 0.9, 0.8, 0.85, 0.3:
+    groups 0 and 2 are kept, so the experts are 0 (0.9), 4 (0.85), 5 (0.2),
+    while plain top-3 would take 0, 4, 2."""
+    s = np.array([[0.9, 0.1, 0.8, 0.7, 0.85, 0.2, 0.3, 0.3]], np.float32)
+    b = np.zeros(8, np.float32)
+    idx, gate = oracle_mod.topk_grouped_from_scores(s, b, 3, 4, 2)
+    assert idx.tolist() == [[0, 4, 5]]
+    assert oracle_mod.topk_from_scores(s, b, 3)[0].tolist() == [[0, 4, 2]]
+    D = np.float32(np.float32(np.float32(0.9) + np.float32(0.85)) + np.float32(0.2))
+    np.testing.assert_array_equal(gate[0], (s[0, [0, 4, 5]] / D).astype(np.float32))
+
+
+def test_grouped_topk_at_most_m_groups_and_bias_invariant_gates(oracle_mod):
+    rng = np.random.default_rng(32)
+    T, E, K, ng, m = 400, 256, 8, 8, 4
+    s = oracle_mod.sigmoid_spec_array(rng.standard_normal((T, E)).astype(np.float32))
+    b = rng.uniform(-0.05, 0.05, E).astype(np.float32)
+    idx, gate = oracle_mod.topk_grouped_from_scores(s, b, K, ng, m)
+    groups = idx // (E // ng)
+    assert max(len(set(r.tolist())) for r in groups) <= m
+    assert all(len(set(r.tolist())) == K for r in idx)
+    assert np.max(np.abs(gate.astype(np.float64).sum(1) - 1.0)) <= K * 2.0 ** -23
+    raw = np.take_along_axis(s, idx, 1).astype(np.float64)
+    np.testing.assert_allclose(gate, raw / raw.sum(1, keepdims=True), rtol=3e-7)
+    # raising the bias of a token's chosen experts keeps its choice and gates
+    bump = np.zeros(E, np.float32)
+    t0 = 0
+    bump[idx[t0]] = 0.5
+    idx2, gate2 = oracle_mod.topk_grouped_from_scores(s[t0:t0 + 1], b + bump, K, ng, m)
+    assert set(idx2[0].tolist()) == set(idx[t0].tolist())
+    np.testing.assert_array_equal(np.sort(gate2[0]), np.sort(gate[t0]))
