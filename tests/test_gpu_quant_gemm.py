@@ -335,3 +335,36 @@ def test_mfma_accumulation_probe(M, N, K):
     say(f"  per-row rel err: promoted {errp:.3e}, chained {errc:.3e}")
     assert errp <= TOL
     assert errc <= 0.1
+
+
+@pytest.mark.parametrize("K", [4096, 16384])
+def test_dense_full_size_sampled(K):
+    """The dense block-scaled GEMM workload at full size (M = 8192, N = 7168;
+    A and B ~ N(0,1) with 0.1% outliers x100), in the launch configuration the
+    benchmark times (one group, FP32 store).  Sampled A rows: their 1x128
+    codes and scales and every 128x128 code and scale of B bit-exact against
+    the oracle's quantisers, then those rows of C (all 7168 columns) within
+    the per-row bound of the oracle's FP64 product of the same operands."""
+    import workloads
+    M, N = workloads.DENSE["M"], workloads.DENSE["N"]
+    say(f"dense full size M={M} N={N} K={K}")
+    a, b = workloads.dense_operands(M, N, K, device=dev())
+    aq, as_ = moe.fp8_quant_1x128(a)
+    bq, bs = moe.fp8_quant_128x128(b)
+    go = torch.tensor([0, M], dtype=torch.int32, device=dev())
+    ws = torch.empty(moe.moe_gemm_workspace_bytes(1, M, N, K), dtype=torch.uint8, device=dev())
+    out = moe.grouped_gemm_fp8_blockscaled(aq, as_, go, M, bq.view(1, N, K), bs.view(1, N // 128, K // 128),
+                                           ws=ws)
+    torch.cuda.synchronize()
+    rows = sorted({0, M - 1} | set(np.random.default_rng(K).integers(0, M, 6).tolist()))
+    a_rows = np_(a[rows])
+    qa_ref, sa_ref = oracle.quant_1x128(a_rows)
+    np.testing.assert_array_equal(np_(aq[rows]), qa_ref)
+    np.testing.assert_array_equal(np_(as_[rows]).view(np.uint32), sa_ref.view(np.uint32))
+    qb_ref, sb_ref = oracle.quant_128x128(np_(b))
+    np.testing.assert_array_equal(np_(bq), qb_ref)
+    np.testing.assert_array_equal(np_(bs).view(np.uint32), sb_ref.view(np.uint32))
+    ref = oracle.gemm_blockscaled(qa_ref, sa_ref, qb_ref, sb_ref)
+    err = rowinf_rel(np_(out[rows]), ref)
+    say(f"  per-row rel err {err:.3e} over {len(rows)} rows")
+    assert err <= TOL
