@@ -237,3 +237,40 @@ def test_layer_full_size_sampled(name):
     busiest = int(cnt.argmax())
     # the busiest expert's FFN is checked on every one of its rows
     check_layer(sh, u, e, b, packed, g_out, token_sample=tokens, expert_check=[busiest])
+
+
+@pytest.mark.parametrize("T", [128, 2048])
+def test_layer_graph_capture_replays(T):
+    """moe_layer_forward captured in a HIP graph (it allocates nothing, reads
+    nothing back to the host and records no memset) and replayed three times,
+    with eager layer calls on other inputs in between: every replay equals the
+    eager result bit for bit.  T = 128 runs the 32-row GEMM tiles, T = 2048
+    (about 600 rows per group) the 128-row tiles."""
+    sh = workloads.custom_shape(T=T, d=512, E=16, K=4, I=256)
+    say(f"layer graph capture T={T}")
+    u = workloads.activations(sh).to(dev())
+    e, b = workloads.centroids(sh).to(dev()), workloads.bias(sh).to(dev())
+    packed = pack_all(sh)
+    ws = torch.empty(moe.load_library().moe_layer_workspace_bytes(T, sh.d, sh.E, sh.K, sh.I),
+                     dtype=torch.uint8, device=dev())
+    out = torch.empty(T, sh.d, device=dev())
+    ref = moe.moe_layer_forward(u, e, b, packed, sh.K, sh.I).clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        moe.moe_layer_forward(u, e, b, packed, sh.K, sh.I, out=out, ws=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        moe.moe_layer_forward(u, e, b, packed, sh.K, sh.I, out=out, ws=ws)
+    torch.cuda.synchronize()
+    u2 = torch.flip(u, dims=[0]).contiguous()
+    for rep in range(3):
+        out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), ref.view(torch.int32)), rep
+        other = moe.moe_layer_forward(u2, e, b, packed, sh.K, sh.I)      # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(other[0].view(torch.int32), ref[T - 1].view(torch.int32))
