@@ -363,6 +363,7 @@ def run_rdc(steps, warmup, with_cpu):
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
     stages = {n: round(ev.avg_ms(n), 4) for n in ev.pairs}
+    balance = balance_loss_timing(st, steps)
     grouped = grouped_router_timing(u, e, b, K, st, steps)
     # algorithmic bytes of the combine: K bf16 rows of X_perm + u read, FP32 h' written, gates and slots
     comb_bytes = T * K * d * 2 + T * d * 2 + T * d * 4 + T * K * 8
@@ -383,6 +384,7 @@ def run_rdc(steps, warmup, with_cpu):
         "stages_ms": stages,
         "permute_gbs": round(perm_bytes / (ev.avg_ms("permute") * 1e-3) / 1e9, 1),
         "grouped_router": grouped,
+        "seq_balance_loss": balance,
         "router_tflops": round(2.0 * T * E * d / (ev.avg_ms("router") * 1e-3) / 1e12, 2),
     }
     if with_cpu:
@@ -419,6 +421,24 @@ def copy_calibration():
         moe.moe_permute_rows(src, ident, out=dst)
     torch.cuda.synchronize()
     del src, dst
+
+
+def balance_loss_timing(st, steps, seq_len=4096, alpha=1e-4):
+    """The sequence-wise balance loss over the batch's scores and choices
+    (sequences of 4096 tokens): time, the bytes it reads per second, values."""
+    T, E = st["scores"].shape
+    K = st["idx"].shape[1]
+    moe.moe_seq_balance_loss(st["scores"], st["idx"], seq_len, alpha)
+    ev = Events()
+    for _ in range(steps):
+        a0 = ev.mark("s")
+        loss = moe.moe_seq_balance_loss(st["scores"], st["idx"], seq_len, alpha)
+        ev.add("loss", a0, ev.mark("e"))
+    torch.cuda.synchronize()
+    ms = ev.avg_ms("loss")
+    return {"seq_len": seq_len, "alpha": alpha, "ms": round(ms, 4),
+            "read_gbs": round((T * E * 4 + T * K * 4) / (ms * 1e-3) / 1e9, 1),
+            "loss": [round(float(x), 8) for x in loss.cpu()]}
 
 
 def grouped_router_timing(u, e, b, K, st, steps, n_groups=8, topk_groups=4):

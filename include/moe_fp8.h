@@ -108,6 +108,28 @@ int moe_router_topk_grouped(const void* u_bf16, const void* centroids_bf16, cons
                             float* scores, int32_t* topk_idx, float* topk_gate,
                             moe_stream_t stream);
 
+/* moe_seq_balance_loss -- [IFS] bias paragraph: a very small sequence-wise
+ * loss remains against extreme imbalance within one sequence.  The pages give
+ * no formula; this library's reading, per sequence of seq_len = L tokens
+ * (tokens [q L, (q+1) L) form sequence q):
+ *   f_i = E / (K L) * #{tokens of the sequence whose topk_idx holds i}
+ *   P_i = (1/L) * sum_t scores[t,i] / sum_j scores[t,j]   (a token whose
+ *         scores sum to 0 adds nothing)
+ *   loss[q] = alpha * sum_i f_i P_i                         (FP32)
+ * Uniform use gives alpha; all tokens on the same K experts, with all their
+ * score there, give alpha * E / K.  scores FP32 [T,E] (moe_router_topk's
+ * scores output); topk_idx int32 [T,K] (values outside [0,E) are not
+ * counted); loss FP32 [T / seq_len].  Deterministic.  ws: scratch of
+ * moe_seq_balance_loss_workspace_bytes(T, seq_len) bytes (per-chunk partial
+ * sums; no setup needed; 0 for invalid sizes).
+ * Limits: T % seq_len == 0, T / seq_len <= 65535, 1 <= E <= 256,
+ * 1 <= K <= min(E, 16).
+ */
+size_t moe_seq_balance_loss_workspace_bytes(int64_t T, int seq_len);
+int moe_seq_balance_loss(const float* scores, const int32_t* topk_idx, int64_t T, int E, int K,
+                         int seq_len, float alpha, float* loss, void* ws, size_t ws_bytes,
+                         moe_stream_t stream);
+
 /* ------------------------------------------------------------------ dispatch
  * moe_dispatch -- turns the routing into GEMM rows.  No token is ever dropped
  * ([LINEAGE] "The idea", load-balancing bullet): there is no capacity limit.

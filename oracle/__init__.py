@@ -57,6 +57,7 @@ def lib():
         L.oracle_router_scores.argtypes = [P, P, i64, i32, i32, P]
         L.oracle_topk_from_scores.argtypes = [P, P, i64, i32, i32, P, P]
         L.oracle_topk_grouped_from_scores.argtypes = [P, P, i64, i32, i32, i32, i32, P, P]
+        L.oracle_seq_balance_loss.argtypes = [P, P, i64, i32, i32, i32, ctypes.c_double, P]
         L.oracle_dispatch.argtypes = [P, i64, i32, i32, i32, P, P, P, P]
         L.oracle_dispatch.restype = i32
         L.oracle_quant_1x128.argtypes = [P, i64, i32, P, P]
@@ -163,6 +164,18 @@ def router_topk(u_bf16, e_bf16, bias, K: int):
     s = router_scores(u_bf16, e_bf16)
     idx, gate = topk_from_scores(s, bias, K)
     return idx, gate, s
+
+
+def seq_balance_loss(s, idx, seq_len: int, alpha: float) -> np.ndarray:
+    """Per-sequence balance loss in FP64 (see moe_oracle.c for the reading)."""
+    s = _c(s, np.float32)
+    idx = _c(idx, np.int32)
+    T, E = s.shape
+    K = idx.shape[1]
+    assert seq_len >= 1 and T % seq_len == 0
+    out = np.empty(T // seq_len, np.float64)
+    lib().oracle_seq_balance_loss(_p(s), _p(idx), T, E, K, seq_len, float(alpha), _p(out))
+    return out
 
 
 # ---------------------------------------------------------------- dispatch

@@ -245,6 +245,39 @@ void oracle_topk_grouped_from_scores(const float* s, const float* bias, int64_t 
 }
 
 /* ------------------------------------------------------------------------ */
+/* Sequence-wise balance loss.  [IFS] bias paragraph: a tiny sequence-wise   */
+/* loss remains against extreme imbalance.  No formula on the pages.         */
+/* READING, per sequence q of L tokens [qL, qL+L):                           */
+/*   f_i = E/(K L) * #{t in q : i among idx[t, 0..K-1]}                      */
+/*   P_i = (1/L) sum_t s[t,i] / sum_j s[t,j]  (a row summing to 0 adds 0)    */
+/*   loss[q] = alpha * sum_i f_i P_i, all in FP64.                           */
+/* ------------------------------------------------------------------------ */
+void oracle_seq_balance_loss(const float* s, const int32_t* idx, int64_t T, int E, int K, int L,
+                             double alpha, double* loss) {
+    const int64_t nseq = T / L;
+    for (int64_t q = 0; q < nseq; ++q) {
+        double* P = (double*)calloc((size_t)E, sizeof(double));
+        double* f = (double*)calloc((size_t)E, sizeof(double));
+        for (int64_t t = q * L; t < (q + 1) * L; ++t) {
+            double rs = 0.0;
+            for (int j = 0; j < E; ++j) rs += (double)s[t * E + j];
+            if (rs != 0.0)
+                for (int i = 0; i < E; ++i) P[i] += (double)s[t * E + i] / rs;
+            for (int k = 0; k < K; ++k) {
+                const int e = idx[t * K + k];
+                if (e >= 0 && e < E) f[e] += 1.0;
+            }
+        }
+        double sum = 0.0;
+        for (int i = 0; i < E; ++i)
+            sum += ((double)E / ((double)K * L) * f[i]) * (P[i] / L);
+        loss[q] = alpha * sum;
+        free(P);
+        free(f);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* A3: dispatch.  Every (token, slot) assignment becomes one GEMM row; no     */
 /* token is dropped ([LINEAGE] "The idea", load-balancing bullet).  READING: */
 /* rows sorted by (expert, token); the shared expert's T rows follow the     */

@@ -24,6 +24,7 @@ MOE_EPI_STORE_F32, MOE_EPI_SWIGLU_F32, MOE_EPI_SWIGLU_QUANT = 0, 1, 2
 EXPORTS = (
     "moe_status_string", "moe_last_error", "moe_version",
     "moe_router_topk", "moe_router_topk_grouped",
+    "moe_seq_balance_loss_workspace_bytes", "moe_seq_balance_loss",
     "moe_dispatch_workspace_bytes", "moe_dispatch", "moe_permute_rows",
     "fp8_quant_1x128", "fp8_quant_128x128",
     "moe_gemm_workspace_bytes", "grouped_gemm_fp8_blockscaled",
@@ -55,6 +56,8 @@ def load_library(path: str = LIB_PATH):
         "moe_version": ([], I32),
         "moe_router_topk": ([P, P, P, I64, I32, I32, I32, P, P, P, P], I32),
         "moe_router_topk_grouped": ([P, P, P, I64, I32, I32, I32, I32, I32, P, P, P, P], I32),
+        "moe_seq_balance_loss_workspace_bytes": ([I64, I32], SZ),
+        "moe_seq_balance_loss": ([P, P, I64, I32, I32, I32, F32, P, P, SZ, P], I32),
         "moe_dispatch_workspace_bytes": ([I64, I32], SZ),
         "moe_dispatch": ([P, I64, I32, I32, I32, P, P, P, P, P, SZ, P], I32),
         "moe_permute_rows": ([P, I32, P, I64, I32, P, P], I32),
@@ -135,6 +138,24 @@ def moe_router_topk(u, centroids, bias, K, scores=None, topk_idx=None, topk_gate
                                          topk_groups, _ptr(scores), _ptr(topk_idx), _ptr(topk_gate),
                                          _stream()), "moe_router_topk_grouped")
     return topk_idx, topk_gate, scores
+
+
+def moe_seq_balance_loss(scores, topk_idx, seq_len, alpha, ws=None):
+    """Per-sequence balance loss (f32 [T/seq_len]) from the router's scores
+    f32 [T,E] and topk_idx i32 [T,K]."""
+    T, E = scores.shape
+    K = topk_idx.shape[1]
+    _want(scores, torch.float32, (T, E), "scores")
+    _want(topk_idx, torch.int32, (T, K), "topk_idx")
+    if seq_len < 1 or T % seq_len:
+        raise MoEError("moe_seq_balance_loss: T must be a multiple of seq_len")
+    loss = _new((T // seq_len,), torch.float32, scores)
+    L = load_library()
+    if ws is None:
+        ws = _new((max(L.moe_seq_balance_loss_workspace_bytes(T, seq_len), 256),), torch.uint8, scores)
+    _check(L.moe_seq_balance_loss(_ptr(scores), _ptr(topk_idx), T, E, K, seq_len, alpha, _ptr(loss),
+                                  _ptr(ws), ws.numel(), _stream()), "moe_seq_balance_loss")
+    return loss
 
 
 # ---------------------------------------------------------------- dispatch

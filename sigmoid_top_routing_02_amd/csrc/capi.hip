@@ -104,6 +104,34 @@ int moe_router_topk_grouped(const void* u_bf16, const void* centroids_bf16, cons
     return hip_status(e, "router top-k launch");
 }
 
+size_t moe_seq_balance_loss_workspace_bytes(int64_t T, int seq_len) {
+    if (T <= 0 || seq_len < 1 || T % seq_len) return 0;
+    return moe::seq_balance_ws_bytes(T / seq_len, seq_len);
+}
+
+int moe_seq_balance_loss(const float* scores, const int32_t* topk_idx, int64_t T, int E, int K,
+                         int seq_len, float alpha, float* loss, void* ws, size_t ws_bytes,
+                         moe_stream_t stream) {
+    REQUIRE(T >= 0, MOE_ERR_SHAPE, "moe_seq_balance_loss: T < 0");
+    REQUIRE(E >= 1 && E <= 256, MOE_ERR_UNSUPPORTED, "moe_seq_balance_loss: E=%d outside [1, 256]", E);
+    REQUIRE(K >= 1 && K <= E && K <= 16, MOE_ERR_UNSUPPORTED, "moe_seq_balance_loss: K=%d outside [1, min(E,16)]", K);
+    REQUIRE(seq_len >= 1 && T % seq_len == 0, MOE_ERR_SHAPE,
+            "moe_seq_balance_loss: T=%lld is not a multiple of seq_len=%d", (long long)T, seq_len);
+    REQUIRE(T / seq_len <= 65535 && (T / seq_len) * ((seq_len + 63) / 64) <= 0x7FFFFFFF, MOE_ERR_UNSUPPORTED,
+            "moe_seq_balance_loss: too many sequences");
+    if (T == 0) return MOE_OK;
+    REQUIRE(ws_bytes >= moe_seq_balance_loss_workspace_bytes(T, seq_len), MOE_ERR_WORKSPACE,
+            "moe_seq_balance_loss: workspace of %zu bytes, %zu needed", ws_bytes,
+            moe_seq_balance_loss_workspace_bytes(T, seq_len));
+    REQUIRE_PTR(scores);
+    REQUIRE_PTR(topk_idx);
+    REQUIRE_PTR(loss);
+    REQUIRE_PTR(ws);
+    return hip_status(moe::launch_seq_balance_loss(scores, topk_idx, T / seq_len, E, K, seq_len, alpha,
+                                                   loss, ws, S(stream)),
+                      "balance loss launch");
+}
+
 size_t moe_dispatch_workspace_bytes(int64_t T, int E) {
     if (T <= 0 || E <= 0) return 0;
     return moe::dispatch_ws_bytes(T, E);

@@ -41,6 +41,11 @@ hipError_t launch_grouped_gemm(const uint8_t* a_q, const float* a_s, const int32
                                float* out, uint8_t* out_q, float* out_s, void* ws,
                                hipStream_t st);
 
+// balance.hip
+size_t seq_balance_ws_bytes(int64_t n_seq, int L);
+hipError_t launch_seq_balance_loss(const float* s, const int32_t* idx, int64_t n_seq, int E, int K,
+                                   int L, float alpha, float* loss, void* ws, hipStream_t st);
+
 // accum_probe.hip
 hipError_t launch_accum_probe(const uint8_t* a_q, const uint8_t* b_q, int M, int N, int K,
                               int chained, float* out, hipStream_t st);

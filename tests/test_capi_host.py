@@ -101,6 +101,20 @@ def test_quant_and_gemm_argument_errors(L):
                                           FAKE, None, None, FAKE, gw, None) == -3
 
 
+def test_balance_loss_argument_errors(L):
+    need = L.moe_seq_balance_loss_workspace_bytes(100, 10)
+    assert need >= 10 * 2048                                              # one 64-token chunk per sequence
+    assert L.moe_seq_balance_loss_workspace_bytes(100, 30) == 0            # 30 does not divide 100
+    f = L.moe_seq_balance_loss
+    assert f(FAKE, FAKE, 100, 16, 4, 30, 1e-3, FAKE, FAKE, need, None) == -2      # T % seq_len
+    assert f(FAKE, FAKE, 100, 300, 4, 10, 1e-3, FAKE, FAKE, need, None) == -3     # E > 256
+    assert f(FAKE, FAKE, 100, 16, 17, 10, 1e-3, FAKE, FAKE, need, None) == -3     # K > 16
+    assert f(FAKE, FAKE, 100, 16, 4, 0, 1e-3, FAKE, FAKE, need, None) == -2       # seq_len 0
+    assert f(FAKE, FAKE, 100, 16, 4, 10, 1e-3, FAKE, FAKE, need - 1, None) == -4  # workspace
+    assert f(FAKE, None, 100, 16, 4, 10, 1e-3, FAKE, FAKE, need, None) == -1
+    assert f(None, None, 0, 16, 4, 10, 1e-3, None, None, 0, None) == 0            # T = 0
+
+
 def test_accumulation_probe_argument_errors(L):
     f = L.moe_fp8_mfma_accumulation_probe
     assert f(FAKE, FAKE, 20, 16, 128, 0, FAKE, None) == -2          # M % 16

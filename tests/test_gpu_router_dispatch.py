@@ -229,3 +229,21 @@ def test_permute_combine_past_grid_rows(ydt):
     err = rowinf_rel(np_(out), ref)
     say(f"  per-row rel err {err:.3e}")
     assert err <= TOL
+
+
+@pytest.mark.parametrize("T,E,K,L", [(8192, 256, 8, 4096), (300, 64, 6, 300), (257, 16, 4, 1), (1040, 200, 8, 80)])
+def test_seq_balance_loss(T, E, K, L):
+    """The sequence-wise balance loss on the router's own scores and choices
+    against the oracle's FP64 value (relative 1e-5: FP32 sums over a sequence)."""
+    d = 256
+    u, e, b = _inputs(T, d, E, seed=T + E + L)
+    say(f"balance loss T={T} E={E} K={K} seq_len={L}")
+    idx, gate, s = moe.moe_router_topk(u.to(dev()), e.to(dev()), b.to(dev()), K)
+    loss = moe.moe_seq_balance_loss(s, idx, L, 1e-4)
+    torch.cuda.synchronize()
+    ref = oracle.seq_balance_loss(np_(s), np_(idx), L, 1e-4)
+    np.testing.assert_allclose(np_(loss), ref, rtol=1e-5)
+    # deterministic: a second call gives the same bits
+    again = moe.moe_seq_balance_loss(s, idx, L, 1e-4)
+    torch.cuda.synchronize()
+    assert torch.equal(again.view(torch.int32), loss.view(torch.int32))

@@ -325,3 +325,51 @@ def test_grouped_topk_at_most_m_groups_and_bias_invariant_gates(oracle_mod):
     idx2, gate2 = oracle_mod.topk_grouped_from_scores(s[t0:t0 + 1], b + bump, K, ng, m)
     assert set(idx2[0].tolist()) == set(idx[t0].tolist())
     np.testing.assert_array_equal(np.sort(gate2[0]), np.sort(gate[t0]))
+
+
+# ---------------------------------------------------------------- sequence-wise balance loss
+# The pages name the loss but give no formula; the reading (frequency times
+# normalised score, per sequence) is pinned by its closed forms and invariances.
+
+def test_seq_balance_loss_uniform_use_gives_alpha(oracle_mod):
+    """Every expert chosen equally often and equal scores: f_i = 1, P_i = 1/E."""
+    E, K, L = 16, 4, 32
+    s = np.full((2 * L, E), 0.3, np.float32)
+    idx = np.array([[(t * K + k) % E for k in range(K)] for t in range(2 * L)], np.int32)
+    np.testing.assert_allclose(oracle_mod.seq_balance_loss(s, idx, L, 0.01), [0.01, 0.01], rtol=1e-14)
+
+
+def test_seq_balance_loss_extreme_imbalance_gives_alpha_e_over_k(oracle_mod):
+    """Every token on experts 0..K-1 with all of its score there: f_i = E/K
+    and P_i = 1/K for those K experts, so the sum is E/K."""
+    E, K, L = 32, 8, 50
+    s = np.zeros((L, E), np.float32)
+    s[:, :K] = 0.7
+    idx = np.tile(np.arange(K, dtype=np.int32), (L, 1))
+    np.testing.assert_allclose(oracle_mod.seq_balance_loss(s, idx, L, 1.0), [E / K], rtol=1e-14)
+
+
+def test_seq_balance_loss_invariances(oracle_mod):
+    """Scaling a token's scores, reordering tokens inside a sequence, or
+    relabelling experts consistently leaves the loss unchanged; it is linear
+    in alpha; sequences are independent."""
+    rng = np.random.default_rng(40)
+    E, K, L, n = 24, 3, 40, 3
+    s = rng.uniform(0.01, 1, (n * L, E)).astype(np.float32)
+    idx = np.stack([rng.permutation(E)[:K] for _ in range(n * L)]).astype(np.int32)
+    base = oracle_mod.seq_balance_loss(s, idx, L, 1.0)
+    s2 = (s * np.float32(4.0)).astype(np.float32)          # exact power-of-two scaling
+    np.testing.assert_allclose(oracle_mod.seq_balance_loss(s2, idx, L, 1.0), base, rtol=1e-13)
+    perm = np.concatenate([q * L + rng.permutation(L) for q in range(n)])
+    np.testing.assert_allclose(oracle_mod.seq_balance_loss(s[perm], idx[perm], L, 1.0), base, rtol=1e-13)
+    relabel = rng.permutation(E)
+    s3 = np.empty_like(s)
+    s3[:, relabel] = s
+    np.testing.assert_allclose(oracle_mod.seq_balance_loss(s3, relabel[idx].astype(np.int32), L, 1.0), base,
+                               rtol=1e-13)
+    np.testing.assert_allclose(oracle_mod.seq_balance_loss(s, idx, L, 0.25), base * 0.25, rtol=1e-15)
+    np.testing.assert_allclose(oracle_mod.seq_balance_loss(s[L:2 * L], idx[L:2 * L], L, 1.0), base[1:2],
+                               rtol=1e-15)
+    # f_i <= E/K and the P_i sum to 1, so the sum is positive and at most E/K
+    whole = oracle_mod.seq_balance_loss(s, idx, n * L, 1.0)[0]
+    assert 0 < whole <= E / K
