@@ -35,6 +35,7 @@
 // block, so one N tile holds the gate and up columns of the same 128 h
 // columns); SwiGLU + 1x128 E4M3 re-quantisation of h, whose row maximum over
 // the tile's 128 h columns is reduced across the N-waves in LDS.
+#include <atomic>
 #include <type_traits>
 
 #include "device_math.h"
@@ -822,16 +823,20 @@ __global__ __launch_bounds__(256) void gemm_prep_kernel(const int32_t* __restric
     tiles[tt] = make_int4(lo, m0, min(BM, go[lo + 1] - m0), (in_chunk / chunk_rows) * BN);
 }
 
+// CU count of the calling thread's current device, cached per device (any
+// thread may call; a lost race only repeats the query)
 int cu_count_for_current_device() {
-    static int cached[64] = {0};
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
+    int c = cached[dev].load(std::memory_order_relaxed);
+    if (c == 0) {
         int n = 0;
-        cached[dev] = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) ==
-                           hipSuccess && n > 0) ? n : 256;
+        c = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+                ? n : 256;
+        cached[dev].store(c, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return c;
 }
 
 }  // namespace
