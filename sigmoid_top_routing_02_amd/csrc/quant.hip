@@ -17,6 +17,11 @@
 namespace moe {
 namespace {
 
+// Each 16-lane group quantises one 1x128 tile (a lane takes 8 values); every
+// thread handles QU tiles at a stride of the whole grid, with all QU loads
+// issued before any arithmetic so that QU loads per lane are in flight.
+constexpr int QU = 4;
+
 template <bool IN_F32>
 __global__ __launch_bounds__(256) void quant_1x128_kernel(const void* __restrict__ x,
                                                           int64_t rows, int cols,
@@ -24,49 +29,59 @@ __global__ __launch_bounds__(256) void quant_1x128_kernel(const void* __restrict
                                                           float* __restrict__ scale) {
     const int ntile = cols / 128;
     const int64_t total = rows * (int64_t)ntile * 16;
-    for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g - threadIdx.x < total;
-         g += (int64_t)gridDim.x * 256) {
-        // every lane of a 16-lane group takes the same branch (total % 16 == 0)
-        const bool live = g < total;
-        const int64_t tile = g >> 4;
-        const int part = (int)(g & 15);
-        const int64_t row = live ? tile / ntile : 0;
-        const int tc = live ? (int)(tile % ntile) : 0;
-        const int64_t off = row * cols + (int64_t)tc * 128 + part * 8;
-        float v[8];
-        if (live) {
-            if constexpr (IN_F32) {
-                const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(x) + off);
-                const float4 a = p[0], b = p[1];
-                v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-                v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t g0 = (int64_t)blockIdx.x * 256 + threadIdx.x; g0 - threadIdx.x < total; g0 += stride * QU) {
+        float v[QU][8];
+        int64_t off[QU], sidx[QU];
+        bool live[QU];
+#pragma unroll
+        for (int u = 0; u < QU; ++u) {
+            // every lane of a 16-lane group has the same `live` (total % 16 == 0)
+            const int64_t g = g0 + u * stride;
+            live[u] = g < total;
+            const int64_t tile = live[u] ? g >> 4 : 0;
+            const int part = (int)(g & 15);
+            const int64_t row = tile / ntile;
+            const int tc = (int)(tile % ntile);
+            off[u] = row * cols + (int64_t)tc * 128 + part * 8;
+            sidx[u] = part == 0 ? row * ntile + tc : -1;
+            if (live[u]) {
+                if constexpr (IN_F32) {
+                    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(x) + off[u]);
+                    const float4 a = p[0], b = p[1];
+                    v[u][0] = a.x; v[u][1] = a.y; v[u][2] = a.z; v[u][3] = a.w;
+                    v[u][4] = b.x; v[u][5] = b.y; v[u][6] = b.z; v[u][7] = b.w;
+                } else {
+                    const uint4 a = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + off[u]);
+                    v[u][0] = bf16_lo(a.x); v[u][1] = bf16_hi(a.x); v[u][2] = bf16_lo(a.y); v[u][3] = bf16_hi(a.y);
+                    v[u][4] = bf16_lo(a.z); v[u][5] = bf16_hi(a.z); v[u][6] = bf16_lo(a.w); v[u][7] = bf16_hi(a.w);
+                }
             } else {
-                const uint4 a = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + off);
-                v[0] = bf16_lo(a.x); v[1] = bf16_hi(a.x); v[2] = bf16_lo(a.y); v[3] = bf16_hi(a.y);
-                v[4] = bf16_lo(a.z); v[5] = bf16_hi(a.z); v[6] = bf16_lo(a.w); v[7] = bf16_hi(a.w);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) v[u][i] = 0.0f;
             }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = 0.0f;
-        }
-        float amax = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float a = __builtin_fabsf(v[i]);
-            amax = a > amax ? a : amax;
         }
 #pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
-            const float other = __shfl_xor(amax, o, 64);
-            amax = other > amax ? other : amax;
-        }
-        float inv, sc;
-        tile_scale(amax, inv, sc);
-        if (live) {
-            const uint32_t lo = e4m3_encode4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
-            const uint32_t hi = e4m3_encode4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
-            *reinterpret_cast<uint2*>(q + off) = make_uint2(lo, hi);
-            if (part == 0) scale[row * ntile + tc] = sc;
+        for (int u = 0; u < QU; ++u) {
+            float amax = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float a = __builtin_fabsf(v[u][i]);
+                amax = a > amax ? a : amax;
+            }
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) {
+                const float other = __shfl_xor(amax, o, 64);
+                amax = other > amax ? other : amax;
+            }
+            float inv, sc;
+            tile_scale(amax, inv, sc);
+            if (live[u]) {
+                const uint32_t lo = e4m3_encode4(v[u][0] * inv, v[u][1] * inv, v[u][2] * inv, v[u][3] * inv);
+                const uint32_t hi = e4m3_encode4(v[u][4] * inv, v[u][5] * inv, v[u][6] * inv, v[u][7] * inv);
+                *reinterpret_cast<uint2*>(q + off[u]) = make_uint2(lo, hi);
+                if (sidx[u] >= 0) scale[sidx[u]] = sc;
+            }
         }
     }
 }
@@ -125,7 +140,7 @@ __global__ __launch_bounds__(256) void quant_128x128_kernel(const float* __restr
 hipError_t launch_quant_1x128(const void* x, int in_is_f32, int64_t rows, int cols, uint8_t* q,
                               float* scale, hipStream_t st) {
     const int64_t threads = rows * (int64_t)(cols / 128) * 16;
-    int64_t blocks = (threads + 255) / 256;
+    int64_t blocks = (threads + 256 * QU - 1) / (256 * QU);
     if (blocks > 65536) blocks = 65536;
     if (in_is_f32)
         hipLaunchKernelGGL(quant_1x128_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, st, x,
