@@ -269,6 +269,75 @@ int moe_prepare_expert_weights(const float* w1, const float* w3, const float* w2
                                int expert_index, int n_groups, int d, int I, void* packed,
                                moe_stream_t stream);
 
+/* ------------------------------------------------------------------ backward (input gradient)
+ * The gradient of a scalar loss L with respect to u and the centroids, given
+ * dh = dL/dh' FP32 [T,d], by the chain rule through [LINEAGE] "The notation"
+ * (h' = u + FFN_shared(u) + sum_k g_k FFN_k(u)), the gate normalisation over
+ * the chosen experts and the sigmoid affinity ([IFS] MoE-routing paragraph);
+ * the bias only selects ([IFS] bias paragraph), so it has no gradient and the
+ * chosen set is held fixed.  The two expert GEMMs run on
+ * grouped_gemm_fp8_blockscaled with transposed weights; their operands are
+ * quantised per 1x128 tile along the contraction like the forward's (the
+ * pages give no backward tiling: this library's reading).  Order:
+ *   moe_gate_backward -> GEMM(dY, W2^T) = dh_row -> GEMM1 recomputed with the
+ *   FP32 store epilogue = z -> moe_swiglu_backward -> GEMM(dz, W13^T) = dx ->
+ *   moe_router_backward.
+ *
+ * moe_prepare_backward_weights: packed_t receives the transposed weights in
+ * the packed layout's slots: W13^T E4M3 [G, d, 2I] (its inner index keeps
+ * W13's interleaved row order), W2^T [G, I, d], and the block scales
+ * transposed to [G, d/128, 2I/128] and [G, I/128, d/128].  An exact byte
+ * transposition (equal to quantising the transposed masters); packed_t has
+ * moe_packed_weight_bytes(n_groups, d, I) bytes and must not overlap packed.
+ */
+int moe_prepare_backward_weights(const void* packed, int n_groups, int d, int I, void* packed_t,
+                                 moe_stream_t stream);
+
+/* moe_gate_backward -- per token t and slot k (g = topk_gate, s = scores at
+ * topk_idx, D = binary32 sum of the chosen s in slot order):
+ *   a_k = sum_c dh[t,c] y[slot_row[t,k],c]                       (FP32)
+ *   dlogit[t,k] = (a_k - sum_j g_j a_j) / D * s_k * (1 - s_k)     (0 if D = 0)
+ *   row_dlogit[slot_row[t,k]] = dlogit[t,k]
+ *   dY[slot_row[t,k]] = fl32(g_k * dh[t]),  dY[shared_row0 + t] = dh[t]
+ *                       (shared_row0 < 0: no shared rows)
+ * dY is written quantised per 1x128 tile (the rule of fp8_quant_1x128) into
+ * dy_q E4M3 [R,d] and dy_scale FP32 [R,d/128].  y FP32 [R,d] is the forward's
+ * GEMM2 output (R = T*K + T with the shared rows); row_dlogit FP32 [R] (the
+ * shared rows' entries are not written).  Limits: d % 128 == 0,
+ * 1 <= K <= min(E, 16), E <= 256.
+ */
+int moe_gate_backward(const float* dh, const float* y, int64_t shared_row0, const float* topk_gate,
+                      const int32_t* slot_row, const float* scores, const int32_t* topk_idx, int64_t T,
+                      int K, int d, int E, uint8_t* dy_q, float* dy_scale, float* dlogit, float* row_dlogit,
+                      moe_stream_t stream);
+
+/* moe_swiglu_backward -- from the GEMM1 output z FP32 [R, 2I] (gate and up
+ * columns interleaved per 256-column block, as the packed W13 lays them out)
+ * and dh_row = dL/dh FP32 [R, I]:
+ *   dz_up = dh_row * SiLU(z_gate),
+ *   dz_gate = dh_row * z_up * sigma(z_gate) * (1 + z_gate * (1 - sigma(z_gate)))
+ * written in z's layout, quantised per 1x128 tile into dz_q E4M3 [R, 2I] and
+ * dz_scale FP32 [R, 2I/128].  sigma uses the hardware exp (not bit-exact).
+ * Limits: I % 128 == 0.
+ */
+int moe_swiglu_backward(const float* z, const float* dh_row, int64_t R, int I, uint8_t* dz_q, float* dz_scale,
+                        moe_stream_t stream);
+
+/* moe_router_backward --
+ *   du[t] = dh[t] + dx[shared_row0 + t] + sum_k dx[slot_row[t,k]]
+ *           + sum_k dlogit[t,k] * e[topk_idx[t,k]]               (FP32, in that order)
+ *   de[i] = sum over the routed rows r of expert i, in row order, of
+ *           row_dlogit[r] * u[row_token[r]]                      (FP32)
+ * dx FP32 [R,d] (the GEMM(dz, W13^T) output); centroids and u bf16 [E,d],
+ * [T,d]; row_token, group_offset from moe_dispatch; du FP32 [T,d]; de FP32
+ * [E,d] (every row written).  Limits as moe_gate_backward.
+ */
+int moe_router_backward(const float* dh, const float* dx, int64_t shared_row0, const int32_t* slot_row,
+                        const float* dlogit, const int32_t* topk_idx, const void* centroids_bf16,
+                        const void* u_bf16, const float* row_dlogit, const int32_t* row_token,
+                        const int32_t* group_offset, int64_t T, int K, int d, int E, float* du, float* de,
+                        moe_stream_t stream);
+
 /* moe_layer_forward -- the whole layer: router, dispatch, 1x128 quantisation
  * of u, GEMM1 with fused SwiGLU and 1x128 re-quantisation, GEMM2, combine.
  * The bias is read only (update it with moe_bias_update).  packed_weights as

@@ -31,6 +31,7 @@ EXPORTS = (
     "moe_fp8_mfma_accumulation_probe", "moe_combine", "moe_bias_update",
     "moe_packed_weight_bytes", "moe_prepare_expert_weights",
     "moe_layer_workspace_bytes", "moe_layer_forward",
+    "moe_prepare_backward_weights", "moe_gate_backward", "moe_swiglu_backward", "moe_router_backward",
 )
 
 
@@ -72,6 +73,10 @@ def load_library(path: str = LIB_PATH):
         "moe_prepare_expert_weights": ([P, P, P, I32, I32, I32, I32, P, P], I32),
         "moe_layer_workspace_bytes": ([I64, I32, I32, I32, I32], SZ),
         "moe_layer_forward": ([P, P, P, P, I64, I32, I32, I32, I32, P, P, P, SZ, P], I32),
+        "moe_prepare_backward_weights": ([P, I32, I32, I32, P, P], I32),
+        "moe_gate_backward": ([P, P, I64, P, P, P, P, I64, I32, I32, I32, P, P, P, P, P], I32),
+        "moe_swiglu_backward": ([P, P, I64, I32, P, P, P], I32),
+        "moe_router_backward": ([P, P, I64, P, P, P, P, P, P, P, P, I64, I32, I32, I32, P, P, P], I32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -351,3 +356,68 @@ def moe_layer_forward(u, centroids, bias, packed, K, I, out=None, expert_count=N
                                _ptr(out), _ptr(expert_count), _ptr(ws), ws.numel(), _stream()),
            "moe_layer_forward")
     return out
+
+
+# ---------------------------------------------------------------- backward (input gradient)
+def moe_prepare_backward_weights(packed, n_groups, d, I, packed_t=None):
+    """The packed weights transposed block by block (W13^T [G,d,2I], W2^T [G,I,d])."""
+    L = load_library()
+    need = L.moe_packed_weight_bytes(n_groups, d, I)
+    packed_t = _new((need,), torch.uint8, packed) if packed_t is None else packed_t
+    _check(L.moe_prepare_backward_weights(_ptr(packed), n_groups, d, I, _ptr(packed_t), _stream()),
+           "moe_prepare_backward_weights")
+    return packed_t
+
+
+def moe_gate_backward(dh, y, topk_gate, slot_row, scores, topk_idx, shared_row0=-1):
+    """-> (dy_q u8 [R,d], dy_scale f32 [R,d/128], dlogit f32 [T,K], row_dlogit f32 [R])."""
+    T, d = dh.shape
+    K = topk_gate.shape[1]
+    E = scores.shape[1]
+    R = y.shape[0]
+    _want(dh, torch.float32, (T, d), "dh")
+    _want(y, torch.float32, (R, d), "y")
+    _want(topk_gate, torch.float32, (T, K), "topk_gate")
+    _want(slot_row, torch.int32, (T, K), "slot_row")
+    _want(scores, torch.float32, (T, E), "scores")
+    _want(topk_idx, torch.int32, (T, K), "topk_idx")
+    dy_q = _new((R, d), torch.uint8, dh)
+    dy_s = _new((R, d // 128), torch.float32, dh)
+    dlogit = _new((T, K), torch.float32, dh)
+    row_dlogit = torch.zeros((R,), dtype=torch.float32, device=dh.device)
+    L = load_library()
+    _check(L.moe_gate_backward(_ptr(dh), _ptr(y), shared_row0, _ptr(topk_gate), _ptr(slot_row), _ptr(scores),
+                               _ptr(topk_idx), T, K, d, E, _ptr(dy_q), _ptr(dy_s), _ptr(dlogit),
+                               _ptr(row_dlogit), _stream()), "moe_gate_backward")
+    return dy_q, dy_s, dlogit, row_dlogit
+
+
+def moe_swiglu_backward(z, dh_row):
+    """z f32 [R,2I] (interleaved gate/up), dh_row f32 [R,I] -> (dz_q u8 [R,2I], dz_scale f32 [R,2I/128])."""
+    R, I2 = z.shape
+    I = I2 // 2
+    _want(z, torch.float32, (R, 2 * I), "z")
+    _want(dh_row, torch.float32, (R, I), "dh_row")
+    dz_q = _new((R, 2 * I), torch.uint8, z)
+    dz_s = _new((R, 2 * I // 128), torch.float32, z)
+    L = load_library()
+    _check(L.moe_swiglu_backward(_ptr(z), _ptr(dh_row), R, I, _ptr(dz_q), _ptr(dz_s), _stream()),
+           "moe_swiglu_backward")
+    return dz_q, dz_s
+
+
+def moe_router_backward(dh, dx, slot_row, dlogit, topk_idx, centroids, u, row_dlogit, row_token,
+                        group_offset, shared_row0=-1):
+    """-> (du f32 [T,d], de f32 [E,d])."""
+    T, d = dh.shape
+    K = slot_row.shape[1]
+    E = centroids.shape[0]
+    _want(u, torch.bfloat16, (T, d), "u")
+    _want(centroids, torch.bfloat16, (E, d), "centroids")
+    du = _new((T, d), torch.float32, dh)
+    de = _new((E, d), torch.float32, dh)
+    L = load_library()
+    _check(L.moe_router_backward(_ptr(dh), _ptr(dx), shared_row0, _ptr(slot_row), _ptr(dlogit), _ptr(topk_idx),
+                                 _ptr(centroids), _ptr(u), _ptr(row_dlogit), _ptr(row_token), _ptr(group_offset),
+                                 T, K, d, E, _ptr(du), _ptr(de), _stream()), "moe_router_backward")
+    return du, de

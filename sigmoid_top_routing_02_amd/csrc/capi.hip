@@ -342,6 +342,91 @@ int moe_prepare_expert_weights(const float* w1, const float* w3, const float* w2
     return hip_status(e, "weight quantisation launch");
 }
 
+int moe_prepare_backward_weights(const void* packed, int n_groups, int d, int I, void* packed_t,
+                                 moe_stream_t stream) {
+    REQUIRE(d > 0 && d % 128 == 0 && I > 0 && I % 128 == 0, MOE_ERR_SHAPE,
+            "moe_prepare_backward_weights: d=%d, I=%d must be positive multiples of 128", d, I);
+    REQUIRE(n_groups >= 1 && n_groups <= 65535, MOE_ERR_UNSUPPORTED, "moe_prepare_backward_weights: %d groups",
+            n_groups);
+    REQUIRE_PTR(packed);
+    REQUIRE_PTR(packed_t);
+    REQUIRE(packed != packed_t, MOE_ERR_SHAPE, "moe_prepare_backward_weights: packed_t must not be packed");
+    Packed in = packed_layout(const_cast<void*>(packed), n_groups, d, I);
+    Packed out = packed_layout(packed_t, n_groups, d, I);
+    hipError_t e = moe::launch_transpose_blocks(in.w13q, in.w13s, n_groups, 2 * I, d, out.w13q, out.w13s, S(stream));
+    if (e == hipSuccess) e = moe::launch_transpose_blocks(in.w2q, in.w2s, n_groups, d, I, out.w2q, out.w2s, S(stream));
+    return hip_status(e, "weight transposition launch");
+}
+
+// ---------------------------------------------------------------- backward (input gradient)
+int moe_gate_backward(const float* dh, const float* y, int64_t shared_row0, const float* topk_gate,
+                      const int32_t* slot_row, const float* scores, const int32_t* topk_idx, int64_t T,
+                      int K, int d, int E, uint8_t* dy_q, float* dy_scale, float* dlogit, float* row_dlogit,
+                      moe_stream_t stream) {
+    REQUIRE(T >= 0, MOE_ERR_SHAPE, "moe_gate_backward: T < 0");
+    REQUIRE(K >= 1 && K <= 16 && K <= E, MOE_ERR_UNSUPPORTED, "moe_gate_backward: K=%d outside [1, min(E,16)]", K);
+    REQUIRE(E >= 1 && E <= 256, MOE_ERR_UNSUPPORTED, "moe_gate_backward: E=%d outside [1, 256]", E);
+    REQUIRE(d > 0 && d % 128 == 0, MOE_ERR_SHAPE, "moe_gate_backward: d=%d not a positive multiple of 128", d);
+    if (T == 0) return MOE_OK;
+    REQUIRE_PTR(dh);
+    REQUIRE_PTR(y);
+    REQUIRE_PTR(topk_gate);
+    REQUIRE_PTR(slot_row);
+    REQUIRE_PTR(scores);
+    REQUIRE_PTR(topk_idx);
+    REQUIRE_PTR(dy_q);
+    REQUIRE_PTR(dy_scale);
+    REQUIRE_PTR(dlogit);
+    REQUIRE_PTR(row_dlogit);
+    return hip_status(moe::launch_gate_backward(dh, y, shared_row0, topk_gate, slot_row, scores, topk_idx, T, K,
+                                                d, E, dy_q, dy_scale, dlogit, row_dlogit, S(stream)),
+                      "gate backward launch");
+}
+
+int moe_swiglu_backward(const float* z, const float* dh_row, int64_t R, int I, uint8_t* dz_q, float* dz_scale,
+                        moe_stream_t stream) {
+    REQUIRE(R >= 0, MOE_ERR_SHAPE, "moe_swiglu_backward: R < 0");
+    REQUIRE(I > 0 && I % 128 == 0, MOE_ERR_SHAPE, "moe_swiglu_backward: I=%d not a positive multiple of 128", I);
+    if (R == 0) return MOE_OK;
+    REQUIRE_PTR(z);
+    REQUIRE_PTR(dh_row);
+    REQUIRE_PTR(dz_q);
+    REQUIRE_PTR(dz_scale);
+    return hip_status(moe::launch_swiglu_backward(z, dh_row, R, I, dz_q, dz_scale, S(stream)),
+                      "SwiGLU backward launch");
+}
+
+int moe_router_backward(const float* dh, const float* dx, int64_t shared_row0, const int32_t* slot_row,
+                        const float* dlogit, const int32_t* topk_idx, const void* centroids_bf16,
+                        const void* u_bf16, const float* row_dlogit, const int32_t* row_token,
+                        const int32_t* group_offset, int64_t T, int K, int d, int E, float* du, float* de,
+                        moe_stream_t stream) {
+    REQUIRE(T >= 0, MOE_ERR_SHAPE, "moe_router_backward: T < 0");
+    REQUIRE(K >= 1 && K <= 16 && K <= E, MOE_ERR_UNSUPPORTED, "moe_router_backward: K=%d outside [1, min(E,16)]", K);
+    REQUIRE(E >= 1 && E <= 256, MOE_ERR_UNSUPPORTED, "moe_router_backward: E=%d outside [1, 256]", E);
+    REQUIRE(d > 0 && d % 128 == 0, MOE_ERR_SHAPE, "moe_router_backward: d=%d not a positive multiple of 128", d);
+    REQUIRE_PTR(de);
+    REQUIRE_PTR(group_offset);
+    if (T > 0) {
+        REQUIRE_PTR(dh);
+        REQUIRE_PTR(dx);
+        REQUIRE_PTR(slot_row);
+        REQUIRE_PTR(dlogit);
+        REQUIRE_PTR(topk_idx);
+        REQUIRE_PTR(centroids_bf16);
+        REQUIRE_PTR(u_bf16);
+        REQUIRE_PTR(row_dlogit);
+        REQUIRE_PTR(row_token);
+        REQUIRE_PTR(du);
+        hipError_t e = moe::launch_du(dh, dx, shared_row0, slot_row, dlogit, topk_idx,
+                                      static_cast<const uint16_t*>(centroids_bf16), T, K, d, du, S(stream));
+        if (e != hipSuccess) return hip_status(e, "du launch");
+    }
+    return hip_status(moe::launch_de(row_dlogit, row_token, group_offset, static_cast<const uint16_t*>(u_bf16), d,
+                                     E, de, S(stream)),
+                      "de launch");
+}
+
 // ---------------------------------------------------------------- whole layer
 namespace {
 struct LayerWs {

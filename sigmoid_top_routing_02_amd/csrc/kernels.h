@@ -41,6 +41,21 @@ hipError_t launch_grouped_gemm(const uint8_t* a_q, const float* a_s, const int32
                                float* out, uint8_t* out_q, float* out_s, void* ws,
                                hipStream_t st);
 
+// backward.hip
+hipError_t launch_gate_backward(const float* dh, const float* y, int64_t shared_row0, const float* gate,
+                                const int32_t* slot_row, const float* s, const int32_t* idx, int64_t T,
+                                int K, int d, int E, uint8_t* dy_q, float* dy_s, float* dlogit,
+                                float* row_dlogit, hipStream_t st);
+hipError_t launch_swiglu_backward(const float* z, const float* dh_row, int64_t R, int I, uint8_t* dz_q,
+                                  float* dz_s, hipStream_t st);
+hipError_t launch_du(const float* dh, const float* dx, int64_t shared_row0, const int32_t* slot_row,
+                     const float* dlogit, const int32_t* idx, const uint16_t* e, int64_t T, int K, int d,
+                     float* du, hipStream_t st);
+hipError_t launch_de(const float* row_dlogit, const int32_t* row_token, const int32_t* group_offset,
+                     const uint16_t* u, int d, int E, float* de, hipStream_t st);
+hipError_t launch_transpose_blocks(const uint8_t* in, const float* in_s, int G, int rows, int cols,
+                                   uint8_t* out, float* out_s, hipStream_t st);
+
 // balance.hip
 size_t seq_balance_ws_bytes(int64_t n_seq, int L);
 hipError_t launch_seq_balance_loss(const float* s, const int32_t* idx, int64_t n_seq, int E, int K,

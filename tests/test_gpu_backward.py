@@ -1,0 +1,182 @@
+"""GPU parity of the input-gradient backward against the backward oracle
+(oracle/backward.py, pinned by finite differences), stage by stage: each
+stage's oracle runs on the GPU's own inputs to that stage, as the forward's
+parity protocol does.
+
+  * the transposed packed weights equal the forward's blocks transposed, bit
+    for bit;
+  * gate backward: dY's 1x128 codes and scales bit-exact (dY = fl32(g * dh) on
+    both sides); dlogit within the per-row bound;
+  * GEMM(dY, W2^T) = dh_row and GEMM(dz, W13^T) = dx within the per-row bound
+    of the oracle's FP64 product of the same codes;
+  * SwiGLU backward: every dz code within half an E4M3 step of the FP64 value
+    (plus the FP32 arithmetic's slack), scales within tolerance;
+  * du and de within the per-row bound.
+The FP8 backward against the unquantised FP64 backward is reported (and only
+loosely bounded): that is the quantisation error, not a parity target."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sigmoid_top_routing_02_amd as moe
+import workloads
+from helpers import TOL, dev, np_, rowinf_rel, say, u16
+from oracle import backward as bw
+from test_gpu_layer import pack_all, run_steps
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf16_f64(t):
+    return (u16(t).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _check_dz_codes(q, s, x_ref, mag):
+    """Codes and scales of a fused-quantised FP32 GPU value, against its exact
+    FP64 value: the scale within tolerance of the oracle's quantiser applied
+    to the FP32-rounded exact value, and every dequantised code within half an
+    E4M3 step of the exact value plus the FP32 arithmetic's error, taken as
+    1e-5 of `mag`, the size of the terms the value is made of (dz_gate's factor
+    1 + z (1 - sigma(z)) cancels near z = -1.28, so the error is not relative
+    to the result)."""
+    q_ref, s_ref = oracle.quant_1x128(x_ref.astype(np.float32))
+    assert np.all(np.abs(s.astype(np.float64) / s_ref.astype(np.float64) - 1) <= TOL)
+    table = oracle.e4m3_table()
+    vals = np.unique(table[np.isfinite(table)])
+    gaps = np.diff(vals)
+    half = np.zeros(256)
+    for c in range(256):
+        if np.isfinite(table[c]):
+            i = np.searchsorted(vals, table[c])
+            half[c] = max(gaps[i - 1] if i > 0 else gaps[0], gaps[i] if i < gaps.size else gaps[-1]) / 2
+    sc = np.repeat(s.astype(np.float64), 128, axis=1)
+    deq = table[q] * sc
+    bound = half[q] * sc * (1 + 1e-6) + 1e-5 * mag + 1e-7 * sc
+    bad = np.abs(deq - x_ref) > bound
+    if bad.any():
+        i = np.argwhere(bad)[0]
+        raise AssertionError(f"{int(bad.sum())} dz codes further from the exact value than allowed; first at "
+                             f"{tuple(i)}: exact {x_ref[tuple(i)]:.6e}, decoded {deq[tuple(i)]:.6e}, "
+                             f"bound {bound[tuple(i)]:.3e}, term size {mag[tuple(i)]:.3e}")
+    return int((q != q_ref).sum())
+
+
+CASES = [
+    # (T, d, E, K, I): 32-row GEMM tiles; 128-row tiles; the decode layer's shapes
+    (128, 512, 16, 4, 256),
+    (2048, 512, 16, 4, 256),
+    (256, 7168, 256, 8, 2048),
+]
+
+
+@pytest.mark.parametrize("T,d,E,K,I", CASES)
+def test_backward_dgrad_staged(T, d, E, K, I):
+    sh = workloads.custom_shape(T=T, d=d, E=E, K=K, I=I)
+    G, R = E + 1, T * K + T
+    say(f"backward T={T} d={d} E={E} K={K} I={I}: forward")
+    u = workloads.activations(sh).to(dev())
+    e, b = workloads.centroids(sh).to(dev()), workloads.bias(sh).to(dev())
+    packed = pack_all(sh)
+    f = run_steps(u, e, b, packed, sh)
+    dh = workloads.normal((T, d), 1.0, workloads.seed_for("backward", "dh", T), device=dev())
+
+    say("  transposed weights")
+    packed_t = moe.moe_prepare_backward_weights(packed, G, d, I)
+    w13q, w2q, w13s, w2s = moe.packed_views(packed, G, d, I)
+    t13q, t2q, t13s, t2s = moe.packed_views(packed_t, G, d, I)
+    t13q, t13s = t13q.view(G, d, 2 * I), t13s.view(G, d // 128, 2 * I // 128)
+    t2q, t2s = t2q.view(G, I, d), t2s.view(G, I // 128, d // 128)
+    torch.cuda.synchronize()
+    assert torch.equal(t13q, w13q.transpose(1, 2)) and torch.equal(t2q, w2q.transpose(1, 2))
+    assert torch.equal(t13s, w13s.transpose(1, 2)) and torch.equal(t2s, w2s.transpose(1, 2))
+
+    say("  GPU backward")
+    go = f["go"]
+    dy_q, dy_s, dlogit, row_dlogit = moe.moe_gate_backward(dh, f["y"], f["gate"], f["slot_row"], f["s"],
+                                                           f["idx"], shared_row0=T * K)
+    dh_row = moe.grouped_gemm_fp8_blockscaled(dy_q, dy_s, go, R, t2q, t2s, epi=moe.MOE_EPI_STORE_F32)
+    z = moe.grouped_gemm_fp8_blockscaled(f["uq"], f["us"], go, R, w13q, w13s, epi=moe.MOE_EPI_STORE_F32,
+                                         a_row_index=f["row_token"])
+    dz_q, dz_s = moe.moe_swiglu_backward(z, dh_row)
+    dx = moe.grouped_gemm_fp8_blockscaled(dz_q, dz_s, go, R, t13q, t13s, epi=moe.MOE_EPI_STORE_F32)
+    du, de = moe.moe_router_backward(dh, dx, f["slot_row"], dlogit, f["idx"], e, u, row_dlogit,
+                                     f["row_token"], go, shared_row0=T * K)
+    torch.cuda.synchronize()
+
+    # ---- gate backward
+    say("  oracle: gate backward")
+    go_h, slot_h, idx_h = np_(go), np_(f["slot_row"]), np_(f["idx"])
+    _, dy_ref, dl_ref = bw.gate_backward(np_(dh), np_(f["y"]), T * K, np_(f["gate"]), slot_h, np_(f["s"]), idx_h)
+    qy_ref, sy_ref = oracle.quant_1x128(dy_ref.astype(np.float32))
+    np.testing.assert_array_equal(np_(dy_q), qy_ref)
+    np.testing.assert_array_equal(np_(dy_s).view(np.uint32), sy_ref.view(np.uint32))
+    err = rowinf_rel(np_(dlogit), dl_ref)
+    say(f"  dlogit per-row rel err {err:.3e}")
+    assert err <= TOL
+    rd = np_(row_dlogit)
+    np.testing.assert_array_equal(rd[slot_h], np_(dlogit))
+
+    # ---- the expert GEMMs and the SwiGLU backward, on sampled groups (all groups when small)
+    cnt = np.diff(go_h)
+    groups = list(range(G)) if R <= 4096 else sorted({0, int(np.argmax(cnt[:E])), E})
+    say(f"  oracle: expert GEMMs and SwiGLU backward on {len(groups)} groups")
+    dyq_h, dys_h = np_(dy_q), np_(dy_s)
+    t2q_h, t2s_h, t13q_h, t13s_h = np_(t2q), np_(t2s), np_(t13q), np_(t13s)
+    dh_row_h, z_h, dzq_h, dzs_h, dx_h = np_(dh_row), np_(z), np_(dz_q), np_(dz_s), np_(dx)
+    flips = 0
+    for g in groups:
+        r0, r1 = int(go_h[g]), int(go_h[g + 1])
+        if r1 == r0:
+            continue
+        ref = oracle.gemm_blockscaled(dyq_h[r0:r1], dys_h[r0:r1], t2q_h[g], t2s_h[g])
+        assert rowinf_rel(dh_row_h[r0:r1], ref) <= TOL
+        zz = z_h[r0:r1].reshape(r1 - r0, I // 128, 2, 128).astype(np.float64)
+        zg_, zu_ = zz[:, :, 0].reshape(r1 - r0, I), zz[:, :, 1].reshape(r1 - r0, I)
+        dhr = dh_row_h[r0:r1].astype(np.float64)
+        dzg, dzu = bw.swiglu_backward(zg_, zu_, dhr)
+        sg = 1 / (1 + np.exp(-zg_))
+        mag_g = np.abs(dhr * zu_) * sg * (1 + np.abs(zg_) * (1 - sg))
+        mag_u = np.abs(dhr * zg_) * sg
+
+        def inter(a, b):   # back to z's layout: per 256 columns, 128 gate then 128 up
+            return np.stack([a.reshape(r1 - r0, I // 128, 128), b.reshape(r1 - r0, I // 128, 128)],
+                            axis=2).reshape(r1 - r0, 2 * I)
+        flips += _check_dz_codes(dzq_h[r0:r1], dzs_h[r0:r1], inter(dzg, dzu), inter(mag_g, mag_u))
+        ref = oracle.gemm_blockscaled(dzq_h[r0:r1], dzs_h[r0:r1], t13q_h[g], t13s_h[g])
+        assert rowinf_rel(dx_h[r0:r1], ref) <= TOL
+    say(f"  dz codes that differ from the oracle's rounding (midpoints): {flips}")
+
+    # ---- du and de
+    say("  oracle: du, de")
+    u_h, e_h = _bf16_f64(u), _bf16_f64(e)
+    du_r, de_ref = bw.router_backward(u_h, e_h, idx_h, np_(dlogit), E)
+    du_ref = bw.assemble_du(np_(dh), dx_h, np_(f["row_token"])) + du_r
+    err_u, err_e = rowinf_rel(np_(du), du_ref), rowinf_rel(np_(de), de_ref)
+    say(f"  du per-row rel err {err_u:.3e}, de {err_e:.3e}")
+    assert err_u <= TOL and err_e <= TOL
+
+    # ---- reported: against the unquantised FP64 backward (small cases only)
+    if d <= 512:
+        w = [workloads.expert_weights(sh, g, device=dev()) for g in range(G)]     # as pack_all drew them
+        W1 = np.stack([np_(x[0]) for x in w]).astype(np.float64)
+        W3 = np.stack([np_(x[1]) for x in w]).astype(np.float64)
+        W2 = np.stack([np_(x[2]) for x in w]).astype(np.float64)
+        rt = np_(f["row_token"])
+        grp = np.searchsorted(go_h, np.arange(R), side="right") - 1
+        x = u_h[rt]
+        zg = np.einsum("rid,rd->ri", W1[grp], x)
+        zu = np.einsum("rid,rd->ri", W3[grp], x)
+        y64 = np.einsum("rdi,ri->rd", W2[grp], zg / (1 + np.exp(-zg)) * zu)
+        s64 = 1 / (1 + np.exp(-(u_h @ e_h.T)))
+        sc = s64[np.arange(T)[:, None], idx_h]
+        _, dy64, dl64 = bw.gate_backward(np_(dh), y64, T * K, sc / sc.sum(1, keepdims=True), slot_h, s64, idx_h)
+        dx64 = np.zeros((R, d))
+        for g in range(G):
+            r0, r1 = int(go_h[g]), int(go_h[g + 1])
+            if r1 > r0:
+                dx64[r0:r1] = bw.expert_dgrad(dy64[r0:r1], zg[r0:r1], zu[r0:r1], W1[g], W3[g], W2[g])[3]
+        du64 = bw.assemble_du(np_(dh), dx64, rt) + bw.router_backward(u_h, e_h, idx_h, dl64, E)[0]
+        q_err = rowinf_rel(np_(du), du64)
+        say(f"  FP8 backward vs unquantised FP64 backward: du per-row rel err {q_err:.3e}")
+        assert q_err < 0.2

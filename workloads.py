@@ -38,7 +38,7 @@ BASE_SEED = 20241227
 _WORKLOAD_IDS = {"tiny": 1, "rdc": 2, "decode": 3, "prefill": 4, "dense": 5, "custom": 9}
 _TENSOR_IDS = {"u": 1, "centroids": 2, "bias": 3, "w1": 4, "w3": 5, "w2": 6,
                "outlier_pos": 7, "a": 8, "b": 9, "a_outlier": 10, "b_outlier": 11,
-               "rank_perm": 12}
+               "rank_perm": 12, "dh": 13}
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 PREFILL_BIAS_FILE = os.path.join(HERE, "tests", "golden", "prefill_bias_zipf.txt")
