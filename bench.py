@@ -258,6 +258,95 @@ def layer_quant_error(sh, st, n_tok=4):
             "vs_unquantised_fp64": round(rel, 6)}
 
 
+def run_layer_backward(sh, steps, warmup):
+    """The input-gradient backward of the layer after one forward step: gate
+    backward (dY quantised), GEMM(dY, W2^T), GEMM1 recomputed with the FP32
+    store epilogue (z), SwiGLU backward (dz quantised), GEMM(dz, W13^T), then
+    du and the centroid gradient.  One step = that chain for the whole batch
+    with dL/dh' ~ N(0,1); the transposed weights are prepared once, untimed
+    (like the forward's weight quantisation)."""
+    log(f"[bench] setup {sh.name} backward: T={sh.T} d={sh.d} E={sh.E} K={sh.K} I={sh.I}")
+    st = layer_setup(sh)
+    layer_step(sh, st)
+    T, d, E, K, I = sh.T, sh.d, sh.E, sh.K, sh.I
+    G, R = E + 1, T * K + T
+    count, go, row_token, slot_row = moe.moe_dispatch(st["idx"], E, True, ws=st["dws"])
+    packed_t = moe.moe_prepare_backward_weights(st["packed"], G, d, I)
+    w13q, w2q, w13s, w2s = st["views"]
+    t13q, t2q, t13s, t2s = moe.packed_views(packed_t, G, d, I)
+    t13q, t13s = t13q.view(G, d, 2 * I), t13s.view(G, d // 128, 2 * I // 128)
+    t2q, t2s = t2q.view(G, I, d), t2s.view(G, I // 128, d // 128)
+    dh = workloads.normal((T, d), 1.0, workloads.seed_for("backward", "dh", T), device="cuda")
+    dev = dh.device
+    nk = max(2 * I, d)
+    b = dict(dh_row=torch.empty(R, I, device=dev), z=torch.empty(R, 2 * I, device=dev),
+             dx=torch.empty(R, d, device=dev),
+             ws=torch.empty(max(moe.moe_gemm_workspace_bytes(G, R, nk, nk), 256), dtype=torch.uint8, device=dev))
+
+    def step(ev=None):
+        m = [ev.mark("start")] if ev else None
+        dy_q, dy_s, dlogit, row_dlogit = moe.moe_gate_backward(dh, st["y"], st["gate"], slot_row, st["scores"],
+                                                               st["idx"], shared_row0=T * K)
+        if ev: m.append(ev.mark("gate_bwd"))
+        moe.grouped_gemm_fp8_blockscaled(dy_q, dy_s, go, R, t2q, t2s, epi=moe.MOE_EPI_STORE_F32,
+                                         out=b["dh_row"], ws=b["ws"])
+        if ev: m.append(ev.mark("gemm2_dgrad"))
+        moe.grouped_gemm_fp8_blockscaled(st["uq"], st["us"], go, R, w13q, w13s, epi=moe.MOE_EPI_STORE_F32,
+                                         a_row_index=row_token, out=b["z"], ws=b["ws"])
+        if ev: m.append(ev.mark("gemm1_recompute"))
+        dz_q, dz_s = moe.moe_swiglu_backward(b["z"], b["dh_row"])
+        if ev: m.append(ev.mark("swiglu_bwd"))
+        moe.grouped_gemm_fp8_blockscaled(dz_q, dz_s, go, R, t13q, t13s, epi=moe.MOE_EPI_STORE_F32,
+                                         out=b["dx"], ws=b["ws"])
+        if ev: m.append(ev.mark("gemm1_dgrad"))
+        moe.moe_router_backward(dh, b["dx"], slot_row, dlogit, st["idx"], st["e"], st["u"], row_dlogit,
+                                row_token, go, shared_row0=T * K)
+        if ev:
+            m.append(ev.mark("router_bwd"))
+            names = ["gate_bwd", "gemm2_dgrad", "gemm1_recompute", "swiglu_bwd", "gemm1_dgrad", "router_bwd"]
+            for i, n in enumerate(names):
+                ev.add(n, m[i], m[i + 1])
+
+    for _ in range(warmup):
+        step()
+    ev = Events()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(ev)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    stages = {n: round(ev.avg_ms(n), 4) for n in ev.pairs}
+    f2 = 2.0 * R * d * I              # GEMM(dY, W2^T)
+    f1 = 2.0 * R * d * 2 * I          # the GEMM1 recompute and GEMM(dz, W13^T) each
+    tf = {"gemm2_dgrad": round(f2 / (ev.avg_ms("gemm2_dgrad") * 1e-3) / 1e12, 1),
+          "gemm1_recompute": round(f1 / (ev.avg_ms("gemm1_recompute") * 1e-3) / 1e12, 1),
+          "gemm1_dgrad": round(f1 / (ev.avg_ms("gemm1_dgrad") * 1e-3) / 1e12, 1)}
+    k_ms = ev.avg_ms("gemm1_dgrad")
+    if T >= 4096:
+        ach = f1 / (k_ms * 1e-3) / 1e12
+        roof = {"kernel": "grouped_gemm_fp8_blockscaled (GEMM(dz, W13^T))", "bound": "mfma", "achieved": round(ach, 2),
+                "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_FP8_TFLOPS, 4), "traffic": None,
+                "algorithmic_per_launch": f1, "avg_launch_ms": round(k_ms, 4)}
+    else:
+        used = int((count.cpu() > 0).sum()) + 1
+        nbytes = used * (d * 2 * I + (d // 128) * (2 * I // 128) * 4) + R * (2 * I + 2 * I // 128 * 4) + R * d * 4
+        ach = nbytes / (k_ms * 1e-3) / 1e9
+        roof = {"kernel": "grouped_gemm_fp8_blockscaled (GEMM(dz, W13^T))", "bound": "hbm", "achieved": round(ach, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                "algorithmic_per_launch": nbytes, "avg_launch_ms": round(k_ms, 4)}
+    log(f"[bench] backward {ms:.3f} ms/step; stages {stages}")
+    return {
+        "metric": "MoE-layer backward (input gradient) tokens/s (d=7168, 256E top-8, FP8)",
+        "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate)", "data": "synthetic (seeded; random-init expert weights)",
+        "config": {"workload": f"moe_layer_{sh.name}_backward", "T": T, "d": d, "routed_experts": E, "top_k": K,
+                   "shared_experts": 1, "inter": I, "parallelism": "single GPU"},
+        "roofline": roof, "stages_ms": stages, "gemm_tflops": tf,
+    }
+
+
 def run_layer(sh, steps, warmup, with_cpu):
     log(f"[bench] setup {sh.name}: T={sh.T} d={sh.d} E={sh.E} K={sh.K} I={sh.I}")
     t = time.time()
@@ -593,7 +682,8 @@ def main():
                     help="timed steps (default 20; 200 for the dense GEMM, whose step is ~0.3 ms)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill",
-                    choices=["prefill", "decode", "tiny", "rdc", "dense", "dense16k"])
+                    choices=["prefill", "decode", "tiny", "rdc", "dense", "dense16k",
+                             "prefill_bwd", "decode_bwd", "tiny_bwd"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--with-copy", action="store_true",
                     help="first run a plain 4 GiB copy kernel (moe_permute_rows with the identity "
@@ -613,6 +703,8 @@ def main():
         copy_calibration()
     if args.workload == "rdc":
         res = run_rdc(args.steps, args.warmup, with_cpu=not args.no_cpu_baseline)
+    elif args.workload.endswith("_bwd"):
+        res = run_layer_backward(workloads.SHAPES[args.workload[:-4]], args.steps, args.warmup)
     elif args.workload in ("dense", "dense16k"):
         res = run_dense(args.steps, args.warmup, K=4096 if args.workload == "dense" else 16384)
     else:
