@@ -326,8 +326,8 @@ int moe_swiglu_backward(const float* z, const float* dh_row, int64_t R, int I, u
 /* moe_router_backward --
  *   du[t] = dh[t] + dx[shared_row0 + t] + sum_k dx[slot_row[t,k]]
  *           + sum_k dlogit[t,k] * e[topk_idx[t,k]]               (FP32, in that order)
- *   de[i] = sum over the routed rows r of expert i, in row order, of
- *           row_dlogit[r] * u[row_token[r]]                      (FP32)
+ *   de[i] = sum over the routed rows r of expert i of
+ *           row_dlogit[r] * u[row_token[r]]       (FP32, a fixed order: deterministic)
  * dx FP32 [R,d] (the GEMM(dz, W13^T) output); centroids and u bf16 [E,d],
  * [T,d]; row_token, group_offset from moe_dispatch; du FP32 [T,d]; de FP32
  * [E,d] (every row written).  Limits as moe_gate_backward.

@@ -47,9 +47,19 @@ __device__ __forceinline__ void quant_tile8(const float (&v)[8], int part, uint8
     if (part == 0) *sp = sc;
 }
 
+typedef float bwd_v4f __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
     const float4 a = reinterpret_cast<const float4*>(p)[0];
     const float4 b = reinterpret_cast<const float4*>(p)[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+// the same for data read once: non-temporal loads keep it from evicting lines
+// that are still useful
+__device__ __forceinline__ void load8_nt(const float* p, float (&v)[8]) {
+    const bwd_v4f a = __builtin_nontemporal_load(reinterpret_cast<const bwd_v4f*>(p));
+    const bwd_v4f b = __builtin_nontemporal_load(reinterpret_cast<const bwd_v4f*>(p) + 1);
     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
     v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
@@ -90,7 +100,7 @@ __global__ __launch_bounds__(256) void gate_backward_kernel(
             for (int k = 0; k < KMAX; ++k) {
                 if (k >= K) break;
                 float yv[8], v[8];
-                load8(y + r[k] * d + col, yv);
+                load8_nt(y + r[k] * d + col, yv);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     acc[k] = __builtin_fmaf(x[i], yv[i], acc[k]);
@@ -149,9 +159,9 @@ __global__ __launch_bounds__(256) void swiglu_backward_kernel(const float* __res
         const int c0 = part * 8;
         const float* zr = z + row * 2 * I + (int64_t)j * 256;
         float zg[8], zu[8], dh[8], dzg[8], dzu[8];
-        load8(zr + c0, zg);
-        load8(zr + 128 + c0, zu);
-        load8(dh_row + row * I + (int64_t)j * 128 + c0, dh);
+        load8_nt(zr + c0, zg);
+        load8_nt(zr + 128 + c0, zu);
+        load8_nt(dh_row + row * I + (int64_t)j * 128 + c0, dh);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-zg[i]));
@@ -179,16 +189,16 @@ __global__ __launch_bounds__(128) void du_kernel(const float* __restrict__ dh, c
     for (int64_t t = blockIdx.y; t < T; t += gridDim.y) {
         float4 a = reinterpret_cast<const float4*>(dh + t * d)[cv];
         if (shared_row0 >= 0) {
-            const float4 v = reinterpret_cast<const float4*>(dx + (shared_row0 + t) * d)[cv];
+            const bwd_v4f v = __builtin_nontemporal_load(reinterpret_cast<const bwd_v4f*>(dx + (shared_row0 + t) * d) + cv);
             a.x = a.x + v.x; a.y = a.y + v.y; a.z = a.z + v.z; a.w = a.w + v.w;
         }
-        float4 xk[KMAX];
+        bwd_v4f xk[KMAX];
         uint2 ek[KMAX];
         float dl[KMAX];
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
             if (k >= K) break;
-            xk[k] = reinterpret_cast<const float4*>(dx + (int64_t)slot_row[t * K + k] * d)[cv];
+            xk[k] = __builtin_nontemporal_load(reinterpret_cast<const bwd_v4f*>(dx + (int64_t)slot_row[t * K + k] * d) + cv);
             ek[k] = reinterpret_cast<const uint2*>(e + (int64_t)idx[t * K + k] * d)[cv];
             dl[k] = dlogit[t * K + k];
         }
@@ -205,49 +215,68 @@ __global__ __launch_bounds__(128) void du_kernel(const float* __restrict__ dh, c
             a.z = __builtin_fmaf(dl[k], bf16_lo(ek[k].y), a.z);
             a.w = __builtin_fmaf(dl[k], bf16_hi(ek[k].y), a.w);
         }
-        reinterpret_cast<float4*>(du + t * d)[cv] = a;
+        const bwd_v4f o = {a.x, a.y, a.z, a.w};
+        __builtin_nontemporal_store(o, reinterpret_cast<bwd_v4f*>(du + t * d) + cv);
     }
 }
 
-// de_i = sum over the routed rows r of expert i (in row order) of
-// row_dlogit[r] * u[row_token[r]]; one block per (expert, 512 columns),
-// 4 columns per thread, four rows' loads in flight.
-__global__ __launch_bounds__(128) void de_kernel(const float* __restrict__ row_dlogit,
-                                                 const int32_t* __restrict__ row_token,
-                                                 const int32_t* __restrict__ group_offset,
-                                                 const uint16_t* __restrict__ u, int d,
-                                                 float* __restrict__ de) {
+// de_i = sum over the routed rows r of expert i of row_dlogit[r] *
+// u[row_token[r]]; one block per (expert, 512 columns): 128 column threads
+// (4 columns each) x DE_PHASES row phases, phase p summing rows r0+p,
+// r0+p+DE_PHASES, ... (four rows' loads in flight), then the phases added in
+// order through LDS, so the result does not depend on timing.
+constexpr int DE_PHASES = 8;
+
+__global__ __launch_bounds__(128 * DE_PHASES) void de_kernel(const float* __restrict__ row_dlogit,
+                                                             const int32_t* __restrict__ row_token,
+                                                             const int32_t* __restrict__ group_offset,
+                                                             const uint16_t* __restrict__ u, int d,
+                                                             float* __restrict__ de) {
+    __shared__ float4 part[DE_PHASES][128];
     const int i = blockIdx.y;
-    const int cv = blockIdx.x * blockDim.x + threadIdx.x;        // 4-column index
-    if (cv >= d / 4) return;
+    const int col = threadIdx.x & 127, ph = threadIdx.x >> 7;
+    const int cv = blockIdx.x * 128 + col;                       // 4-column index
+    const bool live = cv < d / 4;
     const int r0 = group_offset[i], r1 = group_offset[i + 1];
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-    int r = r0;
-    for (; r + 4 <= r1; r += 4) {
-        uint2 uv[4];
-        float w[4];
+    if (live) {
+        int r = r0 + ph;
+        for (; r + 3 * DE_PHASES < r1; r += 4 * DE_PHASES) {
+            uint2 uv[4];
+            float w[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            w[q] = row_dlogit[r + q];
-            uv[q] = reinterpret_cast<const uint2*>(u + (int64_t)row_token[r + q] * d)[cv];
+            for (int q = 0; q < 4; ++q) {
+                w[q] = row_dlogit[r + q * DE_PHASES];
+                uv[q] = reinterpret_cast<const uint2*>(u + (int64_t)row_token[r + q * DE_PHASES] * d)[cv];
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                a.x = __builtin_fmaf(w[q], bf16_lo(uv[q].x), a.x);
+                a.y = __builtin_fmaf(w[q], bf16_hi(uv[q].x), a.y);
+                a.z = __builtin_fmaf(w[q], bf16_lo(uv[q].y), a.z);
+                a.w = __builtin_fmaf(w[q], bf16_hi(uv[q].y), a.w);
+            }
         }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            a.x = __builtin_fmaf(w[q], bf16_lo(uv[q].x), a.x);
-            a.y = __builtin_fmaf(w[q], bf16_hi(uv[q].x), a.y);
-            a.z = __builtin_fmaf(w[q], bf16_lo(uv[q].y), a.z);
-            a.w = __builtin_fmaf(w[q], bf16_hi(uv[q].y), a.w);
+        for (; r < r1; r += DE_PHASES) {
+            const float w = row_dlogit[r];
+            const uint2 uv = reinterpret_cast<const uint2*>(u + (int64_t)row_token[r] * d)[cv];
+            a.x = __builtin_fmaf(w, bf16_lo(uv.x), a.x);
+            a.y = __builtin_fmaf(w, bf16_hi(uv.x), a.y);
+            a.z = __builtin_fmaf(w, bf16_lo(uv.y), a.z);
+            a.w = __builtin_fmaf(w, bf16_hi(uv.y), a.w);
         }
     }
-    for (; r < r1; ++r) {
-        const float w = row_dlogit[r];
-        const uint2 uv = reinterpret_cast<const uint2*>(u + (int64_t)row_token[r] * d)[cv];
-        a.x = __builtin_fmaf(w, bf16_lo(uv.x), a.x);
-        a.y = __builtin_fmaf(w, bf16_hi(uv.x), a.y);
-        a.z = __builtin_fmaf(w, bf16_lo(uv.y), a.z);
-        a.w = __builtin_fmaf(w, bf16_hi(uv.y), a.w);
+    part[ph][col] = a;
+    __syncthreads();
+    if (ph == 0 && live) {
+        float4 t = part[0][col];
+#pragma unroll
+        for (int p = 1; p < DE_PHASES; ++p) {
+            const float4 v = part[p][col];
+            t.x = t.x + v.x; t.y = t.y + v.y; t.z = t.z + v.z; t.w = t.w + v.w;
+        }
+        reinterpret_cast<float4*>(de + (int64_t)i * d)[cv] = t;
     }
-    reinterpret_cast<float4*>(de + (int64_t)i * d)[cv] = a;
 }
 
 // out[g][c][r] = in[g][r][c] for bytes, one 128 x 128 block per workgroup
@@ -330,7 +359,7 @@ hipError_t launch_du(const float* dh, const float* dx, int64_t shared_row0, cons
 hipError_t launch_de(const float* row_dlogit, const int32_t* row_token, const int32_t* group_offset,
                      const uint16_t* u, int d, int E, float* de, hipStream_t st) {
     const dim3 grid((unsigned)((d / 4 + 127) / 128), (unsigned)E);
-    hipLaunchKernelGGL(de_kernel, grid, dim3(128), 0, st, row_dlogit, row_token, group_offset, u, d, de);
+    hipLaunchKernelGGL(de_kernel, grid, dim3(128 * DE_PHASES), 0, st, row_dlogit, row_token, group_offset, u, d, de);
     return hipGetLastError();
 }
 
