@@ -259,10 +259,9 @@ def layer_quant_error(sh, st, n_tok=4):
 
 
 def run_layer_backward(sh, steps, warmup):
-    """The input-gradient backward of the layer after one forward step: gate
-    backward (dY quantised), GEMM(dY, W2^T), GEMM1 recomputed with the FP32
-    store epilogue (z), SwiGLU backward (dz quantised), GEMM(dz, W13^T), then
-    du and the centroid gradient.  One step = that chain for the whole batch
+    """The input-gradient backward of the layer after one forward step whose
+    GEMM1 kept z: gate backward (dY quantised), GEMM(dY, W2^T), SwiGLU backward
+    (dz quantised), GEMM(dz, W13^T), then du and the centroid gradient.  One step = that chain for the whole batch
     with dL/dh' ~ N(0,1); the transposed weights are prepared once, untimed
     (like the forward's weight quantisation)."""
     log(f"[bench] setup {sh.name} backward: T={sh.T} d={sh.d} E={sh.E} K={sh.K} I={sh.I}")
@@ -278,9 +277,29 @@ def run_layer_backward(sh, steps, warmup):
     t2q, t2s = t2q.view(G, I, d), t2s.view(G, I // 128, d // 128)
     dh = workloads.normal((T, d), 1.0, workloads.seed_for("backward", "dh", T), device="cuda")
     dev = dh.device
+    # a training forward keeps GEMM1's output z for the SwiGLU backward: the
+    # quantising epilogue that also stores z; its cost over the inference
+    # epilogue is reported beside the backward
+    z = torch.empty(R, 2 * I, device=dev)
+    ev0 = Events()
+    for kind in ("inference", "training"):
+        for rep in range(3 + steps):
+            a0 = ev0.mark("s")
+            if kind == "inference":
+                moe.grouped_gemm_fp8_blockscaled(st["uq"], st["us"], go, R, w13q, w13s, epi=moe.MOE_EPI_SWIGLU_QUANT,
+                                                 a_row_index=row_token, out_q=st["hq"], out_scale=st["hs"],
+                                                 ws=st["gws"])
+            else:
+                moe.grouped_gemm_fp8_blockscaled(st["uq"], st["us"], go, R, w13q, w13s,
+                                                 epi=moe.MOE_EPI_SWIGLU_QUANT_Z, a_row_index=row_token,
+                                                 out=z, out_q=st["hq"], out_scale=st["hs"], ws=st["gws"])
+            if rep >= 3:
+                ev0.add(kind, a0, ev0.mark("e"))
+    torch.cuda.synchronize()
+    fwd_gemm1 = {"inference_epilogue_ms": round(ev0.avg_ms("inference"), 4),
+                 "training_epilogue_ms": round(ev0.avg_ms("training"), 4)}
     nk = max(2 * I, d)
-    b = dict(dh_row=torch.empty(R, I, device=dev), z=torch.empty(R, 2 * I, device=dev),
-             dx=torch.empty(R, d, device=dev),
+    b = dict(dh_row=torch.empty(R, I, device=dev), z=z, dx=torch.empty(R, d, device=dev),
              ws=torch.empty(max(moe.moe_gemm_workspace_bytes(G, R, nk, nk), 256), dtype=torch.uint8, device=dev))
 
     def step(ev=None):
@@ -291,9 +310,6 @@ def run_layer_backward(sh, steps, warmup):
         moe.grouped_gemm_fp8_blockscaled(dy_q, dy_s, go, R, t2q, t2s, epi=moe.MOE_EPI_STORE_F32,
                                          out=b["dh_row"], ws=b["ws"])
         if ev: m.append(ev.mark("gemm2_dgrad"))
-        moe.grouped_gemm_fp8_blockscaled(st["uq"], st["us"], go, R, w13q, w13s, epi=moe.MOE_EPI_STORE_F32,
-                                         a_row_index=row_token, out=b["z"], ws=b["ws"])
-        if ev: m.append(ev.mark("gemm1_recompute"))
         dz_q, dz_s = moe.moe_swiglu_backward(b["z"], b["dh_row"])
         if ev: m.append(ev.mark("swiglu_bwd"))
         moe.grouped_gemm_fp8_blockscaled(dz_q, dz_s, go, R, t13q, t13s, epi=moe.MOE_EPI_STORE_F32,
@@ -303,7 +319,7 @@ def run_layer_backward(sh, steps, warmup):
                                 row_token, go, shared_row0=T * K)
         if ev:
             m.append(ev.mark("router_bwd"))
-            names = ["gate_bwd", "gemm2_dgrad", "gemm1_recompute", "swiglu_bwd", "gemm1_dgrad", "router_bwd"]
+            names = ["gate_bwd", "gemm2_dgrad", "swiglu_bwd", "gemm1_dgrad", "router_bwd"]
             for i, n in enumerate(names):
                 ev.add(n, m[i], m[i + 1])
 
@@ -318,9 +334,8 @@ def run_layer_backward(sh, steps, warmup):
     ms = (time.perf_counter() - t0) * 1e3 / steps
     stages = {n: round(ev.avg_ms(n), 4) for n in ev.pairs}
     f2 = 2.0 * R * d * I              # GEMM(dY, W2^T)
-    f1 = 2.0 * R * d * 2 * I          # the GEMM1 recompute and GEMM(dz, W13^T) each
+    f1 = 2.0 * R * d * 2 * I          # GEMM(dz, W13^T)
     tf = {"gemm2_dgrad": round(f2 / (ev.avg_ms("gemm2_dgrad") * 1e-3) / 1e12, 1),
-          "gemm1_recompute": round(f1 / (ev.avg_ms("gemm1_recompute") * 1e-3) / 1e12, 1),
           "gemm1_dgrad": round(f1 / (ev.avg_ms("gemm1_dgrad") * 1e-3) / 1e12, 1)}
     k_ms = ev.avg_ms("gemm1_dgrad")
     if T >= 4096:
@@ -344,6 +359,7 @@ def run_layer_backward(sh, steps, warmup):
         "config": {"workload": f"moe_layer_{sh.name}_backward", "T": T, "d": d, "routed_experts": E, "top_k": K,
                    "shared_experts": 1, "inter": I, "parallelism": "single GPU"},
         "roofline": roof, "stages_ms": stages, "gemm_tflops": tf,
+        "forward_gemm1_for_training": fwd_gemm1,
     }
 
 

@@ -56,9 +56,12 @@ typedef enum { MOE_BF16 = 0, MOE_F32 = 1 } moe_dtype;
 typedef enum {
     MOE_EPI_STORE_F32 = 0,   /* out = C, FP32 [M_total, N] */
     MOE_EPI_SWIGLU_F32 = 1,  /* out = SiLU(C_gate) * C_up, FP32 [M_total, N/2] */
-    MOE_EPI_SWIGLU_QUANT = 2 /* the same h, quantised per 1x128 tile into
+    MOE_EPI_SWIGLU_QUANT = 2, /* the same h, quantised per 1x128 tile into
                                 out_q E4M3 [M_total, N/2] + out_scale FP32
                                 [M_total, N/256] */
+    MOE_EPI_SWIGLU_QUANT_Z = 3 /* as MOE_EPI_SWIGLU_QUANT, and also C itself
+                                (the SwiGLU inputs a backward pass needs) in
+                                out FP32 [M_total, N] */
 } moe_epilogue;
 
 const char* moe_status_string(int status);
@@ -198,7 +201,10 @@ int fp8_quant_128x128(const float* w, int64_t rows, int cols, uint8_t* q, float*
  *                             h[m, 128j+c] = SiLU(C[m,256j+c]) * C[m,256j+128+c]
  *        MOE_EPI_SWIGLU_QUANT: the same h, quantised per 1x128 tile with the
  *                             rule above into out_q [M_total, N/2] and
- *                             out_scale [M_total, N/256]; out may be NULL.
+ *                             out_scale [M_total, N/256]; out may be NULL
+ *                             (else it receives h FP32 [M_total, N/2]).
+ *        MOE_EPI_SWIGLU_QUANT_Z: out_q and out_scale as SWIGLU_QUANT, and
+ *                             C in out FP32 [M_total, N] (required).
  *   ws   scratch of moe_gemm_workspace_bytes(G, M_total, N, K) bytes (the
  *        device-built tile map and tile list, and the A scales gathered into
  *        GEMM row order, slice-major; its contents need no setup).

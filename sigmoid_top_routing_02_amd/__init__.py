@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoefp8.so")
 
 MOE_BF16, MOE_F32 = 0, 1
-MOE_EPI_STORE_F32, MOE_EPI_SWIGLU_F32, MOE_EPI_SWIGLU_QUANT = 0, 1, 2
+MOE_EPI_STORE_F32, MOE_EPI_SWIGLU_F32, MOE_EPI_SWIGLU_QUANT, MOE_EPI_SWIGLU_QUANT_Z = 0, 1, 2, 3
 
 # every symbol the header declares (kept in step with include/moe_fp8.h)
 EXPORTS = (
@@ -248,6 +248,8 @@ def grouped_gemm_fp8_blockscaled(a_q, a_scale, group_offset, M_total, b_q, b_sca
     else:
         out_q = _new((M_total, N // 2), torch.uint8, a_q) if out_q is None else out_q
         out_scale = _new((M_total, N // 256), torch.float32, a_q) if out_scale is None else out_scale
+        if epi == MOE_EPI_SWIGLU_QUANT_Z and out is None:
+            out = _new((M_total, N), torch.float32, a_q)
     L = load_library()
     if ws is None:
         ws = _new((max(L.moe_gemm_workspace_bytes(G, M_total, N, K), 256),), torch.uint8, a_q)
@@ -257,6 +259,8 @@ def grouped_gemm_fp8_blockscaled(a_q, a_scale, group_offset, M_total, b_q, b_sca
         _stream()), "grouped_gemm_fp8_blockscaled")
     if epi == MOE_EPI_SWIGLU_QUANT:
         return out_q, out_scale
+    if epi == MOE_EPI_SWIGLU_QUANT_Z:
+        return out_q, out_scale, out
     return out
 
 

@@ -211,7 +211,7 @@ int grouped_gemm_fp8_blockscaled(const uint8_t* a_q, const float* a_scale,
     REQUIRE(G >= 1 && G <= 65535, MOE_ERR_UNSUPPORTED, "grouped_gemm: G=%d outside [1, 65535]", G);
     REQUIRE(M_total >= 0 && M_total < ((int64_t)1 << 31), MOE_ERR_UNSUPPORTED, "grouped_gemm: M_total out of range");
     REQUIRE(K > 0 && K % 128 == 0, MOE_ERR_SHAPE, "grouped_gemm: K=%d not a positive multiple of 128", K);
-    REQUIRE(epi >= MOE_EPI_STORE_F32 && epi <= MOE_EPI_SWIGLU_QUANT, MOE_ERR_UNSUPPORTED, "grouped_gemm: epilogue %d", epi);
+    REQUIRE(epi >= MOE_EPI_STORE_F32 && epi <= MOE_EPI_SWIGLU_QUANT_Z, MOE_ERR_UNSUPPORTED, "grouped_gemm: epilogue %d", epi);
     if (epi == MOE_EPI_STORE_F32)
         REQUIRE(N > 0 && N % 128 == 0, MOE_ERR_SHAPE, "grouped_gemm: N=%d not a positive multiple of 128", N);
     else
@@ -232,6 +232,10 @@ int grouped_gemm_fp8_blockscaled(const uint8_t* a_q, const float* a_scale,
         REQUIRE_PTR(out_q);
         REQUIRE_PTR(out_scale);
         if (out) REQUIRE_PTR(out);
+    } else if (epi == MOE_EPI_SWIGLU_QUANT_Z) {
+        REQUIRE_PTR(out_q);
+        REQUIRE_PTR(out_scale);
+        REQUIRE_PTR(out);
     } else {
         REQUIRE_PTR(out);
     }

@@ -523,7 +523,7 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
                         h[mi][ni][j] = silu(acc[mi][ni][j]) * acc[mi][ni + HALF][j];
-            if constexpr (EPI == EPI_SWIGLU_QUANT) {
+            if constexpr (EPI == EPI_SWIGLU_QUANT || EPI == EPI_SWIGLU_QUANT_Z) {
                 // row maximum over this wave's HC h columns (lanes lr, lr+16, lr+32
                 // and lr+48 hold one row), then across the N-waves in LDS
 #pragma unroll
@@ -571,7 +571,7 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
         if constexpr (EPI != EPI_STORE_F32) {
             const int I = p.N / 2;
             const int h0 = T.n0 / 2;         // first h column of this tile
-            if constexpr (EPI == EPI_SWIGLU_QUANT) {
+            if constexpr (EPI == EPI_SWIGLU_QUANT || EPI == EPI_SWIGLU_QUANT_Z) {
                 // BM rows x 128 bytes, 16-byte stores, and one scale per row
                 for (int c = tid; c < BM * 8; c += NT) {
                     const int r = c >> 3, part = c & 7;
@@ -581,7 +581,7 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
                 }
                 if (tid < BM && tid < T.rows) p.out_s[(int64_t)(T.m0 + tid) * (I / 128) + h0 / 128] = scale_s[tid];
             }
-            if (EPI == EPI_SWIGLU_F32 || p.out) {
+            if (EPI == EPI_SWIGLU_F32 || (EPI == EPI_SWIGLU_QUANT && p.out)) {
 #pragma unroll
                 for (int mi = 0; mi < MI; ++mi) {
                     const int r = sa_row + mi * 16;
@@ -591,6 +591,19 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
                     for (int ni = 0; ni < HALF; ++ni)
                         *reinterpret_cast<float4*>(orow + ni * 16) =
                             make_float4(h[mi][ni][0], h[mi][ni][1], h[mi][ni][2], h[mi][ni][3]);
+                }
+            }
+            if constexpr (EPI == EPI_SWIGLU_QUANT_Z) {
+                // the GEMM output z itself (gate and up columns in B's row order)
+#pragma unroll
+                for (int mi = 0; mi < MI; ++mi) {
+                    const int r = sa_row + mi * 16;
+                    if (r >= T.rows) continue;
+                    float* zrow = p.out + (int64_t)(T.m0 + r) * p.N + T.n0 + 4 * kb;
+#pragma unroll
+                    for (int ni = 0; ni < NI; ++ni)
+                        *reinterpret_cast<float4*>(zrow + ncol<EPI, C>(wn, ni)) =
+                            make_float4(acc[mi][ni][0], acc[mi][ni][1], acc[mi][ni][2], acc[mi][ni][3]);
                 }
             }
         }
@@ -890,12 +903,14 @@ hipError_t launch_grouped_gemm(const uint8_t* a_q, const float* a_s, const int32
         switch (epi) {
             case EPI_STORE_F32: MOE_LAUNCH(EPI_STORE_F32, 32); break;
             case EPI_SWIGLU_F32: MOE_LAUNCH(EPI_SWIGLU_F32, 32); break;
+            case EPI_SWIGLU_QUANT_Z: MOE_LAUNCH(EPI_SWIGLU_QUANT_Z, 32); break;
             default: MOE_LAUNCH(EPI_SWIGLU_QUANT, 32); break;
         }
     } else {
         switch (epi) {
             case EPI_STORE_F32: MOE_LAUNCH(EPI_STORE_F32, 128); break;
             case EPI_SWIGLU_F32: MOE_LAUNCH(EPI_SWIGLU_F32, 128); break;
+            case EPI_SWIGLU_QUANT_Z: MOE_LAUNCH(EPI_SWIGLU_QUANT_Z, 128); break;
             default: MOE_LAUNCH(EPI_SWIGLU_QUANT, 128); break;
         }
     }

@@ -8,7 +8,8 @@ parity protocol does.
   * gate backward: dY's 1x128 codes and scales bit-exact (dY = fl32(g * dh) on
     both sides); dlogit within the per-row bound;
   * GEMM(dY, W2^T) = dh_row and GEMM(dz, W13^T) = dx within the per-row bound
-    of the oracle's FP64 product of the same codes;
+    of the oracle's FP64 product of the same codes (z comes from GEMM1's
+    epilogue that keeps it, whose h codes must equal the forward's);
   * SwiGLU backward: every dz code within half an E4M3 step of the FP64 value
     (plus the FP32 arithmetic's slack), scales within tolerance;
   * du and de within the per-row bound.
@@ -96,13 +97,16 @@ def test_backward_dgrad_staged(T, d, E, K, I):
     dy_q, dy_s, dlogit, row_dlogit = moe.moe_gate_backward(dh, f["y"], f["gate"], f["slot_row"], f["s"],
                                                            f["idx"], shared_row0=T * K)
     dh_row = moe.grouped_gemm_fp8_blockscaled(dy_q, dy_s, go, R, t2q, t2s, epi=moe.MOE_EPI_STORE_F32)
-    z = moe.grouped_gemm_fp8_blockscaled(f["uq"], f["us"], go, R, w13q, w13s, epi=moe.MOE_EPI_STORE_F32,
-                                         a_row_index=f["row_token"])
+    # z as a training forward keeps it (the quantising epilogue that also stores
+    # z); its h codes are the forward's own
+    hq_z, hs_z, z = moe.grouped_gemm_fp8_blockscaled(f["uq"], f["us"], go, R, w13q, w13s,
+                                                     epi=moe.MOE_EPI_SWIGLU_QUANT_Z, a_row_index=f["row_token"])
     dz_q, dz_s = moe.moe_swiglu_backward(z, dh_row)
     dx = moe.grouped_gemm_fp8_blockscaled(dz_q, dz_s, go, R, t13q, t13s, epi=moe.MOE_EPI_STORE_F32)
     du, de = moe.moe_router_backward(dh, dx, f["slot_row"], dlogit, f["idx"], e, u, row_dlogit,
                                      f["row_token"], go, shared_row0=T * K)
     torch.cuda.synchronize()
+    assert torch.equal(hq_z, f["hq"]) and torch.equal(hs_z.view(torch.int32), f["hs"].view(torch.int32))
 
     # ---- gate backward
     say("  oracle: gate backward")

@@ -272,6 +272,20 @@ def test_gemm_swiglu_epilogues(sizes, I, d):
     hq_ref, hs_ref = oracle.quant_1x128(h_ref.astype(np.float32))
     flips = check_codes_close(np_(hq), np_(hs), hq_ref, hs_ref, h_ref, np_(h))
     say(f"  h-code midpoint flips: {flips} of {hq_ref.size}")
+    # the quantising epilogue that also keeps z: the same h codes bit for bit,
+    # and z (gate and up columns interleaved as B's rows) against the oracle
+    hq3, hs3, z = moe.grouped_gemm_fp8_blockscaled(*args, epi=moe.MOE_EPI_SWIGLU_QUANT_Z, a_row_index=rows_d)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(np_(hq3), np_(hq))
+    np.testing.assert_array_equal(np_(hs3).view(np.uint32), np_(hs).view(np.uint32))
+    z_ref = np.zeros((M, 2 * I))
+    for gi in range(G):
+        r0, r1 = go[gi], go[gi + 1]
+        if r1 > r0:
+            z_ref[r0:r1] = oracle.gemm_blockscaled(qa, sa, qb[gi], sb[gi], a_rows=rows_np[r0:r1])
+    err = rowinf_rel(np_(z), z_ref)
+    say(f"  z per-row rel err {err:.3e}")
+    assert err <= TOL
 
 
 def check_codes_close(q, s, q_ref, s_ref, x_ref, x_gpu):
