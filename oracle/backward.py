@@ -1,4 +1,5 @@
-"""CPU oracle for the input-gradient (dgrad) backward of the DeepSeekMoE layer
+"""CPU oracle for the backward of the DeepSeekMoE layer (input and weight
+gradients)
 -- TEST INFRASTRUCTURE ONLY (the tests may import it; the HIP library never
 does, and this module imports nothing from it).
 
@@ -23,7 +24,9 @@ and per expert row, with z_g = W1 x, z_u = W3 x, h = SiLU(z_g) z_u:
     dx       = W1^T dz_g + W3^T dz_u
 and finally
     du_t = dh_t + sum over the token's rows of dx + sum_k dlogit_k e_(i_k)
-    de_i = sum over the (t, k) that chose i of dlogit_k u_t.
+    de_i = sum over the (t, k) that chose i of dlogit_k u_t
+and, per expert, the weight gradients over its rows:
+    dW2 = sum_r dY_r^T h_r,  dW1 = sum_r dz_g,r^T x_r,  dW3 = sum_r dz_u,r^T x_r.
 Each function takes the operands it is given (dequantised FP8 ones for GPU
 parity, unquantised ones for the finite-difference pins) and computes in FP64.
 """
@@ -101,3 +104,17 @@ def assemble_du(dh, dx_rows, row_token):
     du = np.array(dh, np.float64, copy=True)
     np.add.at(du, np.asarray(row_token, np.int64), np.asarray(dx_rows, np.float64))
     return du
+
+
+def expert_wgrad(dy_rows, zg, zu, dh_row, x_rows):
+    """Weight gradients of one expert from its rows (FP64):
+        dW2 [d,I] = sum_r dY_r^T h_r,  h = SiLU(z_g) z_u
+        dW1 [I,d] = sum_r dz_g,r^T x_r,  dW3 [I,d] = sum_r dz_u,r^T x_r
+    with dz from swiglu_backward(z_g, z_u, dh_row)."""
+    zg = np.asarray(zg, np.float64)
+    zu = np.asarray(zu, np.float64)
+    h = zg * _sigmoid(zg) * zu
+    dzg, dzu = swiglu_backward(zg, zu, dh_row)
+    dy = np.asarray(dy_rows, np.float64)
+    x = np.asarray(x_rows, np.float64)
+    return dy.T @ h, dzg.T @ x, dzu.T @ x

@@ -143,3 +143,41 @@ def test_gate_backward_zero_gradient_cases():
     s0[0, :K] = 0.0
     _, _, dl0 = bw.gate_backward(dh, rng.standard_normal((T * K, d)), -1, gate, slot_row, s0, idx)
     assert np.all(dl0[0] == 0.0)
+
+
+@pytest.mark.parametrize("seed", [4, 5])
+def test_weight_gradients_match_finite_differences(seed):
+    """dL/dW1, dW3, dW2 of every expert (shared included) from the oracle's
+    per-expert weight gradients over its rows, against central differences
+    of the FP64 forward on a sample of weight entries."""
+    u, e, W1, W3, W2, idx, dh = _setup(seed)
+    T, K = idx.shape
+    E = e.shape[0]
+    an = _analytic(u, e, W1, W3, W2, idx, dh)
+    pairs = sorted((int(idx[t, k]), t, k) for t in range(T) for k in range(K))
+    row_token = np.array([t for _, t, _ in pairs] + list(range(T)))
+    row_group = np.array([g for g, _, _ in pairs] + [E] * T)
+    x = u[row_token]
+    zg = np.einsum("rid,rd->ri", W1[row_group], x)
+    zu = np.einsum("rid,rd->ri", W3[row_group], x)
+    grads = {}
+    for g in range(E + 1):
+        rows = np.nonzero(row_group == g)[0]
+        dh_row = an["dy"][rows] @ W2[g]
+        grads[g] = bw.expert_wgrad(an["dy"][rows], zg[rows], zu[rows], dh_row, x[rows])
+    rng = np.random.default_rng(seed)
+    eps = 1e-6
+    for which, W in ((0, W2), (1, W1), (2, W3)):
+        for _ in range(12):
+            g = int(rng.integers(0, E + 1))
+            i, j = (int(rng.integers(0, n)) for n in W.shape[1:])
+            Wp, Wm = W.copy(), W.copy()
+            Wp[g, i, j] += eps
+            Wm[g, i, j] -= eps
+            if which == 0:
+                fd = (_loss(u, e, W1, W3, Wp, idx, dh) - _loss(u, e, W1, W3, Wm, idx, dh)) / (2 * eps)
+            elif which == 1:
+                fd = (_loss(u, e, Wp, W3, W2, idx, dh) - _loss(u, e, Wm, W3, W2, idx, dh)) / (2 * eps)
+            else:
+                fd = (_loss(u, e, W1, Wp, W2, idx, dh) - _loss(u, e, W1, Wm, W2, idx, dh)) / (2 * eps)
+            np.testing.assert_allclose(grads[g][which][i, j], fd, rtol=1e-6, atol=1e-8)
