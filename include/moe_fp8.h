@@ -344,6 +344,32 @@ int moe_router_backward(const float* dh, const float* dx, int64_t shared_row0, c
                         const int32_t* group_offset, int64_t T, int K, int d, int E, float* du, float* de,
                         moe_stream_t stream);
 
+/* moe_wgrad_operands -- the operands of the expert weight gradients
+ *   dW2_g  = sum over the rows r of expert g of dY_r^T h_r           [d, I]
+ *   dW13_g = sum over the rows r of expert g of dz_r^T u_(token r)   [2I, d]
+ * (dY_r = topk_gate of the row's slot * dh_(token r), dh on the shared rows
+ * from shared_row0 on; h = SiLU(z_gate) z_up; dz = the SwiGLU backward of
+ * dh_row, in W13's interleaved row order), which contract over each
+ * expert's rows: each is one grouped_gemm_fp8_blockscaled call per expert
+ * with G = 1, M = d (2I), N = I (d), K = Kp_g, FP32 store, on the transposed
+ * operands written here.  Group g's rows [group_offset[g], group_offset[g+1])
+ * are padded with zero rows to Kp_g = 128 * nkb_g; kb_start int32 [G+1]
+ * (device) is the exclusive scan of nkb_g = ceil(rows_g / 128) and n_kb its
+ * total.  Layout, group after group (C = d, I, 2I, d for dY^T, h^T, dz^T,
+ * u^T; CS = C/128 rounded up to a multiple of 4):
+ *   codes E4M3 [C, Kp_g] at byte C * 128 * kb_start[g]
+ *   dY^T, dz^T scales (1x128 along the rows) FP32 [C, nkb_g] at C * kb_start[g]
+ *   h^T, u^T scales (128x128 blocks) FP32 [C/128, nkb_g] at CS * kb_start[g]
+ * so each group's operands satisfy the GEMM's layout and alignment.  The
+ * pages give no backward tiling: this library's reading.  Limits: d, I
+ * multiples of 128, 1 <= K <= 16, n_kb <= 65535.
+ */
+int moe_wgrad_operands(const float* dh, const float* topk_gate, const int32_t* slot_row, const int32_t* row_token,
+                       const float* z, const float* dh_row, const void* u_bf16, const int32_t* group_offset,
+                       const int32_t* kb_start, int G, int n_kb, int64_t T, int K, int d, int I,
+                       int64_t shared_row0, uint8_t* dyT_q, float* dyT_scale, uint8_t* hT_q, float* hT_scale,
+                       uint8_t* dzT_q, float* dzT_scale, uint8_t* xT_q, float* xT_scale, moe_stream_t stream);
+
 /* moe_layer_forward -- the whole layer: router, dispatch, 1x128 quantisation
  * of u, GEMM1 with fused SwiGLU and 1x128 re-quantisation, GEMM2, combine.
  * The bias is read only (update it with moe_bias_update).  packed_weights as

@@ -12,6 +12,8 @@ from __future__ import annotations
 import ctypes
 import os
 
+import numpy as np
+
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -32,6 +34,7 @@ EXPORTS = (
     "moe_packed_weight_bytes", "moe_prepare_expert_weights",
     "moe_layer_workspace_bytes", "moe_layer_forward",
     "moe_prepare_backward_weights", "moe_gate_backward", "moe_swiglu_backward", "moe_router_backward",
+    "moe_wgrad_operands",
 )
 
 
@@ -77,6 +80,8 @@ def load_library(path: str = LIB_PATH):
         "moe_gate_backward": ([P, P, I64, P, P, P, P, I64, I32, I32, I32, P, P, P, P, P], I32),
         "moe_swiglu_backward": ([P, P, I64, I32, P, P, P], I32),
         "moe_router_backward": ([P, P, I64, P, P, P, P, P, P, P, P, I64, I32, I32, I32, P, P, P], I32),
+        "moe_wgrad_operands": ([P, P, P, P, P, P, P, P, P, I32, I32, I64, I32, I32, I32, I64,
+                                P, P, P, P, P, P, P, P, P], I32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -425,3 +430,61 @@ def moe_router_backward(dh, dx, slot_row, dlogit, topk_idx, centroids, u, row_dl
                                  _ptr(centroids), _ptr(u), _ptr(row_dlogit), _ptr(row_token), _ptr(group_offset),
                                  T, K, d, E, _ptr(du), _ptr(de), _stream()), "moe_router_backward")
     return du, de
+
+
+def moe_wgrad(dh, topk_gate, slot_row, row_token, z, dh_row, u, group_offset, shared_row0=-1):
+    """Expert weight gradients -> (dW13 f32 [G, 2I, d] in W13's interleaved row
+    order, dW2 f32 [G, d, I]).  Builds the transposed operands
+    (moe_wgrad_operands), then runs one grouped_gemm_fp8_blockscaled per
+    expert (G = 1, K = its rows padded to 128) on views of them; the expert
+    sizes are read back to the host for those launches."""
+    T, d = dh.shape
+    K = topk_gate.shape[1]
+    R, I2 = z.shape
+    I = I2 // 2
+    G = group_offset.numel() - 1
+    go_h = group_offset.cpu().numpy().astype(np.int64)
+    nkb = (np.diff(go_h) + 127) // 128
+    kb_start = np.concatenate([[0], np.cumsum(nkb)]).astype(np.int32)
+    n_kb = int(kb_start[-1])
+    dev = dh.device
+    cs_h, cs_x = (I // 128 + 3) // 4 * 4, (d // 128 + 3) // 4 * 4
+    bufs = dict(
+        dyT_q=torch.empty(max(d * 128 * n_kb, 16), dtype=torch.uint8, device=dev),
+        dyT_s=torch.empty(max(d * n_kb, 4), dtype=torch.float32, device=dev),
+        hT_q=torch.empty(max(I * 128 * n_kb, 16), dtype=torch.uint8, device=dev),
+        hT_s=torch.empty(max(cs_h * n_kb, 4), dtype=torch.float32, device=dev),
+        dzT_q=torch.empty(max(2 * I * 128 * n_kb, 16), dtype=torch.uint8, device=dev),
+        dzT_s=torch.empty(max(2 * I * n_kb, 4), dtype=torch.float32, device=dev),
+        xT_q=torch.empty(max(d * 128 * n_kb, 16), dtype=torch.uint8, device=dev),
+        xT_s=torch.empty(max(cs_x * n_kb, 4), dtype=torch.float32, device=dev))
+    L = load_library()
+    kbs = torch.from_numpy(kb_start).to(dev)
+    _check(L.moe_wgrad_operands(_ptr(dh), _ptr(topk_gate), _ptr(slot_row), _ptr(row_token), _ptr(z), _ptr(dh_row),
+                                _ptr(u), _ptr(group_offset), _ptr(kbs), G, n_kb, T, K, d, I, shared_row0,
+                                *(_ptr(bufs[k]) for k in ("dyT_q", "dyT_s", "hT_q", "hT_s", "dzT_q", "dzT_s",
+                                                           "xT_q", "xT_s")), _stream()), "moe_wgrad_operands")
+    dw13 = _new((G, 2 * I, d), torch.float32, dh)
+    dw2 = _new((G, d, I), torch.float32, dh)
+    go_d = torch.tensor([0, d], dtype=torch.int32, device=dev)
+    go_2i = torch.tensor([0, 2 * I], dtype=torch.int32, device=dev)
+    kmax = int(nkb.max()) * 128 if n_kb else 128
+    ws = _new((max(L.moe_gemm_workspace_bytes(1, max(d, 2 * I), max(d, I), kmax), 256),), torch.uint8, dh)
+    for g in range(G):
+        n = int(nkb[g])
+        if n == 0:
+            dw2[g].zero_()
+            dw13[g].zero_()
+            continue
+        kb0, kp = int(kb_start[g]), 128 * n
+        a = bufs["dyT_q"][d * 128 * kb0:d * 128 * kb0 + d * kp].view(d, kp)
+        a_s = bufs["dyT_s"][d * kb0:d * kb0 + d * n].view(d, n)
+        b = bufs["hT_q"][I * 128 * kb0:I * 128 * kb0 + I * kp].view(1, I, kp)
+        b_s = bufs["hT_s"][cs_h * kb0:cs_h * kb0 + (I // 128) * n].view(1, I // 128, n)
+        grouped_gemm_fp8_blockscaled(a, a_s, go_d, d, b, b_s, epi=MOE_EPI_STORE_F32, out=dw2[g], ws=ws)
+        a = bufs["dzT_q"][2 * I * 128 * kb0:2 * I * 128 * kb0 + 2 * I * kp].view(2 * I, kp)
+        a_s = bufs["dzT_s"][2 * I * kb0:2 * I * kb0 + 2 * I * n].view(2 * I, n)
+        b = bufs["xT_q"][d * 128 * kb0:d * 128 * kb0 + d * kp].view(1, d, kp)
+        b_s = bufs["xT_s"][cs_x * kb0:cs_x * kb0 + (d // 128) * n].view(1, d // 128, n)
+        grouped_gemm_fp8_blockscaled(a, a_s, go_2i, 2 * I, b, b_s, epi=MOE_EPI_STORE_F32, out=dw13[g], ws=ws)
+    return dw13, dw2, bufs, kb_start

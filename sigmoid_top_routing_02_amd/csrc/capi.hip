@@ -431,6 +431,42 @@ int moe_router_backward(const float* dh, const float* dx, int64_t shared_row0, c
                       "de launch");
 }
 
+int moe_wgrad_operands(const float* dh, const float* topk_gate, const int32_t* slot_row, const int32_t* row_token,
+                       const float* z, const float* dh_row, const void* u_bf16, const int32_t* group_offset,
+                       const int32_t* kb_start, int G, int n_kb, int64_t T, int K, int d, int I,
+                       int64_t shared_row0, uint8_t* dyT_q, float* dyT_scale, uint8_t* hT_q, float* hT_scale,
+                       uint8_t* dzT_q, float* dzT_scale, uint8_t* xT_q, float* xT_scale, moe_stream_t stream) {
+    REQUIRE(G >= 1 && G <= 65535, MOE_ERR_UNSUPPORTED, "moe_wgrad_operands: G=%d outside [1, 65535]", G);
+    REQUIRE(n_kb >= 0 && n_kb <= 65535, MOE_ERR_UNSUPPORTED, "moe_wgrad_operands: n_kb=%d outside [0, 65535]", n_kb);
+    REQUIRE(K >= 1 && K <= 16, MOE_ERR_UNSUPPORTED, "moe_wgrad_operands: K=%d outside [1, 16]", K);
+    REQUIRE(d > 0 && d % 128 == 0 && I > 0 && I % 128 == 0, MOE_ERR_SHAPE,
+            "moe_wgrad_operands: d=%d, I=%d must be positive multiples of 128", d, I);
+    REQUIRE(T >= 0, MOE_ERR_SHAPE, "moe_wgrad_operands: T < 0");
+    if (n_kb == 0) return MOE_OK;
+    REQUIRE_PTR(dh);
+    REQUIRE_PTR(topk_gate);
+    REQUIRE_PTR(slot_row);
+    REQUIRE_PTR(row_token);
+    REQUIRE_PTR(z);
+    REQUIRE_PTR(dh_row);
+    REQUIRE_PTR(u_bf16);
+    REQUIRE_PTR(group_offset);
+    REQUIRE_PTR(kb_start);
+    REQUIRE_PTR(dyT_q);
+    REQUIRE_PTR(dyT_scale);
+    REQUIRE_PTR(hT_q);
+    REQUIRE_PTR(hT_scale);
+    REQUIRE_PTR(dzT_q);
+    REQUIRE_PTR(dzT_scale);
+    REQUIRE_PTR(xT_q);
+    REQUIRE_PTR(xT_scale);
+    return hip_status(moe::launch_wgrad_operands(dh, topk_gate, slot_row, row_token, z, dh_row,
+                                                 static_cast<const uint16_t*>(u_bf16), shared_row0, K, d, I,
+                                                 group_offset, kb_start, G, n_kb, dyT_q, dyT_scale, hT_q, hT_scale,
+                                                 dzT_q, dzT_scale, xT_q, xT_scale, S(stream)),
+                      "wgrad operand launch");
+}
+
 // ---------------------------------------------------------------- whole layer
 namespace {
 struct LayerWs {

@@ -56,6 +56,14 @@ hipError_t launch_de(const float* row_dlogit, const int32_t* row_token, const in
 hipError_t launch_transpose_blocks(const uint8_t* in, const float* in_s, int G, int rows, int cols,
                                    uint8_t* out, float* out_s, hipStream_t st);
 
+// wgrad.hip
+hipError_t launch_wgrad_operands(const float* dh, const float* gate, const int32_t* slot_row,
+                                 const int32_t* row_token, const float* z, const float* dh_row,
+                                 const uint16_t* u, int64_t shared_row0, int K, int d, int I,
+                                 const int32_t* go, const int32_t* kb_start, int G, int n_kb,
+                                 uint8_t* dyT_q, float* dyT_s, uint8_t* hT_q, float* hT_s, uint8_t* dzT_q,
+                                 float* dzT_s, uint8_t* xT_q, float* xT_s, hipStream_t st);
+
 // balance.hip
 size_t seq_balance_ws_bytes(int64_t n_seq, int L);
 hipError_t launch_seq_balance_loss(const float* s, const int32_t* idx, int64_t n_seq, int E, int K,

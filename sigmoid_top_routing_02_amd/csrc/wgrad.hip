@@ -1,0 +1,164 @@
+// Operands of the expert weight gradients.
+//
+// Per expert g, over its GEMM rows r (the forward's dispatch order):
+//     dW2_g = sum_r dY_r^T h_r        ([d, I]),    h = SiLU(z_gate) * z_up
+//     dW13_g = sum_r dz_r^T x_r       ([2I, d], W13's interleaved row order),
+// with dY_r = w_r dh_(token r) (w_r the slot's gate, 1 on the shared rows),
+// dz the SwiGLU backward of dh_row, and x_r = u_(token r).  These contract
+// over the rows, so each runs on the grouped block-scaled GEMM as one group
+// with M = d (or 2I), N = I (or d) and K = the expert's rows padded to a
+// multiple of 128, on transposed operands built here: dY^T and dz^T quantised
+// per 1 x 128 tile along the rows (the contraction), h^T and x^T per 128 x 128
+// block (this library's reading; the pages give no backward tiling).  The
+// padding rows are zero.
+//
+// Layout of each operand, group after group (kb_start[g] = the 128-row blocks
+// before group g, nkb_g = blocks of group g, Kp_g = 128 nkb_g):
+//     codes  [C, Kp_g] at C * 128 * kb_start[g]
+//     1x128 scales  [C, nkb_g] at C * kb_start[g];  128x128 scales
+//     [C/128, nkb_g] at CS * kb_start[g], CS = C/128 rounded up to a multiple
+//     of 4 (every group's scales start 16-byte aligned).
+// One workgroup per (128 columns, 128-row block): the block's values are
+// computed into LDS transposed, then quantised and written 64 bytes per lane.
+#include "device_math.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+enum { SRC_DY = 0, SRC_H = 1, SRC_DZ = 2, SRC_X = 3 };
+
+struct WgradSrc {
+    const float* dh;          // [T, d]
+    const float* gate;        // [T, K]
+    const int32_t* slot_row;  // [T, K]
+    const int32_t* row_token; // [R]
+    const float* z;           // [R, 2I]
+    const float* dh_row;      // [R, I]
+    const uint16_t* u;        // [T, d] bf16
+    int64_t shared_row0;
+    int K, d, I;
+};
+
+__device__ __forceinline__ float sigm(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
+
+// the weight of row r's dY: its slot's gate (routed rows), 1 (shared rows)
+__device__ __forceinline__ float row_weight(const WgradSrc& s, int64_t r, int64_t t) {
+    if (s.shared_row0 >= 0 && r >= s.shared_row0) return 1.0f;
+    for (int k = 0; k < s.K; ++k)
+        if (s.slot_row[t * s.K + k] == r) return s.gate[t * s.K + k];
+    return 0.0f;
+}
+
+template <int SRC, bool BLOCK_SCALE>
+__global__ __launch_bounds__(256) void wgrad_operand_kernel(WgradSrc s, const int32_t* __restrict__ go,
+                                                            const int32_t* __restrict__ kb_start, int G, int C,
+                                                            uint8_t* __restrict__ out_q, float* __restrict__ out_s) {
+    __shared__ float tile[128][129];
+    __shared__ float wmax[4];
+    const int tid = threadIdx.x;
+    const int c0 = blockIdx.x * 128;
+    const int kbi = blockIdx.y;
+    int lo = 0, hi = G - 1;                                    // the group of this row block
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (kb_start[mid] <= kbi) lo = mid; else hi = mid - 1;
+    }
+    const int g = lo;
+    const int kb0 = kb_start[g], nkb = kb_start[g + 1] - kb0, kbl = kbi - kb0;
+    const int64_t rb = (int64_t)go[g] + (int64_t)kbl * 128, rend = go[g + 1];
+    {   // values: thread = column c0 + (tid & 127), rows (tid >> 7), +2, ...
+        const int c = c0 + (tid & 127);
+        for (int i = tid >> 7; i < 128; i += 2) {
+            const int64_t r = rb + i;
+            float v = 0.0f;
+            if (r < rend) {
+                if constexpr (SRC == SRC_DY) {
+                    const int64_t t = s.row_token[r];
+                    v = row_weight(s, r, t) * s.dh[t * s.d + c];
+                } else if constexpr (SRC == SRC_X) {
+                    const int64_t t = s.row_token[r];
+                    v = bf16_lo((uint32_t)s.u[t * s.d + c]);
+                } else if constexpr (SRC == SRC_H) {
+                    const float* zr = s.z + r * 2 * s.I + (c >> 7) * 256 + (c & 127);
+                    const float zg = zr[0], zu = zr[128];
+                    v = zg * sigm(zg) * zu;
+                } else {
+                    const int j = c >> 8, w = c & 255, ic = j * 128 + (w & 127);
+                    const float* zr = s.z + r * 2 * s.I + j * 256 + (w & 127);
+                    const float zg = zr[0], zu = zr[128];
+                    const float dh = s.dh_row[r * s.I + ic];
+                    const float sg = sigm(zg);
+                    v = (w < 128) ? dh * zu * sg * (1.0f + zg * (1.0f - sg)) : dh * (zg * sg);
+                }
+            }
+            tile[i][tid & 127] = v;
+        }
+    }
+    __syncthreads();
+    // output row c0 + (tid >> 1), 64 consecutive k at (tid & 1) * 64
+    const int oc = tid >> 1, half = tid & 1;
+    float amax = 0.0f;
+    for (int q = 0; q < 64; ++q) {
+        const float a = __builtin_fabsf(tile[half * 64 + q][oc]);
+        amax = a > amax ? a : amax;
+    }
+    if constexpr (BLOCK_SCALE) {
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const float other = __shfl_xor(amax, o, 64);
+            amax = other > amax ? other : amax;
+        }
+        if ((tid & 63) == 0) wmax[tid >> 6] = amax;
+        __syncthreads();
+        amax = wmax[0];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) amax = wmax[w] > amax ? wmax[w] : amax;
+    } else {
+        const float other = __shfl_xor(amax, 1, 64);
+        amax = other > amax ? other : amax;
+    }
+    float inv, sc;
+    tile_scale(amax, inv, sc);
+    const int64_t Kp = (int64_t)nkb * 128;
+    uint8_t* dst = out_q + (int64_t)C * 128 * kb0 + (int64_t)(c0 + oc) * Kp + (int64_t)kbl * 128 + half * 64;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        uint32_t w4[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int k = half * 64 + q * 16 + p * 4;
+            w4[p] = e4m3_encode4(tile[k][oc] * inv, tile[k + 1][oc] * inv, tile[k + 2][oc] * inv,
+                                 tile[k + 3][oc] * inv);
+        }
+        *reinterpret_cast<uint4*>(dst + q * 16) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+    }
+    if constexpr (BLOCK_SCALE) {
+        const int cs = ((C / 128) + 3) & ~3;
+        if (tid == 0) out_s[(int64_t)cs * kb0 + (int64_t)(c0 / 128) * nkb + kbl] = sc;
+    } else {
+        if (half == 0) out_s[(int64_t)C * kb0 + (int64_t)(c0 + oc) * nkb + kbl] = sc;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_wgrad_operands(const float* dh, const float* gate, const int32_t* slot_row,
+                                 const int32_t* row_token, const float* z, const float* dh_row,
+                                 const uint16_t* u, int64_t shared_row0, int K, int d, int I,
+                                 const int32_t* go, const int32_t* kb_start, int G, int n_kb,
+                                 uint8_t* dyT_q, float* dyT_s, uint8_t* hT_q, float* hT_s, uint8_t* dzT_q,
+                                 float* dzT_s, uint8_t* xT_q, float* xT_s, hipStream_t st) {
+    WgradSrc s{dh, gate, slot_row, row_token, z, dh_row, u, shared_row0, K, d, I};
+    hipLaunchKernelGGL((wgrad_operand_kernel<SRC_DY, false>), dim3((unsigned)(d / 128), (unsigned)n_kb), dim3(256),
+                       0, st, s, go, kb_start, G, d, dyT_q, dyT_s);
+    hipLaunchKernelGGL((wgrad_operand_kernel<SRC_H, true>), dim3((unsigned)(I / 128), (unsigned)n_kb), dim3(256),
+                       0, st, s, go, kb_start, G, I, hT_q, hT_s);
+    hipLaunchKernelGGL((wgrad_operand_kernel<SRC_DZ, false>), dim3((unsigned)(2 * I / 128), (unsigned)n_kb),
+                       dim3(256), 0, st, s, go, kb_start, G, 2 * I, dzT_q, dzT_s);
+    hipLaunchKernelGGL((wgrad_operand_kernel<SRC_X, true>), dim3((unsigned)(d / 128), (unsigned)n_kb), dim3(256),
+                       0, st, s, go, kb_start, G, d, xT_q, xT_s);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -33,6 +33,25 @@ def _bf16_f64(t):
     return (u16(t).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
+def _check_codes(q, sc, s_ref, x_ref, mag):
+    """Every dequantised code within half an E4M3 step of the exact value plus
+    1e-5 of the size of the value's terms (`mag`), for an expanded (per
+    element) scale sc; the scales within tolerance of the reference ones."""
+    assert np.all(np.abs(sc.astype(np.float64) / s_ref.astype(np.float64) - 1) <= TOL)
+    table = oracle.e4m3_table()
+    vals = np.unique(table[np.isfinite(table)])
+    gaps = np.diff(vals)
+    half = np.zeros(256)
+    for c in range(256):
+        if np.isfinite(table[c]):
+            i = np.searchsorted(vals, table[c])
+            half[c] = max(gaps[i - 1] if i > 0 else gaps[0], gaps[i] if i < gaps.size else gaps[-1]) / 2
+    deq = table[q] * sc
+    bound = half[q] * sc * (1 + 1e-6) + 1e-5 * mag + 1e-7 * sc
+    bad = np.abs(deq - x_ref) > bound
+    assert not bad.any(), f"{int(bad.sum())} codes further from the exact value than allowed"
+
+
 def _check_dz_codes(q, s, x_ref, mag):
     """Codes and scales of a fused-quantised FP32 GPU value, against its exact
     FP64 value: the scale within tolerance of the oracle's quantiser applied
@@ -160,6 +179,79 @@ def test_backward_dgrad_staged(T, d, E, K, I):
     say(f"  du per-row rel err {err_u:.3e}, de {err_e:.3e}")
     assert err_u <= TOL and err_e <= TOL
 
+    # ---- weight gradients
+    say("  GPU weight gradients")
+    dw13, dw2, ops, kb_start = moe.moe_wgrad(dh, f["gate"], f["slot_row"], f["row_token"], z, dh_row, u, go,
+                                             shared_row0=T * K)
+    torch.cuda.synchronize()
+    say(f"  oracle: weight gradients on {len(groups)} groups")
+    rt = np_(f["row_token"])
+    gate_h, dh_h = np_(f["gate"]), np_(dh)
+    row_w = np.ones(R, np.float32)
+    row_w[slot_h.reshape(-1)] = gate_h.reshape(-1)
+    cs_h, cs_x = (I // 128 + 3) // 4 * 4, (d // 128 + 3) // 4 * 4
+    o = {k: np_(v) for k, v in ops.items()}
+    for g in groups:
+        r0, r1 = int(go_h[g]), int(go_h[g + 1])
+        n = int(kb_start[g + 1] - kb_start[g])
+        kb0, kp = int(kb_start[g]), 128 * n
+        if n == 0:
+            assert not np_(dw2[g]).any() and not np_(dw13[g]).any()
+            continue
+        rows = np.arange(r0, r1)
+        pad = kp - (r1 - r0)
+        # dY^T, bit-exact: fl32(w_r * dh) rows, zero padding, 1x128 along the rows
+        dyT = np.zeros((d, kp), np.float32)
+        dyT[:, :r1 - r0] = (row_w[rows, None] * dh_h[rt[rows]]).astype(np.float32).T
+        q_ref, s_ref = oracle.quant_1x128(dyT)
+        aq = o["dyT_q"][d * 128 * kb0:d * 128 * kb0 + d * kp].reshape(d, kp)
+        as_ = o["dyT_s"][d * kb0:d * kb0 + d * n].reshape(d, n)
+        np.testing.assert_array_equal(aq, q_ref)
+        np.testing.assert_array_equal(as_.view(np.uint32), s_ref.view(np.uint32))
+        # u^T, bit-exact: 128x128 blocks
+        xT = np.zeros((d, kp), np.float32)
+        xT[:, :r1 - r0] = u_h[rt[rows]].astype(np.float32).T
+        qx_ref, sx_ref = oracle.quant_128x128(xT)
+        xq = o["xT_q"][d * 128 * kb0:d * 128 * kb0 + d * kp].reshape(d, kp)
+        xs = o["xT_s"][cs_x * kb0:cs_x * kb0 + (d // 128) * n].reshape(d // 128, n)
+        np.testing.assert_array_equal(xq, qx_ref)
+        np.testing.assert_array_equal(xs.view(np.uint32), sx_ref.view(np.uint32))
+        # h^T and dz^T: within half a step plus the FP32 slack
+        zz = z_h[r0:r1].reshape(r1 - r0, I // 128, 2, 128).astype(np.float64)
+        zg_, zu_ = zz[:, :, 0].reshape(r1 - r0, I), zz[:, :, 1].reshape(r1 - r0, I)
+        sg = 1 / (1 + np.exp(-zg_))
+        hT = np.zeros((I, kp))
+        hT[:, :r1 - r0] = (zg_ * sg * zu_).T
+        mag = np.zeros((I, kp))
+        mag[:, :r1 - r0] = np.abs(zg_ * sg * zu_).T
+        hq = o["hT_q"][I * 128 * kb0:I * 128 * kb0 + I * kp].reshape(I, kp)
+        hs = o["hT_s"][cs_h * kb0:cs_h * kb0 + (I // 128) * n].reshape(I // 128, n)
+        _, hs_ref = oracle.quant_128x128(hT.astype(np.float32))
+        _check_codes(hq, np.repeat(np.repeat(hs.astype(np.float64), 128, 0), 128, 1),
+                     np.repeat(np.repeat(hs_ref.astype(np.float64), 128, 0), 128, 1), hT, mag)
+        dhr = dh_row_h[r0:r1].astype(np.float64)
+        dzg, dzu = bw.swiglu_backward(zg_, zu_, dhr)
+        mg = np.abs(dhr * zu_) * sg * (1 + np.abs(zg_) * (1 - sg))
+        mu = np.abs(dhr * zg_) * sg
+
+        def inter(a, b):
+            return np.stack([a.reshape(-1, I // 128, 128), b.reshape(-1, I // 128, 128)], axis=2).reshape(-1, 2 * I)
+        dzT = np.zeros((2 * I, kp))
+        dzT[:, :r1 - r0] = inter(dzg, dzu).T
+        magz = np.zeros((2 * I, kp))
+        magz[:, :r1 - r0] = inter(mg, mu).T
+        zq = o["dzT_q"][2 * I * 128 * kb0:2 * I * 128 * kb0 + 2 * I * kp].reshape(2 * I, kp)
+        zs = o["dzT_s"][2 * I * kb0:2 * I * kb0 + 2 * I * n].reshape(2 * I, n)
+        _, zs_ref = oracle.quant_1x128(dzT.astype(np.float32))
+        _check_codes(zq, np.repeat(zs.astype(np.float64), 128, 1), np.repeat(zs_ref.astype(np.float64), 128, 1),
+                     dzT, magz)
+        # the GEMMs on those codes
+        ref2 = oracle.gemm_blockscaled(aq, as_, hq, hs)
+        ref13 = oracle.gemm_blockscaled(zq, zs, xq, xs)
+        e2, e13 = rowinf_rel(np_(dw2[g]), ref2), rowinf_rel(np_(dw13[g]), ref13)
+        assert e2 <= TOL and e13 <= TOL, (g, e2, e13)
+    say("  weight gradients within the bound")
+
     # ---- reported: against the unquantised FP64 backward (small cases only)
     if d <= 512:
         w = [workloads.expert_weights(sh, g, device=dev()) for g in range(G)]     # as pack_all drew them
@@ -184,3 +276,15 @@ def test_backward_dgrad_staged(T, d, E, K, I):
         q_err = rowinf_rel(np_(du), du64)
         say(f"  FP8 backward vs unquantised FP64 backward: du per-row rel err {q_err:.3e}")
         assert q_err < 0.2
+        w_err = 0.0
+        for g in range(G):
+            r0, r1 = int(go_h[g]), int(go_h[g + 1])
+            if r1 == r0:
+                continue
+            dhr64 = dy64[r0:r1] @ W2[g]
+            dW2, dW1, dW3 = bw.expert_wgrad(dy64[r0:r1], zg[r0:r1], zu[r0:r1], dhr64, x[r0:r1])
+            got13 = np_(dw13[g]).reshape(I // 128, 2, 128, d)
+            w_err = max(w_err, rowinf_rel(np_(dw2[g]), dW2), rowinf_rel(got13[:, 0].reshape(I, d), dW1),
+                        rowinf_rel(got13[:, 1].reshape(I, d), dW3))
+        say(f"  FP8 weight gradients vs unquantised FP64: per-row rel err {w_err:.3e}")
+        assert w_err < 0.5
