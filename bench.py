@@ -259,9 +259,11 @@ def layer_quant_error(sh, st, n_tok=4):
 
 
 def run_layer_backward(sh, steps, warmup):
-    """The input-gradient backward of the layer after one forward step whose
-    GEMM1 kept z: gate backward (dY quantised), GEMM(dY, W2^T), SwiGLU backward
-    (dz quantised), GEMM(dz, W13^T), then du and the centroid gradient.  One step = that chain for the whole batch
+    """The backward of the layer after one forward step whose GEMM1 kept z:
+    gate backward (dY quantised), GEMM(dY, W2^T), SwiGLU backward (dz
+    quantised), GEMM(dz, W13^T), du and the centroid gradient, then the expert
+    weight gradients (transposed operands, one GEMM launch per expert and
+    weight; the expert sizes are read back to the host for those launches).  One step = that chain for the whole batch
     with dL/dh' ~ N(0,1); the transposed weights are prepared once, untimed
     (like the forward's weight quantisation)."""
     log(f"[bench] setup {sh.name} backward: T={sh.T} d={sh.d} E={sh.E} K={sh.K} I={sh.I}")
@@ -317,9 +319,11 @@ def run_layer_backward(sh, steps, warmup):
         if ev: m.append(ev.mark("gemm1_dgrad"))
         moe.moe_router_backward(dh, b["dx"], slot_row, dlogit, st["idx"], st["e"], st["u"], row_dlogit,
                                 row_token, go, shared_row0=T * K)
+        if ev: m.append(ev.mark("router_bwd"))
+        moe.moe_wgrad(dh, st["gate"], slot_row, row_token, b["z"], b["dh_row"], st["u"], go, shared_row0=T * K)
         if ev:
-            m.append(ev.mark("router_bwd"))
-            names = ["gate_bwd", "gemm2_dgrad", "swiglu_bwd", "gemm1_dgrad", "router_bwd"]
+            m.append(ev.mark("wgrad"))
+            names = ["gate_bwd", "gemm2_dgrad", "swiglu_bwd", "gemm1_dgrad", "router_bwd", "wgrad"]
             for i, n in enumerate(names):
                 ev.add(n, m[i], m[i + 1])
 
@@ -336,7 +340,8 @@ def run_layer_backward(sh, steps, warmup):
     f2 = 2.0 * R * d * I              # GEMM(dY, W2^T)
     f1 = 2.0 * R * d * 2 * I          # GEMM(dz, W13^T)
     tf = {"gemm2_dgrad": round(f2 / (ev.avg_ms("gemm2_dgrad") * 1e-3) / 1e12, 1),
-          "gemm1_dgrad": round(f1 / (ev.avg_ms("gemm1_dgrad") * 1e-3) / 1e12, 1)}
+          "gemm1_dgrad": round(f1 / (ev.avg_ms("gemm1_dgrad") * 1e-3) / 1e12, 1),
+          "wgrad_incl_operands": round((f1 + f2) / (ev.avg_ms("wgrad") * 1e-3) / 1e12, 1)}
     k_ms = ev.avg_ms("gemm1_dgrad")
     if T >= 4096:
         ach = f1 / (k_ms * 1e-3) / 1e12
@@ -352,7 +357,7 @@ def run_layer_backward(sh, steps, warmup):
                 "algorithmic_per_launch": nbytes, "avg_launch_ms": round(k_ms, 4)}
     log(f"[bench] backward {ms:.3f} ms/step; stages {stages}")
     return {
-        "metric": "MoE-layer backward (input gradient) tokens/s (d=7168, 256E top-8, FP8)",
+        "metric": "MoE-layer backward (input and weight gradients) tokens/s (d=7168, 256E top-8, FP8)",
         "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp8_e4m3 (fp32 accumulate)", "data": "synthetic (seeded; random-init expert weights)",

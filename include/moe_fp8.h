@@ -370,6 +370,22 @@ int moe_wgrad_operands(const float* dh, const float* topk_gate, const int32_t* s
                        int64_t shared_row0, uint8_t* dyT_q, float* dyT_scale, uint8_t* hT_q, float* hT_scale,
                        uint8_t* dzT_q, float* dzT_scale, uint8_t* xT_q, float* xT_scale, moe_stream_t stream);
 
+/* moe_wgrad -- the expert weight gradients from moe_wgrad_operands' buffers:
+ * for every group g with rows, dW2[g] = GEMM(dY^T_g, h^T_g) FP32 [d, I] and
+ * dW13[g] = GEMM(dz^T_g, u^T_g) FP32 [2I, d] (W13's interleaved row order),
+ * each one grouped_gemm_fp8_blockscaled launch with G = 1 and K = Kp_g;
+ * groups without rows get zero gradients.  group_rows_host int32 [G] is a
+ * HOST array (the rows of each group, as group_offset's differences): the
+ * launches need the sizes.  dw13 FP32 [G, 2I, d], dw2 FP32 [G, d, I]; ws of
+ * moe_wgrad_workspace_bytes(d, I, the largest group's rows) bytes.
+ * Limits: a group has at most 16384 rows; at most 65535 row blocks in all.
+ */
+size_t moe_wgrad_workspace_bytes(int d, int I, int max_group_rows);
+int moe_wgrad(const int32_t* group_rows_host, int G, int d, int I, const uint8_t* dyT_q, const float* dyT_scale,
+              const uint8_t* hT_q, const float* hT_scale, const uint8_t* dzT_q, const float* dzT_scale,
+              const uint8_t* xT_q, const float* xT_scale, float* dw13, float* dw2, void* ws, size_t ws_bytes,
+              moe_stream_t stream);
+
 /* moe_layer_forward -- the whole layer: router, dispatch, 1x128 quantisation
  * of u, GEMM1 with fused SwiGLU and 1x128 re-quantisation, GEMM2, combine.
  * The bias is read only (update it with moe_bias_update).  packed_weights as

@@ -34,7 +34,7 @@ EXPORTS = (
     "moe_packed_weight_bytes", "moe_prepare_expert_weights",
     "moe_layer_workspace_bytes", "moe_layer_forward",
     "moe_prepare_backward_weights", "moe_gate_backward", "moe_swiglu_backward", "moe_router_backward",
-    "moe_wgrad_operands",
+    "moe_wgrad_operands", "moe_wgrad_workspace_bytes", "moe_wgrad",
 )
 
 
@@ -82,6 +82,8 @@ def load_library(path: str = LIB_PATH):
         "moe_router_backward": ([P, P, I64, P, P, P, P, P, P, P, P, I64, I32, I32, I32, P, P, P], I32),
         "moe_wgrad_operands": ([P, P, P, P, P, P, P, P, P, I32, I32, I64, I32, I32, I32, I64,
                                 P, P, P, P, P, P, P, P, P], I32),
+        "moe_wgrad_workspace_bytes": ([I32, I32, I32], SZ),
+        "moe_wgrad": ([P, I32, I32, I32, P, P, P, P, P, P, P, P, P, P, P, SZ, P], I32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -434,10 +436,10 @@ def moe_router_backward(dh, dx, slot_row, dlogit, topk_idx, centroids, u, row_dl
 
 def moe_wgrad(dh, topk_gate, slot_row, row_token, z, dh_row, u, group_offset, shared_row0=-1):
     """Expert weight gradients -> (dW13 f32 [G, 2I, d] in W13's interleaved row
-    order, dW2 f32 [G, d, I]).  Builds the transposed operands
-    (moe_wgrad_operands), then runs one grouped_gemm_fp8_blockscaled per
-    expert (G = 1, K = its rows padded to 128) on views of them; the expert
-    sizes are read back to the host for those launches."""
+    order, dW2 f32 [G, d, I], the operand buffers, kb_start).  Builds the
+    transposed operands (moe_wgrad_operands), then moe_wgrad runs one GEMM per
+    expert and weight; the expert sizes are read back to the host for those
+    launches."""
     T, d = dh.shape
     K = topk_gate.shape[1]
     R, I2 = z.shape
@@ -466,25 +468,9 @@ def moe_wgrad(dh, topk_gate, slot_row, row_token, z, dh_row, u, group_offset, sh
                                                            "xT_q", "xT_s")), _stream()), "moe_wgrad_operands")
     dw13 = _new((G, 2 * I, d), torch.float32, dh)
     dw2 = _new((G, d, I), torch.float32, dh)
-    go_d = torch.tensor([0, d], dtype=torch.int32, device=dev)
-    go_2i = torch.tensor([0, 2 * I], dtype=torch.int32, device=dev)
-    kmax = int(nkb.max()) * 128 if n_kb else 128
-    ws = _new((max(L.moe_gemm_workspace_bytes(1, max(d, 2 * I), max(d, I), kmax), 256),), torch.uint8, dh)
-    for g in range(G):
-        n = int(nkb[g])
-        if n == 0:
-            dw2[g].zero_()
-            dw13[g].zero_()
-            continue
-        kb0, kp = int(kb_start[g]), 128 * n
-        a = bufs["dyT_q"][d * 128 * kb0:d * 128 * kb0 + d * kp].view(d, kp)
-        a_s = bufs["dyT_s"][d * kb0:d * kb0 + d * n].view(d, n)
-        b = bufs["hT_q"][I * 128 * kb0:I * 128 * kb0 + I * kp].view(1, I, kp)
-        b_s = bufs["hT_s"][cs_h * kb0:cs_h * kb0 + (I // 128) * n].view(1, I // 128, n)
-        grouped_gemm_fp8_blockscaled(a, a_s, go_d, d, b, b_s, epi=MOE_EPI_STORE_F32, out=dw2[g], ws=ws)
-        a = bufs["dzT_q"][2 * I * 128 * kb0:2 * I * 128 * kb0 + 2 * I * kp].view(2 * I, kp)
-        a_s = bufs["dzT_s"][2 * I * kb0:2 * I * kb0 + 2 * I * n].view(2 * I, n)
-        b = bufs["xT_q"][d * 128 * kb0:d * 128 * kb0 + d * kp].view(1, d, kp)
-        b_s = bufs["xT_s"][cs_x * kb0:cs_x * kb0 + (d // 128) * n].view(1, d // 128, n)
-        grouped_gemm_fp8_blockscaled(a, a_s, go_2i, 2 * I, b, b_s, epi=MOE_EPI_STORE_F32, out=dw13[g], ws=ws)
+    rows = np.ascontiguousarray(np.diff(go_h).astype(np.int32))
+    ws = _new((max(L.moe_wgrad_workspace_bytes(d, I, int(rows.max()) if G else 0), 256),), torch.uint8, dh)
+    _check(L.moe_wgrad(rows.ctypes.data_as(ctypes.c_void_p), G, d, I,
+                       *(_ptr(bufs[k]) for k in ("dyT_q", "dyT_s", "hT_q", "hT_s", "dzT_q", "dzT_s", "xT_q", "xT_s")),
+                       _ptr(dw13), _ptr(dw2), _ptr(ws), ws.numel(), _stream()), "moe_wgrad")
     return dw13, dw2, bufs, kb_start

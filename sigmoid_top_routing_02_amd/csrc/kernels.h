@@ -64,6 +64,12 @@ hipError_t launch_wgrad_operands(const float* dh, const float* gate, const int32
                                  uint8_t* dyT_q, float* dyT_s, uint8_t* hT_q, float* hT_s, uint8_t* dzT_q,
                                  float* dzT_s, uint8_t* xT_q, float* xT_s, hipStream_t st);
 
+size_t wgrad_ws_bytes(int d, int I, int max_kp);
+hipError_t launch_wgrad_gemms(const int32_t* group_rows, int G, int d, int I, const uint8_t* dyT_q,
+                              const float* dyT_s, const uint8_t* hT_q, const float* hT_s, const uint8_t* dzT_q,
+                              const float* dzT_s, const uint8_t* xT_q, const float* xT_s, float* dw13, float* dw2,
+                              void* ws, hipStream_t st);
+
 // balance.hip
 size_t seq_balance_ws_bytes(int64_t n_seq, int L);
 hipError_t launch_seq_balance_loss(const float* s, const int32_t* idx, int64_t n_seq, int E, int K,

@@ -18,8 +18,10 @@
 //     1x128 scales  [C, nkb_g] at C * kb_start[g];  128x128 scales
 //     [C/128, nkb_g] at CS * kb_start[g], CS = C/128 rounded up to a multiple
 //     of 4 (every group's scales start 16-byte aligned).
-// One workgroup per (128 columns, 128-row block): the block's values are
-// computed into LDS transposed, then quantised and written 64 bytes per lane.
+// One workgroup per (128 columns, 128-row block): each row's token and dY
+// weight are found once, the block's values are computed four columns per
+// lane into LDS, then quantised along the other axis and written 64 bytes
+// per lane.
 #include "device_math.h"
 #include "kernels.h"
 
@@ -67,32 +69,58 @@ __global__ __launch_bounds__(256) void wgrad_operand_kernel(WgradSrc s, const in
     const int g = lo;
     const int kb0 = kb_start[g], nkb = kb_start[g + 1] - kb0, kbl = kbi - kb0;
     const int64_t rb = (int64_t)go[g] + (int64_t)kbl * 128, rend = go[g + 1];
-    {   // values: thread = column c0 + (tid & 127), rows (tid >> 7), +2, ...
-        const int c = c0 + (tid & 127);
-        for (int i = tid >> 7; i < 128; i += 2) {
+    // per row of the block: its token and (for dY) its weight, once
+    __shared__ int64_t s_tok[128];
+    __shared__ float s_w[128];
+    if (tid < 128) {
+        const int64_t r = rb + tid;
+        int64_t t = 0;
+        float w = 0.0f;
+        if (r < rend) {
+            if constexpr (SRC == SRC_DY || SRC == SRC_X) t = s.row_token[r];
+            if constexpr (SRC == SRC_DY) w = row_weight(s, r, t);
+        }
+        s_tok[tid] = t;
+        s_w[tid] = w;
+    }
+    __syncthreads();
+    {   // values: thread = 4 columns c0 + 4 (tid & 31), rows (tid >> 5), +8, ...
+        const int cq = (tid & 31) * 4, c = c0 + cq;
+        for (int i = tid >> 5; i < 128; i += 8) {
             const int64_t r = rb + i;
-            float v = 0.0f;
+            float v[4] = {0.f, 0.f, 0.f, 0.f};
             if (r < rend) {
                 if constexpr (SRC == SRC_DY) {
-                    const int64_t t = s.row_token[r];
-                    v = row_weight(s, r, t) * s.dh[t * s.d + c];
+                    const float4 x = *reinterpret_cast<const float4*>(s.dh + s_tok[i] * s.d + c);
+                    const float w = s_w[i];
+                    v[0] = w * x.x; v[1] = w * x.y; v[2] = w * x.z; v[3] = w * x.w;
                 } else if constexpr (SRC == SRC_X) {
-                    const int64_t t = s.row_token[r];
-                    v = bf16_lo((uint32_t)s.u[t * s.d + c]);
+                    const uint2 x = *reinterpret_cast<const uint2*>(s.u + s_tok[i] * s.d + c);
+                    v[0] = bf16_lo(x.x); v[1] = bf16_hi(x.x); v[2] = bf16_lo(x.y); v[3] = bf16_hi(x.y);
                 } else if constexpr (SRC == SRC_H) {
                     const float* zr = s.z + r * 2 * s.I + (c >> 7) * 256 + (c & 127);
-                    const float zg = zr[0], zu = zr[128];
-                    v = zg * sigm(zg) * zu;
+                    const float4 zg = *reinterpret_cast<const float4*>(zr);
+                    const float4 zu = *reinterpret_cast<const float4*>(zr + 128);
+                    const float g4[4] = {zg.x, zg.y, zg.z, zg.w}, u4[4] = {zu.x, zu.y, zu.z, zu.w};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) v[q] = g4[q] * sigm(g4[q]) * u4[q];
                 } else {
                     const int j = c >> 8, w = c & 255, ic = j * 128 + (w & 127);
                     const float* zr = s.z + r * 2 * s.I + j * 256 + (w & 127);
-                    const float zg = zr[0], zu = zr[128];
-                    const float dh = s.dh_row[r * s.I + ic];
-                    const float sg = sigm(zg);
-                    v = (w < 128) ? dh * zu * sg * (1.0f + zg * (1.0f - sg)) : dh * (zg * sg);
+                    const float4 zg = *reinterpret_cast<const float4*>(zr);
+                    const float4 zu = *reinterpret_cast<const float4*>(zr + 128);
+                    const float4 dh = *reinterpret_cast<const float4*>(s.dh_row + r * s.I + ic);
+                    const float g4[4] = {zg.x, zg.y, zg.z, zg.w}, u4[4] = {zu.x, zu.y, zu.z, zu.w};
+                    const float d4[4] = {dh.x, dh.y, dh.z, dh.w};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float sg = sigm(g4[q]);
+                        v[q] = (w < 128) ? d4[q] * u4[q] * sg * (1.0f + g4[q] * (1.0f - sg)) : d4[q] * (g4[q] * sg);
+                    }
                 }
             }
-            tile[i][tid & 127] = v;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) tile[i][cq + q] = v[q];
         }
     }
     __syncthreads();
@@ -141,7 +169,62 @@ __global__ __launch_bounds__(256) void wgrad_operand_kernel(WgradSrc s, const in
     }
 }
 
+// {0, d, 0, 2I}: the one-group row offsets of the two weight-gradient GEMMs
+__global__ void wgrad_offsets_kernel(int32_t* o, int d, int I) {
+    if (threadIdx.x == 0) {
+        o[0] = 0;
+        o[1] = d;
+        o[2] = 0;
+        o[3] = 2 * I;
+    }
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(float4* __restrict__ p, int64_t n4) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256)
+        p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
 }  // namespace
+
+size_t wgrad_ws_bytes(int d, int I, int max_kp) {
+    return 256 + gemm_ws_bytes(1, (d > 2 * I ? d : 2 * I), (d > I ? d : I), max_kp);
+}
+
+hipError_t launch_wgrad_gemms(const int32_t* group_rows, int G, int d, int I, const uint8_t* dyT_q,
+                              const float* dyT_s, const uint8_t* hT_q, const float* hT_s, const uint8_t* dzT_q,
+                              const float* dzT_s, const uint8_t* xT_q, const float* xT_s, float* dw13, float* dw2,
+                              void* ws, hipStream_t st) {
+    int32_t* offs = static_cast<int32_t*>(ws);
+    void* gws = static_cast<char*>(ws) + 256;
+    hipLaunchKernelGGL(wgrad_offsets_kernel, dim3(1), dim3(64), 0, st, offs, d, I);
+    const int64_t cs_h = ((I / 128) + 3) & ~3, cs_x = ((d / 128) + 3) & ~3;
+    int64_t kb0 = 0;
+    for (int g = 0; g < G; ++g) {
+        const int64_t nkb = (group_rows[g] + 127) / 128;
+        float* o2 = dw2 + (int64_t)g * d * I;
+        float* o13 = dw13 + (int64_t)g * 2 * I * d;
+        hipError_t e;
+        if (nkb == 0) {        // an expert with no rows: zero gradients
+            hipLaunchKernelGGL(fill_zero_kernel, dim3(1024), dim3(256), 0, st, reinterpret_cast<float4*>(o2),
+                               (int64_t)d * I / 4);
+            hipLaunchKernelGGL(fill_zero_kernel, dim3(1024), dim3(256), 0, st, reinterpret_cast<float4*>(o13),
+                               (int64_t)2 * I * d / 4);
+            e = hipGetLastError();
+        } else {
+            const int kp = (int)(nkb * 128);
+            e = launch_grouped_gemm(dyT_q + (int64_t)d * 128 * kb0, dyT_s + (int64_t)d * kb0, nullptr, offs, 1, d,
+                                    hT_q + (int64_t)I * 128 * kb0, hT_s + cs_h * kb0, I, kp, EPI_STORE_F32, o2,
+                                    nullptr, nullptr, gws, st);
+            if (e == hipSuccess)
+                e = launch_grouped_gemm(dzT_q + (int64_t)2 * I * 128 * kb0, dzT_s + (int64_t)2 * I * kb0, nullptr,
+                                        offs + 2, 1, 2 * I, xT_q + (int64_t)d * 128 * kb0, xT_s + cs_x * kb0, d, kp,
+                                        EPI_STORE_F32, o13, nullptr, nullptr, gws, st);
+        }
+        if (e != hipSuccess) return e;
+        kb0 += nkb;
+    }
+    return hipSuccess;
+}
 
 hipError_t launch_wgrad_operands(const float* dh, const float* gate, const int32_t* slot_row,
                                  const int32_t* row_token, const float* z, const float* dh_row,

@@ -115,6 +115,28 @@ def test_balance_loss_argument_errors(L):
     assert f(None, None, 0, 16, 4, 10, 1e-3, None, None, 0, None) == 0            # T = 0
 
 
+def test_backward_argument_errors(L):
+    import numpy as np
+    assert L.moe_gate_backward(FAKE, FAKE, -1, FAKE, FAKE, FAKE, FAKE, 8, 4, 100, 16, FAKE, FAKE, FAKE, FAKE,
+                               None) == -2                                                    # d % 128
+    assert L.moe_gate_backward(FAKE, FAKE, -1, FAKE, FAKE, FAKE, FAKE, 8, 17, 128, 16, FAKE, FAKE, FAKE, FAKE,
+                               None) == -3                                                    # K > 16
+    assert L.moe_swiglu_backward(FAKE, FAKE, 8, 100, FAKE, FAKE, None) == -2                  # I % 128
+    assert L.moe_prepare_backward_weights(FAKE, 3, 128, 128, FAKE, None) == -2                # packed_t == packed
+    rows = np.array([5, 0, 300], np.int32)
+    need = L.moe_wgrad_workspace_bytes(256, 128, 300)
+    assert need > 256
+    p = ctypes.c_void_p(rows.ctypes.data)
+    assert L.moe_wgrad(p, 3, 256, 128, *([FAKE] * 8), FAKE, FAKE, FAKE, need - 1, None) == -4   # workspace
+    bad = np.array([5, -1, 3], np.int32)
+    assert L.moe_wgrad(ctypes.c_void_p(bad.ctypes.data), 3, 256, 128, *([FAKE] * 8), FAKE, FAKE, FAKE, need,
+                       None) == -2                                                            # negative rows
+    big = np.array([20000], np.int32)
+    assert L.moe_wgrad(ctypes.c_void_p(big.ctypes.data), 1, 256, 128, *([FAKE] * 8), FAKE, FAKE, FAKE, need,
+                       None) == -3                                                            # > 16384 rows
+    assert L.moe_wgrad_operands(*([FAKE] * 9), 3, 4, 100, 4, 100, 128, -1, *([FAKE] * 8), None) == -2
+
+
 def test_accumulation_probe_argument_errors(L):
     f = L.moe_fp8_mfma_accumulation_probe
     assert f(FAKE, FAKE, 20, 16, 128, 0, FAKE, None) == -2          # M % 16
