@@ -208,8 +208,12 @@ int fp8_quant_128x128(const float* w, int64_t rows, int cols, uint8_t* q, float*
  *   ws   scratch of moe_gemm_workspace_bytes(G, M_total, N, K) bytes (the
  *        device-built tile map and tile list, and the A scales gathered into
  *        GEMM row order, slice-major; its contents need no setup).
- * Limits: K % 128 == 0, N % 256 == 0 for the SwiGLU epilogues, N % 128 == 0
- * otherwise, G >= 1, (M_total + 128) * K / 32 < 2^32 (the gathered A scales).
+ * Limits: K % 128 == 0 and K <= 16384, N % 256 == 0 for the SwiGLU epilogues,
+ * N % 128 == 0 otherwise, G >= 1, (M_total + 128) * K / 32 < 2^32 (the
+ * gathered A scales); A is addressed with 32-bit byte offsets, so a_q must
+ * hold fewer than 2^32 / K rows (checked as M_total * K < 2^32 when
+ * a_row_index is NULL; with a gather every index must satisfy it, which the
+ * call cannot check).  Limits outside these return MOE_ERR_UNSUPPORTED.
  */
 /* Scratch bytes for a grouped GEMM with G groups, M_total rows, N columns and
  * inner dimension K (0 for G < 1, M_total < 0, N < 1 or K < 1). */
@@ -391,6 +395,9 @@ int moe_wgrad(const int32_t* group_rows_host, int G, int d, int I, const uint8_t
  * The bias is read only (update it with moe_bias_update).  packed_weights as
  * above with G = E + 1; out FP32 [T,d]; expert_count_out int32 [E] (may be
  * NULL); ws of moe_layer_workspace_bytes(T, d, E, K, I).
+ * Limits: d and I multiples of 128 and at most 16384, 1 <= E <= 256,
+ * 1 <= K <= min(E, 16), T*(K+1) < 2^31, T*d < 2^32 and T*(K+1)*I < 2^32
+ * (32-bit byte offsets of the GEMM inputs); MOE_ERR_UNSUPPORTED otherwise.
  */
 size_t moe_layer_workspace_bytes(int64_t T, int d, int E, int K, int I);
 int moe_layer_forward(const void* u_bf16, const void* centroids_bf16, const float* bias,

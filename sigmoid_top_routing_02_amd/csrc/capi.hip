@@ -211,6 +211,9 @@ int grouped_gemm_fp8_blockscaled(const uint8_t* a_q, const float* a_scale,
     REQUIRE(G >= 1 && G <= 65535, MOE_ERR_UNSUPPORTED, "grouped_gemm: G=%d outside [1, 65535]", G);
     REQUIRE(M_total >= 0 && M_total < ((int64_t)1 << 31), MOE_ERR_UNSUPPORTED, "grouped_gemm: M_total out of range");
     REQUIRE(K > 0 && K % 128 == 0, MOE_ERR_SHAPE, "grouped_gemm: K=%d not a positive multiple of 128", K);
+    REQUIRE(K <= 16384, MOE_ERR_UNSUPPORTED, "grouped_gemm: K=%d above 16384 (128 slices)", K);
+    REQUIRE(a_row_index || M_total * K < ((int64_t)1 << 32), MOE_ERR_UNSUPPORTED,
+            "grouped_gemm: A of M_total=%lld rows exceeds 4 GiB (32-bit byte offsets)", (long long)M_total);
     REQUIRE(epi >= MOE_EPI_STORE_F32 && epi <= MOE_EPI_SWIGLU_QUANT_Z, MOE_ERR_UNSUPPORTED, "grouped_gemm: epilogue %d", epi);
     if (epi == MOE_EPI_STORE_F32)
         REQUIRE(N > 0 && N % 128 == 0, MOE_ERR_SHAPE, "grouped_gemm: N=%d not a positive multiple of 128", N);
@@ -573,8 +576,10 @@ int moe_layer_forward(const void* u_bf16, const void* centroids_bf16, const floa
     REQUIRE(I > 0 && I % 128 == 0, MOE_ERR_SHAPE, "moe_layer_forward: I=%d must be a multiple of 128", I);
     REQUIRE(E >= 1 && E <= 256, MOE_ERR_UNSUPPORTED, "moe_layer_forward: E=%d outside [1, 256]", E);
     REQUIRE(K >= 1 && K <= E && K <= 16, MOE_ERR_UNSUPPORTED, "moe_layer_forward: K=%d", K);
-    REQUIRE(T * (K + 1) < ((int64_t)1 << 31) && T * (int64_t)d < ((int64_t)1 << 32), MOE_ERR_UNSUPPORTED,
-            "moe_layer_forward: T=%lld too large", (long long)T);
+    REQUIRE(d <= 16384 && I <= 16384, MOE_ERR_UNSUPPORTED, "moe_layer_forward: d=%d or I=%d above 16384", d, I);
+    REQUIRE(T * (K + 1) < ((int64_t)1 << 31) && T * (int64_t)d < ((int64_t)1 << 32) &&
+                T * (K + 1) * (int64_t)I < ((int64_t)1 << 32),
+            MOE_ERR_UNSUPPORTED, "moe_layer_forward: T=%lld too large", (long long)T);
     if (T == 0) return MOE_OK;
     REQUIRE_PTR(u_bf16);
     REQUIRE_PTR(centroids_bf16);

@@ -99,6 +99,13 @@ def test_quant_and_gemm_argument_errors(L):
                                           FAKE, None, None, FAKE, gw - 1, None) == -4
     assert L.grouped_gemm_fp8_blockscaled(FAKE, FAKE, None, FAKE, 3, 10, FAKE, FAKE, 256, 128, 9,
                                           FAKE, None, None, FAKE, gw, None) == -3
+    # K above the 128 slices the kernel's scale table holds
+    assert L.grouped_gemm_fp8_blockscaled(FAKE, FAKE, None, FAKE, 3, 10, FAKE, FAKE, 256, 16512, 0,
+                                          FAKE, None, None, FAKE, gw, None) == -3
+    # an ungathered A past 4 GiB (32-bit byte offsets); with a gather the rows are not known
+    big = L.moe_gemm_workspace_bytes(3, 300_000, 256, 16384)
+    assert L.grouped_gemm_fp8_blockscaled(FAKE, FAKE, None, FAKE, 3, 300_000, FAKE, FAKE, 256, 16384, 0,
+                                          FAKE, None, None, FAKE, big, None) == -3
 
 
 def test_balance_loss_argument_errors(L):
@@ -158,6 +165,11 @@ def test_combine_bias_layer_argument_errors(L):
                                need - 1, None) == -4
     assert L.moe_layer_forward(FAKE, FAKE, FAKE, FAKE, 128, 500, 16, 4, 256, FAKE, None, FAKE,
                                need, None) == -2
+    # d above 16384, and a GEMM2 input (T*(K+1) rows x I) past 4 GiB
+    assert L.moe_layer_forward(FAKE, FAKE, FAKE, FAKE, 128, 16512, 16, 4, 256, FAKE, None, FAKE,
+                               1 << 40, None) == -3
+    assert L.moe_layer_forward(FAKE, FAKE, FAKE, FAKE, 400_000, 1024, 16, 8, 2048, FAKE, None, FAKE,
+                               1 << 40, None) == -3
 
 
 def test_packed_weight_size(L):
