@@ -375,17 +375,20 @@ int moe_wgrad_operands(const float* dh, const float* topk_gate, const int32_t* s
                        uint8_t* dzT_q, float* dzT_scale, uint8_t* xT_q, float* xT_scale, moe_stream_t stream);
 
 /* moe_wgrad -- the expert weight gradients from moe_wgrad_operands' buffers:
- * for every group g with rows, dW2[g] = GEMM(dY^T_g, h^T_g) FP32 [d, I] and
+ * for every group g, dW2[g] = GEMM(dY^T_g, h^T_g) FP32 [d, I] and
  * dW13[g] = GEMM(dz^T_g, u^T_g) FP32 [2I, d] (W13's interleaved row order),
- * each one grouped_gemm_fp8_blockscaled launch with G = 1 and K = Kp_g;
- * groups without rows get zero gradients.  group_rows_host int32 [G] is a
- * HOST array (the rows of each group, as group_offset's differences): the
- * launches need the sizes.  dw13 FP32 [G, 2I, d], dw2 FP32 [G, d, I]; ws of
- * moe_wgrad_workspace_bytes(d, I, the largest group's rows) bytes.
- * Limits: a group has at most 16384 rows; at most 65535 row blocks in all.
+ * with group g's inner dimension its K-blocks [kb_start[g], kb_start[g+1])
+ * (the rows of the group padded to 128); groups without rows get zero
+ * gradients.  Two launches in all (one per weight), each K-grouped: every
+ * group's inner dimension is its own, and nothing is read back to the host.
+ * kb_start int32 [G+1] (device), the array moe_wgrad_operands took; n_kb =
+ * kb_start[G] (host-known); dw13 FP32 [G, 2I, d], dw2 FP32 [G, d, I]; ws of
+ * moe_wgrad_workspace_bytes(G, d, I) bytes.
+ * Limits: n_kb * 128 * max(d, 2I) < 2^32 (32-bit byte offsets into one
+ * group's operands), G * max(d, 2I) < 2^31; MOE_ERR_UNSUPPORTED otherwise.
  */
-size_t moe_wgrad_workspace_bytes(int d, int I, int max_group_rows);
-int moe_wgrad(const int32_t* group_rows_host, int G, int d, int I, const uint8_t* dyT_q, const float* dyT_scale,
+size_t moe_wgrad_workspace_bytes(int G, int d, int I);
+int moe_wgrad(const int32_t* kb_start, int G, int n_kb, int d, int I, const uint8_t* dyT_q, const float* dyT_scale,
               const uint8_t* hT_q, const float* hT_scale, const uint8_t* dzT_q, const float* dzT_scale,
               const uint8_t* xT_q, const float* xT_scale, float* dw13, float* dw2, void* ws, size_t ws_bytes,
               moe_stream_t stream);

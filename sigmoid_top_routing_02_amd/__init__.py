@@ -83,7 +83,7 @@ def load_library(path: str = LIB_PATH):
         "moe_wgrad_operands": ([P, P, P, P, P, P, P, P, P, I32, I32, I64, I32, I32, I32, I64,
                                 P, P, P, P, P, P, P, P, P], I32),
         "moe_wgrad_workspace_bytes": ([I32, I32, I32], SZ),
-        "moe_wgrad": ([P, I32, I32, I32, P, P, P, P, P, P, P, P, P, P, P, SZ, P], I32),
+        "moe_wgrad": ([P, I32, I32, I32, I32, P, P, P, P, P, P, P, P, P, P, P, SZ, P], I32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -437,9 +437,9 @@ def moe_router_backward(dh, dx, slot_row, dlogit, topk_idx, centroids, u, row_dl
 def moe_wgrad(dh, topk_gate, slot_row, row_token, z, dh_row, u, group_offset, shared_row0=-1):
     """Expert weight gradients -> (dW13 f32 [G, 2I, d] in W13's interleaved row
     order, dW2 f32 [G, d, I], the operand buffers, kb_start).  Builds the
-    transposed operands (moe_wgrad_operands), then moe_wgrad runs one GEMM per
-    expert and weight; the expert sizes are read back to the host for those
-    launches."""
+    transposed operands (moe_wgrad_operands), then moe_wgrad runs one K-grouped
+    GEMM per weight over all experts.  The expert sizes are read back to the
+    host once, to size the operand buffers."""
     T, d = dh.shape
     K = topk_gate.shape[1]
     R, I2 = z.shape
@@ -468,9 +468,8 @@ def moe_wgrad(dh, topk_gate, slot_row, row_token, z, dh_row, u, group_offset, sh
                                                            "xT_q", "xT_s")), _stream()), "moe_wgrad_operands")
     dw13 = _new((G, 2 * I, d), torch.float32, dh)
     dw2 = _new((G, d, I), torch.float32, dh)
-    rows = np.ascontiguousarray(np.diff(go_h).astype(np.int32))
-    ws = _new((max(L.moe_wgrad_workspace_bytes(d, I, int(rows.max()) if G else 0), 256),), torch.uint8, dh)
-    _check(L.moe_wgrad(rows.ctypes.data_as(ctypes.c_void_p), G, d, I,
+    ws = _new((max(L.moe_wgrad_workspace_bytes(G, d, I), 256),), torch.uint8, dh)
+    _check(L.moe_wgrad(_ptr(kbs), G, n_kb, d, I,
                        *(_ptr(bufs[k]) for k in ("dyT_q", "dyT_s", "hT_q", "hT_s", "dzT_q", "dzT_s", "xT_q", "xT_s")),
                        _ptr(dw13), _ptr(dw2), _ptr(ws), ws.numel(), _stream()), "moe_wgrad")
     return dw13, dw2, bufs, kb_start

@@ -470,36 +470,31 @@ int moe_wgrad_operands(const float* dh, const float* topk_gate, const int32_t* s
                       "wgrad operand launch");
 }
 
-size_t moe_wgrad_workspace_bytes(int d, int I, int max_group_rows) {
-    if (d <= 0 || I <= 0 || max_group_rows < 0) return 0;
-    const int max_kp = ((max_group_rows + 127) / 128) * 128;
-    return moe::wgrad_ws_bytes(d, I, max_kp > 0 ? max_kp : 128);
+size_t moe_wgrad_workspace_bytes(int G, int d, int I) {
+    if (G < 1 || G > 65535 || d <= 0 || I <= 0) return 0;
+    return moe::wgrad_ws_bytes(G, d, I);
 }
 
-int moe_wgrad(const int32_t* group_rows_host, int G, int d, int I, const uint8_t* dyT_q, const float* dyT_scale,
+int moe_wgrad(const int32_t* kb_start, int G, int n_kb, int d, int I, const uint8_t* dyT_q, const float* dyT_scale,
               const uint8_t* hT_q, const float* hT_scale, const uint8_t* dzT_q, const float* dzT_scale,
               const uint8_t* xT_q, const float* xT_scale, float* dw13, float* dw2, void* ws, size_t ws_bytes,
               moe_stream_t stream) {
     REQUIRE(G >= 1 && G <= 65535, MOE_ERR_UNSUPPORTED, "moe_wgrad: G=%d outside [1, 65535]", G);
     REQUIRE(d > 0 && d % 128 == 0 && I > 0 && I % 128 == 0, MOE_ERR_SHAPE,
             "moe_wgrad: d=%d, I=%d must be positive multiples of 128", d, I);
-    REQUIRE(group_rows_host, MOE_ERR_NULLPTR, "moe_wgrad: group_rows_host is NULL");
-    int max_rows = 0;
-    int64_t total_kb = 0;
-    for (int g = 0; g < G; ++g) {
-        REQUIRE(group_rows_host[g] >= 0, MOE_ERR_SHAPE, "moe_wgrad: group %d has %d rows", g, group_rows_host[g]);
-        REQUIRE(group_rows_host[g] <= 16384, MOE_ERR_UNSUPPORTED,
-                "moe_wgrad: group %d has %d rows (at most 16384: K of one GEMM)", g, group_rows_host[g]);
-        max_rows = group_rows_host[g] > max_rows ? group_rows_host[g] : max_rows;
-        total_kb += (group_rows_host[g] + 127) / 128;
-    }
-    REQUIRE(total_kb <= 65535, MOE_ERR_UNSUPPORTED, "moe_wgrad: %lld row blocks", (long long)total_kb);
+    REQUIRE(n_kb >= 0, MOE_ERR_SHAPE, "moe_wgrad: n_kb=%d < 0", n_kb);
+    // one group's operands are addressed with 32-bit byte offsets
+    REQUIRE((int64_t)n_kb * 128 * (d > 2 * I ? d : 2 * I) < ((int64_t)1 << 32), MOE_ERR_UNSUPPORTED,
+            "moe_wgrad: %d row blocks of up to %d columns exceed 4 GiB", n_kb, d > 2 * I ? d : 2 * I);
+    REQUIRE((int64_t)G * (d > 2 * I ? d : 2 * I) < ((int64_t)1 << 31), MOE_ERR_UNSUPPORTED,
+            "moe_wgrad: G=%d groups of gradient rows exceed int32", G);
+    REQUIRE_PTR(kb_start);
     REQUIRE_PTR(dw13);
     REQUIRE_PTR(dw2);
     REQUIRE_PTR(ws);
-    REQUIRE(ws_bytes >= moe_wgrad_workspace_bytes(d, I, max_rows), MOE_ERR_WORKSPACE,
-            "moe_wgrad: workspace %zu < %zu bytes", ws_bytes, moe_wgrad_workspace_bytes(d, I, max_rows));
-    if (total_kb > 0) {
+    REQUIRE(ws_bytes >= moe_wgrad_workspace_bytes(G, d, I), MOE_ERR_WORKSPACE, "moe_wgrad: workspace %zu < %zu bytes",
+            ws_bytes, moe_wgrad_workspace_bytes(G, d, I));
+    if (n_kb > 0) {
         REQUIRE_PTR(dyT_q);
         REQUIRE_PTR(dyT_scale);
         REQUIRE_PTR(hT_q);
@@ -509,7 +504,7 @@ int moe_wgrad(const int32_t* group_rows_host, int G, int d, int I, const uint8_t
         REQUIRE_PTR(xT_q);
         REQUIRE_PTR(xT_scale);
     }
-    return hip_status(moe::launch_wgrad_gemms(group_rows_host, G, d, I, dyT_q, dyT_scale, hT_q, hT_scale, dzT_q,
+    return hip_status(moe::launch_wgrad_gemms(kb_start, G, d, I, dyT_q, dyT_scale, hT_q, hT_scale, dzT_q,
                                               dzT_scale, xT_q, xT_scale, dw13, dw2, ws, S(stream)),
                       "wgrad GEMM launch");
 }

@@ -105,6 +105,14 @@ struct GemmArgs {
     float* out;
     uint8_t* out_q;
     float* out_s;
+    // K-grouped launches only (the weight gradients): group g's inner dimension
+    // is its own [kb_start[g], kb_start[g+1]) 128-blocks; its A ([group_rows, Kg]
+    // row-major, 1x128 scales [group_rows, Kg/128]) starts at block kb_start[g]
+    // of a_q / a_sT, its B ([N, Kg], 128x128 scales [N/128, Kg/128] in rows of
+    // b_cs blocks) at that block of b_q / b_s.
+    const int32_t* kb_start;
+    int group_rows;
+    int b_cs;
 };
 
 // The three pipeline stages are separate LDS objects and every access names
@@ -202,9 +210,15 @@ __device__ __forceinline__ int ncol(int wn, int ni) {
     }
 }
 
-template <int EPI, int BM_>
+// KG: K-grouped (see GemmArgs).  Every tile then takes its slice count and its
+// A, B and scale bases from its group, the A scales are read row-major, and the
+// B scales of each slice travel in the scale DMA of wave BM/64 (floats BM and
+// BM+1 of the stage's scale buffer) instead of one LDS table per tile, so a
+// group's K has no upper bound.
+template <int EPI, int BM_, bool KG = false>
 __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
     using C = Cfg<BM_>;
+    static_assert(!KG || (EPI == EPI_STORE_F32 && BM_ == 128), "K-grouped tiles store FP32 from 128-row tiles");
     constexpr int BM = C::BM, MI = C::MI, NI = C::NI, WAVES_N = C::WAVES_N;
     constexpr int WN_COLS = C::WN_COLS, WROWS = C::WROWS, A_DMA = C::A_DMA, B_DMA = C::B_DMA;
     constexpr int NS = C::NSTAGES;
@@ -215,8 +229,8 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
     // rows of one column, and its stores cover 16 consecutive columns per row,
     // which measured faster for the large FP32 output than 4-column pieces.
     constexpr bool TR = (EPI != EPI_STORE_F32);
-    const int K = p.K;
-    const int ns = K / BK;
+    int K = p.K;          // K-grouped: the current tile's group's (set by setup)
+    int ns = K / BK;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -258,9 +272,9 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
     };
 
     // ---- per-tile DMA sources (byte offsets; the slice moves soffset)
-    const auto a_rsrc = make_rsrc(p.a_q, 0xFFFFFFFFu);
+    auto a_rsrc = make_rsrc(p.a_q, 0xFFFFFFFFu);
     // every row past M_total (the padding of the last tile) reads scale 0
-    const auto sa_rsrc = make_rsrc(p.a_sT, p.sa_stride * (uint32_t)ns);
+    auto sa_rsrc = make_rsrc(p.a_sT, p.sa_stride * (uint32_t)ns);
     // A descriptor with no records: every access is out of range, so no memory
     // is touched (the target stage is a spare one).  Past the last slice the
     // pipeline still issues its DMAs through this descriptor, which keeps the
@@ -271,6 +285,8 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
     uint32_t a_off[A_DMA], b_off[2], sa_off = 0;
     uint32_t am_pre[A_DMA];                      // gathered A rows of the next tile's DMA lanes
     __amdgpu_buffer_rsrc_t b_rsrc = null_rsrc;
+    __amdgpu_buffer_rsrc_t bs_rsrc = null_rsrc;   // K-grouped: the group's B scales
+    const uint8_t* b_group = p.b_q;               // K-grouped: the group's B
     // A-row indices of this lane's A DMAs (the gather)
     auto load_rows = [&](const Tile& T) {
 #pragma unroll
@@ -278,10 +294,21 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
             // A DMA li = wave*A_DMA + i fills LDS bytes [li*1 KiB, +1 KiB): copy li / A_INSTR
             const int r = ((wave * A_DMA + i) % C::A_INSTR) * 8 + (lane >> 3);
             const int m = T.m0 + min(r, T.rows - 1);
-            am_pre[i] = p.a_rows ? (uint32_t)p.a_rows[m] : (uint32_t)m;
+            if constexpr (KG) am_pre[i] = (uint32_t)(m - T.g * p.group_rows);   // row inside the group's A
+            else am_pre[i] = p.a_rows ? (uint32_t)p.a_rows[m] : (uint32_t)m;
         }
     };
     auto setup = [&](const Tile& T) {
+        if constexpr (KG) {
+            const int kb0 = __builtin_amdgcn_readfirstlane(p.kb_start[T.g]);
+            ns = __builtin_amdgcn_readfirstlane(p.kb_start[T.g + 1]) - kb0;
+            K = ns * BK;
+            const int64_t rows_g = p.group_rows;
+            a_rsrc = make_rsrc(p.a_q + rows_g * BK * kb0, (uint32_t)(rows_g * K));
+            sa_rsrc = make_rsrc(p.a_sT + rows_g * kb0, (uint32_t)(rows_g * ns * 4));
+            bs_rsrc = make_rsrc(p.b_s + (int64_t)p.b_cs * kb0, (uint32_t)((p.N / 128) * ns * 4));
+            b_group = p.b_q + (int64_t)p.N * BK * kb0;
+        }
 #pragma unroll
         for (int i = 0; i < A_DMA; ++i) {
             const int r = ((wave * A_DMA + i) % C::A_INSTR) * 8 + (lane >> 3);
@@ -289,8 +316,20 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
         }
         // A scales: the tile's rows are contiguous in the slice-major copy; wave w
         // moves rows 64w .. 64w+63 (waves past the tile's rows move nothing)
-        sa_off = (uint32_t)(T.m0 + wave * 64 + lane) * 4u;
-        b_rsrc = make_rsrc(p.b_q + (int64_t)T.g * p.N * K, (uint32_t)p.N * (uint32_t)K);
+        if constexpr (KG) {
+            // waves below BM/64: rows of the group's row-major A scales; wave
+            // BM/64, lanes 0 and 1: the tile's two B-scale blocks (the second
+            // clamped when N % 256 == 128); every other lane reads past the end
+            if (wave * 64 < BM)
+                sa_off = (uint32_t)((T.m0 - T.g * p.group_rows) + wave * 64 + lane) * (uint32_t)ns * 4u;
+            else
+                sa_off = lane < 2 ? (uint32_t)min(T.n0 / 128 + lane, p.N / 128 - 1) * (uint32_t)ns * 4u
+                                  : 0x80000000u;
+            b_rsrc = make_rsrc(b_group, (uint32_t)p.N * (uint32_t)K);
+        } else {
+            sa_off = (uint32_t)(T.m0 + wave * 64 + lane) * 4u;
+            b_rsrc = make_rsrc(p.b_q + (int64_t)T.g * p.N * K, (uint32_t)p.N * (uint32_t)K);
+        }
         // B rows of DMA i are r0 + 8i; the swizzle of r0 + 8i only depends on i & 1
 #pragma unroll
         for (int par = 0; par < 2; ++par) {
@@ -299,7 +338,7 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
         }
         // B scales of the tile's two 128-row blocks, all slices, into LDS
         const float* bs_g = p.b_s + (int64_t)T.g * nblk_per_g * ns;
-        for (int i = tid; i < 2 * ns; i += NT) {
+        for (int i = tid; !KG && i < 2 * ns; i += NT) {
             const int blk = min(T.n0 / 128 + i / ns, nblk_per_g - 1);
             g_bscale[(i / ns) * MAX_SLICES + (i % ns)] = bs_g[(int64_t)blk * ns + (i % ns)];
         }
@@ -315,6 +354,9 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
             const int i = k - A_DMA;
             lds_dma16<C::B_AUX>(live ? b_rsrc : null_rsrc, b_off[i & 1] + (uint32_t)((i & ~1) * 8) * (uint32_t)K, koff,
                       b_buf<ST>() + (wave * B_DMA + i) * 1024);
+        } else if constexpr (KG) {
+            lds_dma4(live ? (wave * 64 < BM ? sa_rsrc : wave * 64 == BM ? bs_rsrc : null_rsrc) : null_rsrc, sa_off,
+                     live ? (uint32_t)slice * 4u : 0u, reinterpret_cast<char*>(sa_buf<ST>()) + wave * 256);
         } else {
             lds_dma4((live && wave * 64 < BM) ? sa_rsrc : null_rsrc, sa_off,
                      live ? (uint32_t)slice * p.sa_stride : 0u,
@@ -427,8 +469,13 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
                 sav[mi][0] = t.x; sav[mi][1] = t.y; sav[mi][2] = t.z; sav[mi][3] = t.w;
             }
         }
-        sb0 = g_bscale[sbrow0 * MAX_SLICES + s];
-        sb1 = g_bscale[sbrow1 * MAX_SLICES + s];
+        if constexpr (KG) {
+            sb0 = SAt[BM + sbrow0];
+            sb1 = SAt[BM + sbrow1];
+        } else {
+            sb0 = g_bscale[sbrow0 * MAX_SLICES + s];
+            sb1 = g_bscale[sbrow1 * MAX_SLICES + s];
+        }
         if constexpr (FIRST) issue(IC<(ST + 1) % NS>{}, s + 1);
         issue(IC<(ST + 2) % NS>{}, s + 2);
     };
@@ -499,7 +546,12 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
 #pragma unroll
                     for (int ni = 0; ni < NI; ++ni) {
                         const int n = T.n0 + ncol<EPI, C>(wn, ni) + lr;
-                        if (n < p.N) orow[n] = acc[mi][ni][j];
+                        if (n < p.N) {
+                            // K-grouped tiles (a few slices each) are bound by
+                            // this store: the non-temporal hint measured 4% faster
+                            if constexpr (KG) __builtin_nontemporal_store(acc[mi][ni][j], orow + n);
+                            else orow[n] = acc[mi][ni][j];
+                        }
                     }
                 }
         }
@@ -915,6 +967,47 @@ hipError_t launch_grouped_gemm(const uint8_t* a_q, const float* a_s, const int32
         }
     }
 #undef MOE_LAUNCH
+    return hipGetLastError();
+}
+
+namespace {
+// go[g] = g * rows for g = 0..G: the row offsets of G groups of equal height
+__global__ __launch_bounds__(256) void equal_groups_kernel(int32_t* __restrict__ go, int G, int rows) {
+    for (int g = blockIdx.x * 256 + threadIdx.x; g <= G; g += gridDim.x * 256) go[g] = g * rows;
+}
+int64_t equal_groups_bytes(int G) { return ((int64_t)(G + 1) * 4 + 255) / 256 * 256; }
+}  // namespace
+
+size_t gemm_kgrouped_ws_bytes(int G, int rows, int N) {
+    return (size_t)(equal_groups_bytes(G) + scale_copy_offset(G, (int64_t)G * rows, N));
+}
+
+hipError_t launch_grouped_gemm_kgrouped(const uint8_t* a_q, const float* a_s, const int32_t* kb_start, int G,
+                                        int rows, const uint8_t* b_q, const float* b_s, int b_cs, int N,
+                                        float* out, void* ws, hipStream_t st) {
+    int32_t* go = static_cast<int32_t*>(ws);
+    char* gws = static_cast<char*>(ws) + equal_groups_bytes(G);
+    int32_t* ts = reinterpret_cast<int32_t*>(gws);
+    int4* tiles = reinterpret_cast<int4*>(gws + tile_list_offset(G));
+    const int64_t M_total = (int64_t)G * rows;
+    const int bm = 128;
+    hipLaunchKernelGGL(equal_groups_kernel, dim3((unsigned)((G + 256) / 256)), dim3(256), 0, st, go, G, rows);
+    const int64_t list_bound = ((M_total + bm - 1) / bm + G) * (int64_t)((N + BN - 1) / BN);
+    const int64_t nl = (list_bound + 255) / 256;
+    if (G <= PREP_MAX_G) {
+        // the tile-list blocks only: the A scales are read in place
+        hipLaunchKernelGGL(gemm_prep_kernel, dim3((unsigned)nl), dim3(256), 0, st, go, G, bm, N, (int)nl, ts, tiles,
+                           nullptr, nullptr, M_total, 1, nullptr);
+    } else {
+        hipLaunchKernelGGL(gemm_tile_map_kernel, dim3(1), dim3(256), 0, st, go, G, bm, ts);
+        hipLaunchKernelGGL(gemm_tile_list_kernel, dim3((unsigned)nl), dim3(256), 0, st, go, ts, G, bm, N, tiles);
+    }
+    GemmArgs p{a_q, a_s, 0u, nullptr, go, ts, ts + G + 1, tiles, G, b_q, b_s, N, BK,
+               out, nullptr, nullptr, kb_start, rows, b_cs};
+    const int64_t persistent = ((int64_t)cu_count_for_current_device() + 7) / 8 * 8;
+    const int64_t needed = (list_bound + 7) / 8 * 8;
+    hipLaunchKernelGGL((grouped_gemm_kernel<EPI_STORE_F32, 128, true>),
+                       dim3((unsigned)(needed < persistent ? needed : persistent)), dim3(NT), 0, st, p);
     return hipGetLastError();
 }
 

@@ -40,6 +40,15 @@ hipError_t launch_grouped_gemm(const uint8_t* a_q, const float* a_s, const int32
                                const uint8_t* b_q, const float* b_s, int N, int K, int epi,
                                float* out, uint8_t* out_q, float* out_s, void* ws,
                                hipStream_t st);
+// K-grouped FP32-store GEMM: G groups of `rows` A rows; group g's inner
+// dimension is the 128-blocks [kb_start[g], kb_start[g+1]) (device array), its
+// A [rows, Kg] and 1x128 scales [rows, Kg/128] start at block kb_start[g] of
+// a_q / a_s, its B [N, Kg] and 128x128 scales [N/128, Kg/128] (rows of b_cs
+// blocks) at that block of b_q / b_s; out FP32 [G*rows, N].  Empty groups give 0.
+size_t gemm_kgrouped_ws_bytes(int G, int rows, int N);
+hipError_t launch_grouped_gemm_kgrouped(const uint8_t* a_q, const float* a_s, const int32_t* kb_start, int G,
+                                        int rows, const uint8_t* b_q, const float* b_s, int b_cs, int N,
+                                        float* out, void* ws, hipStream_t st);
 
 // backward.hip
 hipError_t launch_gate_backward(const float* dh, const float* y, int64_t shared_row0, const float* gate,
@@ -64,8 +73,8 @@ hipError_t launch_wgrad_operands(const float* dh, const float* gate, const int32
                                  uint8_t* dyT_q, float* dyT_s, uint8_t* hT_q, float* hT_s, uint8_t* dzT_q,
                                  float* dzT_s, uint8_t* xT_q, float* xT_s, hipStream_t st);
 
-size_t wgrad_ws_bytes(int d, int I, int max_kp);
-hipError_t launch_wgrad_gemms(const int32_t* group_rows, int G, int d, int I, const uint8_t* dyT_q,
+size_t wgrad_ws_bytes(int G, int d, int I);
+hipError_t launch_wgrad_gemms(const int32_t* kb_start, int G, int d, int I, const uint8_t* dyT_q,
                               const float* dyT_s, const uint8_t* hT_q, const float* hT_s, const uint8_t* dzT_q,
                               const float* dzT_s, const uint8_t* xT_q, const float* xT_s, float* dw13, float* dw2,
                               void* ws, hipStream_t st);

@@ -169,61 +169,24 @@ __global__ __launch_bounds__(256) void wgrad_operand_kernel(WgradSrc s, const in
     }
 }
 
-// {0, d, 0, 2I}: the one-group row offsets of the two weight-gradient GEMMs
-__global__ void wgrad_offsets_kernel(int32_t* o, int d, int I) {
-    if (threadIdx.x == 0) {
-        o[0] = 0;
-        o[1] = d;
-        o[2] = 0;
-        o[3] = 2 * I;
-    }
-}
-
-__global__ __launch_bounds__(256) void fill_zero_kernel(float4* __restrict__ p, int64_t n4) {
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256)
-        p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-}
-
 }  // namespace
 
-size_t wgrad_ws_bytes(int d, int I, int max_kp) {
-    return 256 + gemm_ws_bytes(1, (d > 2 * I ? d : 2 * I), (d > I ? d : I), max_kp);
+size_t wgrad_ws_bytes(int G, int d, int I) {
+    const size_t a = gemm_kgrouped_ws_bytes(G, d, I), b = gemm_kgrouped_ws_bytes(G, 2 * I, d);
+    return a > b ? a : b;
 }
 
-hipError_t launch_wgrad_gemms(const int32_t* group_rows, int G, int d, int I, const uint8_t* dyT_q,
+// dW2 = GEMM(dY^T, h^T) and dW13 = GEMM(dz^T, u^T), each one K-grouped launch
+// over all groups (group g's inner dimension is its padded row count); the two
+// run one after the other on st and share the workspace.
+hipError_t launch_wgrad_gemms(const int32_t* kb_start, int G, int d, int I, const uint8_t* dyT_q,
                               const float* dyT_s, const uint8_t* hT_q, const float* hT_s, const uint8_t* dzT_q,
                               const float* dzT_s, const uint8_t* xT_q, const float* xT_s, float* dw13, float* dw2,
                               void* ws, hipStream_t st) {
-    int32_t* offs = static_cast<int32_t*>(ws);
-    void* gws = static_cast<char*>(ws) + 256;
-    hipLaunchKernelGGL(wgrad_offsets_kernel, dim3(1), dim3(64), 0, st, offs, d, I);
-    const int64_t cs_h = ((I / 128) + 3) & ~3, cs_x = ((d / 128) + 3) & ~3;
-    int64_t kb0 = 0;
-    for (int g = 0; g < G; ++g) {
-        const int64_t nkb = (group_rows[g] + 127) / 128;
-        float* o2 = dw2 + (int64_t)g * d * I;
-        float* o13 = dw13 + (int64_t)g * 2 * I * d;
-        hipError_t e;
-        if (nkb == 0) {        // an expert with no rows: zero gradients
-            hipLaunchKernelGGL(fill_zero_kernel, dim3(1024), dim3(256), 0, st, reinterpret_cast<float4*>(o2),
-                               (int64_t)d * I / 4);
-            hipLaunchKernelGGL(fill_zero_kernel, dim3(1024), dim3(256), 0, st, reinterpret_cast<float4*>(o13),
-                               (int64_t)2 * I * d / 4);
-            e = hipGetLastError();
-        } else {
-            const int kp = (int)(nkb * 128);
-            e = launch_grouped_gemm(dyT_q + (int64_t)d * 128 * kb0, dyT_s + (int64_t)d * kb0, nullptr, offs, 1, d,
-                                    hT_q + (int64_t)I * 128 * kb0, hT_s + cs_h * kb0, I, kp, EPI_STORE_F32, o2,
-                                    nullptr, nullptr, gws, st);
-            if (e == hipSuccess)
-                e = launch_grouped_gemm(dzT_q + (int64_t)2 * I * 128 * kb0, dzT_s + (int64_t)2 * I * kb0, nullptr,
-                                        offs + 2, 1, 2 * I, xT_q + (int64_t)d * 128 * kb0, xT_s + cs_x * kb0, d, kp,
-                                        EPI_STORE_F32, o13, nullptr, nullptr, gws, st);
-        }
-        if (e != hipSuccess) return e;
-        kb0 += nkb;
-    }
-    return hipSuccess;
+    const int cs_h = ((I / 128) + 3) & ~3, cs_x = ((d / 128) + 3) & ~3;
+    hipError_t e = launch_grouped_gemm_kgrouped(dyT_q, dyT_s, kb_start, G, d, hT_q, hT_s, cs_h, I, dw2, ws, st);
+    if (e != hipSuccess) return e;
+    return launch_grouped_gemm_kgrouped(dzT_q, dzT_s, kb_start, G, 2 * I, xT_q, xT_s, cs_x, d, dw13, ws, st);
 }
 
 hipError_t launch_wgrad_operands(const float* dh, const float* gate, const int32_t* slot_row,

@@ -130,17 +130,17 @@ def test_backward_argument_errors(L):
                                None) == -3                                                    # K > 16
     assert L.moe_swiglu_backward(FAKE, FAKE, 8, 100, FAKE, FAKE, None) == -2                  # I % 128
     assert L.moe_prepare_backward_weights(FAKE, 3, 128, 128, FAKE, None) == -2                # packed_t == packed
-    rows = np.array([5, 0, 300], np.int32)
-    need = L.moe_wgrad_workspace_bytes(256, 128, 300)
+    need = L.moe_wgrad_workspace_bytes(3, 256, 128)
     assert need > 256
-    p = ctypes.c_void_p(rows.ctypes.data)
-    assert L.moe_wgrad(p, 3, 256, 128, *([FAKE] * 8), FAKE, FAKE, FAKE, need - 1, None) == -4   # workspace
-    bad = np.array([5, -1, 3], np.int32)
-    assert L.moe_wgrad(ctypes.c_void_p(bad.ctypes.data), 3, 256, 128, *([FAKE] * 8), FAKE, FAKE, FAKE, need,
-                       None) == -2                                                            # negative rows
-    big = np.array([20000], np.int32)
-    assert L.moe_wgrad(ctypes.c_void_p(big.ctypes.data), 1, 256, 128, *([FAKE] * 8), FAKE, FAKE, FAKE, need,
-                       None) == -3                                                            # > 16384 rows
+    assert L.moe_wgrad_workspace_bytes(0, 256, 128) == 0
+    # the tile lists grow with the groups, not with their rows
+    assert L.moe_wgrad_workspace_bytes(300, 256, 128) > need
+    assert L.moe_wgrad(FAKE, 3, 4, 256, 128, *([FAKE] * 8), FAKE, FAKE, FAKE, need - 1, None) == -4   # workspace
+    assert L.moe_wgrad(FAKE, 3, -1, 256, 128, *([FAKE] * 8), FAKE, FAKE, FAKE, need, None) == -2     # n_kb < 0
+    assert L.moe_wgrad(None, 3, 4, 256, 128, *([FAKE] * 8), FAKE, FAKE, FAKE, need, None) == -1      # kb_start
+    assert L.moe_wgrad(FAKE, 3, 4, 200, 128, *([FAKE] * 8), FAKE, FAKE, FAKE, need, None) == -2      # d % 128
+    # one group's operands past 4 GiB (32-bit byte offsets)
+    assert L.moe_wgrad(FAKE, 3, 40_000, 1024, 512, *([FAKE] * 8), FAKE, FAKE, FAKE, 1 << 40, None) == -3
     assert L.moe_wgrad_operands(*([FAKE] * 9), 3, 4, 100, 4, 100, 128, -1, *([FAKE] * 8), None) == -2
 
 

@@ -288,3 +288,61 @@ def test_backward_dgrad_staged(T, d, E, K, I):
                         rowinf_rel(got13[:, 1].reshape(I, d), dW3))
         say(f"  FP8 weight gradients vs unquantised FP64: per-row rel err {w_err:.3e}")
         assert w_err < 0.5
+
+
+@pytest.mark.gpu
+def test_wgrad_groups_of_uneven_depth_and_empty_groups():
+    """The weight-gradient GEMMs run K-grouped: each expert's inner dimension is
+    its own padded row count.  Routing built by hand so that two experts get no
+    rows, two get 260 rows (three 128-blocks, a ragged last one) and two get 40;
+    the shared block has 300 rows.  dW2 has N = I = 128, half a 256-column tile.
+    Every expert's dW2 and dW13 must match the oracle's FP64 product of the
+    operand codes (the operands themselves are pinned by the staged test), and
+    the empty experts must get exact zeros."""
+    T, K, E, d, I = 300, 2, 6, 256, 128
+    G = E + 1
+    gen = torch.Generator().manual_seed(11)
+    idx = np.zeros((T, K), np.int64)
+    idx[:260] = (0, 2)
+    idx[260:] = (3, 5)
+    pairs = sorted((int(idx[t, k]), t, k) for t in range(T) for k in range(K))
+    R = T * K + T
+    row_token = np.zeros(R, np.int32)
+    slot_row = np.zeros((T, K), np.int32)
+    for r, (g, t, k) in enumerate(pairs):
+        row_token[r], slot_row[t, k] = t, r
+    row_token[T * K:] = np.arange(T)
+    counts = np.bincount(idx.reshape(-1), minlength=E).tolist() + [T]
+    go_h = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    assert counts[1] == 0 and counts[4] == 0 and counts[0] == 260
+    dh = torch.randn(T, d, generator=gen).to(dev())
+    gate = torch.rand(T, K, generator=gen).add_(0.1).to(dev())
+    z = torch.randn(R, 2 * I, generator=gen).to(dev())
+    dh_row = torch.randn(R, I, generator=gen).mul_(0.5).to(dev())
+    u = torch.randn(T, d, generator=gen).to(torch.bfloat16).to(dev())
+    go = torch.from_numpy(go_h).to(dev())
+    say(f"wgrad K-grouped: T={T} K={K} E={E} d={d} I={I}, rows per group {counts}")
+    dw13, dw2, ops, kb_start = moe.moe_wgrad(dh, gate, torch.from_numpy(slot_row).to(dev()),
+                                             torch.from_numpy(row_token).to(dev()), z, dh_row, u, go,
+                                             shared_row0=T * K)
+    torch.cuda.synchronize()
+    o = {k: np_(v) for k, v in ops.items()}
+    cs_h, cs_x = (I // 128 + 3) // 4 * 4, (d // 128 + 3) // 4 * 4
+    for g in range(G):
+        n = int(kb_start[g + 1] - kb_start[g])
+        kb0, kp = int(kb_start[g]), 128 * n
+        if n == 0:
+            assert not np_(dw2[g]).any() and not np_(dw13[g]).any(), g
+            continue
+        aq = o["dyT_q"][d * 128 * kb0:d * 128 * kb0 + d * kp].reshape(d, kp)
+        as_ = o["dyT_s"][d * kb0:d * kb0 + d * n].reshape(d, n)
+        hq = o["hT_q"][I * 128 * kb0:I * 128 * kb0 + I * kp].reshape(I, kp)
+        hs = o["hT_s"][cs_h * kb0:cs_h * kb0 + (I // 128) * n].reshape(I // 128, n)
+        zq = o["dzT_q"][2 * I * 128 * kb0:2 * I * 128 * kb0 + 2 * I * kp].reshape(2 * I, kp)
+        zs = o["dzT_s"][2 * I * kb0:2 * I * kb0 + 2 * I * n].reshape(2 * I, n)
+        xq = o["xT_q"][d * 128 * kb0:d * 128 * kb0 + d * kp].reshape(d, kp)
+        xs = o["xT_s"][cs_x * kb0:cs_x * kb0 + (d // 128) * n].reshape(d // 128, n)
+        e2 = rowinf_rel(np_(dw2[g]), oracle.gemm_blockscaled(aq, as_, hq, hs))
+        e13 = rowinf_rel(np_(dw13[g]), oracle.gemm_blockscaled(zq, zs, xq, xs))
+        say(f"  group {g}: {n} K-blocks, dW2 {e2:.2e}, dW13 {e13:.2e}")
+        assert e2 <= TOL and e13 <= TOL, (g, e2, e13)
