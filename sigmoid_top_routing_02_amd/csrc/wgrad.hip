@@ -59,8 +59,13 @@ __global__ __launch_bounds__(256) void wgrad_operand_kernel(WgradSrc s, const in
     __shared__ float tile[128][129];
     __shared__ float wmax[4];
     const int tid = threadIdx.x;
-    const int c0 = blockIdx.x * 128;
-    const int kbi = blockIdx.y;
+    // Sources gathered by token (dY from dh, u^T from u) read each token's row
+    // once per GEMM row of the token (K + 1 times): their grids run the row
+    // blocks fastest, so those reads of one 128-column block fall close
+    // together in time and hit in cache (the other order takes them from HBM).
+    constexpr bool GATHER = (SRC == SRC_DY || SRC == SRC_X);
+    const int c0 = (GATHER ? blockIdx.y : blockIdx.x) * 128;
+    const int kbi = GATHER ? blockIdx.x : blockIdx.y;
     int lo = 0, hi = G - 1;                                    // the group of this row block
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -196,13 +201,13 @@ hipError_t launch_wgrad_operands(const float* dh, const float* gate, const int32
                                  uint8_t* dyT_q, float* dyT_s, uint8_t* hT_q, float* hT_s, uint8_t* dzT_q,
                                  float* dzT_s, uint8_t* xT_q, float* xT_s, hipStream_t st) {
     WgradSrc s{dh, gate, slot_row, row_token, z, dh_row, u, shared_row0, K, d, I};
-    hipLaunchKernelGGL((wgrad_operand_kernel<SRC_DY, false>), dim3((unsigned)(d / 128), (unsigned)n_kb), dim3(256),
+    hipLaunchKernelGGL((wgrad_operand_kernel<SRC_DY, false>), dim3((unsigned)n_kb, (unsigned)(d / 128)), dim3(256),
                        0, st, s, go, kb_start, G, d, dyT_q, dyT_s);
     hipLaunchKernelGGL((wgrad_operand_kernel<SRC_H, true>), dim3((unsigned)(I / 128), (unsigned)n_kb), dim3(256),
                        0, st, s, go, kb_start, G, I, hT_q, hT_s);
     hipLaunchKernelGGL((wgrad_operand_kernel<SRC_DZ, false>), dim3((unsigned)(2 * I / 128), (unsigned)n_kb),
                        dim3(256), 0, st, s, go, kb_start, G, 2 * I, dzT_q, dzT_s);
-    hipLaunchKernelGGL((wgrad_operand_kernel<SRC_X, true>), dim3((unsigned)(d / 128), (unsigned)n_kb), dim3(256),
+    hipLaunchKernelGGL((wgrad_operand_kernel<SRC_X, true>), dim3((unsigned)n_kb, (unsigned)(d / 128)), dim3(256),
                        0, st, s, go, kb_start, G, d, xT_q, xT_s);
     return hipGetLastError();
 }
