@@ -132,6 +132,7 @@ __shared__ __attribute__((aligned(16))) float g_sa0[64 * NWAVES];
 __shared__ __attribute__((aligned(16))) float g_sa1[64 * NWAVES];
 __shared__ __attribute__((aligned(16))) float g_sa2[64 * NWAVES];
 __shared__ __attribute__((aligned(16))) float g_bscale[2 * MAX_SLICES];
+static_assert(MAX_SLICES == 128, "four 64-lane DMAs fill the B-scale table");
 
 
 template <int ST, int BM_>
@@ -336,11 +337,17 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
             const int r = (wave * B_DMA + par) * 8 + (lane >> 3);
             b_off[par] = (uint32_t)(T.n0 + r) * (uint32_t)K + ((lane & 7) ^ swz(r)) * 16;  // rows past N read 0
         }
-        // B scales of the tile's two 128-row blocks, all slices, into LDS
-        const float* bs_g = p.b_s + (int64_t)T.g * nblk_per_g * ns;
-        for (int i = tid; !KG && i < 2 * ns; i += NT) {
-            const int blk = min(T.n0 / 128 + i / ns, nblk_per_g - 1);
-            g_bscale[(i / ns) * MAX_SLICES + (i % ns)] = bs_g[(int64_t)blk * ns + (i % ns)];
+        // B scales of the tile's two 128-row blocks, all slices, into LDS by DMA
+        // (no register round trip, so nothing here waits for them: they land
+        // with slice 0).  Waves 0-3: block wave/2 (the second clamped when
+        // N % 256 == 128), slices 64*(wave&1) + lane; lanes past the slice
+        // count read past the end of the descriptor and write 0.
+        if (!KG && wave < 4) {
+            const int blk = min(T.n0 / 128 + (wave >> 1), nblk_per_g - 1);
+            const int sl = (wave & 1) * 64 + lane;
+            const auto bs_g = make_rsrc(p.b_s + (int64_t)T.g * nblk_per_g * ns, (uint32_t)(nblk_per_g * ns * 4));
+            lds_dma4(bs_g, sl < ns ? (uint32_t)(blk * ns + sl) * 4u : 0x80000000u, 0u,
+                     reinterpret_cast<char*>(g_bscale) + ((wave >> 1) * MAX_SLICES + (wave & 1) * 64) * 4);
         }
     };
     // DMA k (0 <= k < D) of one stage: A chunks, then B chunks, then the A scales
