@@ -540,27 +540,56 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
         mat_phase();
     };
 
-    // FP32-store epilogue (A-first layout: lane holds rows 4*kb + j of column lr)
+    // FP32-store epilogue, through LDS: the tile's rows go 64 at a time into the
+    // B buffers of stages 1 and 2 (32 rows of 1 KiB each; idle until the next
+    // tile's second slice is issued), then every wave writes whole rows, one
+    // 16-byte piece per lane (128 store instructions per tile instead of 512
+    // single floats).  In LDS the 16-float halves of each 32-float bank row
+    // swap when bit 2 of the row is set: the four row groups of a fragment
+    // write (A-first layout: lane holds rows 4*kb + j of column lr) then fall
+    // on distinct banks, and a row read stays 1 KiB of whole 16-byte chunks.
     auto store_f32 = [&](const Tile& T) {
         if constexpr (EPI == EPI_STORE_F32) {
+            constexpr int PASS_ROWS = BM < 64 ? BM : 64;
+            constexpr int RPW = PASS_ROWS / NWAVES;            // rows each wave writes out per pass
+            float* const buf0 = reinterpret_cast<float*>(g_b1);
+            float* const buf1 = reinterpret_cast<float*>(g_b2);
+            auto lds_at = [&](int lrow, int col) -> float* {      // lrow < PASS_ROWS
+                float* b = lrow < 32 ? buf0 : buf1;
+                return b + (lrow & 31) * 256 + (col ^ (((lrow >> 2) & 1) << 4));
+            };
 #pragma unroll
-            for (int mi = 0; mi < MI; ++mi)
+            for (int h = 0; h < BM / PASS_ROWS; ++h) {
+                if ((wm * WROWS) / PASS_ROWS == h) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int r = wm * WROWS + mi * 16 + kb * 4 + j;
-                    if (r >= T.rows) continue;
-                    float* orow = p.out + (int64_t)(T.m0 + r) * p.N;
+                    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-                    for (int ni = 0; ni < NI; ++ni) {
-                        const int n = T.n0 + ncol<EPI, C>(wn, ni) + lr;
-                        if (n < p.N) {
-                            // K-grouped tiles (a few slices each) are bound by
-                            // this store: the non-temporal hint measured 4% faster
-                            if constexpr (KG) __builtin_nontemporal_store(acc[mi][ni][j], orow + n);
-                            else orow[n] = acc[mi][ni][j];
+                        for (int j = 0; j < 4; ++j) {
+                            const int lrow = wm * WROWS - h * PASS_ROWS + mi * 16 + kb * 4 + j;
+#pragma unroll
+                            for (int ni = 0; ni < NI; ++ni)
+                                *lds_at(lrow, ncol<EPI, C>(wn, ni) + lr) = acc[mi][ni][j];
                         }
+                }
+                __syncthreads();
+#pragma unroll
+                for (int i = 0; i < RPW; ++i) {
+                    const int lrow = wave * RPW + i;
+                    const int r = h * PASS_ROWS + lrow;
+                    const float* src = (lrow < 32 ? buf0 : buf1) + (lrow & 31) * 256 +
+                                       4 * (lane ^ (((lrow >> 2) & 1) << 2));
+                    const v4f v = *reinterpret_cast<const v4f*>(src);
+                    const int n = T.n0 + 4 * lane;
+                    if (r < T.rows && n < p.N) {
+                        v4f* dst = reinterpret_cast<v4f*>(p.out + (int64_t)(T.m0 + r) * p.N + n);
+                        // K-grouped tiles (a few slices each) are bound by this
+                        // store: the non-temporal hint measured 4% faster there
+                        if constexpr (KG) __builtin_nontemporal_store(v, dst);
+                        else *dst = v;
                     }
                 }
+                if (h + 1 < BM / PASS_ROWS) __syncthreads();
+            }
         }
     };
 
