@@ -24,7 +24,8 @@
 // chunks of each row permuted (see swz) so that fragment reads are free of
 // bank conflicts.  The A scales are first gathered into GEMM row order and
 // made slice-major in the workspace (one slice of a tile's scales is one
-// contiguous 512-byte run); the B scales of the tile are staged in LDS once.
+// contiguous 512-byte run); the B scales of the tile reach LDS once per tile, by
+// DMA like the operands.
 //
 // Schedule: persistent, one block per CU.  A device-built tile list (exclusive
 // scan of ceil(rows_g / BM) per group, then one record per tile) fixes the
@@ -226,9 +227,9 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
     constexpr int D = C::DMA_PER_STAGE;
     // MFMA operand order.  SwiGLU tiles put B first, so a lane's four results
     // share one output row and one scale (one multiply per row tile instead
-    // of four).  FP32-store tiles keep A first: a lane's results are then four
-    // rows of one column, and its stores cover 16 consecutive columns per row,
-    // which measured faster for the large FP32 output than 4-column pieces.
+    // of four).  FP32-store tiles keep A first (a lane's results are four rows
+    // of one column); their output leaves through LDS in whole rows, so the
+    // register layout only shapes the LDS writes.
     constexpr bool TR = (EPI != EPI_STORE_F32);
     int K = p.K;          // K-grouped: the current tile's group's (set by setup)
     int ns = K / BK;
