@@ -75,7 +75,7 @@ def main():
     lines = [f"# {a.name}", ""]
     if a.note:
         lines += [a.note, ""]
-    lines += ["Commands (run from the repository root on the GPU box):", ""]
+    lines += ["Commands (run from the repository root on an MI355X):", ""]
     lines += [f"    {c}" for c in a.command] + [""]
     lines += ["## Kernel durations (rocprofv3 --kernel-trace --stats)", "",
               "| kernel | calls | avg us | total ms | % |", "|---|---|---|---|---|"]
