@@ -66,6 +66,8 @@ def lib():
         L.oracle_swiglu.argtypes = [P, P, i64, P]
         L.oracle_combine.argtypes = [P, P, i64, P, P, i64, i32, i32, P]
         L.oracle_bias_update.argtypes = [P, P, i32, i64, f32]
+        L.oracle_set_threads.argtypes = [i32]
+        L.oracle_max_threads.restype = i32
         _lib = L
     return _lib
 
@@ -77,6 +79,15 @@ def _p(a: np.ndarray):
 
 def _c(a, dtype):
     return np.ascontiguousarray(a, dtype=dtype)
+
+
+def set_threads(n: int) -> None:
+    """Threads of the oracle's OpenMP loops (results do not depend on it)."""
+    lib().oracle_set_threads(int(n))
+
+
+def max_threads() -> int:
+    return int(lib().oracle_max_threads())
 
 
 # ---------------------------------------------------------------- scalars

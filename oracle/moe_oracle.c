@@ -26,6 +26,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 
 /* ------------------------------------------------------------------------ */
@@ -128,6 +131,7 @@ void oracle_exp_spec_n(const float* x, int64_t n, float* out) {
 }
 
 void oracle_e4m3_encode_n(const float* x, int64_t n, uint8_t* out) {
+#pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3_encode(x[i]);
 }
 
@@ -445,11 +449,10 @@ void oracle_combine(const uint16_t* u, const double* y, int64_t shared_row0, con
 }
 
 /* ------------------------------------------------------------------------ */
-/* A9: bias update.  [IFS] bias paragraph: after each step an overloaded     */
-/* expert's bias is lowered by gamma and an underloaded one's raised;        */
-/* [LINEAGE] "The idea" says the same.  READING: overloaded means count*E > */
-/* T*K (above the batch mean), underloaded means count*E < T*K; an expert   */
-/* exactly at the mean keeps its bias.  FP32 add.                            */
+/* A9: bias update.  [IFS] bias paragraph and [LINEAGE] "The idea": the    */
+/* sign rule of the balancing bias, applied once per step.  READING:         */
+/* count*E > T*K -> b - gamma; count*E < T*K -> b + gamma; equality (an     */
+/* expert exactly at the batch mean) keeps b.  FP32 add.                     */
 /* ------------------------------------------------------------------------ */
 void oracle_bias_update(float* bias, const int32_t* count, int E, int64_t total_assignments, float gamma) {
     for (int e = 0; e < E; ++e) {
@@ -457,4 +460,24 @@ void oracle_bias_update(float* bias, const int32_t* count, int E, int64_t total_
         if (lhs > total_assignments) bias[e] = bias[e] - gamma;
         else if (lhs < total_assignments) bias[e] = bias[e] + gamma;
     }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Thread count of the OpenMP loops above (timing only: every output's       */
+/* reduction is sequential, so the count never changes a result).            */
+/* ------------------------------------------------------------------------ */
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
 }
