@@ -167,17 +167,36 @@ def gemm1_bytes(sh, count):
     return w + a + h
 
 
-# ----------------------------------------------------------------------------- CPU baseline
-def cpu_baseline_layer(sh, st, budget_s=15.0):
-    """The oracle (untuned) timed on a bounded sample of the same batch:
-    router for a token slice, then the FFNs (GEMM1 + SwiGLU + h quant + GEMM2)
-    of a few experts' rows with weights the oracle quantised beforehand
-    (untimed, like the GPU's), dispatch, quantisation of u and combine on the
-    slice; the per-token cost is scaled to tokens/s."""
-    import oracle
-    oracle.lib()
+def layer_bytes(sh, count):
+    """Algorithmic HBM bytes of one layer step as this path moves them: the
+    W13 and W2 codes + scales of every expert with at least one row (and the
+    shared one), u read once and the centroids, quantised u written and read,
+    h codes + scales written and read, Y (FP32) written and read, h' written,
+    and the routing arrays (scores, idx, gates, dispatch)."""
     T, d, E, K, I = sh.T, sh.d, sh.E, sh.K, sh.I
-    nt = min(T, 4096)
+    R = T * (K + 1)
+    used = int((count > 0).sum()) + 1
+    parts = {
+        "weights": used * (3 * I * d + (2 * I // 128 + I // 128) * (d // 128) * 4),
+        "u_centroids": T * d * 2 + E * d * 2,
+        "u_quant": 2 * T * (d + d // 128 * 4),
+        "h": 2 * R * (I + I // 128 * 4),
+        "y": 2 * R * d * 4,
+        "out": T * d * 4,
+        "routing": T * E * 4 * 2 + T * K * 8 * 2 + R * 4 * 2 + T * K * 4 * 2,
+    }
+    parts["total"] = sum(parts.values())
+    return parts
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+def _oracle_layer_sample(sh, st, nt, groups, max_rows, budget_s, wq):
+    """One timed oracle pass: router + dispatch + quant(u) on the first nt
+    tokens, the FFN (GEMM1 + SwiGLU + h quant + GEMM2) of up to max_rows rows
+    of each expert in `groups` (weights quantised beforehand, untimed), then
+    combine + bias update.  Returns (per-token seconds, rows, seconds)."""
+    import oracle
+    T, d, E, K, I = sh.T, sh.d, sh.E, sh.K, sh.I
     u_h = st["u"][:nt].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
     e_h = st["e"].view(torch.int16).cpu().numpy().view(np.uint16)
     b_h = st["b"].cpu().numpy()
@@ -187,43 +206,74 @@ def cpu_baseline_layer(sh, st, budget_s=15.0):
     uf = (u_h.astype(np.uint32) << 16).view(np.float32)
     uq, us = oracle.quant_1x128(uf)
     t_route = time.perf_counter() - t0
-    # FFN rows of a few experts (the shared expert and the busiest routed ones in the slice)
-    groups = [E] + [int(g) for g in np.argsort(-count)[:7]]
-    wq = {}
-    for g in groups:
-        w1, w3, w2 = (w.cpu().numpy() for w in workloads.expert_weights(sh, g, device="cuda"))
-        wq[g] = (oracle.quant_128x128(w1), oracle.quant_128x128(w3), oracle.quant_128x128(w2))
     rows_done, t_ffn = 0, 0.0
-    y_rows = {}
+    yfull = np.zeros((nt * (K + 1), d))
     for g in groups:
         r0, r1 = int(go[g]), int(go[g + 1])
-        rows = np.arange(r0, min(r1, r0 + 256))
+        rows = np.arange(r0, min(r1, r0 + max_rows))
+        if rows.size == 0:
+            continue
         (q1, s1), (q3, s3), (q2, s2) = wq[g]
         t1 = time.perf_counter()
         zg = oracle.gemm_blockscaled(uq, us, q1, s1, a_rows=rt[rows])
         zu = oracle.gemm_blockscaled(uq, us, q3, s3, a_rows=rt[rows])
         h = oracle.swiglu(zg, zu).astype(np.float32)
         hq, hs = oracle.quant_1x128(h)
-        y = oracle.gemm_blockscaled(hq, hs, q2, s2)
+        yfull[rows] = oracle.gemm_blockscaled(hq, hs, q2, s2)
         t_ffn += time.perf_counter() - t1
         rows_done += rows.size
-        for i, r in enumerate(rows):
-            y_rows[int(r)] = y[i]
         if t_route + t_ffn > budget_s:
             break
     t2 = time.perf_counter()
-    yfull = np.zeros((nt * (K + 1), d))
     oracle.combine(u_h, yfull, nt * K, gate, sr)
     oracle.bias_update(b_h, count, nt * K, sh.gamma)
     t_comb = time.perf_counter() - t2
-    per_token = (t_route + t_comb) / nt + (K + 1) * t_ffn / rows_done
-    return {
-        "value": round(1.0 / per_token, 2), "unit": "tokens/s", "cores": _cores(),
-        "kind": "oracle",
-        "sample": f"router+dispatch+quant+combine+bias on the first {nt} tokens ({t_route + t_comb:.1f}s); "
-                  f"FFN on {rows_done} rows of experts {groups} ({t_ffn:.1f}s); per-token cost = "
-                  f"slice cost/{nt} + {K + 1} x per-row FFN cost",
+    whole = rows_done == nt * (K + 1)
+    per_token = (t_route + t_ffn + t_comb) / nt if whole else \
+        (t_route + t_comb) / nt + (K + 1) * t_ffn / rows_done
+    return per_token, rows_done, t_route + t_ffn + t_comb, whole, [int(g) for g in groups]
+
+
+def cpu_baseline_layer(sh, st, budget_s=15.0):
+    """The oracle (untuned) timed on the host cores: on the tiny layer the
+    whole layer over every token (with all threads, then on one thread); on
+    the large layers a bounded sample -- router, dispatch, quant and combine
+    on up to 4096 tokens, the FFNs of the shared expert and the 7 busiest
+    experts' first 256 rows -- scaled to tokens/s (labelled extrapolated)."""
+    import oracle
+    oracle.lib()
+    T, d, E, K, I = sh.T, sh.d, sh.E, sh.K, sh.I
+    whole_layer = T * (K + 1) <= 4096
+    nt = T if whole_layer else min(T, 4096)
+    if whole_layer:
+        groups = list(range(E + 1))
+    else:
+        idx = st["idx"][:nt].cpu().numpy()
+        busiest = np.argsort(-np.bincount(idx.reshape(-1), minlength=E), kind="stable")[:7]
+        groups = [E] + [int(g) for g in busiest]
+    wq = {}
+    for g in groups:
+        w1, w3, w2 = (w.cpu().numpy() for w in workloads.expert_weights(sh, g, device="cuda"))
+        wq[g] = (oracle.quant_128x128(w1), oracle.quant_128x128(w3), oracle.quant_128x128(w2))
+    threads = oracle.max_threads()
+    max_rows = nt * (K + 1) if whole_layer else 256
+    per_token, rows, secs, whole, groups = _oracle_layer_sample(sh, st, nt, groups, max_rows, budget_s, wq)
+    res = {
+        "value": round(1.0 / per_token, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+        "cpu_model": cpu_model(), "extrapolated": not whole,
+        "sample": (f"the whole layer on all {nt} tokens ({secs:.1f}s)" if whole else
+                   f"router+dispatch+quant+combine+bias on the first {nt} tokens; FFN on {rows} rows of experts "
+                   f"{groups}; per-token cost = slice cost/{nt} + {K + 1} x per-row FFN cost ({secs:.1f}s)"),
     }
+    if whole_layer:
+        oracle.set_threads(1)
+        try:
+            pt1, _, secs1, _, _ = _oracle_layer_sample(sh, st, nt, groups, max_rows, budget_s, wq)
+        finally:
+            oracle.set_threads(threads)
+        res["single_thread"] = {"value": round(1.0 / pt1, 2), "unit": "tokens/s", "cores": 1,
+                                "sample": f"the whole layer on all {nt} tokens ({secs1:.1f}s)"}
+    return res
 
 
 # ----------------------------------------------------------------------------- runners
@@ -378,32 +428,52 @@ def run_layer(sh, steps, warmup, with_cpu):
     torch.cuda.synchronize()
     log("[bench] warmup done")
     ev = Events()
+    clocks_before = gpu_clocks()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
         layer_step(sh, st, ev)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    clocks_after = gpu_clocks()
     ms = wall * 1e3 / steps
     count = st["count"].cpu().numpy()
     stages = {n: round(ev.avg_ms(n), 4) for n in ev.pairs}
     g1, g2 = layer_flops(sh)
-    g1_ms = ev.avg_ms("gemm1")
+    g1_ms, g2_ms = ev.avg_ms("gemm1"), ev.avg_ms("gemm2")
     if sh.T >= 4096:
-        achieved = g1 / (g1_ms * 1e-3) / 1e12
-        roof = {"kernel": "grouped_gemm_fp8_blockscaled (GEMM1, SwiGLU + 1x128 requant epilogue)",
+        # the grouped GEMM as the pair of launches one step makes (GEMM1 with
+        # the SwiGLU + requant epilogue, GEMM2 with the FP32 store): their
+        # flops over their summed time, each launch also reported on its own
+        achieved = (g1 + g2) / ((g1_ms + g2_ms) * 1e-3) / 1e12
+        t1 = traffic_for(f"gemm1_{sh.name}", "gemm.hip")
+        t2 = traffic_for(f"gemm2_{sh.name}", "gemm.hip")
+        roof = {"kernel": "grouped_gemm_fp8_blockscaled (GEMM1 + GEMM2, the two launches of a step)",
                 "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
-                "traffic": traffic_for(f"gemm1_{sh.name}", "gemm.hip"),
-                "algorithmic_per_launch": g1, "avg_launch_ms": round(g1_ms, 4)}
+                "traffic": (t1 + t2) / 2 if t1 is not None and t2 is not None else None,
+                "algorithmic_per_launch": (g1 + g2) / 2, "avg_launch_ms": round((g1_ms + g2_ms) / 2, 4),
+                "gemm1": {"achieved": round(g1 / (g1_ms * 1e-3) / 1e12, 2),
+                          "frac": round(g1 / (g1_ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+                          "algorithmic_per_launch": g1, "avg_launch_ms": round(g1_ms, 4), "traffic": t1},
+                "gemm2": {"achieved": round(g2 / (g2_ms * 1e-3) / 1e12, 2),
+                          "frac": round(g2 / (g2_ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+                          "algorithmic_per_launch": g2, "avg_launch_ms": round(g2_ms, 4), "traffic": t2}}
     else:
-        nbytes = gemm1_bytes(sh, count)
-        achieved = nbytes / (g1_ms * 1e-3) / 1e9
-        roof = {"kernel": "grouped_gemm_fp8_blockscaled (GEMM1, SwiGLU + 1x128 requant epilogue)",
+        # weight streaming: the whole layer step against HBM, with GEMM1 (the
+        # largest stream) on its own
+        nbytes = layer_bytes(sh, count)
+        achieved = nbytes["total"] / (ms * 1e-3) / 1e9
+        b1 = gemm1_bytes(sh, count)
+        a1 = b1 / (g1_ms * 1e-3) / 1e9
+        roof = {"kernel": "the whole layer step (all kernels, one stream)",
                 "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "traffic": traffic_for(f"gemm1_{sh.name}", "gemm.hip"),
-                "algorithmic_per_launch": nbytes, "avg_launch_ms": round(g1_ms, 4)}
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                "algorithmic_per_launch": nbytes["total"], "avg_launch_ms": round(ms, 4),
+                "bytes": nbytes,
+                "gemm1": {"achieved": round(a1, 1), "frac": round(a1 / PEAK_HBM_GBS, 4),
+                          "algorithmic_per_launch": b1, "avg_launch_ms": round(g1_ms, 4),
+                          "traffic": traffic_for(f"gemm1_{sh.name}", "gemm.hip")}}
     log(f"[bench] {ms:.3f} ms/step; stages {stages}")
     qerr = layer_quant_error(sh, st)
     log(f"[bench] quantisation error vs the unquantised layer: {qerr}")
@@ -422,6 +492,7 @@ def run_layer(sh, steps, warmup, with_cpu):
         "stages_ms": stages,
         "gemm_tflops": {"gemm1": round(g1 / (ev.avg_ms("gemm1") * 1e-3) / 1e12, 1),
                         "gemm2": round(g2 / (ev.avg_ms("gemm2") * 1e-3) / 1e12, 1)},
+        "gpu_clocks_mhz": {"before": clocks_before, "after": clocks_after},
     }
     if with_cpu:
         log("[bench] CPU oracle baseline")
@@ -466,12 +537,14 @@ def run_rdc(steps, warmup, with_cpu):
     for _ in range(warmup):
         step()
     ev = Events()
+    clocks_before = gpu_clocks()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
         step(ev)
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
+    clocks_after = gpu_clocks()
     stages = {n: round(ev.avg_ms(n), 4) for n in ev.pairs}
     balance = balance_loss_timing(st, steps)
     grouped = grouped_router_timing(u, e, b, K, st, steps)
@@ -496,23 +569,38 @@ def run_rdc(steps, warmup, with_cpu):
         "grouped_router": grouped,
         "seq_balance_loss": balance,
         "router_tflops": round(2.0 * T * E * d / (ev.avg_ms("router") * 1e-3) / 1e12, 2),
+        "gpu_clocks_mhz": {"before": clocks_before, "after": clocks_after},
     }
     if with_cpu:
         import oracle
         oracle.lib()
+
+        def rdc_pass(nt):
+            u_h = u[:nt].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+            e_h = e.view(torch.int16).cpu().numpy().view(np.uint16)
+            t0 = time.perf_counter()
+            idx, gate, s = oracle.router_topk(u_h, e_h, b.cpu().numpy(), K)
+            cnt, go, rt, sr = oracle.dispatch(idx, E, False)
+            uf = (u_h.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+            y = uf[rt]
+            oracle.combine(u_h, y, -1, gate, sr)
+            oracle.bias_update(b.cpu().numpy(), cnt, nt * K, sh.gamma)
+            return time.perf_counter() - t0
+        threads = oracle.max_threads()
         nt = 2048
-        u_h = u[:nt].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-        e_h = e.view(torch.int16).cpu().numpy().view(np.uint16)
-        t0 = time.perf_counter()
-        idx, gate, s = oracle.router_topk(u_h, e_h, b.cpu().numpy(), K)
-        cnt, go, rt, sr = oracle.dispatch(idx, E, False)
-        uf = (u_h.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-        y = uf[rt]
-        oracle.combine(u_h, y, -1, gate, sr)
-        oracle.bias_update(b.cpu().numpy(), cnt, nt * K, sh.gamma)
-        dt = time.perf_counter() - t0
-        res["cpu_baseline"] = {"value": round(nt / dt, 1), "unit": "tokens/s", "cores": _cores(), "kind": "oracle",
-                               "sample": f"the whole rdc pass on the first {nt} tokens ({dt:.1f}s)"}
+        dt = rdc_pass(nt)
+        oracle.set_threads(1)
+        try:
+            nt1 = 256
+            dt1 = rdc_pass(nt1)
+        finally:
+            oracle.set_threads(threads)
+        res["cpu_baseline"] = {"value": round(nt / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                               "cpu_model": cpu_model(), "extrapolated": True,
+                               "sample": f"the whole rdc pass on the first {nt} of {T} tokens ({dt:.1f}s); "
+                                         f"per-token work is independent, so tokens/s carries over",
+                               "single_thread": {"value": round(nt1 / dt1, 1), "unit": "tokens/s", "cores": 1,
+                                                 "sample": f"the same pass on the first {nt1} tokens ({dt1:.1f}s)"}}
     res["copy_ceiling_gbs"] = copy_ceiling_gbs()
     return res
 
@@ -593,11 +681,38 @@ def copy_ceiling_gbs(reps=10):
     return round(2.0 * rows * d * 2 / (float(np.median(ts)) * 1e-3) / 1e9, 1)
 
 
-def _cores():
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo)."""
     try:
-        return len(os.sched_getaffinity(0)) if not os.environ.get("OMP_NUM_THREADS") else int(os.environ["OMP_NUM_THREADS"])
-    except Exception:
-        return os.cpu_count() or 1
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def gpu_clocks():
+    """Current GPU clocks in MHz as rocm-smi reports them (shader clock sclk,
+    memory clock mclk, ...), or the reason they could not be read.  Read in a
+    child process; a failure never stops the benchmark."""
+    import re
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=30)
+        data = json.loads(r.stdout)
+    except Exception as exc:              # tool missing, no permission, unparsable output
+        return {"error": type(exc).__name__}
+    out = {}
+    for card, vals in data.items():
+        if not isinstance(vals, dict):
+            continue
+        for k, v in vals.items():
+            m = re.search(r"\(?(\d+)\s*Mhz", str(v), re.I)
+            if m:
+                out[f"{card}:{k}"] = int(m.group(1))
+    return out or {"error": "no clock values in rocm-smi output"}
 
 
 def run_dense(steps, warmup, K=4096):
@@ -618,6 +733,7 @@ def run_dense(steps, warmup, K=4096):
     for _ in range(warmup):
         moe.grouped_gemm_fp8_blockscaled(aq, as_, go, M, bq3, bs3, out=out, ws=ws)
     ev = Events()
+    clocks_before = gpu_clocks()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
@@ -626,6 +742,7 @@ def run_dense(steps, warmup, K=4096):
         ev.add("gemm", a0, ev.mark("e"))
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
+    clocks_after = gpu_clocks()
     flops = 2.0 * M * N * K
     g_ms = ev.avg_ms("gemm")
     ach = flops / (g_ms * 1e-3) / 1e12
@@ -642,6 +759,7 @@ def run_dense(steps, warmup, K=4096):
                      "frac": round(ach / PEAK_FP8_TFLOPS, 4), "traffic": traffic_for(f"dense_k{K}", "gemm.hip")},
         "error": err,
         "accumulation": acc,
+        "gpu_clocks_mhz": {"before": clocks_before, "after": clocks_after},
     }
 
 

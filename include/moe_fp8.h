@@ -70,11 +70,10 @@ const char* moe_last_error(void);
 int moe_version(void);
 
 /* ------------------------------------------------------------------ router
- * moe_router_topk -- [IFS] MoE-routing paragraph: each token picks the top K
- * of E routed experts by sigmoid affinity to the expert's centroid, and the
- * gates are normalised over the chosen ones; [IFS] bias paragraph and
- * [LINEAGE] "The notation": a per-expert bias is added to the score for the
- * choice only, the gate uses the raw score.
+ * moe_router_topk -- [IFS] MoE-routing paragraph (affinity = sigmoid of the
+ * token-centroid dot product; K experts chosen per token; gates divided by
+ * the sum over the chosen set); [IFS] bias paragraph and [LINEAGE] "The
+ * notation" (the balancing bias enters the ranking only, never the gate).
  *
  *   s[t,i]   = sigmoid(sum_k u[t,k] e[i,k])   FP32, summed in increasing k with
  *              one FMA per term; the sigmoid is the library's fixed binary32
@@ -154,8 +153,40 @@ int moe_dispatch(const int32_t* topk_idx, int64_t T, int K, int E, int include_s
                  int32_t* expert_count, int32_t* group_offset, int32_t* row_token,
                  int32_t* slot_row, void* ws, size_t ws_bytes, moe_stream_t stream);
 
+/* moe_dispatch_check -- the debug status word of a dispatch result: the
+ * invariants of a drop-free dispatch ([LINEAGE] "The idea": no token is
+ * dropped, so the counts sum to exactly T*K) checked on the device and written
+ * to *status (uint32, device) as a bitmask of moe_check; 0 = every invariant
+ * holds.  Not part of the layer's path: debug code and tests call it after
+ * moe_dispatch and read the word back.  expert_count, group_offset as
+ * moe_dispatch wrote them (required); topk_idx, row_token, slot_row may all
+ * be NULL, else every assignment's row is checked too.  Every index is
+ * range-checked before use, so corrupted arrays are reported, never
+ * dereferenced out of range.  Limits as moe_dispatch.
+ */
+enum moe_check {
+    MOE_CHECK_COUNT_SUM = 1u << 0,            /* sum of expert_count != T*K */
+    MOE_CHECK_OFFSETS_NOT_MONOTONE = 1u << 1, /* group_offset decreases somewhere */
+    MOE_CHECK_FIRST_OFFSET = 1u << 2,         /* group_offset[0] != 0 */
+    MOE_CHECK_COUNT_NE_OFFSETS = 1u << 3,     /* group_offset[e+1] - group_offset[e] != expert_count[e] */
+    MOE_CHECK_ROUTED_TOTAL = 1u << 4,         /* group_offset[E] != T*K */
+    MOE_CHECK_SHARED_GROUP = 1u << 5,         /* with the shared group: its size != T */
+    MOE_CHECK_NEGATIVE_COUNT = 1u << 6,       /* a negative expert_count */
+    MOE_CHECK_SLOT_ROW = 1u << 7,             /* slot_row[t,k] outside expert idx[t,k]'s group, or its row's token != t */
+    MOE_CHECK_SHARED_ROWS = 1u << 8           /* row_token[T*K + t] != t */
+};
+int moe_dispatch_check(const int32_t* expert_count, const int32_t* group_offset, const int32_t* topk_idx,
+                       const int32_t* row_token, const int32_t* slot_row, int64_t T, int K, int E,
+                       int include_shared, uint32_t* status, moe_stream_t stream);
+
 /* moe_permute_rows -- out[r] = x[row_token[r]] for r < rows, rows of d
- * elements of type dt (the dispatch's data movement, made explicit). */
+ * elements of type dt: the data movement of the dispatch made explicit
+ * ([IFS] DualPipe/EP paragraph: tokens are sent to their experts and the
+ * results gathered back; on one GPU this is an in-memory gather).  x [*, d],
+ * row_token int32 [rows] with values indexing rows of x (not checked: the
+ * call cannot see x's row count), out [rows, d] of the same type; dt is
+ * MOE_BF16 or MOE_F32; d >= 1.  Used by the router/dispatch/combine workload
+ * (identity experts); the FFN path gathers rows inside the GEMM instead. */
 int moe_permute_rows(const void* x, int dt, const int32_t* row_token, int64_t rows, int d,
                      void* out, moe_stream_t stream);
 
@@ -253,11 +284,14 @@ int moe_combine(const void* u_bf16, const void* y, int y_dt, int64_t shared_row0
                 float* out, moe_stream_t stream);
 
 /* ------------------------------------------------------------------ bias update
- * moe_bias_update -- [IFS] bias paragraph: after each step the bias of an
- * overloaded expert is lowered by gamma and that of an underloaded one raised.
- * Overloaded: expert_count[i]*E > total_assignments; underloaded: <; an expert
- * exactly at the batch mean keeps its bias.  bias FP32 [E] is updated in place
- * (binary32 add).  total_assignments = T*K of the batch the counts came from.
+ * moe_bias_update -- [IFS] bias paragraph and batch-wise-balance paragraph
+ * (the sign rule of the auxiliary-loss-free balancing, once per step, on the
+ * counts of the whole batch):
+ *   expert_count[i]*E > total_assignments:  bias[i] -= gamma
+ *   expert_count[i]*E < total_assignments:  bias[i] += gamma
+ *   equal (exactly at the batch mean):      bias[i] unchanged
+ * bias FP32 [E] is updated in place (binary32 add).  total_assignments = T*K
+ * of the batch the counts came from.
  */
 int moe_bias_update(float* bias, const int32_t* expert_count, int E, int64_t total_assignments,
                     float gamma, moe_stream_t stream);
@@ -289,9 +323,9 @@ int moe_prepare_expert_weights(const float* w1, const float* w3, const float* w2
  * grouped_gemm_fp8_blockscaled with transposed weights; their operands are
  * quantised per 1x128 tile along the contraction like the forward's (the
  * pages give no backward tiling: this library's reading).  Order:
- *   moe_gate_backward -> GEMM(dY, W2^T) = dh_row -> GEMM1 recomputed with the
- *   FP32 store epilogue = z -> moe_swiglu_backward -> GEMM(dz, W13^T) = dx ->
- *   moe_router_backward.
+ *   (forward GEMM1 with MOE_EPI_SWIGLU_QUANT_Z, which keeps z) ->
+ *   moe_gate_backward -> GEMM(dY, W2^T) = dh_row -> moe_swiglu_backward(z) ->
+ *   GEMM(dz, W13^T) = dx -> moe_router_backward.
  *
  * moe_prepare_backward_weights: packed_t receives the transposed weights in
  * the packed layout's slots: W13^T E4M3 [G, d, 2I] (its inner index keeps
@@ -348,19 +382,33 @@ int moe_router_backward(const float* dh, const float* dx, int64_t shared_row0, c
                         const int32_t* group_offset, int64_t T, int K, int d, int E, float* du, float* de,
                         moe_stream_t stream);
 
+/* moe_wgrad_block_starts -- kb_start int32 [G+1] (device) = the exclusive
+ * scan of nkb_g = ceil(rows_g / 128), rows_g = group_offset[g+1] -
+ * group_offset[g]: where each group's zero-padded 128-row blocks start in the
+ * weight-gradient operands below.  Computed on the device, so nothing is read
+ * back to the host; kb_start[G] <= ceil(R / 128) + G for R = group_offset[G],
+ * the host-side bound the callers size their buffers with.
+ * Limits: 1 <= G <= 65535.
+ */
+int moe_wgrad_block_starts(const int32_t* group_offset, int G, int32_t* kb_start, moe_stream_t stream);
+
 /* moe_wgrad_operands -- the operands of the expert weight gradients
  *   dW2_g  = sum over the rows r of expert g of dY_r^T h_r           [d, I]
  *   dW13_g = sum over the rows r of expert g of dz_r^T u_(token r)   [2I, d]
- * (dY_r = topk_gate of the row's slot * dh_(token r), dh on the shared rows
+ * (the chain rule through [LINEAGE] "The notation" and the SwiGLU form;
+ * dY_r = topk_gate of the row's slot * dh_(token r), dh on the shared rows
  * from shared_row0 on; h = SiLU(z_gate) z_up; dz = the SwiGLU backward of
  * dh_row, in W13's interleaved row order), which contract over each
- * expert's rows: each is one grouped_gemm_fp8_blockscaled call per expert
- * with G = 1, M = d (2I), N = I (d), K = Kp_g, FP32 store, on the transposed
- * operands written here.  Group g's rows [group_offset[g], group_offset[g+1])
- * are padded with zero rows to Kp_g = 128 * nkb_g; kb_start int32 [G+1]
- * (device) is the exclusive scan of nkb_g = ceil(rows_g / 128) and n_kb its
- * total.  Layout, group after group (C = d, I, 2I, d for dY^T, h^T, dz^T,
- * u^T; CS = C/128 rounded up to a multiple of 4):
+ * expert's rows: moe_wgrad runs them as K-grouped GEMMs (group g's inner
+ * dimension Kp_g) on the transposed operands written here.  Group g's rows
+ * [group_offset[g], group_offset[g+1]) are padded with zero rows to
+ * Kp_g = 128 * nkb_g; kb_start int32 [G+1] (device, from
+ * moe_wgrad_block_starts) is the exclusive scan of nkb_g = ceil(rows_g / 128),
+ * and n_kb is any host-known upper bound of its total kb_start[G] (such as
+ * ceil(R / 128) + G): it sizes the launch grids, and blocks past kb_start[G]
+ * do nothing.  Layout, group after group (C = d, I, 2I, d for dY^T, h^T,
+ * dz^T, u^T; CS = C/128 rounded up to a multiple of 4), in buffers of at
+ * least n_kb blocks:
  *   codes E4M3 [C, Kp_g] at byte C * 128 * kb_start[g]
  *   dY^T, dz^T scales (1x128 along the rows) FP32 [C, nkb_g] at C * kb_start[g]
  *   h^T, u^T scales (128x128 blocks) FP32 [C/128, nkb_g] at CS * kb_start[g]
@@ -382,7 +430,8 @@ int moe_wgrad_operands(const float* dh, const float* topk_gate, const int32_t* s
  * gradients.  Two launches in all (one per weight), each K-grouped: every
  * group's inner dimension is its own, and nothing is read back to the host.
  * kb_start int32 [G+1] (device), the array moe_wgrad_operands took; n_kb =
- * kb_start[G] (host-known); dw13 FP32 [G, 2I, d], dw2 FP32 [G, d, I]; ws of
+ * the same host-known upper bound of kb_start[G] (only checked against the
+ * limits below); dw13 FP32 [G, 2I, d], dw2 FP32 [G, d, I]; ws of
  * moe_wgrad_workspace_bytes(G, d, I) bytes.
  * Limits: n_kb * 128 * max(d, 2I) < 2^32 (32-bit byte offsets into one
  * group's operands), G * max(d, 2I) < 2^31; MOE_ERR_UNSUPPORTED otherwise.
@@ -393,8 +442,12 @@ int moe_wgrad(const int32_t* kb_start, int G, int n_kb, int d, int I, const uint
               const uint8_t* xT_q, const float* xT_scale, float* dw13, float* dw2, void* ws, size_t ws_bytes,
               moe_stream_t stream);
 
-/* moe_layer_forward -- the whole layer: router, dispatch, 1x128 quantisation
- * of u, GEMM1 with fused SwiGLU and 1x128 re-quantisation, GEMM2, combine.
+/* moe_layer_forward -- the whole layer, [LINEAGE] "The notation":
+ *   h'[t] = u[t] + FFN_shared(u[t]) + sum_k g[t,k] FFN_{idx[t,k]}(u[t])
+ * as router ([IFS] MoE-routing and bias paragraphs), dispatch, 1x128
+ * quantisation of u ([IFS] FP8-tiling paragraph), GEMM1 with fused SwiGLU and
+ * 1x128 re-quantisation, GEMM2 (both promoting per 128-wide slice, [IFS]
+ * FP8-accumulation paragraph), combine: the calls above in that order.
  * The bias is read only (update it with moe_bias_update).  packed_weights as
  * above with G = E + 1; out FP32 [T,d]; expert_count_out int32 [E] (may be
  * NULL); ws of moe_layer_workspace_bytes(T, d, E, K, I).

@@ -27,14 +27,14 @@ EXPORTS = (
     "moe_status_string", "moe_last_error", "moe_version",
     "moe_router_topk", "moe_router_topk_grouped",
     "moe_seq_balance_loss_workspace_bytes", "moe_seq_balance_loss",
-    "moe_dispatch_workspace_bytes", "moe_dispatch", "moe_permute_rows",
+    "moe_dispatch_workspace_bytes", "moe_dispatch", "moe_dispatch_check", "moe_permute_rows",
     "fp8_quant_1x128", "fp8_quant_128x128",
     "moe_gemm_workspace_bytes", "grouped_gemm_fp8_blockscaled",
     "moe_fp8_mfma_accumulation_probe", "moe_combine", "moe_bias_update",
     "moe_packed_weight_bytes", "moe_prepare_expert_weights",
     "moe_layer_workspace_bytes", "moe_layer_forward",
     "moe_prepare_backward_weights", "moe_gate_backward", "moe_swiglu_backward", "moe_router_backward",
-    "moe_wgrad_operands", "moe_wgrad_workspace_bytes", "moe_wgrad",
+    "moe_wgrad_block_starts", "moe_wgrad_operands", "moe_wgrad_workspace_bytes", "moe_wgrad",
 )
 
 
@@ -64,6 +64,7 @@ def load_library(path: str = LIB_PATH):
         "moe_seq_balance_loss": ([P, P, I64, I32, I32, I32, F32, P, P, SZ, P], I32),
         "moe_dispatch_workspace_bytes": ([I64, I32], SZ),
         "moe_dispatch": ([P, I64, I32, I32, I32, P, P, P, P, P, SZ, P], I32),
+        "moe_dispatch_check": ([P, P, P, P, P, I64, I32, I32, I32, P, P], I32),
         "moe_permute_rows": ([P, I32, P, I64, I32, P, P], I32),
         "fp8_quant_1x128": ([P, I32, I64, I32, P, P, P], I32),
         "fp8_quant_128x128": ([P, I64, I32, P, P, P], I32),
@@ -80,6 +81,7 @@ def load_library(path: str = LIB_PATH):
         "moe_gate_backward": ([P, P, I64, P, P, P, P, I64, I32, I32, I32, P, P, P, P, P], I32),
         "moe_swiglu_backward": ([P, P, I64, I32, P, P, P], I32),
         "moe_router_backward": ([P, P, I64, P, P, P, P, P, P, P, P, I64, I32, I32, I32, P, P, P], I32),
+        "moe_wgrad_block_starts": ([P, I32, P, P], I32),
         "moe_wgrad_operands": ([P, P, P, P, P, P, P, P, P, I32, I32, I64, I32, I32, I32, I64,
                                 P, P, P, P, P, P, P, P, P], I32),
         "moe_wgrad_workspace_bytes": ([I32, I32, I32], SZ),
@@ -194,6 +196,35 @@ def moe_dispatch(topk_idx, E, include_shared=True, ws=None):
     return count, go, row_token[:R], slot_row
 
 
+MOE_CHECK_BITS = {
+    "count_sum": 1 << 0, "offsets_not_monotone": 1 << 1, "first_offset": 1 << 2, "count_ne_offsets": 1 << 3,
+    "routed_total": 1 << 4, "shared_group": 1 << 5, "negative_count": 1 << 6, "slot_row": 1 << 7,
+    "shared_rows": 1 << 8,
+}
+
+
+def moe_dispatch_check(expert_count, group_offset, T, K, topk_idx=None, row_token=None, slot_row=None):
+    """The debug status word of a dispatch result: a uint32 bitmask
+    (MOE_CHECK_BITS) left on the device in an int32 [1] tensor; 0 = every
+    invariant holds."""
+    E = expert_count.numel()
+    sh = group_offset.numel() - E - 1
+    if sh not in (0, 1):
+        raise MoEError("group_offset must hold E+1 or E+2 entries")
+    _want(expert_count, torch.int32, (E,), "expert_count")
+    _want(group_offset, torch.int32, (E + 1 + sh,), "group_offset")
+    if topk_idx is not None:
+        _want(topk_idx, torch.int32, (T, K), "topk_idx")
+        _want(slot_row, torch.int32, (T, K), "slot_row")
+        if row_token.dtype != torch.int32 or row_token.numel() < T * K + sh * T:
+            raise MoEError("row_token: int32 with T*K (+T) entries expected")
+    status = _new((1,), torch.int32, expert_count)
+    L = load_library()
+    _check(L.moe_dispatch_check(_ptr(expert_count), _ptr(group_offset), _ptr(topk_idx), _ptr(row_token),
+                                _ptr(slot_row), T, K, E, sh, _ptr(status), _stream()), "moe_dispatch_check")
+    return status
+
+
 def moe_permute_rows(x, row_token, out=None):
     rows = row_token.shape[0]
     T, d = x.shape
@@ -243,21 +274,41 @@ def grouped_gemm_fp8_blockscaled(a_q, a_scale, group_offset, M_total, b_q, b_sca
     """a_q uint8 [*,K], a_scale f32 [*,K/128], group_offset i32 [G+1] (device),
     b_q uint8 [G,N,K], b_scale f32 [G,N/128,K/128]."""
     G, N, K = b_q.shape
+    if b_q.dtype != torch.uint8:
+        raise MoEError(f"b_q: dtype {b_q.dtype}, expected torch.uint8")
     _want(b_scale, torch.float32, (G, N // 128, K // 128), "b_scale")
-    if a_q.shape[1] != K:
-        raise MoEError("a_q: inner dimension differs from b_q")
-    if group_offset.numel() < G + 1:
-        raise MoEError("group_offset must hold G+1 entries")
+    if a_q.dim() != 2 or a_q.dtype != torch.uint8 or a_q.shape[1] != K:
+        raise MoEError(f"a_q: {a_q.dtype} {tuple(a_q.shape)}, expected torch.uint8 [*, {K}]")
+    _want(a_scale, torch.float32, (a_q.shape[0], K // 128), "a_scale")
+    if group_offset.dtype != torch.int32 or group_offset.numel() < G + 1:
+        raise MoEError("group_offset must be int32 with G+1 entries")
+    # the rows each GEMM row reads: a gather through a_row_index, else row m
+    # itself (the index values cannot be checked without reading them back)
+    if a_row_index is None:
+        if a_q.shape[0] < M_total:
+            raise MoEError(f"a_q holds {a_q.shape[0]} rows, fewer than M_total = {M_total}")
+    elif a_row_index.dtype != torch.int32 or a_row_index.numel() < M_total:
+        raise MoEError(f"a_row_index: {a_row_index.dtype} with {a_row_index.numel()} entries, "
+                       f"expected int32 with at least M_total = {M_total}")
     if epi == MOE_EPI_STORE_F32:
         out = _new((M_total, N), torch.float32, a_q) if out is None else out
+        _want(out, torch.float32, (M_total, N), "out")
     elif epi == MOE_EPI_SWIGLU_F32:
         out = _new((M_total, N // 2), torch.float32, a_q) if out is None else out
+        _want(out, torch.float32, (M_total, N // 2), "out")
     else:
         out_q = _new((M_total, N // 2), torch.uint8, a_q) if out_q is None else out_q
         out_scale = _new((M_total, N // 256), torch.float32, a_q) if out_scale is None else out_scale
-        if epi == MOE_EPI_SWIGLU_QUANT_Z and out is None:
-            out = _new((M_total, N), torch.float32, a_q)
+        _want(out_q, torch.uint8, (M_total, N // 2), "out_q")
+        _want(out_scale, torch.float32, (M_total, N // 256), "out_scale")
+        if epi == MOE_EPI_SWIGLU_QUANT_Z:
+            out = _new((M_total, N), torch.float32, a_q) if out is None else out
+            _want(out, torch.float32, (M_total, N), "out")
+        elif out is not None:
+            _want(out, torch.float32, (M_total, N // 2), "out")
     L = load_library()
+    if ws is not None and ws.numel() < L.moe_gemm_workspace_bytes(G, M_total, N, K):
+        raise MoEError("ws: smaller than moe_gemm_workspace_bytes")
     if ws is None:
         ws = _new((max(L.moe_gemm_workspace_bytes(G, M_total, N, K), 256),), torch.uint8, a_q)
     _check(L.grouped_gemm_fp8_blockscaled(
@@ -293,8 +344,15 @@ def moe_combine(u, y, topk_gate, slot_row, shared_row0=-1, out=None):
     _want(u, torch.bfloat16, (T, d), "u")
     _want(topk_gate, torch.float32, (T, K), "topk_gate")
     _want(slot_row, torch.int32, (T, K), "slot_row")
+    if y.dtype not in (torch.bfloat16, torch.float32) or y.dim() != 2 or y.shape[1] != d:
+        raise MoEError(f"y: {y.dtype} {tuple(y.shape)}, expected bf16 or f32 [rows, {d}]")
+    # rows read: shared_row0 + t for every token (the slot rows' values cannot
+    # be checked without reading them back)
+    if T > 0 and shared_row0 >= 0 and y.shape[0] < shared_row0 + T:
+        raise MoEError(f"y holds {y.shape[0]} rows; the shared rows need {shared_row0 + T}")
     dt = {torch.bfloat16: MOE_BF16, torch.float32: MOE_F32}[y.dtype]
     out = _new((T, d), torch.float32, u) if out is None else out
+    _want(out, torch.float32, (T, d), "out")
     L = load_library()
     _check(L.moe_combine(_ptr(u), _ptr(y), dt, shared_row0, _ptr(topk_gate), _ptr(slot_row), T, K,
                          d, _ptr(out), _stream()), "moe_combine")
@@ -436,19 +494,20 @@ def moe_router_backward(dh, dx, slot_row, dlogit, topk_idx, centroids, u, row_dl
 
 def moe_wgrad(dh, topk_gate, slot_row, row_token, z, dh_row, u, group_offset, shared_row0=-1):
     """Expert weight gradients -> (dW13 f32 [G, 2I, d] in W13's interleaved row
-    order, dW2 f32 [G, d, I], the operand buffers, kb_start).  Builds the
-    transposed operands (moe_wgrad_operands), then moe_wgrad runs one K-grouped
-    GEMM per weight over all experts.  The expert sizes are read back to the
-    host once, to size the operand buffers."""
+    order, dW2 f32 [G, d, I], the operand buffers, kb_start i32 [G+1] on the
+    device).  moe_wgrad_block_starts places each expert's padded row blocks
+    (on the device), moe_wgrad_operands builds the transposed operands, then
+    moe_wgrad runs one K-grouped GEMM per weight over all experts.  Nothing is
+    read back to the host: the buffers are sized by the bound
+    ceil(R / 128) + G of the row-block count, so the whole chain can be
+    captured in a graph."""
     T, d = dh.shape
     K = topk_gate.shape[1]
     R, I2 = z.shape
     I = I2 // 2
     G = group_offset.numel() - 1
-    go_h = group_offset.cpu().numpy().astype(np.int64)
-    nkb = (np.diff(go_h) + 127) // 128
-    kb_start = np.concatenate([[0], np.cumsum(nkb)]).astype(np.int32)
-    n_kb = int(kb_start[-1])
+    _want(group_offset, torch.int32, (G + 1,), "group_offset")
+    n_kb = (R + 127) // 128 + G
     dev = dh.device
     cs_h, cs_x = (I // 128 + 3) // 4 * 4, (d // 128 + 3) // 4 * 4
     bufs = dict(
@@ -461,7 +520,8 @@ def moe_wgrad(dh, topk_gate, slot_row, row_token, z, dh_row, u, group_offset, sh
         xT_q=torch.empty(max(d * 128 * n_kb, 16), dtype=torch.uint8, device=dev),
         xT_s=torch.empty(max(cs_x * n_kb, 4), dtype=torch.float32, device=dev))
     L = load_library()
-    kbs = torch.from_numpy(kb_start).to(dev)
+    kbs = torch.empty(G + 1, dtype=torch.int32, device=dev)
+    _check(L.moe_wgrad_block_starts(_ptr(group_offset), G, _ptr(kbs), _stream()), "moe_wgrad_block_starts")
     _check(L.moe_wgrad_operands(_ptr(dh), _ptr(topk_gate), _ptr(slot_row), _ptr(row_token), _ptr(z), _ptr(dh_row),
                                 _ptr(u), _ptr(group_offset), _ptr(kbs), G, n_kb, T, K, d, I, shared_row0,
                                 *(_ptr(bufs[k]) for k in ("dyT_q", "dyT_s", "hT_q", "hT_s", "dzT_q", "dzT_s",
@@ -472,4 +532,4 @@ def moe_wgrad(dh, topk_gate, slot_row, row_token, z, dh_row, u, group_offset, sh
     _check(L.moe_wgrad(_ptr(kbs), G, n_kb, d, I,
                        *(_ptr(bufs[k]) for k in ("dyT_q", "dyT_s", "hT_q", "hT_s", "dzT_q", "dzT_s", "xT_q", "xT_s")),
                        _ptr(dw13), _ptr(dw2), _ptr(ws), ws.numel(), _stream()), "moe_wgrad")
-    return dw13, dw2, bufs, kb_start
+    return dw13, dw2, bufs, kbs

@@ -1,9 +1,10 @@
 // FP8 MFMA accumulation probe (a measurement, not a step of the layer).
 //
 // "DeepSeek-V3 Technical Report" notes (learn.ifs.name), FP8-accumulation
-// paragraph: the tensor cores of the pages' GPU keep only about 14 bits while
-// accumulating FP8 products, so a long inner dimension loses accuracy (about 2%
-// at K = 4096) unless partial sums are promoted to FP32 every 128 elements.
+// paragraph: on the pages' GPU the matrix-unit accumulator of FP8 products
+// has limited precision (the pages put the resulting error near 2% for an
+// inner dimension of 4096), which the pages fix by moving each 128-element
+// partial sum into FP32 registers.
 // This kernel measures the same effect for gfx950's FP8 MFMA with unit scales:
 //     chained:  acc = MFMA(a_j, b_j, acc) over all slices j  (the matrix core
 //               carries the accumulator from slice to slice)

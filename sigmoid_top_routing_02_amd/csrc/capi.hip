@@ -105,7 +105,8 @@ int moe_router_topk_grouped(const void* u_bf16, const void* centroids_bf16, cons
 }
 
 size_t moe_seq_balance_loss_workspace_bytes(int64_t T, int seq_len) {
-    if (T <= 0 || seq_len < 1 || T % seq_len) return 0;
+    // 0 outside what moe_seq_balance_loss accepts (also keeps the sizes from overflowing)
+    if (T <= 0 || seq_len < 1 || T % seq_len || T / seq_len > 65535) return 0;
     return moe::seq_balance_ws_bytes(T / seq_len, seq_len);
 }
 
@@ -133,7 +134,7 @@ int moe_seq_balance_loss(const float* scores, const int32_t* topk_idx, int64_t T
 }
 
 size_t moe_dispatch_workspace_bytes(int64_t T, int E) {
-    if (T <= 0 || E <= 0) return 0;
+    if (T <= 0 || E <= 0 || E > 256 || T >= ((int64_t)1 << 31)) return 0;   // outside moe_dispatch's limits
     return moe::dispatch_ws_bytes(T, E);
 }
 
@@ -157,6 +158,25 @@ int moe_dispatch(const int32_t* topk_idx, int64_t T, int K, int E, int include_s
     return hip_status(moe::launch_dispatch(topk_idx, T, K, E, include_shared, expert_count,
                                            group_offset, row_token, slot_row, ws, S(stream)),
                       "dispatch launch");
+}
+
+int moe_dispatch_check(const int32_t* expert_count, const int32_t* group_offset, const int32_t* topk_idx,
+                       const int32_t* row_token, const int32_t* slot_row, int64_t T, int K, int E,
+                       int include_shared, uint32_t* status, moe_stream_t stream) {
+    REQUIRE(T >= 0, MOE_ERR_SHAPE, "moe_dispatch_check: T < 0");
+    REQUIRE(E >= 1 && E <= 256, MOE_ERR_UNSUPPORTED, "moe_dispatch_check: E=%d outside [1, 256]", E);
+    REQUIRE(K >= 1 && K <= E && K <= 16, MOE_ERR_UNSUPPORTED, "moe_dispatch_check: K=%d outside [1, min(E,16)]", K);
+    REQUIRE(include_shared == 0 || include_shared == 1, MOE_ERR_SHAPE,
+            "moe_dispatch_check: include_shared must be 0 or 1");
+    REQUIRE(T * (K + 1) < (int64_t)1 << 31, MOE_ERR_UNSUPPORTED, "moe_dispatch_check: T*(K+1) exceeds int32 rows");
+    REQUIRE_PTR(expert_count);
+    REQUIRE_PTR(group_offset);
+    REQUIRE_PTR(status);
+    REQUIRE((topk_idx == nullptr) == (row_token == nullptr) && (row_token == nullptr) == (slot_row == nullptr),
+            MOE_ERR_NULLPTR, "moe_dispatch_check: topk_idx, row_token and slot_row must all be given or all NULL");
+    return hip_status(moe::launch_dispatch_check(expert_count, group_offset, topk_idx, row_token, slot_row, T, K, E,
+                                                 include_shared, status, S(stream)),
+                      "dispatch check launch");
 }
 
 int moe_permute_rows(const void* x, int dt, const int32_t* row_token, int64_t rows, int d,
@@ -200,7 +220,9 @@ int fp8_quant_128x128(const float* w, int64_t rows, int cols, uint8_t* q, float*
 }
 
 size_t moe_gemm_workspace_bytes(int G, int64_t M_total, int N, int K) {
-    return (G > 0 && M_total >= 0 && N > 0 && K > 0) ? moe::gemm_ws_bytes(G, M_total, N, K) : 0;
+    // 0 outside the grouped GEMM's limits (which also keep the sizes below from overflowing)
+    return (G > 0 && G <= 65535 && M_total >= 0 && M_total < ((int64_t)1 << 31) && N > 0 && K > 0 && K <= 16384)
+               ? moe::gemm_ws_bytes(G, M_total, N, K) : 0;
 }
 
 int grouped_gemm_fp8_blockscaled(const uint8_t* a_q, const float* a_scale,
@@ -319,7 +341,8 @@ Packed packed_layout(void* base, int G, int d, int I) {
 }  // namespace
 
 size_t moe_packed_weight_bytes(int n_groups, int d, int I) {
-    if (n_groups <= 0 || d <= 0 || I <= 0) return 0;
+    // 0 for sizes no call takes (keeps the products below from wrapping)
+    if (n_groups <= 0 || n_groups > 65537 || d <= 0 || I <= 0 || d > 65536 || I > 65536) return 0;
     const size_t G = (size_t)n_groups;
     return al256(G * 2 * I * d) + al256(G * d * I) +
            al256(G * (2 * I / 128) * (d / 128) * sizeof(float)) +
@@ -434,6 +457,13 @@ int moe_router_backward(const float* dh, const float* dx, int64_t shared_row0, c
                       "de launch");
 }
 
+int moe_wgrad_block_starts(const int32_t* group_offset, int G, int32_t* kb_start, moe_stream_t stream) {
+    REQUIRE(G >= 1 && G <= 65535, MOE_ERR_UNSUPPORTED, "moe_wgrad_block_starts: G=%d outside [1, 65535]", G);
+    REQUIRE_PTR(group_offset);
+    REQUIRE_PTR(kb_start);
+    return hip_status(moe::launch_wgrad_block_starts(group_offset, G, kb_start, S(stream)), "kb_start launch");
+}
+
 int moe_wgrad_operands(const float* dh, const float* topk_gate, const int32_t* slot_row, const int32_t* row_token,
                        const float* z, const float* dh_row, const void* u_bf16, const int32_t* group_offset,
                        const int32_t* kb_start, int G, int n_kb, int64_t T, int K, int d, int I,
@@ -471,7 +501,7 @@ int moe_wgrad_operands(const float* dh, const float* topk_gate, const int32_t* s
 }
 
 size_t moe_wgrad_workspace_bytes(int G, int d, int I) {
-    if (G < 1 || G > 65535 || d <= 0 || I <= 0) return 0;
+    if (G < 1 || G > 65535 || d <= 0 || I <= 0 || d > 65536 || I > 65536) return 0;   // no overflow below
     return moe::wgrad_ws_bytes(G, d, I);
 }
 
@@ -558,7 +588,10 @@ LayerWs layer_ws(void* base, int64_t T, int d, int E, int K, int I) {
 }  // namespace
 
 size_t moe_layer_workspace_bytes(int64_t T, int d, int E, int K, int I) {
-    if (T <= 0 || d <= 0 || E <= 0 || K <= 0 || I <= 0) return 0;
+    // 0 outside moe_layer_forward's limits (which also keep the sizes from overflowing)
+    if (T <= 0 || d <= 0 || E <= 0 || K <= 0 || I <= 0 || E > 256 || K > 16 || d > 16384 || I > 16384 ||
+        T * (K + 1) >= ((int64_t)1 << 31))
+        return 0;
     return layer_ws(nullptr, T, d, E, K, I).total;
 }
 

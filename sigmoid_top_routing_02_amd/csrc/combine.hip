@@ -1,16 +1,15 @@
 // Combine and bias update.
 //
-// Combine -- nlp-lineage summary, "The notation": the layer output is the
-// input plus the shared experts plus the chosen routed experts weighted by
-// their gates,
+// Combine -- nlp-lineage summary, "The notation" (the layer's output
+// equation), written for GEMM rows:
 //     h'[t] = u[t] + y[shared_row0 + t] + sum_k g[t,k] * y[slot_row[t,k]]
 // evaluated per element in FP32 in that order (one FMA per routed term);
 // bandwidth bound.
 //
-// Bias update -- "DeepSeek-V3 Technical Report" notes, bias paragraph: after
-// each step an overloaded expert's bias is lowered by gamma and an
-// underloaded one's raised.  Overloaded: count * E > T*K (above the batch
-// mean); an expert exactly at the mean is left alone.
+// Bias update -- "DeepSeek-V3 Technical Report" notes, bias paragraph (the
+// sign rule of the auxiliary-loss-free balancing):
+//     count * E > T*K:  b -= gamma;   count * E < T*K:  b += gamma;
+//     count * E == T*K: b unchanged.
 #include "device_math.h"
 #include "kernels.h"
 

@@ -14,6 +14,7 @@
 //              + popcount(mask[c][e] & lanes-below-t).
 #include "device_math.h"
 #include "kernels.h"
+#include "moe_fp8.h"
 
 namespace moe {
 namespace {
@@ -142,7 +143,78 @@ __global__ __launch_bounds__(PERMUTE_THREADS) void permute_rows_kernel(const per
     }
 }
 
+// Invariant checks of a dispatch result (the debug status word).  The first
+// kernel (one block) overwrites *status with the count/offset checks; the
+// second ORs in the per-assignment checks.  Every index is range-checked
+// before it is used, so a corrupted result is reported, never dereferenced.
+__global__ __launch_bounds__(256) void dispatch_check_counts_kernel(const int32_t* __restrict__ count,
+                                                                    const int32_t* __restrict__ go, int64_t T,
+                                                                    int K, int E, int include_shared,
+                                                                    uint32_t* __restrict__ status) {
+    __shared__ uint32_t bits;
+    __shared__ unsigned long long total;
+    if (threadIdx.x == 0) { bits = 0; total = 0; }
+    __syncthreads();
+    uint32_t b = 0;
+    long long sum = 0;
+    for (int e = threadIdx.x; e < E; e += 256) {
+        const int32_t c = count[e];
+        if (c < 0) b |= MOE_CHECK_NEGATIVE_COUNT;
+        sum += c;
+        if (go[e + 1] < go[e]) b |= MOE_CHECK_OFFSETS_NOT_MONOTONE;
+        if ((int64_t)go[e + 1] - go[e] != c) b |= MOE_CHECK_COUNT_NE_OFFSETS;
+    }
+    if (threadIdx.x == 0) {
+        if (go[0] != 0) b |= MOE_CHECK_FIRST_OFFSET;
+        if ((int64_t)go[E] != T * K) b |= MOE_CHECK_ROUTED_TOTAL;
+        if (include_shared && (int64_t)go[E + 1] - go[E] != T) b |= MOE_CHECK_SHARED_GROUP;
+        if (include_shared && go[E + 1] < go[E]) b |= MOE_CHECK_OFFSETS_NOT_MONOTONE;
+    }
+    atomicOr(&bits, b);
+    atomicAdd(&total, (unsigned long long)sum);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t r = bits;
+        if ((long long)total != T * K) r |= MOE_CHECK_COUNT_SUM;
+        *status = r;
+    }
+}
+
+__global__ __launch_bounds__(256) void dispatch_check_rows_kernel(const int32_t* __restrict__ idx,
+                                                                  const int32_t* __restrict__ go,
+                                                                  const int32_t* __restrict__ row_token,
+                                                                  const int32_t* __restrict__ slot_row,
+                                                                  int64_t T, int K, int E, int include_shared,
+                                                                  uint32_t* __restrict__ status) {
+    const int64_t R = T * K + (include_shared ? T : 0);
+    uint32_t b = 0;
+    for (int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x; j < T * K; j += (int64_t)gridDim.x * 256) {
+        const int64_t t = j / K;
+        const int ex = idx[j];
+        const int32_t r = slot_row[j];
+        if (ex < 0 || ex >= E || r < 0 || r >= R) { b |= MOE_CHECK_SLOT_ROW; continue; }
+        if (r < go[ex] || r >= go[ex + 1] || row_token[r] != t) b |= MOE_CHECK_SLOT_ROW;
+    }
+    if (include_shared)
+        for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < T; t += (int64_t)gridDim.x * 256)
+            if (row_token[T * K + t] != t) b |= MOE_CHECK_SHARED_ROWS;
+    if (b) atomicOr(status, b);
+}
+
 }  // namespace
+
+hipError_t launch_dispatch_check(const int32_t* count, const int32_t* group_offset, const int32_t* idx,
+                                 const int32_t* row_token, const int32_t* slot_row, int64_t T, int K, int E,
+                                 int include_shared, uint32_t* status, hipStream_t st) {
+    hipLaunchKernelGGL(dispatch_check_counts_kernel, dim3(1), dim3(256), 0, st, count, group_offset, T, K, E,
+                       include_shared, status);
+    if (idx && row_token && slot_row && T > 0) {
+        const int64_t blocks = (T * K + 255) / 256;
+        hipLaunchKernelGGL(dispatch_check_rows_kernel, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(256), 0,
+                           st, idx, group_offset, row_token, slot_row, T, K, E, include_shared, status);
+    }
+    return hipGetLastError();
+}
 
 size_t dispatch_ws_bytes(int64_t T, int E) {
     const int64_t nchunk = (T + CHUNK - 1) / CHUNK;

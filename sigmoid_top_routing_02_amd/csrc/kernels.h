@@ -65,6 +65,11 @@ hipError_t launch_de(const float* row_dlogit, const int32_t* row_token, const in
 hipError_t launch_transpose_blocks(const uint8_t* in, const float* in_s, int G, int rows, int cols,
                                    uint8_t* out, float* out_s, hipStream_t st);
 
+// dispatch.hip: status word of moe_dispatch_check (bits of enum moe_check in the header)
+hipError_t launch_dispatch_check(const int32_t* count, const int32_t* group_offset, const int32_t* idx,
+                                 const int32_t* row_token, const int32_t* slot_row, int64_t T, int K, int E,
+                                 int include_shared, uint32_t* status, hipStream_t st);
+
 // wgrad.hip
 hipError_t launch_wgrad_operands(const float* dh, const float* gate, const int32_t* slot_row,
                                  const int32_t* row_token, const float* z, const float* dh_row,
@@ -74,6 +79,7 @@ hipError_t launch_wgrad_operands(const float* dh, const float* gate, const int32
                                  float* dzT_s, uint8_t* xT_q, float* xT_s, hipStream_t st);
 
 size_t wgrad_ws_bytes(int G, int d, int I);
+hipError_t launch_wgrad_block_starts(const int32_t* go, int G, int32_t* kb_start, hipStream_t st);
 hipError_t launch_wgrad_gemms(const int32_t* kb_start, int G, int d, int I, const uint8_t* dyT_q,
                               const float* dyT_s, const uint8_t* hT_q, const float* hT_s, const uint8_t* dzT_q,
                               const float* dzT_s, const uint8_t* xT_q, const float* xT_s, float* dw13, float* dw2,

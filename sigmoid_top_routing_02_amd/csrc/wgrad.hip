@@ -66,6 +66,9 @@ __global__ __launch_bounds__(256) void wgrad_operand_kernel(WgradSrc s, const in
     constexpr bool GATHER = (SRC == SRC_DY || SRC == SRC_X);
     const int c0 = (GATHER ? blockIdx.y : blockIdx.x) * 128;
     const int kbi = GATHER ? blockIdx.x : blockIdx.y;
+    // the grid covers an upper bound of the row blocks (the host does not read
+    // the group sizes back); blocks past the last one have nothing to do
+    if (kbi >= kb_start[G]) return;
     int lo = 0, hi = G - 1;                                    // the group of this row block
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -174,7 +177,39 @@ __global__ __launch_bounds__(256) void wgrad_operand_kernel(WgradSrc s, const in
     }
 }
 
+// kb_start[g] = sum_{g' < g} ceil(rows_g' / 128) for g = 0..G, one block:
+// per chunk of 256 groups a Hillis-Steele scan in LDS plus the running carry.
+__global__ __launch_bounds__(256) void wgrad_block_starts_kernel(const int32_t* __restrict__ go, int G,
+                                                                 int32_t* __restrict__ kb_start) {
+    __shared__ int32_t buf[256];
+    __shared__ int32_t carry;
+    if (threadIdx.x == 0) carry = 0;
+    __syncthreads();
+    for (int base = 0; base < G; base += 256) {
+        const int g = base + threadIdx.x;
+        const int32_t v = (g < G) ? (go[g + 1] - go[g] + 127) / 128 : 0;
+        buf[threadIdx.x] = v;
+        __syncthreads();
+        for (int off = 1; off < 256; off <<= 1) {
+            const int32_t x = (threadIdx.x >= (unsigned)off) ? buf[threadIdx.x - off] : 0;
+            __syncthreads();
+            buf[threadIdx.x] += x;
+            __syncthreads();
+        }
+        if (g < G) kb_start[g] = carry + buf[threadIdx.x] - v;
+        __syncthreads();
+        if (threadIdx.x == 255) carry += buf[255];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) kb_start[G] = carry;
+}
+
 }  // namespace
+
+hipError_t launch_wgrad_block_starts(const int32_t* go, int G, int32_t* kb_start, hipStream_t st) {
+    hipLaunchKernelGGL(wgrad_block_starts_kernel, dim3(1), dim3(256), 0, st, go, G, kb_start);
+    return hipGetLastError();
+}
 
 size_t wgrad_ws_bytes(int G, int d, int I) {
     const size_t a = gemm_kgrouped_ws_bytes(G, d, I), b = gemm_kgrouped_ws_bytes(G, 2 * I, d);

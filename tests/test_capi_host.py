@@ -141,6 +141,11 @@ def test_backward_argument_errors(L):
     assert L.moe_wgrad(FAKE, 3, 4, 200, 128, *([FAKE] * 8), FAKE, FAKE, FAKE, need, None) == -2      # d % 128
     # one group's operands past 4 GiB (32-bit byte offsets)
     assert L.moe_wgrad(FAKE, 3, 40_000, 1024, 512, *([FAKE] * 8), FAKE, FAKE, FAKE, 1 << 40, None) == -3
+    # the device-side row-block starts
+    assert L.moe_wgrad_block_starts(FAKE, 0, FAKE, None) == -3
+    assert L.moe_wgrad_block_starts(FAKE, 70_000, FAKE, None) == -3
+    assert L.moe_wgrad_block_starts(None, 3, FAKE, None) == -1
+    assert L.moe_wgrad_block_starts(FAKE, 3, None, None) == -1
     assert L.moe_wgrad_operands(*([FAKE] * 9), 3, 4, 100, 4, 100, 128, -1, *([FAKE] * 8), None) == -2
 
 
@@ -180,3 +185,64 @@ def test_packed_weight_size(L):
     # the decode/prefill layers: 257 experts of 3 x 2048 x 7168 E4M3 weights
     big = L.moe_packed_weight_bytes(257, 7168, 2048)
     assert 257 * 3 * 2048 * 7168 < big < 257 * 3 * 2048 * 7168 + 3_000_000
+
+
+def test_binding_checks_caller_buffers():
+    """The C ABI cannot see buffer sizes, so the Python binding checks every
+    caller-supplied buffer of the GEMM and the combine before any launch: a
+    wrong size raises MoEError naming the buffer (host tensors here, so the
+    error must come from the size check, which runs before the device check)."""
+    import torch
+    M, N, K, G = 64, 256, 256, 2
+    aq = torch.zeros(M, K, dtype=torch.uint8)
+    as_ = torch.ones(M, K // 128)
+    go = torch.tensor([0, 32, 64], dtype=torch.int32)
+    bq = torch.zeros(G, N, K, dtype=torch.uint8)
+    bs = torch.ones(G, N // 128, K // 128)
+    gemm = moe.grouped_gemm_fp8_blockscaled
+    cases = [
+        (dict(out=torch.empty(M, N - 128)), "out"),
+        (dict(out=torch.empty(M, N, dtype=torch.float64)), "out"),
+        (dict(epi=moe.MOE_EPI_SWIGLU_QUANT, out_q=torch.empty(M, N, dtype=torch.uint8)), "out_q"),
+        (dict(epi=moe.MOE_EPI_SWIGLU_QUANT, out_scale=torch.empty(M, N // 128)), "out_scale"),
+        (dict(epi=moe.MOE_EPI_SWIGLU_QUANT_Z, out=torch.empty(M, N // 2)), "out"),
+        (dict(epi=moe.MOE_EPI_SWIGLU_F32, out=torch.empty(M, N)), "out"),
+        (dict(a_row_index=torch.zeros(M - 1, dtype=torch.int32)), "a_row_index"),
+        (dict(a_row_index=torch.zeros(M, dtype=torch.int64)), "a_row_index"),
+        (dict(ws=torch.empty(16, dtype=torch.uint8)), "ws"),
+    ]
+    for kw, name in cases:
+        with pytest.raises(moe.MoEError, match=name):
+            gemm(aq, as_, go, M, bq, bs, **kw)
+    with pytest.raises(moe.MoEError, match="a_scale"):
+        gemm(aq, torch.ones(M, K // 128 + 1), go, M, bq, bs)
+    with pytest.raises(moe.MoEError, match="a_q"):
+        gemm(aq.float(), as_, go, M, bq, bs)
+    with pytest.raises(moe.MoEError, match="M_total"):
+        gemm(aq, as_, go, M + 1, bq, bs)
+    with pytest.raises(moe.MoEError, match="group_offset"):
+        gemm(aq, as_, go[:2], M, bq, bs)
+    # combine: y's width, the shared rows, out
+    T, d, Kc = 8, 256, 2
+    u = torch.zeros(T, d, dtype=torch.bfloat16)
+    gate = torch.zeros(T, Kc)
+    slot = torch.zeros(T, Kc, dtype=torch.int32)
+    with pytest.raises(moe.MoEError, match="y"):
+        moe.moe_combine(u, torch.zeros(T * 3, d + 128), gate, slot, shared_row0=T * Kc)
+    with pytest.raises(moe.MoEError, match="shared rows"):
+        moe.moe_combine(u, torch.zeros(T * 3 - 1, d), gate, slot, shared_row0=T * Kc)
+    with pytest.raises(moe.MoEError, match="out"):
+        moe.moe_combine(u, torch.zeros(T * 3, d), gate, slot, shared_row0=T * Kc, out=torch.empty(T, d - 128))
+    # a well-formed call gets past every size check and stops at the device check
+    with pytest.raises(moe.MoEError, match="GPU"):
+        gemm(aq, as_, go, M, bq, bs)
+
+
+def test_dispatch_check_argument_errors(L):
+    ok = (FAKE, FAKE, FAKE, FAKE, FAKE, 64, 4, 16, 1, FAKE, None)
+    assert L.moe_dispatch_check(*ok[:6], 17, *ok[7:]) == -3          # K > E
+    assert L.moe_dispatch_check(*ok[:7], 300, *ok[8:]) == -3         # E > 256
+    assert L.moe_dispatch_check(*ok[:8], 2, *ok[9:]) == -2           # include_shared
+    assert L.moe_dispatch_check(None, *ok[1:]) == -1
+    assert L.moe_dispatch_check(*ok[:9], None, None) == -1           # status
+    assert L.moe_dispatch_check(FAKE, FAKE, None, FAKE, FAKE, *ok[5:]) == -1   # partial row arrays

@@ -82,6 +82,16 @@ def _check_dz_codes(q, s, x_ref, mag):
     return int((q != q_ref).sum())
 
 
+
+def _check_block_starts(kb_start, go_h):
+    """The device-built row-block starts equal the exclusive scan of
+    ceil(rows_g / 128), integer for integer; returned on the host."""
+    kb = np_(kb_start).astype(np.int64)
+    nkb = (np.diff(np.asarray(go_h, np.int64)) + 127) // 128
+    np.testing.assert_array_equal(kb, np.concatenate([[0], np.cumsum(nkb)]))
+    return kb
+
+
 CASES = [
     # (T, d, E, K, I): 32-row GEMM tiles; 128-row tiles; the decode layer's shapes
     (128, 512, 16, 4, 256),
@@ -184,6 +194,7 @@ def test_backward_dgrad_staged(T, d, E, K, I):
     dw13, dw2, ops, kb_start = moe.moe_wgrad(dh, f["gate"], f["slot_row"], f["row_token"], z, dh_row, u, go,
                                              shared_row0=T * K)
     torch.cuda.synchronize()
+    kb_start = _check_block_starts(kb_start, go_h)
     say(f"  oracle: weight gradients on {len(groups)} groups")
     rt = np_(f["row_token"])
     gate_h, dh_h = np_(f["gate"]), np_(dh)
@@ -326,6 +337,7 @@ def test_wgrad_groups_of_uneven_depth_and_empty_groups():
                                              torch.from_numpy(row_token).to(dev()), z, dh_row, u, go,
                                              shared_row0=T * K)
     torch.cuda.synchronize()
+    kb_start = _check_block_starts(kb_start, go_h)
     o = {k: np_(v) for k, v in ops.items()}
     cs_h, cs_x = (I // 128 + 3) // 4 * 4, (d // 128 + 3) // 4 * 4
     for g in range(G):
@@ -346,3 +358,68 @@ def test_wgrad_groups_of_uneven_depth_and_empty_groups():
         e13 = rowinf_rel(np_(dw13[g]), oracle.gemm_blockscaled(zq, zs, xq, xs))
         say(f"  group {g}: {n} K-blocks, dW2 {e2:.2e}, dW13 {e13:.2e}")
         assert e2 <= TOL and e13 <= TOL, (g, e2, e13)
+
+
+@pytest.mark.parametrize("T", [128, 2048])
+def test_backward_graph_capture_replays(T):
+    """The whole backward step (gate backward, the two dgrad GEMMs, SwiGLU
+    backward, du and de, then the weight gradients with their device-built
+    row-block starts) captured in a HIP graph: it reads nothing back to the
+    host.  Replayed three times, with eager backward work on other inputs in
+    between; every replay's du, de, dW13 and dW2 equal the eager result bit
+    for bit.  T = 128 runs the 32-row GEMM tiles, T = 2048 the 128-row ones."""
+    d, E, K, I = 512, 16, 4, 256
+    sh = workloads.custom_shape(T=T, d=d, E=E, K=K, I=I)
+    G, R = E + 1, T * K + T
+    say(f"backward graph capture T={T}")
+    u = workloads.activations(sh).to(dev())
+    e, b = workloads.centroids(sh).to(dev()), workloads.bias(sh).to(dev())
+    packed = pack_all(sh)
+    f = run_steps(u, e, b, packed, sh)
+    packed_t = moe.moe_prepare_backward_weights(packed, G, d, I)
+    w13q, w2q, w13s, w2s = moe.packed_views(packed, G, d, I)
+    t13q, t2q, t13s, t2s = moe.packed_views(packed_t, G, d, I)
+    t13q, t13s = t13q.view(G, d, 2 * I), t13s.view(G, d // 128, 2 * I // 128)
+    t2q, t2s = t2q.view(G, I, d), t2s.view(G, I // 128, d // 128)
+    go = f["go"]
+    _, _, z = moe.grouped_gemm_fp8_blockscaled(f["uq"], f["us"], go, R, w13q, w13s,
+                                               epi=moe.MOE_EPI_SWIGLU_QUANT_Z, a_row_index=f["row_token"])
+    ws = torch.empty(moe.moe_gemm_workspace_bytes(G, R, max(2 * I, d), max(2 * I, d)), dtype=torch.uint8,
+                     device=dev())
+
+    def step(dh):
+        dy_q, dy_s, dlogit, row_dlogit = moe.moe_gate_backward(dh, f["y"], f["gate"], f["slot_row"], f["s"],
+                                                               f["idx"], shared_row0=T * K)
+        dh_row = moe.grouped_gemm_fp8_blockscaled(dy_q, dy_s, go, R, t2q, t2s, epi=moe.MOE_EPI_STORE_F32, ws=ws)
+        dz_q, dz_s = moe.moe_swiglu_backward(z, dh_row)
+        dx = moe.grouped_gemm_fp8_blockscaled(dz_q, dz_s, go, R, t13q, t13s, epi=moe.MOE_EPI_STORE_F32, ws=ws)
+        du, de = moe.moe_router_backward(dh, dx, f["slot_row"], dlogit, f["idx"], e, u, row_dlogit,
+                                         f["row_token"], go, shared_row0=T * K)
+        dw13, dw2, _, _ = moe.moe_wgrad(dh, f["gate"], f["slot_row"], f["row_token"], z, dh_row, u, go,
+                                        shared_row0=T * K)
+        return du, de, dw13, dw2
+
+    dh = workloads.normal((T, d), 1.0, workloads.seed_for("backward", "dh", T), device=dev())
+    dh2 = torch.flip(dh, dims=[0]).contiguous()
+    ref = [x.clone() for x in step(dh)]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(dh)                                   # warm the allocator on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        outs = step(dh)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for x in outs:
+            x.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, x, r in zip(("du", "de", "dw13", "dw2"), outs, ref):
+            assert torch.equal(x.view(torch.int32), r.view(torch.int32)), (rep, name)
+        other = step(dh2)                          # eager work between replays
+        torch.cuda.synchronize()
+        assert other[0].shape == ref[0].shape

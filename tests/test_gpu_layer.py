@@ -17,8 +17,9 @@ the same inputs:
     oracle's own dequantised W2).
 The composite moe_layer_forward must equal the step-by-step calls bit for bit.
 Small workload: every token.  Decode and prefill workloads (full size, the
-configuration the benchmark times): every token for routing/dispatch/quant,
-sampled tokens and experts for the FFNs.
+configuration the benchmark times): every token for routing/dispatch/quant;
+the FFN stages on rows of every non-empty group and on every row of the 64
+largest-|u|_inf tokens (plus the first and last), whose outputs are checked.
 """
 import numpy as np
 import pytest
@@ -74,13 +75,18 @@ def deq_block(q, s):
     return t[q] * np.repeat(np.repeat(s.astype(np.float64), 128, 0), 128, 1)
 
 
-def flip_allowance(hq_gpu, hq_ref, hs_ref, w2_deq):
-    """Per-element bound of how much Y may move because of midpoint flips in h's codes."""
+def flip_allowance(hq_gpu, hq_ref, hs_ref, q2, s2):
+    """Per-element bound of how much Y may move because of midpoint flips in
+    h's codes: |deq(hq_gpu) - deq(hq_ref)| @ |W2|^T, computed for the rows
+    that have a flip (W2 dequantised from its codes only then)."""
     table = oracle.e4m3_table()
-    dv = np.abs(table[hq_gpu] - table[hq_ref]) * np.repeat(hs_ref.astype(np.float64), 128, 1)
-    if not dv.any():
-        return np.zeros((hq_gpu.shape[0], w2_deq.shape[0]))
-    return dv @ np.abs(w2_deq).T
+    out = np.zeros((hq_gpu.shape[0], q2.shape[0]))
+    rows = np.nonzero((hq_gpu != hq_ref).any(axis=1))[0]
+    if rows.size == 0:
+        return out
+    dv = np.abs(table[hq_gpu[rows]] - table[hq_ref[rows]]) * np.repeat(hs_ref[rows].astype(np.float64), 128, 1)
+    out[rows] = dv @ np.abs(deq_block(q2, s2)).T
+    return out
 
 
 def check_y(y_gpu, y_ref, allow):
@@ -89,7 +95,34 @@ def check_y(y_gpu, y_ref, allow):
     return float((excess / np.where(den == 0, 1, den)).max())
 
 
-def check_layer(sh, u, e, b, packed, g_out, token_sample=None, expert_check=None):
+def _check_packed_expert(sh, g, w13q, w2q, w13s, w2s):
+    """The packed 128x128 codes and scales of expert g equal the oracle's
+    quantiser on the expert's FP32 masters (gate/up blocks interleaved)."""
+    I = sh.I
+    w1, w3, w2 = host_weights(sh, g)
+    q1, s1 = oracle.quant_128x128(w1)
+    q3, s3 = oracle.quant_128x128(w3)
+    q2, s2 = oracle.quant_128x128(w2)
+    for j in range(I // 128):
+        np.testing.assert_array_equal(w13q[256 * j:256 * j + 128], q1[128 * j:128 * j + 128])
+        np.testing.assert_array_equal(w13q[256 * j + 128:256 * j + 256], q3[128 * j:128 * j + 128])
+        np.testing.assert_array_equal(w13s[2 * j], s1[j])
+        np.testing.assert_array_equal(w13s[2 * j + 1], s3[j])
+    np.testing.assert_array_equal(w2q, q2)
+    np.testing.assert_array_equal(w2s, s2)
+
+
+def check_layer(sh, u, e, b, packed, g_out, token_sample=None, group_rows=None, quant_check=None):
+    """Staged parity of the layer (bit-exact routing, dispatch and quant(u) on
+    every token; h, h codes, Y and h' on the checked rows and tokens).
+
+    token_sample: the tokens whose output h' is checked (all of their K + 1
+    GEMM rows are checked); None = every token.  group_rows: extra GEMM rows
+    to check, as {group: [rows]} (the survey's "at least one row of every
+    non-empty group").  quant_check: the experts whose packed weight codes and
+    scales are checked bit-exact against the oracle's quantiser of their FP32
+    masters; None = every expert.  The oracle's GEMMs take the packed codes as
+    operands (checked experts: the oracle's own codes, equal to them)."""
     T, d, E, K, I = sh.T, sh.d, sh.E, sh.K, sh.I
     u_h, e_h, b_h = u16(u), u16(e), np_(b)
     # ---- bit-exact stages, every token
@@ -107,61 +140,46 @@ def check_layer(sh, u, e, b, packed, g_out, token_sample=None, expert_check=None
     np.testing.assert_array_equal(np_(g_out["uq"]), uq_r)
     np.testing.assert_array_equal(np_(g_out["us"]).view(np.uint32), us_r.view(np.uint32))
 
-    # ---- which tokens / experts get the FFN checks
+    # ---- which rows get the FFN checks
     tokens = np.arange(T) if token_sample is None else np.asarray(token_sample)
-    experts = set()
+    want = {}
     for t in tokens:
-        experts.update(int(x) for x in idx_r[t])
-    experts.add(E)                                  # shared
-    if expert_check:
-        experts.update(expert_check)
+        for k in range(K):
+            want.setdefault(int(idx_r[t, k]), set()).add(int(sr_r[t, k]))
+        want.setdefault(E, set()).add(T * K + int(t))       # the shared row
+    for g, rows in (group_rows or {}).items():
+        want.setdefault(int(g), set()).update(int(r) for r in rows)
     w13q_d, w2q_d, w13s_d, w2s_d = moe.packed_views(packed, E + 1, d, I)
+    gate_cols = np.concatenate([np.arange(256 * j, 256 * j + 128) for j in range(I // 128)])
 
     def rows_of(name, rows):   # copy only the rows the oracle checks
         return np_(g_out[name][torch.from_numpy(np.asarray(rows, np.int64)).to(dev())])
     y_ref_rows, allow_rows = {}, {}
-    worst = dict(h=0.0, y=0.0, flips=0)
-    for g in sorted(experts):
-        say(f"  expert {g}: weights + FFN rows")
-        w1, w3, w2 = host_weights(sh, g)
-        q1, s1 = oracle.quant_128x128(w1)
-        q3, s3 = oracle.quant_128x128(w3)
-        q2, s2 = oracle.quant_128x128(w2)
+    worst = dict(h=0.0, y=0.0, flips=0, rows=0, groups=0, quant_checked=0)
+    for g in sorted(want):
+        rows = np.array(sorted(want[g]), dtype=np.int64)
+        assert np.all((rows >= go_r[g]) & (rows < go_r[g + 1])), g
         w13q, w2q, w13s, w2s = (np_(v[g]) for v in (w13q_d, w2q_d, w13s_d, w2s_d))
-        # packed layout: 128-row blocks of W1 and W3 alternate
-        for j in range(I // 128):
-            np.testing.assert_array_equal(w13q[256 * j:256 * j + 128], q1[128 * j:128 * j + 128])
-            np.testing.assert_array_equal(w13q[256 * j + 128:256 * j + 256], q3[128 * j:128 * j + 128])
-            np.testing.assert_array_equal(w13s[2 * j], s1[j])
-            np.testing.assert_array_equal(w13s[2 * j + 1], s3[j])
-        np.testing.assert_array_equal(w2q, q2)
-        np.testing.assert_array_equal(w2s, s2)
-        r0, r1 = int(go_r[g]), int(go_r[g + 1])
-        rows = np.arange(r0, r1)
-        if token_sample is not None:
-            own = [int(sr_r[t, k]) for t in tokens for k in range(K) if idx_r[t, k] == g]
-            if g == E:
-                own = list(T * K + tokens)
-            if expert_check and g in expert_check:
-                # first and last rows of the group: the first and the ragged last M tile
-                own += list(range(r0, min(r0 + 16, r1))) + list(range(max(r1 - 16, r0), r1))
-            rows = np.array(sorted(set(own)), dtype=np.int64)
-        if rows.size == 0:
-            continue
-        zg = oracle.gemm_blockscaled(uq_r, us_r, q1, s1, a_rows=rt_r[rows])
-        zu = oracle.gemm_blockscaled(uq_r, us_r, q3, s3, a_rows=rt_r[rows])
-        h_r = oracle.swiglu(zg, zu)
+        if quant_check is None or g in quant_check:
+            say(f"  expert {g}: packed weights vs the oracle's quantiser")
+            _check_packed_expert(sh, g, w13q, w2q, w13s, w2s)
+            worst["quant_checked"] += 1
+        z_r = oracle.gemm_blockscaled(uq_r, us_r, w13q, w13s, a_rows=rt_r[rows])
+        h_r = oracle.swiglu(z_r[:, gate_cols], z_r[:, gate_cols + 128])
         h_g, hq_g, hs_g, y_g = (rows_of(k, rows) for k in ("h", "hq", "hs", "y"))
         worst["h"] = max(worst["h"], rowinf_rel(h_g, h_r))
         hq_r, hs_r = oracle.quant_1x128(h_r.astype(np.float32))
         worst["flips"] += check_codes_close(hq_g, hs_g, hq_r, hs_r, h_r, h_g)
-        y_r = oracle.gemm_blockscaled(hq_r, hs_r, q2, s2)
-        allow = flip_allowance(hq_g, hq_r, hs_r, deq_block(q2, s2))
+        y_r = oracle.gemm_blockscaled(hq_r, hs_r, w2q, w2s)
+        allow = flip_allowance(hq_g, hq_r, hs_r, w2q, w2s)
         worst["y"] = max(worst["y"], check_y(y_g, y_r, allow))
+        worst["rows"] += rows.size
+        worst["groups"] += 1
         for i, r in enumerate(rows):
             y_ref_rows[int(r)] = y_r[i]
             allow_rows[int(r)] = allow[i]
-    say(f"  h err {worst['h']:.3e}  y err {worst['y']:.3e}  h-code midpoint flips {worst['flips']}")
+    say(f"  {worst['rows']} rows of {worst['groups']} groups: h err {worst['h']:.3e}  y err {worst['y']:.3e}  "
+        f"h-code midpoint flips {worst['flips']}")
     assert worst["h"] <= TOL and worst["y"] <= TOL
     # ---- h' for the checked tokens
     ref = np.empty((len(tokens), d))
@@ -176,8 +194,9 @@ def check_layer(sh, u, e, b, packed, g_out, token_sample=None, expert_check=None
         ref[i] = v
         allow_t[i] = a
     err = check_y(rows_of("out", tokens), ref, allow_t)
-    say(f"  h' err {err:.3e}")
+    say(f"  h' err {err:.3e} over {len(tokens)} tokens")
     assert err <= TOL
+    worst["out"] = err
     return worst
 
 
@@ -212,13 +231,37 @@ def test_layer_tiny_quantisation_error_report():
     assert fro < 0.1
 
 
-def _sample_tokens(u_h, T, n_extra=0):
-    uf = np.abs((u_h.astype(np.uint32) << 16).view(np.float32))
-    return sorted({0, T - 1, int(uf.max(axis=1).argmax())} | set(range(1, 1 + n_extra)))
+def _sample_tokens(u_h, T, n_big=64):
+    """The first and last token and the n_big tokens with the largest
+    |u|_inf (the 0.1% x100 outliers sit there)."""
+    uf = np.abs((u_h.astype(np.uint32) << 16).view(np.float32)).max(axis=1)
+    big = np.argsort(-uf, kind="stable")[:n_big]
+    return sorted({0, T - 1} | set(int(t) for t in big))
+
+
+def _group_rows(go, rng):
+    """At least one GEMM row of every non-empty group: its last row (the
+    group's ragged last tile), its first row and one seeded row between."""
+    out = {}
+    for g in range(go.size - 1):
+        r0, r1 = int(go[g]), int(go[g + 1])
+        if r1 > r0:
+            out[g] = {r0, r1 - 1, int(rng.integers(r0, r1))}
+    return out
 
 
 @pytest.mark.parametrize("name", ["decode", "prefill"])
 def test_layer_full_size_sampled(name):
+    """The decode and prefill layers at full size, in the launch configuration
+    the benchmark times: routing, dispatch and quant(u) bit-exact on every
+    token; GEMM1/SwiGLU/requant and GEMM2 checked on the first, last and a
+    seeded row of every non-empty group (all 257) and on every row of the 64
+    largest-|u|_inf tokens plus the first and last token, whose outputs h' are
+    checked too.  The packed weights of the shared expert, the busiest and the
+    least-loaded routed expert and two seeded others are checked bit-exact
+    against the oracle's quantiser of their FP32 masters; every other
+    expert's GEMMs take the GPU's packed codes as the oracle's operands (a
+    stage boundary of the staged protocol)."""
     sh = workloads.SHAPES[name]
     say(f"layer {name}: inputs")
     u_c = workloads.activations(sh)
@@ -233,10 +276,15 @@ def test_layer_full_size_sampled(name):
     say(f"  load max/mean {cnt.max() / cnt.mean():.3f}")
     if name == "prefill":
         assert 3.5 < cnt.max() / cnt.mean() < 4.5
+    rng = np.random.default_rng(17)
     tokens = _sample_tokens(u16(u_c), sh.T)
-    busiest = int(cnt.argmax())
-    # the busiest expert's FFN is checked on every one of its rows
-    check_layer(sh, u, e, b, packed, g_out, token_sample=tokens, expert_check=[busiest])
+    used = np.nonzero(cnt)[0]
+    quant_check = {sh.E, int(cnt.argmax()), int(used[np.argmin(cnt[used])])} | \
+        set(int(x) for x in rng.choice(used, 2, replace=False))
+    worst = check_layer(sh, u, e, b, packed, g_out, token_sample=tokens,
+                        group_rows=_group_rows(np_(g_out["go"]), rng), quant_check=quant_check)
+    assert worst["groups"] == int((cnt > 0).sum()) + 1      # every non-empty group, and the shared one
+    assert worst["quant_checked"] == len(quant_check)
 
 
 @pytest.mark.parametrize("T", [128, 2048])

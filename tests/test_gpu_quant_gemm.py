@@ -382,3 +382,177 @@ def test_dense_full_size_sampled(K):
     err = rowinf_rel(np_(out[rows]), ref)
     say(f"  per-row rel err {err:.3e} over {len(rows)} rows")
     assert err <= TOL
+
+
+# ------------------------------------------------------------------ persistent multi-tile path
+def _pow2_operands(sizes, N, K, seed):
+    """Integer E4M3 codes (|v| <= 8) with power-of-two scales: 1x128 A scales
+    per row and slice and 128x128 B scales per group, block and slice, in
+    2^-2 .. 2^2.  Every per-slice product is an exact integer below 2^13 and
+    every scaled partial sum a multiple of 2^-4 below 2^19, so the FP32 result
+    is exact and must equal the oracle's FP64 value bit for bit; a wrong,
+    stale or misplaced scale changes it."""
+    rng = np.random.default_rng(seed)
+    G = len(sizes)
+    M = int(np.sum(sizes))
+    codes = oracle.e4m3_encode_array(np.arange(-8, 9, dtype=np.float32))   # codes of -8..8
+    qa = codes[rng.integers(0, 17, (M, K))]
+    qb = np.empty((G, N, K), np.uint8)
+    for gi in range(G):                 # group by group: no G x N x K index array
+        qb[gi] = codes[rng.integers(0, 17, (N, K))]
+    sa = np.ldexp(1.0, rng.integers(-2, 3, (M, K // 128))).astype(np.float32)
+    sb = np.ldexp(1.0, rng.integers(-2, 3, (G, N // 128, K // 128))).astype(np.float32)
+    return qa, sa, qb, sb
+
+
+def _zipf_sizes(n, total, rng):
+    w = 1.0 / (np.arange(1, n + 1) + 3.0) ** 1.1
+    s = np.floor(w / w.sum() * total).astype(np.int64)
+    s = s[rng.permutation(n)]
+    s[rng.integers(0, n, 2)] = 0                    # two empty groups
+    return s
+
+
+@pytest.mark.parametrize("kind", ["rows128", "rows32"])
+def test_gemm_multi_tile_exact_pow2_scales(kind):
+    """The persistent schedule over many more tiles than CUs (each block runs
+    several tiles, so the tile-to-tile hand-over -- the next tile's DMAs
+    overlapping this tile's epilogue, the per-tile B-scale table, the per-XCD
+    tile counters -- is exercised everywhere), with a gather and ragged,
+    Zipf-sized groups, compared element by element with the oracle.  rows128:
+    26 groups, ~40k rows (128-row tiles); rows32: 1500 groups of 0..60 rows
+    (32-row tiles)."""
+    rng = np.random.default_rng(7 if kind == "rows128" else 8)
+    N, K = 512, 384
+    if kind == "rows128":
+        sizes = _zipf_sizes(26, 40_000, rng)
+    else:
+        sizes = rng.integers(0, 61, 1500)
+    G = len(sizes)
+    go = _groups(sizes)
+    M = int(go[-1])
+    bm = 32 if M <= 64 * G else 128
+    n_tiles = int(np.sum((sizes + bm - 1) // bm)) * (N // 256)
+    say(f"gemm multi-tile {kind}: G={G} M={M} N={N} K={K}, {bm}-row tiles, {n_tiles} tiles")
+    assert (bm == 128) == (kind == "rows128") and n_tiles > 2 * 256
+    qa, sa, qb, sb = _pow2_operands(sizes, N, K, seed=M)
+    extra = 37
+    rows = rng.permutation(M + extra)[:M].astype(np.int32)           # gather from a larger A
+    qa_full = np.zeros((M + extra, K), np.uint8)
+    sa_full = np.ones((M + extra, K // 128), np.float32)
+    qa_full[rows], sa_full[rows] = qa, sa
+    args = (torch.from_numpy(qa_full).to(dev()), torch.from_numpy(sa_full).to(dev()),
+            torch.from_numpy(go).to(dev()), M, torch.from_numpy(qb).to(dev()), torch.from_numpy(sb).to(dev()))
+    rows_d = torch.from_numpy(rows).to(dev())
+    out = moe.grouped_gemm_fp8_blockscaled(*args, epi=moe.MOE_EPI_STORE_F32, a_row_index=rows_d)
+    torch.cuda.synchronize()
+    say("  oracle")
+    ref = np.zeros((M, N))
+    for gi in range(G):
+        r0, r1 = go[gi], go[gi + 1]
+        if r1 > r0:
+            ref[r0:r1] = oracle.gemm_blockscaled(qa_full, sa_full, qb[gi], sb[gi], a_rows=rows[r0:r1])
+    assert np.array_equal(ref.astype(np.float32).astype(np.float64), ref), "reference not exact in FP32"
+    got = np_(out)
+    bad = got != ref.astype(np.float32)
+    assert not bad.any(), f"{int(bad.sum())} of {bad.size} elements differ; first at {np.argwhere(bad)[0]}"
+    if kind != "rows128":
+        return
+    # the SwiGLU epilogue that keeps z: z exact, the fused h codes equal
+    # SwiGLU_F32 followed by the quantiser, h within the bound of the oracle's
+    # FP64 SwiGLU of the exact z, its codes per the midpoint rule
+    say("  SwiGLU epilogues")
+    hq, hs, z = moe.grouped_gemm_fp8_blockscaled(*args, epi=moe.MOE_EPI_SWIGLU_QUANT_Z, a_row_index=rows_d)
+    h = moe.grouped_gemm_fp8_blockscaled(*args, epi=moe.MOE_EPI_SWIGLU_F32, a_row_index=rows_d)
+    hq2, hs2 = moe.fp8_quant_1x128(h)
+    torch.cuda.synchronize()
+    zg = np_(z)
+    bad = zg != ref.astype(np.float32)
+    assert not bad.any(), f"z: {int(bad.sum())} elements differ; first at {np.argwhere(bad)[0]}"
+    np.testing.assert_array_equal(np_(hq), np_(hq2))
+    np.testing.assert_array_equal(np_(hs).view(np.uint32), np_(hs2).view(np.uint32))
+    gate_cols = np.concatenate([np.arange(256 * j, 256 * j + 128) for j in range(N // 256)])
+    h_ref = oracle.swiglu(ref[:, gate_cols], ref[:, gate_cols + 128])
+    assert rowinf_rel(np_(h), h_ref) <= TOL
+    hq_ref, hs_ref = oracle.quant_1x128(h_ref.astype(np.float32))
+    flips = check_codes_close(np_(hq), np_(hs), hq_ref, hs_ref, h_ref, np_(h))
+    say(f"  h-code midpoint flips: {flips} of {hq_ref.size}")
+
+
+# ------------------------------------------------------------------ the E4M3 encoder, exhaustively
+_E4M3_P = 0x43E00001          # the non-negative binary32 patterns +0.0 .. 448.0
+_E4M3_NAN = (1 << 23) - 1     # NaN payloads of one sign
+
+
+def _binary32_patterns(lo, hi):
+    """Positions [lo, hi) of the enumeration: +0 .. 448, then -0 .. -448, then
+    the positive NaNs, then the negative NaNs (uint32 bit patterns)."""
+    p = np.arange(lo, hi, dtype=np.int64)
+    out = np.empty(p.size, np.int64)
+    P, NN = _E4M3_P, _E4M3_NAN
+    m = p < P
+    out[m] = p[m]
+    m = (p >= P) & (p < 2 * P)
+    out[m] = (p[m] - P) | 0x80000000
+    m = (p >= 2 * P) & (p < 2 * P + NN)
+    out[m] = 0x7F800001 + (p[m] - 2 * P)
+    m = p >= 2 * P + NN
+    out[m] = 0xFF800001 + (p[m] - 2 * P - NN)
+    return out.astype(np.uint32)
+
+
+def test_quant_1x128_every_encoder_input():
+    """The quantiser's E4M3 step (gfx950's conversion instruction with the
+    library's clamp and NaN-sign handling) against the oracle's encoder on
+    every input the quantiser can give it.  Each 1x128 tile holds 448 and 127
+    test values, so amax = 448, inv = 1, scale = 1 and each code is the
+    encoding of the value itself: every binary32 pattern with |x| <= 448
+    (both zeros, the subnormals, every midpoint) and every NaN of either sign,
+    about 2.29e9 values in chunks.  Above 448 the encoder only ever sees a
+    tile maximum times its rounded inverse, which can round to 448.00003:
+    tiles with such maxima check the clamp."""
+    total = 2 * _E4M3_P + 2 * _E4M3_NAN
+    per_chunk = 127 * (1 << 21)
+    checked = 0
+    for c0 in range(0, total, per_chunk):
+        c1 = min(total, c0 + per_chunk)
+        n = c1 - c0
+        say(f"E4M3 encoder inputs {c0}..{c1} of {total}")
+        vals = _binary32_patterns(c0, c1).view(np.float32)
+        tiles = (n + 126) // 127
+        body = np.zeros(tiles * 127, np.float32)
+        body[:n] = vals
+        x = np.empty((tiles, 128), np.float32)
+        x[:, 0] = 448.0
+        x[:, 1:] = body.reshape(tiles, 127)
+        del body
+        q, sc = moe.fp8_quant_1x128(torch.from_numpy(x).to(dev()))
+        torch.cuda.synchronize()
+        assert np.all(np_(sc).view(np.uint32) == np.float32(1.0).view(np.uint32))
+        qh = np_(q)
+        del q, sc
+        assert np.all(qh[:, 0] == 0x7E)
+        got = qh[:, 1:].reshape(-1)[:n]
+        ref = oracle.e4m3_encode_array(vals)
+        bad = got != ref
+        if bad.any():
+            i = int(np.argmax(bad))
+            raise AssertionError(f"{int(bad.sum())} codes differ; first input bits 0x{vals.view(np.uint32)[i]:08x}: "
+                                 f"GPU 0x{got[i]:02x}, oracle 0x{ref[i]:02x}")
+        checked += n
+    assert checked == total
+    # the clamp: maxima a with fl32(a * fl32(448 / a)) = 448.00003, in tiles
+    # of +-a and values below a, against the oracle's quantiser
+    a = (np.float32(1.0) + np.arange(200_000, dtype=np.float32) * np.float32(1e-5)).astype(np.float32)
+    a = np.unique(a)
+    a = a[(a * (np.float32(448.0) / a).astype(np.float32)).astype(np.float32) > np.float32(448.0)][:4096]
+    rng = np.random.default_rng(3)
+    x = (rng.uniform(-1, 1, (a.size, 128)).astype(np.float32) * a[:, None]).astype(np.float32)
+    x[:, 0], x[:, 1] = a, -a
+    say(f"E4M3 clamp tiles: {a.size}")
+    q, sc = moe.fp8_quant_1x128(torch.from_numpy(x).to(dev()))
+    torch.cuda.synchronize()
+    q_ref, sc_ref = oracle.quant_1x128(x)
+    np.testing.assert_array_equal(np_(sc).view(np.uint32), sc_ref.view(np.uint32))
+    np.testing.assert_array_equal(np_(q), q_ref)
+    assert np.all(q_ref[:, 0] == 0x7E) and np.all(q_ref[:, 1] == 0xFE)

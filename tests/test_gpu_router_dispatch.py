@@ -150,6 +150,48 @@ def test_dispatch_all_tokens_one_expert():
     np.testing.assert_array_equal(np_(slot_row), sr_ref)
 
 
+@pytest.mark.parametrize("T,E,K,shared", [(3000, 256, 8, True), (777, 40, 6, False), (64, 16, 16, True)])
+def test_dispatch_status_word(T, E, K, shared):
+    """The debug status word: 0 on every dispatch result, and each broken
+    invariant (planted by editing the arrays with torch, never by a kernel)
+    raises its own bit; out-of-range slots and tokens are reported, not
+    followed."""
+    say(f"dispatch status word T={T} E={E} K={K} shared={shared}")
+    bits = moe.MOE_CHECK_BITS
+    rng = np.random.default_rng(T + E)
+    idx = torch.from_numpy(np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)).to(dev())
+    count, go, row_token, slot_row = moe.moe_dispatch(idx, E, shared)
+
+    def word(c=count, g=go, rt=row_token, sr=slot_row, full=True):
+        st = moe.moe_dispatch_check(c, g, T, K, *((idx, rt, sr) if full else (None, None, None)))
+        torch.cuda.synchronize()
+        return int(np_(st)[0]) & 0xFFFFFFFF
+
+    assert word() == 0 and word(full=False) == 0
+    c = count.clone(); c[3] += 1
+    assert word(c=c) == bits["count_sum"] | bits["count_ne_offsets"]
+    c = count.clone(); c[0] = -c[0] - 1
+    assert word(c=c) & bits["negative_count"]
+    g = go.clone(); g[1], g[2] = go[2].item() + 1, go[1].item()
+    w = word(g=g, full=False)
+    assert w & bits["offsets_not_monotone"] and w & bits["count_ne_offsets"]
+    g = go.clone(); g[0] = 1
+    assert word(g=g, full=False) & bits["first_offset"]
+    g = go.clone(); g[E] += 1
+    assert word(g=g, full=False) & bits["routed_total"]
+    sr = slot_row.clone(); sr[5, 0] = -7
+    assert word(sr=sr) == bits["slot_row"]
+    sr = slot_row.clone(); sr[T - 1, K - 1] = T * (K + 1) + 1000        # past every row
+    assert word(sr=sr) == bits["slot_row"]
+    sr = slot_row.clone(); sr[2, 0], sr[2, 1] = slot_row[2, 1].item(), slot_row[2, 0].item()
+    assert word(sr=sr) == bits["slot_row"]
+    if shared:
+        rt = row_token.clone(); rt[T * K + 2] = 0
+        assert word(rt=rt) == bits["shared_rows"]
+        g = go.clone(); g[E + 1] -= 1
+        assert word(g=g, full=False) & bits["shared_group"]
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_permute_rows_and_unpermute(dtype):
     T, E, K, d = 333, 32, 4, 384
