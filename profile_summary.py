@@ -71,16 +71,32 @@ def main():
     ap.add_argument("--kernel", action="append", default=[], help="KEY=substring of the kernel name")
     ap.add_argument("--command", action="append", default=[], help="command lines to record")
     ap.add_argument("--note", default="")
+    ap.add_argument("--step", action="append", default=[],
+                    help="substring of a kernel that belongs to the benchmark's timed step; with any given, "
+                         "the other kernels of the process (input generation, weight preparation, the copy "
+                         "calibration, error checks) are listed in a table of their own")
     a = ap.parse_args()
     lines = [f"# {a.name}", ""]
     if a.note:
         lines += [a.note, ""]
     lines += ["Commands (run from the repository root on an MI355X):", ""]
     lines += [f"    {c}" for c in a.command] + [""]
-    lines += ["## Kernel durations (rocprofv3 --kernel-trace --stats)", "",
-              "| kernel | calls | avg us | total ms | % |", "|---|---|---|---|---|"]
-    for n, c, avg, tot, pct in sorted(kernel_stats(a.stats), key=lambda x: -x[3]):
+    stats = sorted(kernel_stats(a.stats), key=lambda x: -x[3])
+    in_step = [r for r in stats if not a.step or any(sub in r[0] for sub in a.step)]
+    other = [r for r in stats if a.step and not any(sub in r[0] for sub in a.step)]
+    head = ["| kernel | calls | avg us | total ms | % |", "|---|---|---|---|---|"]
+    lines += ["## Kernel durations (rocprofv3 --kernel-trace --stats)", ""]
+    if a.step:
+        lines += ["Kernels of the timed step (calls include the warm-up steps):", ""]
+    lines += head
+    for n, c, avg, tot, pct in in_step:
         lines.append(f"| {n} | {c} | {avg:.1f} | {tot:.2f} | {pct:.1f} |")
+    if other:
+        lines += ["", "Other kernels of the same process, outside the timed step (input and weight "
+                  "generation, offline weight quantisation, the copy calibration and copy ceiling, "
+                  "error checks):", ""] + head
+        for n, c, avg, tot, pct in other:
+            lines.append(f"| {n} | {c} | {avg:.1f} | {tot:.2f} | {pct:.1f} |")
     if a.fetch and a.write:
         fetch, write = counter(a.fetch, "FETCH_SIZE"), counter(a.write, "WRITE_SIZE")
         copy_key = next(k for k in fetch if "permute_rows" in k)

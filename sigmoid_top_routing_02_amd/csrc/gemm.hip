@@ -762,6 +762,524 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
 #undef MOE_STAGE_BARRIER
 }
 
+// ============================================================================
+// The ring kernel: the tile computation above (non-K-grouped tiles), with one
+// DMA ring that runs on across tiles.  Each block takes a static, XCD-aware
+// share of the tile sequence (the same contiguous share per XCD as above, its
+// tiles dealt round-robin to the XCD's blocks, so the 32 blocks of an XCD
+// start and finish their tiles together and share A rows and B columns in
+// the XCD's L2).  The next tile's first two slices are fetched during the
+// last two slices of the current one, so a tile boundary costs no pipeline
+// restart; the epilogues store straight from registers (the stores the
+// barriers count are issued by every lane, and a lane without an output
+// writes out of the buffer's range, which drops it), and the waits at the two
+// barriers after an epilogue count those stores.  The next tile's record comes by one scalar load per tile; its
+// gathered row indices and B-scale table reach LDS through the spare
+// per-stage DMA slot, ahead of their use.  Everything per tile is set up once
+// per tile, so a slice's memory phase issues little beyond its DMAs and LDS
+// reads (a SIMD issues a few scalar instructions per cycle at most, and the
+// memory phase must stay shorter than the other wave's matrix phase).
+//
+// The three stages are one LDS object addressed at run time (a tile may start
+// on any stage), so the DMAs are issued from inline asm: the compiler adds no
+// waits of its own for them, and every wait is the explicit one in a barrier.
+// Null DMAs (out-of-range offsets) still write zeros to their LDS slots; each
+// one targets a slot nothing reads at that time.
+// ============================================================================
+constexpr int RING_MIN_SLICES = 4;           // the next tile's rows are fetched 4 slices ahead
+constexpr int RING_SA_BYTES = 64 * NWAVES * 4;
+constexpr int RING_A = 0, RING_B = A_MAX_BYTES, RING_SA = A_MAX_BYTES + B_BYTES;
+constexpr int RING_STAGE = A_MAX_BYTES + B_BYTES + RING_SA_BYTES;   // 50 KiB
+static_assert(RING_STAGE % 1024 == 0, "stage bases keep the swizzle's 1 KiB alignment");
+__shared__ __attribute__((aligned(1024))) char g_ring[3 * RING_STAGE];
+__shared__ __attribute__((aligned(16))) float g_btab[2][2 * MAX_SLICES];   // B scales of a tile, by tile parity
+__shared__ __attribute__((aligned(16))) int32_t g_rowbuf[128];             // the next tile's gathered A rows
+__shared__ __attribute__((aligned(16))) float g_rmax[512];                 // [WAVES_N][BM] row maxima of h
+
+// Ring tile shape: 128 rows, 2 x 4 waves of 64 x 64 (one row group per half
+// of the workgroup, so the SwiGLU row maxima are exchanged inside one
+// ping-pong group).  Every epilogue puts B first in the MFMA: a lane's four
+// results are four consecutive columns of one row, stored as one 16-byte (or
+// 4-code) piece.
+template <int BM_>
+struct RCfg {
+    static_assert(BM_ == 128, "the ring kernel runs 128-row tiles");
+    static constexpr int BM = BM_;
+    static constexpr int WAVES_M = 2, WAVES_N = 4;
+    static constexpr int WROWS = BM_ / 2;
+    static constexpr int MI = WROWS / 16;
+    static constexpr int WN_COLS = BN / WAVES_N;           // 64
+    static constexpr int NI = WN_COLS / 16;                // 4
+    static constexpr int A_INSTR = BM_ * BK / 1024;
+    static constexpr int A_COPIES = A_INSTR >= NWAVES ? 1 : NWAVES / A_INSTR;
+    static constexpr int A_DMA = A_INSTR * A_COPIES / NWAVES;
+    static constexpr int B_DMA = B_BYTES / 1024 / NWAVES;
+    static constexpr int D = A_DMA + B_DMA + 1;            // + the per-wave dword slot
+};
+
+typedef int ring_v4i __attribute__((ext_vector_type(4)));
+typedef unsigned ring_v4u __attribute__((ext_vector_type(4)));
+
+// buffer descriptor in SGPRs (stride 0, byte-granular range check)
+__device__ __forceinline__ ring_v4i ring_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    ring_v4i r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));
+    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    r[3] = 0x00020000;
+    return r;
+}
+// the value of lane 0 in an SGPR: inline asm's "s" operands must be wave-uniform
+// values the compiler can see as such
+__device__ __forceinline__ uint32_t uni(uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)x); }
+__device__ __forceinline__ ring_v4i uni(ring_v4i r) {
+    ring_v4i o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = __builtin_amdgcn_readfirstlane(r[i]);
+    return o;
+}
+// global -> LDS DMA: lane l's bytes land at lds + l * size (lds wave-uniform)
+__device__ __forceinline__ void ring_dma16(ring_v4i r_, uint32_t voff, uint32_t soff_, uint32_t lds_) {
+    const ring_v4i r = uni(r_);
+    const uint32_t soff = uni(soff_), lds = uni(lds_);
+    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :: "v"(voff), "s"(r), "s"(soff), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void ring_dma4(ring_v4i r_, uint32_t voff, uint32_t soff_, uint32_t lds_) {
+    const ring_v4i r = uni(r_);
+    const uint32_t soff = uni(soff_), lds = uni(lds_);
+    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dword %0, %1, %2 offen lds"
+                 :: "v"(voff), "s"(r), "s"(soff), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)reinterpret_cast<uintptr_t>(p);
+}
+
+template <int EPI, int BM_>
+__global__ __launch_bounds__(NT) void grouped_gemm_ring_kernel(GemmArgs p) {
+    using C = RCfg<BM_>;
+    constexpr int BM = C::BM, MI = C::MI, NI = C::NI, WAVES_N = C::WAVES_N;
+    constexpr int WN_COLS = C::WN_COLS, WROWS = C::WROWS, A_DMA = C::A_DMA, B_DMA = C::B_DMA;
+    constexpr int D = C::D;
+    constexpr int HALF = NI / 2;
+    constexpr int HC = WN_COLS / 2;                        // h columns per wave (SwiGLU)
+    constexpr bool QUANT = (EPI == EPI_SWIGLU_QUANT || EPI == EPI_SWIGLU_QUANT_Z);
+    // stores every wave issues per tile, unconditionally (see the epilogue).
+    // A wave may issue more (the row scales from the waves of the first
+    // column group, FP32 h when requested): more stores than counted only
+    // make the waits below stricter, never looser.
+    constexpr int S = EPI == EPI_STORE_F32 ? MI * NI
+                    : EPI == EPI_SWIGLU_QUANT_Z ? MI * HALF + MI * NI
+                    : MI * HALF;
+    static_assert(D + S <= 63, "vmcnt holds 6 bits");
+    static_assert(BM * WAVES_N <= 512, "row-maximum buffer");
+    const int K = p.K, ns = K / BK;                        // ns >= RING_MIN_SLICES (host-checked)
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    const int kb = lane >> 4;
+    const int lr = lane & 15;
+    const bool lead = wave < NWAVES / 2;
+
+    // ---- static schedule: XCD x owns tiles [x*share, (x+1)*share) of the
+    // sequence; its blocks take every nbx-th of them
+    const int n_tiles = (p.N + BN - 1) / BN;
+    const int total = __builtin_amdgcn_readfirstlane(p.tile_start[p.G]) * n_tiles;
+    const int xcd = blockIdx.x & 7, jx = blockIdx.x >> 3, nbx = gridDim.x >> 3;
+    const int share = (total + 7) >> 3;
+    const int t_first = xcd * share + jx;
+    const int t_end = min(total, xcd * share + share);
+    if (t_first >= t_end) return;
+    auto tile_no = [&](int k) {            // the k-th tile of this block, -1 past its share
+        const int t = t_first + k * nbx;
+        return t < t_end ? t : -1;
+    };
+
+    struct Tile { int g, m0, rows, n0; };
+    const int m_total = (int)(p.sa_stride / 4u);
+    // a record with every field clamped into range: whatever a record holds,
+    // the DMA and store descriptors built from it stay inside their buffers
+    auto clamp_tile = [&](int g, int m0, int rows, int n0) {
+        Tile T;
+        T.g = __builtin_amdgcn_readfirstlane(min(max(g, 0), p.G - 1));
+        T.m0 = __builtin_amdgcn_readfirstlane(min(max(m0, 0), m_total - 1));
+        T.rows = __builtin_amdgcn_readfirstlane(min(max(rows, 1), min(BM, m_total - T.m0)));
+        T.n0 = __builtin_amdgcn_readfirstlane(min(max(n0, 0), p.N - 1));
+        return T;
+    };
+    // the record of tile t, by one scalar load (waited for in the same asm block)
+    auto load_tile = [&](int t) {
+        const int4* ptr = p.tiles + t;
+        int4 v;
+        asm volatile("s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr) : "memory");
+        return clamp_tile(v.x, v.y, v.z, v.w);
+    };
+
+    // ---- descriptors and LDS addresses (wave-uniform)
+    const ring_v4i a_rsrc = ring_rsrc(p.a_q, 0xFFFFFFFFu);
+    const ring_v4i sa_rsrc = ring_rsrc(p.a_sT, p.sa_stride * (uint32_t)ns);   // rows past M_total read 0
+    const int nblk = p.N / 128;
+    const uint32_t ring0 = lds_addr(g_ring);
+    const uint32_t ring_last = ring0 + 2 * RING_STAGE;
+    constexpr uint32_t OOR = 0x80000000u;  // an offset past every descriptor's range
+    // the per-stage dword slot of each wave: A scales (waves below BM/64,
+    // every slice), the next tile's B-scale table (waves 2-5, at its slice
+    // ns-2), the next tile's gathered rows (waves 6-7, at slice ns-4), or
+    // nothing: an inactive slot DMAs out of range into the wave's unused
+    // scale slot of the stage being written
+    const bool x_ascale = wave * 64 < BM;
+    const bool x_btab = !x_ascale && wave >= 2 && wave <= 5;
+    const bool x_rows = !x_ascale && wave >= 6 && p.a_rows != nullptr;
+    const ring_v4i x_rsrc = uni(x_ascale ? sa_rsrc
+                                : x_btab ? ring_rsrc(p.b_s, (uint32_t)p.G * (uint32_t)nblk * (uint32_t)ns * 4u)
+                                : ring_rsrc(p.a_rows ? (const void*)p.a_rows : (const void*)p.a_q,
+                                            p.a_rows ? p.sa_stride : 0u));
+    uint32_t x_voff = OOR, x_dst = 0;
+    int x_phase = -1;                      // the slice whose memory phase issues this wave's slot DMA
+    // slot parameters for the next tile nx (par: its B-table buffer)
+    auto set_slot = [&](const Tile& nx, bool has_nx, int par) {
+        x_phase = -1;
+        if (x_btab) {
+            const int q = wave - 2;
+            const int blk = min(nx.n0 / 128 + (q >> 1), nblk - 1), sl = (q & 1) * 64 + lane;
+            x_voff = sl < ns ? (uint32_t)((nx.g * nblk + blk) * ns + sl) * 4u : OOR;
+            x_dst = lds_addr(&g_btab[par][(q >> 1) * MAX_SLICES + (q & 1) * 64]);
+            x_phase = has_nx ? ns - 2 : -1;
+        } else if (x_rows) {
+            const int r = (wave - 6) * 64 + lane;
+            x_voff = r < BM ? (uint32_t)(nx.m0 + r) * 4u : OOR;
+            x_dst = lds_addr(&g_rowbuf[(wave - 6) * 64]);
+            x_phase = has_nx ? ns - 4 : -1;
+        }
+        x_phase = __builtin_amdgcn_readfirstlane(x_phase);
+        x_dst = uni(x_dst);
+    };
+
+    // ---- the fetch cursor: the tile whose slices the DMAs read (the current
+    // one, then from its slice ns-2 on the next), its per-lane sources, and
+    // the slice issued next
+    uint32_t fa_off[A_DMA], fb_off[2], f_sa_off;
+    ring_v4i fb_rsrc;
+    int fslice;
+    auto set_fetch = [&](const Tile& T, bool rows_in_lds) {
+#pragma unroll
+        for (int i = 0; i < A_DMA; ++i) {
+            const int r = ((wave * A_DMA + i) % C::A_INSTR) * 8 + (lane >> 3);
+            const int rr = min(r, T.rows - 1);
+            uint32_t am;
+            if (!p.a_rows) am = (uint32_t)(T.m0 + rr);
+            else if (rows_in_lds) am = (uint32_t)g_rowbuf[rr];   // indices of rows of a_q, or 0
+            else am = (uint32_t)p.a_rows[T.m0 + rr];
+            fa_off[i] = am * (uint32_t)K + ((lane & 7) ^ swz(r)) * 16;
+        }
+#pragma unroll
+        for (int par = 0; par < 2; ++par) {
+            const int r = (wave * B_DMA + par) * 8 + (lane >> 3);
+            fb_off[par] = (uint32_t)(T.n0 + r) * (uint32_t)K + ((lane & 7) ^ swz(r)) * 16;   // rows past N read 0
+        }
+        f_sa_off = (uint32_t)(T.m0 + wave * 64 + lane) * 4u;
+        fb_rsrc = uni(ring_rsrc(p.b_q + (int64_t)T.g * p.N * K, (uint32_t)p.N * (uint32_t)K));
+    };
+    // the DMAs of the cursor's slice into the stage at LDS address dst
+    auto issue = [&](uint32_t dst) {
+        const uint32_t koff = uni((uint32_t)fslice * BK);
+#pragma unroll
+        for (int i = 0; i < A_DMA; ++i) ring_dma16(a_rsrc, fa_off[i], koff, dst + RING_A + (wave * A_DMA + i) * 1024);
+#pragma unroll
+        for (int i = 0; i < B_DMA; ++i)
+            ring_dma16(fb_rsrc, fb_off[i & 1] + (uint32_t)((i & ~1) * 8) * (uint32_t)K, koff,
+                                 dst + RING_B + (wave * B_DMA + i) * 1024);
+    };
+    auto issue_slot = [&](uint32_t dst, int s) {
+        if (x_ascale) {
+            ring_dma4(x_rsrc, f_sa_off, uni((uint32_t)fslice * p.sa_stride), dst + RING_SA + wave * 256);
+        } else {
+            const bool on = s == x_phase;
+            ring_dma4(x_rsrc, on ? x_voff : OOR, 0u, uni(on ? x_dst : dst + RING_SA + wave * 256));
+        }
+    };
+
+    // ---- fragment offsets (as in grouped_gemm_kernel; B first)
+    const uint32_t sw0 = (uint32_t)(((2 * kb) ^ swz(lr)) << 4);
+    const uint32_t sw1 = (uint32_t)(((2 * kb + 1) ^ swz(lr)) << 4);
+    const uint32_t a_lo0 = (uint32_t)(wm * WROWS + lr) * 128 + sw0;
+    const uint32_t a_lo1 = (uint32_t)(wm * WROWS + lr) * 128 + sw1;
+    const uint32_t bcol = (uint32_t)(ncol<EPI, C>(wn, 0) - ncol<EPI, C>(0, 0) + lr);
+    const uint32_t b_lo0 = bcol * 128 + sw0;
+    const uint32_t b_lo1 = bcol * 128 + sw1;
+    const int sa_row = wm * WROWS + lr;
+    int sbrow0, sbrow1;
+    if constexpr (EPI == EPI_STORE_F32) {
+        sbrow0 = (wn * WN_COLS) / 128;
+        sbrow1 = sbrow0;
+    } else {
+        sbrow0 = 0;
+        sbrow1 = 1;
+    }
+
+    v4f acc[MI][NI];
+    v8i bfr[NI], afr[MI];
+    float sav[MI];
+    float sb0 = 0.f, sb1 = 0.f;
+    auto mem_reads = [&](const char* stage, int s, int par) {
+        const char* At = stage + RING_A;
+        const char* Bt = stage + RING_B;
+        const float* SAt = reinterpret_cast<const float*>(stage + RING_SA);
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) bfr[ni] = frag(Bt, ncol<EPI, C>(0, ni) * 128, b_lo0, b_lo1);
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) {
+            afr[mi] = frag(At, mi * 16 * 128, a_lo0, a_lo1);
+            sav[mi] = SAt[sa_row + mi * 16];
+        }
+        sb0 = g_btab[par][sbrow0 * MAX_SLICES + s];
+        sb1 = g_btab[par][sbrow1 * MAX_SLICES + s];
+    };
+    // MFMA (mi, ni) into a fresh accumulator, then the four scale FMAs of
+    // (mi-1, ni), whose partial finished four MFMAs earlier
+    auto mat_phase = [&]() {
+        auto fma4 = [&](const v4f& part, int mi, int ni, float c0, float c1) {
+            const float c = ((EPI != EPI_STORE_F32) && ni >= HALF) ? c1 : c0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[mi][ni][j] = __builtin_fmaf(part[j], c, acc[mi][ni][j]);
+        };
+        v4f prev[NI];
+        float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) {
+            float q0 = 0.f, q1 = 0.f;
+            v4f cur[NI];
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni) {
+                cur[ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    bfr[ni], afr[mi], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+                if (mi > 0) fma4(prev[ni], mi - 1, ni, p0, p1);
+                if (ni == NI - 1) {
+                    q0 = sav[mi] * sb0;
+                    q1 = (EPI != EPI_STORE_F32) ? sav[mi] * sb1 : 0.f;
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni) prev[ni] = cur[ni];
+            p0 = q0;
+            p1 = q1;
+        }
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) fma4(prev[ni], MI - 1, ni, p0, p1);
+    };
+
+    // ---- barriers.  Group 1 (waves 4-7) runs one barrier behind group 0, so
+    // each hardware barrier is one group's "memory" barrier and the other's
+    // "matrix" barrier; the waits below follow from each wave's own stream of
+    // vector-memory ops (D DMAs per memory phase, S stores per epilogue).
+    //   barrier_mem (before reading slice s): slice s landed; the most recent
+    //     ops are the D DMAs of slice s+1, plus, for the first two slices
+    //     after an epilogue (pend > 0), that epilogue's S stores: vmcnt(D) or
+    //     vmcnt(D + S).
+    //   barrier_mat: group 0 needs nothing (group 1 then reads a slice that
+    //     the previous barrier saw land); group 1's coincides with group 0's
+    //     next memory barrier, so it waits for slice s+1: vmcnt(D), or
+    //     vmcnt(D + S) at the first slice after an epilogue (pend == 2), or
+    //     nothing at the last slice of a SwiGLU-quant tile (the row-maximum
+    //     barrier that follows takes that wait).
+    auto barrier_mem = [&](int pend) {
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_cmp_eq_u32 %0, 0\n\ts_cbranch_scc1 1f\n\ts_waitcnt vmcnt(%1)\n\ts_branch 2f\n"
+                     "1:\n\ts_waitcnt vmcnt(%2)\n2:\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier"
+                     :: "s"(pend), "n"(D + S), "n"(D) : "memory", "scc");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto barrier_sel = [&](int sel) {      // 0: no vector-memory wait, 1: vmcnt(D + S), 2: vmcnt(D)
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_cmp_eq_u32 %0, 2\n\ts_cbranch_scc1 3f\n\ts_cmp_eq_u32 %0, 1\n\ts_cbranch_scc1 4f\n"
+                     "\ts_branch 5f\n3:\n\ts_waitcnt vmcnt(%1)\n\ts_branch 5f\n4:\n\ts_waitcnt vmcnt(%2)\n"
+                     "5:\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier"
+                     :: "s"(sel), "n"(D), "n"(D + S) : "memory", "scc");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto plain_barrier = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // ---- epilogues: the S counted stores are issued by every lane of every
+    // wave; a lane without an output (row past the tile, column past N) gets
+    // an offset past its buffer's range, so the hardware drops it.
+    auto store_b128 = [&](const v4f& v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(ring_v4u, v), r, (int)off, 0, 0);
+    };
+    // off if ok, else an offset past any range below 2^31 (every output
+    // descriptor here covers less): bitwise, so no lane-dependent branch
+    // splits a store in two
+    auto keep = [](uint32_t off, bool ok) -> uint32_t { return off | (OOR & (0u - (uint32_t)!ok)); };
+    auto epilogue = [&](const Tile& T) {
+        const int I = p.N / 2;
+        const int h0 = T.n0 / 2;
+        if constexpr (EPI == EPI_STORE_F32) {
+            const auto orsrc = make_rsrc(p.out + (int64_t)T.m0 * p.N, (uint32_t)T.rows * (uint32_t)p.N * 4u);
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < NI; ++ni) {
+                    const int r = wm * WROWS + mi * 16 + lr;
+                    const int c = T.n0 + ncol<EPI, C>(wn, ni) + 4 * kb;
+                    store_b128(acc[mi][ni], orsrc,
+                               keep(((uint32_t)r * (uint32_t)p.N + (uint32_t)c) * 4u, (r < T.rows) & (c < p.N)));
+                }
+        } else {
+            float h[MI][HALF][4];
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < HALF; ++ni)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) h[mi][ni][j] = silu(acc[mi][ni][j]) * acc[mi][ni + HALF][j];
+            // h columns h0 + wn*HC + ni*16 + 4*kb .. +3 of row m0 + r
+            auto h_off = [&](int r, int ni, uint32_t elem) -> uint32_t {
+                return keep(((uint32_t)r * (uint32_t)I + (uint32_t)(h0 + wn * HC + ni * 16 + 4 * kb)) * elem, r < T.rows);
+            };
+            if (EPI == EPI_SWIGLU_F32 || (EPI == EPI_SWIGLU_QUANT && p.out)) {
+                // FP32 h (required for SWIGLU_F32, optional for SWIGLU_QUANT;
+                // counted in S only for SWIGLU_F32)
+                const auto hrsrc = make_rsrc(p.out + (int64_t)T.m0 * I, (uint32_t)T.rows * (uint32_t)I * 4u);
+#pragma unroll
+                for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+                    for (int ni = 0; ni < HALF; ++ni)
+                        store_b128(v4f{h[mi][ni][0], h[mi][ni][1], h[mi][ni][2], h[mi][ni][3]}, hrsrc,
+                                   h_off(wm * WROWS + mi * 16 + lr, ni, 4u));
+            }
+            if constexpr (QUANT) {
+                // row maxima over the tile's 128 h columns: lanes lr, lr+16,
+                // lr+32, lr+48 hold one row; then across the N-waves of the
+                // row group through LDS
+#pragma unroll
+                for (int mi = 0; mi < MI; ++mi) {
+                    float m = 0.0f;
+#pragma unroll
+                    for (int ni = 0; ni < HALF; ++ni)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const float a = __builtin_fabsf(h[mi][ni][j]);
+                            m = a > m ? a : m;
+                        }
+#pragma unroll
+                    for (int o = 16; o < 64; o <<= 1) {
+                        const float other = __shfl_xor(m, o, 64);
+                        m = other > m ? other : m;
+                    }
+                    if (kb == 0) g_rmax[wn * BM + wm * WROWS + mi * 16 + lr] = m;
+                }
+                barrier_sel(lead ? 0 : 2);      // group 1: the next tile's slice 0 (group 0 reads it next)
+                const auto qrsrc = make_rsrc(p.out_q + (int64_t)T.m0 * I, (uint32_t)T.rows * (uint32_t)I);
+                const auto srsrc = make_rsrc(p.out_s + (int64_t)T.m0 * (I / 128), (uint32_t)T.rows * (uint32_t)(I / 128) * 4u);
+#pragma unroll
+                for (int mi = 0; mi < MI; ++mi) {
+                    const int r = wm * WROWS + mi * 16 + lr;
+                    float amax = g_rmax[wm * WROWS + mi * 16 + lr];
+#pragma unroll
+                    for (int w = 1; w < WAVES_N; ++w) {
+                        const float a = g_rmax[w * BM + wm * WROWS + mi * 16 + lr];
+                        amax = a > amax ? a : amax;
+                    }
+                    float inv, sc;
+                    tile_scale(amax, inv, sc);
+#pragma unroll
+                    for (int ni = 0; ni < HALF; ++ni) {
+                        const uint32_t w4 = e4m3_encode4(h[mi][ni][0] * inv, h[mi][ni][1] * inv,
+                                                         h[mi][ni][2] * inv, h[mi][ni][3] * inv);
+                        __builtin_amdgcn_raw_buffer_store_b32(w4, qrsrc, (int)h_off(r, ni, 1u), 0, 0);
+                    }
+                    if (wn == 0) {                 // one scale per row, from the first column group
+                        const uint32_t soff = keep(((uint32_t)r * (uint32_t)(I / 128) + (uint32_t)(h0 / 128)) * 4u,
+                                                   (kb == 0) & (r < T.rows));
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sc), srsrc, (int)soff, 0, 0);
+                    }
+                }
+            }
+            if constexpr (EPI == EPI_SWIGLU_QUANT_Z) {
+                // the GEMM output z itself (gate and up columns in B's row order)
+                const auto zrsrc = make_rsrc(p.out + (int64_t)T.m0 * p.N, (uint32_t)T.rows * (uint32_t)p.N * 4u);
+#pragma unroll
+                for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+                    for (int ni = 0; ni < NI; ++ni) {
+                        const int r = wm * WROWS + mi * 16 + lr;
+                        store_b128(acc[mi][ni], zrsrc,
+                                   keep(((uint32_t)r * (uint32_t)p.N + (uint32_t)(T.n0 + ncol<EPI, C>(wn, ni) + 4 * kb)) * 4u,
+                                        r < T.rows));
+                    }
+            }
+        }
+    };
+
+    // ---- prologue: tile 0's record, rows and B scales read directly, slices
+    // 0 and 1 of tile 0 issued, the next tile's record loaded; everything
+    // drained before the ping-pong starts
+    int k = 0;
+    Tile cur = load_tile(t_first);
+    int t_nx = tile_no(1);
+    Tile nx = cur;
+    if (t_nx >= 0) nx = load_tile(t_nx);
+    for (int i = tid; i < 2 * MAX_SLICES; i += NT) {
+        const int blk = min(cur.n0 / 128 + i / MAX_SLICES, nblk - 1), sl = i % MAX_SLICES;
+        g_btab[0][i] = sl < ns ? p.b_s[((int64_t)cur.g * nblk + blk) * ns + sl] : 0.0f;
+    }
+    set_fetch(cur, false);
+    for (fslice = 0; fslice < 2; ++fslice) {
+        const uint32_t dst = ring0 + (uint32_t)fslice * RING_STAGE;
+        issue(dst);
+        issue_slot(dst, -2);               // A scales; every other slot is inactive here
+    }
+    set_slot(nx, t_nx >= 0, 1);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (!lead) plain_barrier();            // group 1: one barrier behind from here on
+
+    uint32_t rd = ring0, wr = ring_last;   // LDS stages read and written by the current memory phase
+    int pend = 0;                          // slices left whose waits must count an epilogue's stores
+    for (;;) {
+        const bool has_nx = t_nx >= 0;
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < ns; ++s) {
+            barrier_mem(pend);
+            mem_reads(g_ring + (rd - ring0), s, k & 1);
+            if (s == ns - 2) {
+                // the cursor moves to the next tile (its gathered rows landed
+                // with slice ns-2); past the last tile it re-reads this tile's
+                // first slices into stages nothing reads again
+                if (has_nx) set_fetch(nx, true);
+                fslice = 0;
+            }
+            issue(wr);
+            issue_slot(wr, s);
+            ++fslice;
+            barrier_sel(lead ? 0 : pend == 2 ? 1 : (QUANT && s == ns - 1) ? 0 : 2);
+            mat_phase();
+            rd = rd == ring_last ? ring0 : rd + RING_STAGE;
+            wr = wr == ring_last ? ring0 : wr + RING_STAGE;
+            pend = pend > 0 ? pend - 1 : 0;
+        }
+        epilogue(cur);
+        if (!has_nx) break;
+        ++k;
+        cur = nx;
+        t_nx = tile_no(k + 1);
+        if (t_nx >= 0) nx = load_tile(t_nx);
+        set_slot(nx, t_nx >= 0, (k + 1) & 1);
+        pend = 2;
+    }
+    if (lead) plain_barrier();             // group 0: catch up
+    // every DMA lands before the workgroup's LDS is released
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+}
+
 // tile_start[g] = sum_{g' < g} ceil(rows_g' / BM), for g = 0..G; zeroes the
 // 8 per-XCD tile counters that follow it.
 __global__ __launch_bounds__(256) void gemm_tile_map_kernel(const int32_t* __restrict__ go,
@@ -987,20 +1505,35 @@ hipError_t launch_grouped_gemm(const uint8_t* a_q, const float* a_s, const int32
     const int64_t persistent = ((int64_t)cu_count_for_current_device() + 7) / 8 * 8;
     const int64_t needed = (blocks + 7) / 8 * 8;
     dim3 grid((unsigned)(needed < persistent ? needed : persistent));
-#define MOE_LAUNCH(E, B) hipLaunchKernelGGL((grouped_gemm_kernel<E, B>), grid, dim3(NT), 0, st, p)
+#define MOE_LAUNCH(K, E, B) hipLaunchKernelGGL((K<E, B>), grid, dim3(NT), 0, st, p)
+    // The ring kernel (no pipeline restart between tiles) for 128-row tiles of
+    // at most 16 slices, where that restart is a large share of a tile: it
+    // measured 5% faster on the expert down-projection (K = 2048) and 1-5%
+    // slower on tiles of 32 or more slices and on 32-row tiles.  It needs four
+    // slices to fetch the next tile's rows ahead, and one tile's rows of the
+    // output below 2 GiB (its out-of-range store offsets have bit 31 set).
+    const bool ring = bm == 128 && ns >= RING_MIN_SLICES && ns <= 16 &&
+                      (int64_t)128 * N * 4 < ((int64_t)1 << 31);
     if (bm == 32) {
         switch (epi) {
-            case EPI_STORE_F32: MOE_LAUNCH(EPI_STORE_F32, 32); break;
-            case EPI_SWIGLU_F32: MOE_LAUNCH(EPI_SWIGLU_F32, 32); break;
-            case EPI_SWIGLU_QUANT_Z: MOE_LAUNCH(EPI_SWIGLU_QUANT_Z, 32); break;
-            default: MOE_LAUNCH(EPI_SWIGLU_QUANT, 32); break;
+            case EPI_STORE_F32: MOE_LAUNCH(grouped_gemm_kernel, EPI_STORE_F32, 32); break;
+            case EPI_SWIGLU_F32: MOE_LAUNCH(grouped_gemm_kernel, EPI_SWIGLU_F32, 32); break;
+            case EPI_SWIGLU_QUANT_Z: MOE_LAUNCH(grouped_gemm_kernel, EPI_SWIGLU_QUANT_Z, 32); break;
+            default: MOE_LAUNCH(grouped_gemm_kernel, EPI_SWIGLU_QUANT, 32); break;
+        }
+    } else if (ring) {
+        switch (epi) {
+            case EPI_STORE_F32: MOE_LAUNCH(grouped_gemm_ring_kernel, EPI_STORE_F32, 128); break;
+            case EPI_SWIGLU_F32: MOE_LAUNCH(grouped_gemm_ring_kernel, EPI_SWIGLU_F32, 128); break;
+            case EPI_SWIGLU_QUANT_Z: MOE_LAUNCH(grouped_gemm_ring_kernel, EPI_SWIGLU_QUANT_Z, 128); break;
+            default: MOE_LAUNCH(grouped_gemm_ring_kernel, EPI_SWIGLU_QUANT, 128); break;
         }
     } else {
         switch (epi) {
-            case EPI_STORE_F32: MOE_LAUNCH(EPI_STORE_F32, 128); break;
-            case EPI_SWIGLU_F32: MOE_LAUNCH(EPI_SWIGLU_F32, 128); break;
-            case EPI_SWIGLU_QUANT_Z: MOE_LAUNCH(EPI_SWIGLU_QUANT_Z, 128); break;
-            default: MOE_LAUNCH(EPI_SWIGLU_QUANT, 128); break;
+            case EPI_STORE_F32: MOE_LAUNCH(grouped_gemm_kernel, EPI_STORE_F32, 128); break;
+            case EPI_SWIGLU_F32: MOE_LAUNCH(grouped_gemm_kernel, EPI_SWIGLU_F32, 128); break;
+            case EPI_SWIGLU_QUANT_Z: MOE_LAUNCH(grouped_gemm_kernel, EPI_SWIGLU_QUANT_Z, 128); break;
+            default: MOE_LAUNCH(grouped_gemm_kernel, EPI_SWIGLU_QUANT, 128); break;
         }
     }
 #undef MOE_LAUNCH

@@ -387,11 +387,15 @@ def test_dense_full_size_sampled(K):
 # ------------------------------------------------------------------ persistent multi-tile path
 def _pow2_operands(sizes, N, K, seed):
     """Integer E4M3 codes (|v| <= 8) with power-of-two scales: 1x128 A scales
-    per row and slice and 128x128 B scales per group, block and slice, in
-    2^-2 .. 2^2.  Every per-slice product is an exact integer below 2^13 and
-    every scaled partial sum a multiple of 2^-4 below 2^19, so the FP32 result
-    is exact and must equal the oracle's FP64 value bit for bit; a wrong,
-    stale or misplaced scale changes it."""
+    per row and slice and 128x128 B scales per group, block and slice.  Every
+    per-slice product is an exact integer of magnitude at most 2^13.  With the
+    scales in 2^-2 .. 2^2 when K <= 512 (at most 4 slices: partial sums below
+    4 * 2^17 = 2^19) and in 2^-2 .. 2^0 otherwise (at most 128 slices: below
+    128 * 2^13 = 2^20), every scaled partial sum is a multiple of 2^-4 below
+    2^20, which FP32 holds exactly: the result must equal the oracle's FP64
+    value bit for bit, and a wrong, stale or misplaced scale changes it."""
+    assert K // 128 <= 128
+    e_hi = 3 if K <= 512 else 1
     rng = np.random.default_rng(seed)
     G = len(sizes)
     M = int(np.sum(sizes))
@@ -400,8 +404,8 @@ def _pow2_operands(sizes, N, K, seed):
     qb = np.empty((G, N, K), np.uint8)
     for gi in range(G):                 # group by group: no G x N x K index array
         qb[gi] = codes[rng.integers(0, 17, (N, K))]
-    sa = np.ldexp(1.0, rng.integers(-2, 3, (M, K // 128))).astype(np.float32)
-    sb = np.ldexp(1.0, rng.integers(-2, 3, (G, N // 128, K // 128))).astype(np.float32)
+    sa = np.ldexp(1.0, rng.integers(-2, e_hi, (M, K // 128))).astype(np.float32)
+    sb = np.ldexp(1.0, rng.integers(-2, e_hi, (G, N // 128, K // 128))).astype(np.float32)
     return qa, sa, qb, sb
 
 
@@ -413,18 +417,21 @@ def _zipf_sizes(n, total, rng):
     return s
 
 
-@pytest.mark.parametrize("kind", ["rows128", "rows32"])
+@pytest.mark.parametrize("kind", ["rows128_short_k", "rows128_long_k", "rows32"])
 def test_gemm_multi_tile_exact_pow2_scales(kind):
-    """The persistent schedule over many more tiles than CUs (each block runs
+    """The persistent schedules over many more tiles than CUs (each block runs
     several tiles, so the tile-to-tile hand-over -- the next tile's DMAs
-    overlapping this tile's epilogue, the per-tile B-scale table, the per-XCD
-    tile counters -- is exercised everywhere), with a gather and ragged,
-    Zipf-sized groups, compared element by element with the oracle.  rows128:
-    26 groups, ~40k rows (128-row tiles); rows32: 1500 groups of 0..60 rows
-    (32-row tiles)."""
-    rng = np.random.default_rng(7 if kind == "rows128" else 8)
-    N, K = 512, 384
-    if kind == "rows128":
+    overlapping this tile's epilogue, the per-tile B-scale table and gathered
+    rows, the tile sequence of each XCD -- is exercised everywhere), with a
+    gather and ragged, Zipf-sized groups, compared element by element with the
+    oracle.  rows128_short_k: 26 groups, ~40k rows, 128-row tiles of 5 K
+    slices (the kernel whose DMA ring runs on across tiles); rows128_long_k:
+    the same groups with 18 K slices (the kernel that restarts its pipeline
+    per tile); rows32: 1500 groups of 0..60 rows (32-row tiles)."""
+    rng = np.random.default_rng(8 if kind == "rows32" else 7)
+    N = 512
+    K = {"rows128_short_k": 640, "rows128_long_k": 2304, "rows32": 384}[kind]
+    if kind != "rows32":
         sizes = _zipf_sizes(26, 40_000, rng)
     else:
         sizes = rng.integers(0, 61, 1500)
@@ -434,7 +441,7 @@ def test_gemm_multi_tile_exact_pow2_scales(kind):
     bm = 32 if M <= 64 * G else 128
     n_tiles = int(np.sum((sizes + bm - 1) // bm)) * (N // 256)
     say(f"gemm multi-tile {kind}: G={G} M={M} N={N} K={K}, {bm}-row tiles, {n_tiles} tiles")
-    assert (bm == 128) == (kind == "rows128") and n_tiles > 2 * 256
+    assert (bm == 128) == (kind != "rows32") and n_tiles > 2 * 256
     qa, sa, qb, sb = _pow2_operands(sizes, N, K, seed=M)
     extra = 37
     rows = rng.permutation(M + extra)[:M].astype(np.int32)           # gather from a larger A
@@ -456,7 +463,7 @@ def test_gemm_multi_tile_exact_pow2_scales(kind):
     got = np_(out)
     bad = got != ref.astype(np.float32)
     assert not bad.any(), f"{int(bad.sum())} of {bad.size} elements differ; first at {np.argwhere(bad)[0]}"
-    if kind != "rows128":
+    if kind == "rows32":
         return
     # the SwiGLU epilogue that keeps z: z exact, the fused h codes equal
     # SwiGLU_F32 followed by the quantiser, h within the bound of the oracle's
