@@ -256,6 +256,28 @@ int grouped_gemm_fp8_blockscaled(const uint8_t* a_q, const float* a_scale,
                                  uint8_t* out_q, float* out_scale, void* ws, size_t ws_bytes,
                                  moe_stream_t stream);
 
+/* grouped_gemm_fp8_blockscaled_noalloc -- for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): grouped_gemm_fp8_blockscaled with the same arguments, kernels and
+ * results, minus the workspace.  Its scratch (the tile map, tile list and the
+ * slice-major copy of the A scales, moe_gemm_workspace_bytes(G, M_total, N, K)
+ * bytes) lives in a static device array of MOE_GEMM_SCRATCH_BYTES that every
+ * GPU the library runs on holds from module load until the process ends; the
+ * call itself allocates and frees nothing.  Calls that need more scratch than
+ * that return MOE_ERR_WORKSPACE before anything is enqueued.  Every call
+ * rewrites the scratch it uses (its counters are cleared by the call's own
+ * preparation kernel), so no state carries over between calls; but all calls
+ * on one GPU share the one array, so calls that may overlap on that GPU (on
+ * different streams, or from several threads) race and must be serialised by
+ * the caller.
+ */
+#define MOE_GEMM_SCRATCH_BYTES (64u << 20)
+int grouped_gemm_fp8_blockscaled_noalloc(const uint8_t* a_q, const float* a_scale,
+                                         const int32_t* a_row_index, const int32_t* group_offset,
+                                         int G, int64_t M_total, const uint8_t* b_q,
+                                         const float* b_scale, int N, int K, int epi, float* out,
+                                         uint8_t* out_q, float* out_scale, moe_stream_t stream);
+
 /* moe_fp8_mfma_accumulation_probe -- a measurement beside the GEMM, not a
  * step of the layer.  [IFS] FP8-accumulation paragraph: FP8 products summed
  * inside a matrix core with limited accumulation precision lose accuracy over

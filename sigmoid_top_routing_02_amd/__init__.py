@@ -29,7 +29,7 @@ EXPORTS = (
     "moe_seq_balance_loss_workspace_bytes", "moe_seq_balance_loss",
     "moe_dispatch_workspace_bytes", "moe_dispatch", "moe_dispatch_check", "moe_permute_rows",
     "fp8_quant_1x128", "fp8_quant_128x128",
-    "moe_gemm_workspace_bytes", "grouped_gemm_fp8_blockscaled",
+    "moe_gemm_workspace_bytes", "grouped_gemm_fp8_blockscaled", "grouped_gemm_fp8_blockscaled_noalloc",
     "moe_fp8_mfma_accumulation_probe", "moe_combine", "moe_bias_update",
     "moe_packed_weight_bytes", "moe_prepare_expert_weights",
     "moe_layer_workspace_bytes", "moe_layer_forward",
@@ -70,6 +70,7 @@ def load_library(path: str = LIB_PATH):
         "fp8_quant_128x128": ([P, I64, I32, P, P, P], I32),
         "moe_gemm_workspace_bytes": ([I32, I64, I32, I32], SZ),
         "grouped_gemm_fp8_blockscaled": ([P, P, P, P, I32, I64, P, P, I32, I32, I32, P, P, P, P, SZ, P], I32),
+        "grouped_gemm_fp8_blockscaled_noalloc": ([P, P, P, P, I32, I64, P, P, I32, I32, I32, P, P, P, P], I32),
         "moe_fp8_mfma_accumulation_probe": ([P, P, I32, I32, I32, I32, P, P], I32),
         "moe_combine": ([P, P, I32, I64, P, P, I64, I32, I32, P, P], I32),
         "moe_bias_update": ([P, P, I32, I64, F32, P], I32),
@@ -273,6 +274,23 @@ def grouped_gemm_fp8_blockscaled(a_q, a_scale, group_offset, M_total, b_q, b_sca
                                  out_scale=None, ws=None):
     """a_q uint8 [*,K], a_scale f32 [*,K/128], group_offset i32 [G+1] (device),
     b_q uint8 [G,N,K], b_scale f32 [G,N/128,K/128]."""
+    return _grouped_gemm(a_q, a_scale, group_offset, M_total, b_q, b_scale, epi, a_row_index, out, out_q,
+                         out_scale, ws, noalloc=False)
+
+
+def grouped_gemm_fp8_blockscaled_noalloc(a_q, a_scale, group_offset, M_total, b_q, b_scale,
+                                         epi=MOE_EPI_STORE_F32, a_row_index=None, out=None, out_q=None,
+                                         out_scale=None):
+    """As grouped_gemm_fp8_blockscaled, through the C entry point that takes no
+    workspace (its scratch is the library's static device array; the C call
+    allocates nothing -- pass preallocated outputs to keep this binding from
+    allocating them)."""
+    return _grouped_gemm(a_q, a_scale, group_offset, M_total, b_q, b_scale, epi, a_row_index, out, out_q,
+                         out_scale, None, noalloc=True)
+
+
+def _grouped_gemm(a_q, a_scale, group_offset, M_total, b_q, b_scale, epi, a_row_index, out, out_q, out_scale,
+                  ws, noalloc):
     G, N, K = b_q.shape
     if b_q.dtype != torch.uint8:
         raise MoEError(f"b_q: dtype {b_q.dtype}, expected torch.uint8")
@@ -307,14 +325,20 @@ def grouped_gemm_fp8_blockscaled(a_q, a_scale, group_offset, M_total, b_q, b_sca
         elif out is not None:
             _want(out, torch.float32, (M_total, N // 2), "out")
     L = load_library()
-    if ws is not None and ws.numel() < L.moe_gemm_workspace_bytes(G, M_total, N, K):
-        raise MoEError("ws: smaller than moe_gemm_workspace_bytes")
-    if ws is None:
-        ws = _new((max(L.moe_gemm_workspace_bytes(G, M_total, N, K), 256),), torch.uint8, a_q)
-    _check(L.grouped_gemm_fp8_blockscaled(
-        _ptr(a_q), _ptr(a_scale), _ptr(a_row_index), _ptr(group_offset), G, M_total, _ptr(b_q),
-        _ptr(b_scale), N, K, epi, _ptr(out), _ptr(out_q), _ptr(out_scale), _ptr(ws), ws.numel(),
-        _stream()), "grouped_gemm_fp8_blockscaled")
+    if noalloc:
+        _check(L.grouped_gemm_fp8_blockscaled_noalloc(
+            _ptr(a_q), _ptr(a_scale), _ptr(a_row_index), _ptr(group_offset), G, M_total, _ptr(b_q),
+            _ptr(b_scale), N, K, epi, _ptr(out), _ptr(out_q), _ptr(out_scale), _stream()),
+            "grouped_gemm_fp8_blockscaled_noalloc")
+    else:
+        if ws is not None and ws.numel() < L.moe_gemm_workspace_bytes(G, M_total, N, K):
+            raise MoEError("ws: smaller than moe_gemm_workspace_bytes")
+        if ws is None:
+            ws = _new((max(L.moe_gemm_workspace_bytes(G, M_total, N, K), 256),), torch.uint8, a_q)
+        _check(L.grouped_gemm_fp8_blockscaled(
+            _ptr(a_q), _ptr(a_scale), _ptr(a_row_index), _ptr(group_offset), G, M_total, _ptr(b_q),
+            _ptr(b_scale), N, K, epi, _ptr(out), _ptr(out_q), _ptr(out_scale), _ptr(ws), ws.numel(),
+            _stream()), "grouped_gemm_fp8_blockscaled")
     if epi == MOE_EPI_SWIGLU_QUANT:
         return out_q, out_scale
     if epi == MOE_EPI_SWIGLU_QUANT_Z:

@@ -225,11 +225,12 @@ size_t moe_gemm_workspace_bytes(int G, int64_t M_total, int N, int K) {
                ? moe::gemm_ws_bytes(G, M_total, N, K) : 0;
 }
 
-int grouped_gemm_fp8_blockscaled(const uint8_t* a_q, const float* a_scale,
-                                 const int32_t* a_row_index, const int32_t* group_offset, int G,
-                                 int64_t M_total, const uint8_t* b_q, const float* b_scale, int N,
-                                 int K, int epi, float* out, uint8_t* out_q, float* out_scale,
-                                 void* ws, size_t ws_bytes, moe_stream_t stream) {
+namespace {
+// Argument checks shared by grouped_gemm_fp8_blockscaled and its allocation-free variant.
+int gemm_check_args(const uint8_t* a_q, const float* a_scale, const int32_t* a_row_index,
+                    const int32_t* group_offset, int G, int64_t M_total, const uint8_t* b_q,
+                    const float* b_scale, int N, int K, int epi, float* out, uint8_t* out_q,
+                    float* out_scale) {
     REQUIRE(G >= 1 && G <= 65535, MOE_ERR_UNSUPPORTED, "grouped_gemm: G=%d outside [1, 65535]", G);
     REQUIRE(M_total >= 0 && M_total < ((int64_t)1 << 31), MOE_ERR_UNSUPPORTED, "grouped_gemm: M_total out of range");
     REQUIRE(K > 0 && K % 128 == 0, MOE_ERR_SHAPE, "grouped_gemm: K=%d not a positive multiple of 128", K);
@@ -264,11 +265,44 @@ int grouped_gemm_fp8_blockscaled(const uint8_t* a_q, const float* a_scale,
     } else {
         REQUIRE_PTR(out);
     }
+    return MOE_OK;
+}
+}  // namespace
+
+int grouped_gemm_fp8_blockscaled(const uint8_t* a_q, const float* a_scale,
+                                 const int32_t* a_row_index, const int32_t* group_offset, int G,
+                                 int64_t M_total, const uint8_t* b_q, const float* b_scale, int N,
+                                 int K, int epi, float* out, uint8_t* out_q, float* out_scale,
+                                 void* ws, size_t ws_bytes, moe_stream_t stream) {
+    const int st = gemm_check_args(a_q, a_scale, a_row_index, group_offset, G, M_total, b_q, b_scale, N, K, epi,
+                                   out, out_q, out_scale);
+    if (st != MOE_OK || M_total == 0) return st;
     REQUIRE_PTR(ws);
     REQUIRE(ws_bytes >= moe::gemm_ws_bytes(G, M_total, N, K), MOE_ERR_WORKSPACE,
             "grouped_gemm: workspace %zu < %zu bytes", ws_bytes, moe::gemm_ws_bytes(G, M_total, N, K));
     return hip_status(moe::launch_grouped_gemm(a_q, a_scale, a_row_index, group_offset, G, M_total,
                                                b_q, b_scale, N, K, epi, out, out_q, out_scale, ws,
+                                               S(stream)),
+                      "grouped gemm launch");
+}
+
+int grouped_gemm_fp8_blockscaled_noalloc(const uint8_t* a_q, const float* a_scale,
+                                         const int32_t* a_row_index, const int32_t* group_offset, int G,
+                                         int64_t M_total, const uint8_t* b_q, const float* b_scale, int N,
+                                         int K, int epi, float* out, uint8_t* out_q, float* out_scale,
+                                         moe_stream_t stream) {
+    const int st = gemm_check_args(a_q, a_scale, a_row_index, group_offset, G, M_total, b_q, b_scale, N, K, epi,
+                                   out, out_q, out_scale);
+    if (st != MOE_OK || M_total == 0) return st;
+    const size_t need = moe::gemm_ws_bytes(G, M_total, N, K);
+    REQUIRE(need <= (size_t)MOE_GEMM_SCRATCH_BYTES, MOE_ERR_WORKSPACE,
+            "grouped_gemm_noalloc: needs %zu bytes of scratch, above the library's static %zu-byte array "
+            "(use grouped_gemm_fp8_blockscaled with a workspace)", need, (size_t)MOE_GEMM_SCRATCH_BYTES);
+    void* scratch = nullptr;
+    const hipError_t e = moe::gemm_static_scratch(&scratch);
+    if (e != hipSuccess) return hip_status(e, "grouped_gemm_noalloc: static scratch address");
+    return hip_status(moe::launch_grouped_gemm(a_q, a_scale, a_row_index, group_offset, G, M_total,
+                                               b_q, b_scale, N, K, epi, out, out_q, out_scale, scratch,
                                                S(stream)),
                       "grouped gemm launch");
 }

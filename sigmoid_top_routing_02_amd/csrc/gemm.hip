@@ -41,6 +41,7 @@
 
 #include "device_math.h"
 #include "kernels.h"
+#include "moe_fp8.h"
 
 namespace moe {
 namespace {
@@ -1538,6 +1539,30 @@ hipError_t launch_grouped_gemm(const uint8_t* a_q, const float* a_s, const int32
     }
 #undef MOE_LAUNCH
     return hipGetLastError();
+}
+
+// ---- static scratch of the allocation-free GEMM entry point.  Each GPU the
+// library runs on holds its own copy of this array (the tile map, tile list
+// and slice-major A scales of one call) from module load until the process
+// ends.  In host code `scratch` only names the symbol: kernels get the
+// device address hipGetSymbolAddress returns, looked up once per device.
+static __device__ __attribute__((aligned(256))) unsigned char scratch[MOE_GEMM_SCRATCH_BYTES];
+
+hipError_t gemm_static_scratch(void** ptr) {
+    static std::atomic<void*> addr[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    void* p = addr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {          // first call on this device (a lost race repeats the lookup)
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        addr[dev].store(p, std::memory_order_release);
+    }
+    *ptr = p;
+    return hipSuccess;
 }
 
 namespace {

@@ -35,6 +35,8 @@ hipError_t launch_quant_128x128(const float* w, int64_t rows, int cols, uint8_t*
 // gemm.hip
 enum { EPI_STORE_F32 = 0, EPI_SWIGLU_F32 = 1, EPI_SWIGLU_QUANT = 2, EPI_SWIGLU_QUANT_Z = 3 };
 size_t gemm_ws_bytes(int G, int64_t M_total, int N, int K);
+// device address of the static scratch array (MOE_GEMM_SCRATCH_BYTES) on the current device
+hipError_t gemm_static_scratch(void** ptr);
 hipError_t launch_grouped_gemm(const uint8_t* a_q, const float* a_s, const int32_t* a_rows,
                                const int32_t* group_offset, int G, int64_t M_total,
                                const uint8_t* b_q, const float* b_s, int N, int K, int epi,

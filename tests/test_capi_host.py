@@ -246,3 +246,22 @@ def test_dispatch_check_argument_errors(L):
     assert L.moe_dispatch_check(None, *ok[1:]) == -1
     assert L.moe_dispatch_check(*ok[:9], None, None) == -1           # status
     assert L.moe_dispatch_check(FAKE, FAKE, None, FAKE, FAKE, *ok[5:]) == -1   # partial row arrays
+
+
+def test_noalloc_gemm_rejects_oversized_scratch(L):
+    """The allocation-free GEMM checks its scratch need against the static
+    array before touching a device: too large a call returns
+    MOE_ERR_WORKSPACE and names the limit; argument errors come first, as in
+    the workspace variant."""
+    limit = 64 << 20
+    G, N, K = 257, 7168, 16384
+    M = limit // (K // 128 * 4) + 1024            # its slice-major A scales alone exceed the array
+    assert L.moe_gemm_workspace_bytes(G, M, N, K) > limit
+    r = L.grouped_gemm_fp8_blockscaled_noalloc(FAKE, FAKE, FAKE, FAKE, G, M, FAKE, FAKE, N, K, 0, FAKE, None, None, None)
+    assert r == -4 and b"static" in L.moe_last_error()
+    assert L.grouped_gemm_fp8_blockscaled_noalloc(FAKE, FAKE, None, FAKE, 2, 64, FAKE, FAKE, 256, 200, 0, FAKE,
+                                                  None, None, None) == -2
+    assert L.grouped_gemm_fp8_blockscaled_noalloc(None, FAKE, None, FAKE, 2, 64, FAKE, FAKE, 256, 256, 0, FAKE,
+                                                  None, None, None) == -1
+    assert L.grouped_gemm_fp8_blockscaled_noalloc(None, None, None, None, 2, 0, None, None, 256, 256, 0, None,
+                                                  None, None, None) == 0      # no rows: nothing to do
