@@ -37,6 +37,7 @@ import sigmoid_top_routing_02_amd as moe  # noqa: E402
 import workloads  # noqa: E402
 
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
+MAX_SCLK_MHZ = 2400.0         # the shader clock the published peaks assume
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -475,6 +476,10 @@ def run_layer(sh, steps, warmup, with_cpu):
                           "algorithmic_per_launch": b1, "avg_launch_ms": round(g1_ms, 4),
                           "traffic": traffic_for(f"gemm1_{sh.name}", "gemm.hip")}}
     log(f"[bench] {ms:.3f} ms/step; stages {stages}")
+    clk = sustained_clock(lambda: layer_step(sh, st))
+    log(f"[bench] sustained shader clock under this step: {clk}")
+    if roof["bound"] == "mfma":
+        at_clock(roof, clk)
     qerr = layer_quant_error(sh, st)
     log(f"[bench] quantisation error vs the unquantised layer: {qerr}")
     res = {
@@ -492,7 +497,7 @@ def run_layer(sh, steps, warmup, with_cpu):
         "stages_ms": stages,
         "gemm_tflops": {"gemm1": round(g1 / (ev.avg_ms("gemm1") * 1e-3) / 1e12, 1),
                         "gemm2": round(g2 / (ev.avg_ms("gemm2") * 1e-3) / 1e12, 1)},
-        "gpu_clocks_mhz": {"before": clocks_before, "after": clocks_after},
+        "gpu_clocks_mhz": {"before": clocks_before, "after": clocks_after, "sustained": clk},
     }
     if with_cpu:
         log("[bench] CPU oracle baseline")
@@ -715,6 +720,57 @@ def gpu_clocks():
     return out or {"error": "no clock values in rocm-smi output"}
 
 
+CLOCK_SECONDS = 3.0            # 0: skip the sustained-clock reading (--no-clock, for profiler runs)
+
+
+def sustained_clock(step_fn, seconds=None):
+    """The shader clock the GPU holds under this workload: step_fn runs back
+    to back for `seconds` (synchronising every few calls) while a thread reads
+    rocm-smi's current sclk every 0.25 s; the median of the samples after the
+    first second (the clock starts near its maximum and settles as power
+    rises).  Run after the timed region, so it never disturbs the timing."""
+    import threading
+    seconds = CLOCK_SECONDS if seconds is None else seconds
+    if seconds <= 0:
+        return {"skipped": "--no-clock"}
+    samples, done = [], threading.Event()
+
+    def sample():
+        t0 = time.perf_counter()
+        while not done.is_set():
+            c = gpu_clocks()
+            v = next((val for key, val in c.items() if "sclk clock speed" in key), None)
+            if v is not None:
+                samples.append((time.perf_counter() - t0, v))
+            done.wait(0.25)
+
+    th = threading.Thread(target=sample, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(4):
+            step_fn()
+        torch.cuda.synchronize()
+    done.set()
+    th.join(timeout=35)
+    late = [v for t, v in samples if t >= 1.0] or [v for _, v in samples]
+    if not late:
+        return {"error": "rocm-smi gave no sclk"}
+    return {"sclk_median_mhz": int(np.median(late)), "sclk_min_mhz": int(min(late)),
+            "sclk_max_mhz": int(max(late)), "samples": len(late), "seconds": seconds}
+
+
+def at_clock(roof, clk):
+    """Adds the MFMA peak at the measured sustained shader clock (the
+    published peak assumes the 2.4 GHz maximum) and the fraction of it."""
+    mhz = clk.get("sclk_median_mhz") if isinstance(clk, dict) else None
+    if mhz:
+        peak = PEAK_FP8_TFLOPS * mhz / MAX_SCLK_MHZ
+        roof["peak_at_sustained_sclk"] = round(peak, 1)
+        roof["frac_at_sustained_sclk"] = round(roof["achieved"] / peak, 4)
+    return roof
+
+
 def run_dense(steps, warmup, K=4096):
     M, N = workloads.DENSE["M"], workloads.DENSE["N"]
     log(f"[bench] dense GEMM M={M} N={N} K={K}")
@@ -746,6 +802,8 @@ def run_dense(steps, warmup, K=4096):
     flops = 2.0 * M * N * K
     g_ms = ev.avg_ms("gemm")
     ach = flops / (g_ms * 1e-3) / 1e12
+    clk = sustained_clock(lambda: moe.grouped_gemm_fp8_blockscaled(aq, as_, go, M, bq3, bs3, out=out, ws=ws))
+    log(f"[bench] sustained shader clock under this GEMM: {clk}")
     err = dense_errors(out, aq, as_, bq, bs, rows, a_rows, b_host)
     del b_host
     acc = accumulation_probe(aq, bq, K)
@@ -754,12 +812,13 @@ def run_dense(steps, warmup, K=4096):
         "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3 (fp32 accumulate)",
         "data": "synthetic", "config": {"workload": "dense_blockscaled_gemm", "M": M, "N": N, "K": K},
-        "roofline": {"kernel": "grouped_gemm_fp8_blockscaled (1 group)", "bound": "mfma",
-                     "achieved": round(ach, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(ach / PEAK_FP8_TFLOPS, 4), "traffic": traffic_for(f"dense_k{K}", "gemm.hip")},
+        "roofline": at_clock({"kernel": "grouped_gemm_fp8_blockscaled (1 group)", "bound": "mfma",
+                              "achieved": round(ach, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                              "frac": round(ach / PEAK_FP8_TFLOPS, 4),
+                              "traffic": traffic_for(f"dense_k{K}", "gemm.hip")}, clk),
         "error": err,
         "accumulation": acc,
-        "gpu_clocks_mhz": {"before": clocks_before, "after": clocks_after},
+        "gpu_clocks_mhz": {"before": clocks_before, "after": clocks_after, "sustained": clk},
     }
 
 
@@ -827,7 +886,12 @@ def main():
     ap.add_argument("--with-copy", action="store_true",
                     help="first run a plain 4 GiB copy kernel (moe_permute_rows with the identity "
                          "permutation) so a counter profile can calibrate FETCH_SIZE / WRITE_SIZE")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the ~3 s sustained-clock reading after the timed region (profiler runs)")
     args = ap.parse_args()
+    if args.no_clock:
+        global CLOCK_SECONDS
+        CLOCK_SECONDS = 0.0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this layer forward is a single-GPU path "
               f"(--gpus {args.gpus} is not supported)", file=sys.stderr)

@@ -774,12 +774,13 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
 // restart; the epilogues store straight from registers (the stores the
 // barriers count are issued by every lane, and a lane without an output
 // writes out of the buffer's range, which drops it), and the waits at the two
-// barriers after an epilogue count those stores.  The next tile's record comes by one scalar load per tile; its
-// gathered row indices and B-scale table reach LDS through the spare
-// per-stage DMA slot, ahead of their use.  Everything per tile is set up once
-// per tile, so a slice's memory phase issues little beyond its DMAs and LDS
-// reads (a SIMD issues a few scalar instructions per cycle at most, and the
-// memory phase must stay shorter than the other wave's matrix phase).
+// barriers after an epilogue count those stores.  The next tile's record
+// comes by one scalar load per tile; its gathered row indices and B-scale
+// table reach LDS through the spare per-stage DMA slot, ahead of their use.
+// Everything per tile is set up once per tile, so a slice's memory phase
+// issues little beyond its DMAs and LDS reads (a SIMD issues a few scalar
+// instructions per cycle at most, and the memory phase must stay shorter than
+// the other wave's matrix phase).
 //
 // The three stages are one LDS object addressed at run time (a tile may start
 // on any stage), so the DMAs are issued from inline asm: the compiler adds no
