@@ -225,6 +225,11 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
     constexpr int BM = C::BM, MI = C::MI, NI = C::NI, WAVES_N = C::WAVES_N;
     constexpr int WN_COLS = C::WN_COLS, WROWS = C::WROWS, A_DMA = C::A_DMA, B_DMA = C::B_DMA;
     constexpr int NS = C::NSTAGES;
+    // Whether a tile's second slice is issued with its first, before the
+    // previous tile's epilogue: when that epilogue leaves stage 1 alone (the
+    // SwiGLU epilogues use stage 2 as scratch, the FP32 store of a 32-row tile
+    // stages through stage 2 only), so the slice's latency hides behind it.
+    constexpr bool EARLY1 = !KG && (EPI != EPI_STORE_F32 || BM_ == 32);
     constexpr int D = C::DMA_PER_STAGE;
     // MFMA operand order.  SwiGLU tiles put B first, so a lane's four results
     // share one output row and one scale (one multiply per row tile instead
@@ -485,7 +490,7 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
             sb0 = g_bscale[sbrow0 * MAX_SLICES + s];
             sb1 = g_bscale[sbrow1 * MAX_SLICES + s];
         }
-        if constexpr (FIRST) issue(IC<(ST + 1) % NS>{}, s + 1);
+        if constexpr (FIRST && !EARLY1) issue(IC<(ST + 1) % NS>{}, s + 1);
         issue(IC<(ST + 2) % NS>{}, s + 2);
     };
 
@@ -544,7 +549,9 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
 
     // FP32-store epilogue, through LDS: the tile's rows go 64 at a time into the
     // B buffers of stages 1 and 2 (32 rows of 1 KiB each; idle until the next
-    // tile's second slice is issued), then every wave writes whole rows, one
+    // tile's second slice is issued), or for 32-row tiles into stage 2's alone
+    // (stage 1 then takes the next tile's second slice during the
+    // epilogue), then every wave writes whole rows, one
     // 16-byte piece per lane (128 store instructions per tile instead of 512
     // single floats).  In LDS the 16-float halves of each 32-float bank row
     // swap when bit 2 of the row is set: the four row groups of a fragment
@@ -554,7 +561,7 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
         if constexpr (EPI == EPI_STORE_F32) {
             constexpr int PASS_ROWS = BM < 64 ? BM : 64;
             constexpr int RPW = PASS_ROWS / NWAVES;            // rows each wave writes out per pass
-            float* const buf0 = reinterpret_cast<float*>(g_b1);
+            float* const buf0 = reinterpret_cast<float*>(BM == 32 ? g_b2 : g_b1);
             float* const buf1 = reinterpret_cast<float*>(g_b2);
             auto lds_at = [&](int lrow, int col) -> float* {      // lrow < PASS_ROWS
                 float* b = lrow < 32 ? buf0 : buf1;
@@ -708,6 +715,7 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
     load_rows(cur);
     setup(cur);
     issue(IC<0>{}, 0);
+    if constexpr (EARLY1) issue(IC<1>{}, 1);
     // The tile after this one.  Its result is only needed after the K loop;
     // the library is built without the compiler's atomic optimizer, which
     // would otherwise consume it (and drain every DMA in flight) right here.
@@ -752,6 +760,7 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(GemmArgs p) {
         if (t_nxt >= 0) {
             setup(nxt);
             issue(IC<0>{}, 0);
+            if constexpr (EARLY1) issue(IC<1>{}, 1);
             if (tid == 0) nxt_raw = atomicAdd(p.counters + xcd, 1);
         }
         store_f32(cur);

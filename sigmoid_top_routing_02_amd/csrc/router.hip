@@ -161,84 +161,110 @@ __global__ __launch_bounds__(NTHREADS) void router_scores_kernel(
 
 // Few tokens, centroids shared: one block per (4 tokens, 64 experts), one
 // logit per lane (wave w = token, lane = expert).  Chunks of SM_KC k-values of
-// the block's 64 centroid rows are loaded with coalesced 16-byte loads into
-// LDS (double-buffered through registers) and read by all four waves, so each
-// centroid crosses from L2 once per 4 tokens instead of once per token; the
-// tokens' u chunk is widened to FP32 in LDS and read as a broadcast.  Every
-// logit is still one FMA chain in increasing k.
+// the block's 64 centroid rows and 4 token rows are loaded with coalesced
+// 16-byte loads, widened to FP32 once as they are put into LDS, and read by
+// all four waves (each centroid crosses from L2 once per 4 tokens, and the
+// chain's loop holds nothing but its FMAs and 16-byte LDS reads; the u chunk
+// is read as a broadcast).  The loads run SM_PF chunks ahead through a ring of
+// registers, so their latency hides behind the FMAs of the chunks between.
+// Every logit is still one FMA chain in increasing k.
 constexpr int SM_TOK = 4, SM_EXP = 64;
 
-template <int SM_KC>      // k-values per chunk; divides every d that is a multiple of 128
-                          // (measured: 64 beats 128 and 256, whose unrolled chunk
-                          // the compiler holds in registers)
+template <int SM_KC, int SM_PF>   // SM_KC divides d (the launcher picks it)
 __global__ __launch_bounds__(256) void router_scores_small_kernel(
     const uint16_t* __restrict__ u, const uint16_t* __restrict__ e, int64_t T, int d, int E,
     float* __restrict__ s) {
-    // centroid chunk: 64 rows of SM_KC bf16 plus one 16-byte pad per row so
+    // centroid chunk: 64 rows of SM_KC floats plus one 16-byte pad per row so
     // that the 64 lanes' row reads spread over the banks
-    __shared__ uint4 es[2][SM_EXP][SM_KC / 8 + 1];
-    __shared__ float us[2][SM_TOK][SM_KC];
+    constexpr int Q = SM_KC / 4;                 // float4 per row of a chunk
+    constexpr int PARTS = SM_KC / 8;             // 16-byte pieces (8 bf16) per row of a chunk
+    constexpr int NP = SM_EXP * PARTS / 256;     // centroid pieces per thread per chunk
+    constexpr int UT = SM_TOK * PARTS;           // u pieces per chunk
+    static_assert(SM_EXP * PARTS % 256 == 0 && UT <= 256, "loader roles");
+    __shared__ float4 es[2][SM_EXP][Q + 1];
+    __shared__ float4 us[2][SM_TOK][Q];
     const int egroups = (E + SM_EXP - 1) / SM_EXP;
     const int64_t t0 = (int64_t)(blockIdx.x / egroups) * SM_TOK;
     const int e0 = (blockIdx.x % egroups) * SM_EXP;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    // loader roles: the chunk's 8 16-byte pieces per centroid row are moved
-    // two per thread (piece p = tid and tid + 256: row p / 8, part p % 8);
-    // threads 0 .. 31 move one piece of the u chunk (token tid / 8, part tid % 8)
-    constexpr int PARTS = SM_KC / 8, UT = SM_TOK * PARTS;
-    static_assert(SM_EXP * PARTS == 512 && UT <= 256, "loader roles assume 64-wide chunks");
-    const int p0 = tid, p1 = tid + 256;
-    const uint4* eg0 = reinterpret_cast<const uint4*>(e + (int64_t)min(e0 + p0 / PARTS, E - 1) * d) + p0 % PARTS;
-    const uint4* eg1 = reinterpret_cast<const uint4*>(e + (int64_t)min(e0 + p1 / PARTS, E - 1) * d) + p1 % PARTS;
-    const int64_t ut = min(t0 + tid / PARTS, T - 1);
+    // loader roles: centroid piece p = tid + 256 q (q < NP) is row p / PARTS,
+    // part p % PARTS; u piece tid % UT is token (tid % UT) / PARTS, part
+    // tid % PARTS (threads past UT load a copy of one and drop it, so every
+    // thread issues the same loads and the compiler's wait counts stay exact)
+    const uint4* eg[NP];
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
+        const int pc = tid + 256 * q;
+        eg[q] = reinterpret_cast<const uint4*>(e + (int64_t)min(e0 + pc / PARTS, E - 1) * d) + pc % PARTS;
+    }
+    const int64_t ut = min(t0 + (tid % UT) / PARTS, T - 1);
     const uint4* ug = reinterpret_cast<const uint4*>(u + ut * d) + tid % PARTS;
     const int nch = d / SM_KC;
-    uint4 r0 = eg0[0], r1 = eg1[0], ru = tid < UT ? ug[0] : uint4{0, 0, 0, 0};
-    float* const udst0 = &us[0][tid / PARTS % SM_TOK][(tid % PARTS) * 8];
-    const int ustride = SM_TOK * SM_KC;          // floats from us[0] to us[1]
-#define MOE_SMALL_PUT(B)                                                      \
-    do {                                                                      \
-        es[B][p0 / PARTS][p0 % PARTS] = r0;                                   \
-        es[B][p1 / PARTS][p1 % PARTS] = r1;                                   \
-        if (tid < UT) {                                                       \
-            float* dst = udst0 + (B) * ustride;                               \
-            dst[0] = bf16_lo(ru.x); dst[1] = bf16_hi(ru.x);                   \
-            dst[2] = bf16_lo(ru.y); dst[3] = bf16_hi(ru.y);                   \
-            dst[4] = bf16_lo(ru.z); dst[5] = bf16_hi(ru.z);                   \
-            dst[6] = bf16_lo(ru.w); dst[7] = bf16_hi(ru.w);                   \
-        }                                                                     \
-    } while (0)
-    MOE_SMALL_PUT(0);
+    uint4 re[SM_PF][NP], ru[SM_PF];
+    auto load = [&](int slot, int c) {           // chunk min(c, nch - 1) into ring slot `slot`
+        const int off = min(c, nch - 1) * PARTS;
+#pragma unroll
+        for (int q = 0; q < NP; ++q) re[slot][q] = eg[q][off];
+        ru[slot] = ug[off];
+    };
+    // 8 bf16 (k .. k+7, k in the low half of each word) as two float4
+    auto widen = [](const uint4& v, float4& lo, float4& hi) {
+        lo = float4{bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y)};
+        hi = float4{bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+    };
+    auto put = [&](int B, int slot) {
+        float4 lo, hi;
+#pragma unroll
+        for (int q = 0; q < NP; ++q) {
+            const int pc = tid + 256 * q;
+            widen(re[slot][q], lo, hi);
+            es[B][pc / PARTS][(pc % PARTS) * 2] = lo;
+            es[B][pc / PARTS][(pc % PARTS) * 2 + 1] = hi;
+        }
+        if (tid < UT) {
+            widen(ru[slot], lo, hi);
+            us[B][tid / PARTS][(tid % PARTS) * 2] = lo;
+            us[B][tid / PARTS][(tid % PARTS) * 2 + 1] = hi;
+        }
+    };
+#pragma unroll
+    for (int i = 0; i < SM_PF; ++i) load(i, i);
+    put(0, 0);
     __syncthreads();
     float acc = 0.0f;
-    for (int c = 0; c < nch; ++c) {
-        const int b = c & 1;
-        // next chunk into registers (the last step re-reads the last chunk into
-        // the spare buffer: the loop body has no branch around the loads)
-        const int off = min(c + 1, nch - 1) * PARTS;
-        r0 = eg0[off];
-        r1 = eg1[off];
-        if (tid < UT) ru = ug[off];
+    for (int cb = 0; cb < nch; cb += SM_PF) {
 #pragma unroll
-        for (int j = 0; j < PARTS; ++j) {
-            const uint4 ev = es[b][lane][j];
-            const uint32_t wd[4] = {ev.x, ev.y, ev.z, ev.w};
-            const float* uv = &us[b][w][j * 8];
+        for (int i = 0; i < SM_PF; ++i) {
+            const int c = cb + i;
+            if (c >= nch) break;
+            const int b = c & 1;
+            load(i, c + SM_PF);                  // slot i held chunk c, already in LDS
+            // batches of 8 float4 of the centroid row and of u read before
+            // their 32 FMAs, so the LDS latency is paid once per batch
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                acc = __builtin_fmaf(uv[2 * q], bf16_lo(wd[q]), acc);
-                acc = __builtin_fmaf(uv[2 * q + 1], bf16_hi(wd[q]), acc);
+            for (int jb = 0; jb < Q; jb += 8) {
+                float4 ev[8], uv[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    ev[i] = es[b][lane][jb + i];
+                    uv[i] = us[b][w][jb + i];
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    acc = __builtin_fmaf(uv[i].x, ev[i].x, acc);
+                    acc = __builtin_fmaf(uv[i].y, ev[i].y, acc);
+                    acc = __builtin_fmaf(uv[i].z, ev[i].z, acc);
+                    acc = __builtin_fmaf(uv[i].w, ev[i].w, acc);
+                }
             }
+            // the chunk's FMAs stay before the barrier (the compiler would
+            // otherwise sink them below the next chunk's LDS writes)
+            asm volatile("" :: "v"(acc));
+            __syncthreads();                     // every wave is done with buffer b ^ 1's last use
+            put(b ^ 1, (i + 1) % SM_PF);         // chunk c + 1 (past the end: unused)
+            __syncthreads();
         }
-        // the chunk's FMAs stay before the barrier (the compiler would otherwise
-        // sink them below the next chunk's LDS writes, whose wait for the
-        // global loads would then hide nothing)
-        asm volatile("" :: "v"(acc));
-        __syncthreads();                         // every wave is done with buffer b ^ 1's last use
-        MOE_SMALL_PUT(b ^ 1);
-        __syncthreads();
     }
-#undef MOE_SMALL_PUT
     const int64_t t = t0 + w;
     const int ex = e0 + lane;
     if (t < T && ex < E) s[t * E + ex] = sigmoid_fixed(acc);
@@ -359,8 +385,13 @@ hipError_t launch_router_scores(const uint16_t* u, const uint16_t* e, int64_t T,
     if (E > 64) {
         if (T >= 4096) return launch_scores<32, 128, 4, 4>(u, e, T, d, E, s, st);
         if (T >= 1024) return launch_scores<16, 128, 2, 4>(u, e, T, d, E, s, st);
+        // fewer tokens: one logit per lane, chunks of 256 k-values (128 when d
+        // is an odd multiple of 128) fetched two ahead
         const unsigned grid = (unsigned)((T + SM_TOK - 1) / SM_TOK * ((E + SM_EXP - 1) / SM_EXP));
-        hipLaunchKernelGGL(router_scores_small_kernel<64>, dim3(grid), dim3(256), 0, st, u, e, T, d, E, s);
+        if (d % 256 == 0)
+            hipLaunchKernelGGL((router_scores_small_kernel<256, 2>), dim3(grid), dim3(256), 0, st, u, e, T, d, E, s);
+        else
+            hipLaunchKernelGGL((router_scores_small_kernel<128, 2>), dim3(grid), dim3(256), 0, st, u, e, T, d, E, s);
         return hipGetLastError();
     }
     if (T >= 4096) return launch_scores<64, 64, 4, 4>(u, e, T, d, E, s, st);
