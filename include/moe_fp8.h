@@ -338,8 +338,8 @@ int moe_prepare_expert_weights(const float* w1, const float* w3, const float* w2
 /* ------------------------------------------------------------------ backward (input gradient)
  * The gradient of a scalar loss L with respect to u and the centroids, given
  * dh = dL/dh' FP32 [T,d], by the chain rule through [LINEAGE] "The notation"
- * (h' = u + FFN_shared(u) + sum_k g_k FFN_k(u)), the gate normalisation over
- * the chosen experts and the sigmoid affinity ([IFS] MoE-routing paragraph);
+ * (h' = u + FFN_shared(u) + sum_k g_k FFN_k(u)), g = s / (sum of s over the
+ * chosen set) and s = sigmoid(u . e) ([IFS] MoE-routing paragraph);
  * the bias only selects ([IFS] bias paragraph), so it has no gradient and the
  * chosen set is held fixed.  The two expert GEMMs run on
  * grouped_gemm_fp8_blockscaled with transposed weights; their operands are

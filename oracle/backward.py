@@ -7,10 +7,9 @@ Plain FP64 numpy, written from the layer's output equation (nlp-lineage
 summary, "The notation"):
     h'_t = u_t + FFN_shared(u_t) + sum_k g_(k,t) FFN_(i_k)(u_t),
     g_(k,t) = s_(i_k,t) / D_t,  D_t = sum_k s_(i_k,t),  s_(i,t) = sigmoid(u_t . e_i)
-("DeepSeek-V3 Technical Report" notes, MoE-routing paragraph: sigmoid
-affinity, gates normalised over the chosen experts; bias paragraph: the bias
-only picks the experts, so it has no gradient and the chosen set is constant
-under small changes).  FFN(x) = W2 (SiLU(W1 x) * W3 x) is this build's reading
+("DeepSeek-V3 Technical Report" notes, MoE-routing paragraph: the two
+formulas on the second line; bias paragraph: b only ranks the experts, so it
+has no gradient and the chosen set is constant under small changes).  FFN(x) = W2 (SiLU(W1 x) * W3 x) is this build's reading
 of the expert form.  Given dL/dh' = dh for a scalar loss L, the chain rule
 gives, for token t and slot k:
     a_k      = <dh, Y_k>                          (dL/dg_k, Y_k the expert output)

@@ -137,7 +137,7 @@ void oracle_e4m3_encode_n(const float* x, int64_t n, uint8_t* out) {
 
 /* ------------------------------------------------------------------------ */
 /* A1: router affinity  s[t,i] = sigmoid(u_t . e_i)                          */
-/* [IFS] MoE paragraph (sigmoid affinity to each expert's centroid);         */
+/* [IFS] MoE-routing paragraph: s = sigmoid of the token-centroid product;   */
 /* [LINEAGE] "The notation" (score s_(i,t)).                                 */
 /* READING: bf16 inputs; FP32 sum in increasing k, one fma per term (every   */
 /* bf16*bf16 product is exact in FP32); no temperature, no 1/sqrt(d).        */
@@ -157,10 +157,9 @@ void oracle_router_scores(const uint16_t* u, const uint16_t* e, int64_t T, int d
 
 /* ------------------------------------------------------------------------ */
 /* A2: biased top-K selection and gate normalisation                         */
-/* [IFS] bias paragraph: a per-expert bias is added to the affinity for the  */
-/* top-K choice only; the gate uses the raw score.  [IFS] MoE paragraph:     */
-/* gates are normalised over the chosen experts.  [LINEAGE] "The notation":  */
-/* chosen iff s+b is among the top K; b does not affect g.                   */
+/* [IFS] bias paragraph: b_i shifts expert i's rank, not its gate.  [IFS]    */
+/* MoE-routing paragraph: g = s / (sum of s over the chosen set).            */
+/* [LINEAGE] "The notation": chosen iff s+b is among the top K; g uses s.    */
 /* READING: key = fl32(s + b) with -0 -> +0 and NaN -> -inf; rank experts by */
 /* (key descending, index ascending) and the first K are slots 0..K-1;       */
 /* D = FP32 sum of the chosen raw s in slot order; g = fl32(s / D); if D = 0 */
@@ -203,7 +202,7 @@ void oracle_topk_from_scores(const float* s, const float* bias, int64_t T, int E
 }
 
 /* ------------------------------------------------------------------------ */
-/* A2, group-limited variant.  [IFS] MoE-routing paragraph: each token is    */
+/* A2, group-limited variant.  [IFS] MoE-routing paragraph: each token is   */
 /* sent to at most 4 nodes.  The pages give no rule for picking the nodes.   */
 /* READING: the E experts form n_groups groups of E/n_groups consecutive     */
 /* indices; a group's score is the largest key (as above) of its experts;    */

@@ -1,12 +1,10 @@
-// Router: sigmoid affinity of every token to every expert centroid, then the
-// biased top-K choice with gates normalised over the chosen experts.
+// Router: s = sigmoid(u . e_i) for every token and routed expert, then the
+// biased top-K choice and the gates.
 //
-// "DeepSeek-V3 Technical Report" notes (learn.ifs.name), MoE-routing
-// paragraph: each token picks the top 8 of 256 routed experts by sigmoid
-// affinity to the expert's centroid, gates normalised over the chosen ones;
-// bias paragraph: a per-expert bias enters the top-K choice only.
-// nlp-lineage summary, "The notation": chosen iff s + b is among the top K,
-// b never changes the gate g.
+// Sources: "DeepSeek-V3 Technical Report" notes (learn.ifs.name), MoE-routing
+// and bias paragraphs; nlp-lineage summary, "The notation".  As computed here:
+// expert i is in token t's set iff s[t,i] + b_i ranks among the token's K
+// largest; g = s / (sum of s over the set); b takes part in the ranking only.
 //
 // Affinity kernel: a register-tiled FP32 VALU GEMM.  Each output's dot product
 // is one FMA chain in increasing k (bf16 products are exact in FP32, so the
