@@ -202,7 +202,7 @@ void oracle_topk_from_scores(const float* s, const float* bias, int64_t T, int E
 }
 
 /* ------------------------------------------------------------------------ */
-/* A2, group-limited variant.  [IFS] MoE-routing paragraph: each token is   */
+/* A2, group-limited variant.  [IFS] MoE-routing paragraph: each token is    */
 /* sent to at most 4 nodes.  The pages give no rule for picking the nodes.   */
 /* READING: the E experts form n_groups groups of E/n_groups consecutive     */
 /* indices; a group's score is the largest key (as above) of its experts;    */
