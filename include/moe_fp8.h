@@ -148,6 +148,7 @@ int moe_seq_balance_loss(const float* scores, const int32_t* topk_idx, int64_t T
  * moe_router_topk writes); other input gives unspecified rows but no
  * out-of-bounds access.  ws: scratch of moe_dispatch_workspace_bytes(T, E).
  */
+/* 0 outside moe_dispatch's limits (T outside [1, 2^31), E outside [1, 256]). */
 size_t moe_dispatch_workspace_bytes(int64_t T, int E);
 int moe_dispatch(const int32_t* topk_idx, int64_t T, int K, int E, int include_shared,
                  int32_t* expert_count, int32_t* group_offset, int32_t* row_token,
@@ -247,7 +248,8 @@ int fp8_quant_128x128(const float* w, int64_t rows, int cols, uint8_t* q, float*
  * call cannot check).  Limits outside these return MOE_ERR_UNSUPPORTED.
  */
 /* Scratch bytes for a grouped GEMM with G groups, M_total rows, N columns and
- * inner dimension K (0 for G < 1, M_total < 0, N < 1 or K < 1). */
+ * inner dimension K; 0 outside the call's limits (G outside [1, 65535],
+ * M_total outside [0, 2^31), N < 1, K outside [1, 16384]). */
 size_t moe_gemm_workspace_bytes(int G, int64_t M_total, int N, int K);
 int grouped_gemm_fp8_blockscaled(const uint8_t* a_q, const float* a_scale,
                                  const int32_t* a_row_index, const int32_t* group_offset,
@@ -330,6 +332,8 @@ int moe_bias_update(float* bias, const int32_t* expert_count, int E, int64_t tot
  * its slots of `packed`.  The pages name the expert only as FFN_i; the SwiGLU
  * form is this library's reading.
  */
+/* Bytes of the packed weights of n_groups experts; 0 for sizes no call takes
+ * (n_groups outside [1, 65537], d or I outside [1, 65536]). */
 size_t moe_packed_weight_bytes(int n_groups, int d, int I);
 int moe_prepare_expert_weights(const float* w1, const float* w3, const float* w2,
                                int expert_index, int n_groups, int d, int I, void* packed,
@@ -458,6 +462,7 @@ int moe_wgrad_operands(const float* dh, const float* topk_gate, const int32_t* s
  * Limits: n_kb * 128 * max(d, 2I) < 2^32 (32-bit byte offsets into one
  * group's operands), G * max(d, 2I) < 2^31; MOE_ERR_UNSUPPORTED otherwise.
  */
+/* 0 outside [1, 65535] groups or d, I outside [1, 65536]. */
 size_t moe_wgrad_workspace_bytes(int G, int d, int I);
 int moe_wgrad(const int32_t* kb_start, int G, int n_kb, int d, int I, const uint8_t* dyT_q, const float* dyT_scale,
               const uint8_t* hT_q, const float* hT_scale, const uint8_t* dzT_q, const float* dzT_scale,
@@ -477,6 +482,9 @@ int moe_wgrad(const int32_t* kb_start, int G, int n_kb, int d, int I, const uint
  * 1 <= K <= min(E, 16), T*(K+1) < 2^31, T*d < 2^32 and T*(K+1)*I < 2^32
  * (32-bit byte offsets of the GEMM inputs); MOE_ERR_UNSUPPORTED otherwise.
  */
+/* 0 outside moe_layer_forward's limits (the ones above that involve only
+ * these sizes: T >= 1, E in [1, 256], K in [1, 16], d and I in [1, 16384],
+ * T*(K+1) < 2^31). */
 size_t moe_layer_workspace_bytes(int64_t T, int d, int E, int K, int I);
 int moe_layer_forward(const void* u_bf16, const void* centroids_bf16, const float* bias,
                       const void* packed_weights, int64_t T, int d, int E, int K, int I,
