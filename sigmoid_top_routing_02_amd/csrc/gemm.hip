@@ -850,7 +850,13 @@ __device__ __forceinline__ ring_v4i uni(ring_v4i r) {
     for (int i = 0; i < 4; ++i) o[i] = __builtin_amdgcn_readfirstlane(r[i]);
     return o;
 }
-// global -> LDS DMA: lane l's bytes land at lds + l * size (lds wave-uniform)
+// global -> LDS DMA: lane l's bytes land at lds + l * size (lds wave-uniform).
+// The LDS address goes through m0, set in the same asm block as the DMA that
+// reads it.  The compiler warns that a clobbered m0 may not be preserved; the
+// ring kernel's code has no other m0 user (its assembly writes m0 only in
+// these blocks), so nothing live is lost.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void ring_dma16(ring_v4i r_, uint32_t voff, uint32_t soff_, uint32_t lds_) {
     const ring_v4i r = uni(r_);
     const uint32_t soff = uni(soff_), lds = uni(lds_);
@@ -863,6 +869,7 @@ __device__ __forceinline__ void ring_dma4(ring_v4i r_, uint32_t voff, uint32_t s
     asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dword %0, %1, %2 offen lds"
                  :: "v"(voff), "s"(r), "s"(soff), "s"(lds) : "memory", "m0");
 }
+#pragma clang diagnostic pop
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)reinterpret_cast<uintptr_t>(p);
 }
