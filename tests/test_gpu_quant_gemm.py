@@ -122,6 +122,8 @@ def _int_operands(M, N, K, G, seed):
     ([300], 384, 256),                 # N % 256 == 128, masked half tile (128)
     ([5, 40, 0, 33, 9, 64], 512, 384), # ragged groups, 32-row tiles
     ([7, 31, 70], 384, 256),           # N % 256 == 128 with 32-row tiles
+    ([5, 40, 0, 33, 9, 64], 512, 640), # 32-row tiles of five slices
+    ([7, 31, 70], 384, 1024),          # N % 256 == 128, 32-row tiles of eight slices
 ])
 def test_gemm_integer_exact(sizes, N, K):
     """Exact integer results pin the MFMA operand/accumulator layouts, the
@@ -294,8 +296,11 @@ def check_codes_close(q, s, q_ref, s_ref, x_ref, x_gpu):
     output tolerance, and every dequantised GPU value lies within half an E4M3
     step (at its code) of the GPU's own value plus the GPU-vs-oracle
     difference of that value: a code can only differ from the oracle's where
-    the two (both within tolerance) values round differently.  A wrong scale
-    or a wrong code fails.  Returns how many codes differ from the oracle's."""
+    the two (both within tolerance) values round differently.  The quantiser
+    scales in FP32 (the value times the rounded 448/amax, dequantised by the
+    rounded amax/448): three roundings of at most 2^-24 each, so the bound
+    also holds 2^-22 |x|.  A wrong scale or a wrong code fails.  Returns how
+    many codes differ from the oracle's."""
     s64, sr64 = s.astype(np.float64), s_ref.astype(np.float64)
     assert np.all(np.abs(s64 / sr64 - 1) <= TOL)
     table = oracle.e4m3_table()
@@ -312,7 +317,7 @@ def check_codes_close(q, s, q_ref, s_ref, x_ref, x_gpu):
     deq = table[q] * sc
     xg = np.asarray(x_gpu, np.float64)
     xr = np.asarray(x_ref, np.float64)
-    bound = half[q] * sc * (1 + 1e-6) + np.abs(xg - xr) * (1 + 1e-6) + 1e-7 * sc
+    bound = half[q] * sc * (1 + 1e-6) + np.abs(xg - xr) * (1 + 1e-6) + 1e-7 * sc + 2.0 ** -22 * np.abs(xr)
     bad = np.abs(deq - xr) > bound
     assert not bad.any(), f"{int(bad.sum())} E4M3 codes further from the exact value than allowed"
     return int((table[q] != table[q_ref]).sum())
@@ -417,7 +422,7 @@ def _zipf_sizes(n, total, rng):
     return s
 
 
-@pytest.mark.parametrize("kind", ["rows128_short_k", "rows128_long_k", "rows32"])
+@pytest.mark.parametrize("kind", ["rows128_short_k", "rows128_long_k", "rows32", "rows32_long_k"])
 def test_gemm_multi_tile_exact_pow2_scales(kind):
     """The persistent schedules over many more tiles than CUs (each block runs
     several tiles, so the tile-to-tile hand-over -- the next tile's DMAs
@@ -427,11 +432,14 @@ def test_gemm_multi_tile_exact_pow2_scales(kind):
     oracle.  rows128_short_k: 26 groups, ~40k rows, 128-row tiles of 5 K
     slices (the kernel whose DMA ring runs on across tiles); rows128_long_k:
     the same groups with 18 K slices (the kernel that restarts its pipeline
-    per tile); rows32: 1500 groups of 0..60 rows (32-row tiles)."""
-    rng = np.random.default_rng(8 if kind == "rows32" else 7)
+    per tile); rows32: 1500 groups of 0..60 rows (32-row tiles of 3 slices);
+    rows32_long_k: the same groups with 8 slices, through the SwiGLU
+    epilogues too."""
+    rows32 = kind.startswith("rows32")
+    rng = np.random.default_rng(8 if rows32 else 7)
     N = 512
-    K = {"rows128_short_k": 640, "rows128_long_k": 2304, "rows32": 384}[kind]
-    if kind != "rows32":
+    K = {"rows128_short_k": 640, "rows128_long_k": 2304, "rows32": 384, "rows32_long_k": 1024}[kind]
+    if not rows32:
         sizes = _zipf_sizes(26, 40_000, rng)
     else:
         sizes = rng.integers(0, 61, 1500)
@@ -441,7 +449,7 @@ def test_gemm_multi_tile_exact_pow2_scales(kind):
     bm = 32 if M <= 64 * G else 128
     n_tiles = int(np.sum((sizes + bm - 1) // bm)) * (N // 256)
     say(f"gemm multi-tile {kind}: G={G} M={M} N={N} K={K}, {bm}-row tiles, {n_tiles} tiles")
-    assert (bm == 128) == (kind != "rows32") and n_tiles > 2 * 256
+    assert (bm == 128) == (not rows32) and n_tiles > 2 * 256
     qa, sa, qb, sb = _pow2_operands(sizes, N, K, seed=M)
     extra = 37
     rows = rng.permutation(M + extra)[:M].astype(np.int32)           # gather from a larger A
