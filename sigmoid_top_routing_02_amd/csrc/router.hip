@@ -166,7 +166,7 @@ __global__ __launch_bounds__(NTHREADS) void router_scores_kernel(
 // is read as a broadcast).  The loads run SM_PF chunks ahead through a ring of
 // registers, so their latency hides behind the FMAs of the chunks between.
 // Every logit is still one FMA chain in increasing k.
-constexpr int SM_TOK = 4, SM_EXP = 64;
+constexpr int SM_TOK = 4, SM_EXP = 64, SM_WIN = 8;
 
 template <int SM_KC, int SM_PF>   // SM_KC divides d (the launcher picks it)
 __global__ __launch_bounds__(256) void router_scores_small_kernel(
@@ -237,28 +237,37 @@ __global__ __launch_bounds__(256) void router_scores_small_kernel(
             if (c >= nch) break;
             const int b = c & 1;
             load(i, c + SM_PF);                  // slot i held chunk c, already in LDS
-            // batches of 8 float4 of the centroid row and of u read before
-            // their 32 FMAs, so the LDS latency is paid once per batch
+            // a window of SM_WIN steps (one float4 of the centroid row and
+            // one of u, four FMAs each): the reads of step j + SM_WIN go out
+            // as step j's FMAs retire, so the LDS latency hides behind the
+            // chain (at most 2 (SM_WIN - 1) reads outstanding when a step
+            // waits, within the LDS counter's range)
+            const float4* erow = es[b][lane];
+            const float4* urow = us[b][w];
+            float4 ev[SM_WIN], uv[SM_WIN];
 #pragma unroll
-            for (int jb = 0; jb < Q; jb += 8) {
-                float4 ev[8], uv[8];
+            for (int j = 0; j < SM_WIN; ++j) {
+                ev[j] = erow[j];
+                uv[j] = urow[j];
+            }
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    ev[i] = es[b][lane][jb + i];
-                    uv[i] = us[b][w][jb + i];
+            for (int j = 0; j < Q; ++j) {
+                const int r = j % SM_WIN;
+                acc = __builtin_fmaf(uv[r].x, ev[r].x, acc);
+                acc = __builtin_fmaf(uv[r].y, ev[r].y, acc);
+                acc = __builtin_fmaf(uv[r].z, ev[r].z, acc);
+                acc = __builtin_fmaf(uv[r].w, ev[r].w, acc);
+                if (j + SM_WIN < Q) {
+                    ev[r] = erow[j + SM_WIN];
+                    uv[r] = urow[j + SM_WIN];
                 }
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    acc = __builtin_fmaf(uv[i].x, ev[i].x, acc);
-                    acc = __builtin_fmaf(uv[i].y, ev[i].y, acc);
-                    acc = __builtin_fmaf(uv[i].z, ev[i].z, acc);
-                    acc = __builtin_fmaf(uv[i].w, ev[i].w, acc);
-                }
+                __builtin_amdgcn_sched_barrier(0);   // keep the window's order
             }
             // the chunk's FMAs stay before the barrier (the compiler would
             // otherwise sink them below the next chunk's LDS writes)
             asm volatile("" :: "v"(acc));
-            __syncthreads();                     // every wave is done with buffer b ^ 1's last use
+            // buffer b ^ 1 was last read in chunk c - 1, before the barrier
+            // that ended it, so it can be refilled while others still read b
             put(b ^ 1, (i + 1) % SM_PF);         // chunk c + 1 (past the end: unused)
             __syncthreads();
         }
