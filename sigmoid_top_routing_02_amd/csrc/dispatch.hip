@@ -12,6 +12,9 @@
 //              scan over experts gives group_offset.
 //  3. scatter: row = group_offset[e] + chunk_prefix[c][e]
 //              + popcount(mask[c][e] & lanes-below-t).
+// Up to SMALL_T tokens the three steps run in one block with the masks and
+// prefixes in LDS (one launch instead of three; the same arithmetic, so the
+// same result).
 #include "device_math.h"
 #include "kernels.h"
 #include "moe_fp8.h"
@@ -122,6 +125,68 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     }
 }
 
+// The three steps above in one 1024-thread block for T <= SMALL_T (at most
+// SMALL_T / CHUNK chunks of masks and prefixes, held in LDS).
+constexpr int SMALL_T = 1024;
+constexpr int SMALL_CH = SMALL_T / CHUNK;
+
+__global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t* __restrict__ idx, int64_t T, int K,
+                                                              int E, int include_shared,
+                                                              int32_t* __restrict__ count,
+                                                              int32_t* __restrict__ group_offset,
+                                                              int32_t* __restrict__ row_token,
+                                                              int32_t* __restrict__ slot_row) {
+    __shared__ unsigned long long m[SMALL_CH][256];
+    __shared__ int32_t pre[SMALL_CH][256];
+    __shared__ int32_t cnt[256], inc[256];
+    const int tid = threadIdx.x;
+    const int nch = (int)((T + CHUNK - 1) / CHUNK);
+    const int n = (int)T * K;
+    for (int i = tid; i < nch * 256; i += 1024) m[i / 256][i % 256] = 0ull;
+    __syncthreads();
+    for (int j = tid; j < n; j += 1024) {
+        const int t = j / K;
+        const int ex = idx[j];
+        if (ex >= 0 && ex < E) atomicOr(&m[t / CHUNK][ex], 1ull << (t % CHUNK));
+    }
+    __syncthreads();
+    if (tid < 256) {
+        int32_t run = 0;
+        for (int c = 0; c < nch; ++c) {
+            pre[c][tid] = run;
+            run += __popcll(m[c][tid]);     // experts >= E have empty masks
+        }
+        cnt[tid] = run;
+        inc[tid] = run;
+        if (tid < E) count[tid] = run;
+    }
+    __syncthreads();
+    // inclusive Hillis-Steele scan over the 256 expert totals
+    for (int off = 1; off < 256; off <<= 1) {
+        const int32_t v = (tid < 256 && tid >= off) ? inc[tid - off] : 0;
+        __syncthreads();
+        if (tid < 256) inc[tid] += v;
+        __syncthreads();
+    }
+    if (tid < E) group_offset[tid] = inc[tid] - cnt[tid];
+    if (tid == 0) {
+        group_offset[E] = inc[255];
+        if (include_shared) group_offset[E + 1] = inc[255] + (int32_t)T;
+    }
+    for (int j = tid; j < n; j += 1024) {
+        const int t = j / K;
+        const int ex = idx[j];
+        if (ex < 0 || ex >= E) continue;
+        const int c = t / CHUNK, tl = t % CHUNK;
+        const uint64_t below = (tl == 0) ? 0ull : (m[c][ex] & ((1ull << tl) - 1ull));
+        const int32_t row = inc[ex] - cnt[ex] + pre[c][ex] + __popcll(below);
+        row_token[row] = t;
+        slot_row[j] = row;
+    }
+    if (include_shared)
+        for (int t = tid; t < (int)T; t += 1024) row_token[(int64_t)T * K + t] = t;
+}
+
 typedef uint32_t perm_v4u __attribute__((ext_vector_type(4)));
 
 // One wave per 64 16-byte words of one output row (grid.x: column blocks,
@@ -225,6 +290,11 @@ size_t dispatch_ws_bytes(int64_t T, int E) {
 hipError_t launch_dispatch(const int32_t* idx, int64_t T, int K, int E, int include_shared,
                            int32_t* count, int32_t* group_offset, int32_t* row_token,
                            int32_t* slot_row, void* ws, hipStream_t st) {
+    if (T <= SMALL_T) {
+        hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(1024), 0, st, idx, T, K, E, include_shared,
+                           count, group_offset, row_token, slot_row);
+        return hipGetLastError();
+    }
     const int64_t nchunk = (T + CHUNK - 1) / CHUNK;
     DispatchWs w = carve(ws, nchunk, E);
     hipLaunchKernelGGL(dispatch_hist_kernel, dim3((unsigned)nchunk), dim3(256), 0, st, idx, T, K,

@@ -119,8 +119,9 @@ def _rand_idx(T, E, K, seed, skew=False):
     return np.stack([rng.choice(E, K, replace=False, p=p) for _ in range(T)]).astype(np.int32)
 
 
+# T <= 1024 runs the one-block kernel, larger T the three-launch path
 DISPATCH_CASES = [(1, 4, 2), (63, 16, 4), (64, 16, 4), (65, 16, 4), (1000, 256, 8), (4097, 256, 8),
-                  (300, 8, 8), (2000, 200, 16)]
+                  (300, 8, 8), (2000, 200, 16), (1024, 256, 16), (1025, 256, 8)]
 
 
 @pytest.mark.parametrize("T,E,K", DISPATCH_CASES)
