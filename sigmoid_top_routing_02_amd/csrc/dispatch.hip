@@ -76,9 +76,18 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(int64_t nchunk, int6
     const int e = threadIdx.x;
     int32_t run = 0;
     if (e < E) {
-        for (int64_t c = 0; c < nchunk; ++c) {
-            w.prefix[c * E + e] = run;
-            run += w.cnt[c * E + e];
+        // the chunk counts are loaded SCAN_BATCH at a time, so the running
+        // sum waits for one memory latency per batch, not per chunk
+        constexpr int SCAN_BATCH = 16;
+        for (int64_t c0 = 0; c0 < nchunk; c0 += SCAN_BATCH) {
+            int32_t v[SCAN_BATCH];
+#pragma unroll
+            for (int i = 0; i < SCAN_BATCH; ++i) v[i] = (c0 + i < nchunk) ? w.cnt[(c0 + i) * E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < SCAN_BATCH; ++i) {
+                if (c0 + i < nchunk) w.prefix[(c0 + i) * E + e] = run;
+                run += v[i];
+            }
         }
         count[e] = run;
     }
