@@ -67,43 +67,71 @@ __global__ __launch_bounds__(256) void dispatch_hist_kernel(const int32_t* __res
     }
 }
 
-// One block: expert e is thread e (E <= 256).
-__global__ __launch_bounds__(256) void dispatch_scan_kernel(int64_t nchunk, int64_t T, int K,
-                                                            int E, int include_shared,
-                                                            DispatchWs w, int32_t* count,
-                                                            int32_t* group_offset) {
+// One block of 1024 threads: expert e is handled by threads e, e+256, e+512
+// and e+768, each owning a quarter of the chunks.  A quarter's total is summed
+// first, the quarters before it give its starting offset, and then its chunk
+// prefixes are written (integer sums: the result is the same as one thread
+// walking all chunks).  The chunk counts are loaded SCAN_BATCH at a time, so
+// each running sum waits for one memory latency per batch, not per chunk.
+constexpr int SCAN_PARTS = 4;
+__global__ __launch_bounds__(256 * SCAN_PARTS) void dispatch_scan_kernel(int64_t nchunk, int64_t T, int K,
+                                                                         int E, int include_shared,
+                                                                         DispatchWs w, int32_t* count,
+                                                                         int32_t* group_offset) {
+    constexpr int SCAN_BATCH = 16;
+    __shared__ int32_t psum[SCAN_PARTS][256];
     __shared__ int32_t tot[256];
-    const int e = threadIdx.x;
-    int32_t run = 0;
+    const int e = threadIdx.x & 255, part = threadIdx.x >> 8;
+    const int64_t q = (nchunk + SCAN_PARTS - 1) / SCAN_PARTS;
+    const int64_t c_lo = min(nchunk, part * q), c_hi = min(nchunk, c_lo + q);
+    // the sum of this quarter's counts
+    int32_t qsum = 0;
     if (e < E) {
-        // the chunk counts are loaded SCAN_BATCH at a time, so the running
-        // sum waits for one memory latency per batch, not per chunk
-        constexpr int SCAN_BATCH = 16;
-        for (int64_t c0 = 0; c0 < nchunk; c0 += SCAN_BATCH) {
+        for (int64_t c0 = c_lo; c0 < c_hi; c0 += SCAN_BATCH) {
             int32_t v[SCAN_BATCH];
 #pragma unroll
-            for (int i = 0; i < SCAN_BATCH; ++i) v[i] = (c0 + i < nchunk) ? w.cnt[(c0 + i) * E + e] : 0;
+            for (int i = 0; i < SCAN_BATCH; ++i) v[i] = (c0 + i < c_hi) ? w.cnt[(c0 + i) * E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < SCAN_BATCH; ++i) qsum += v[i];
+        }
+    }
+    psum[part][e] = qsum;
+    __syncthreads();
+    // the chunk prefixes of this quarter, starting after the quarters before it
+    int32_t run = 0;
+    for (int p = 0; p < part; ++p) run += psum[p][e];
+    if (e < E) {
+        for (int64_t c0 = c_lo; c0 < c_hi; c0 += SCAN_BATCH) {
+            int32_t v[SCAN_BATCH];
+#pragma unroll
+            for (int i = 0; i < SCAN_BATCH; ++i) v[i] = (c0 + i < c_hi) ? w.cnt[(c0 + i) * E + e] : 0;
 #pragma unroll
             for (int i = 0; i < SCAN_BATCH; ++i) {
-                if (c0 + i < nchunk) w.prefix[(c0 + i) * E + e] = run;
+                if (c0 + i < c_hi) w.prefix[(c0 + i) * E + e] = run;
                 run += v[i];
             }
         }
-        count[e] = run;
     }
-    tot[e] = (e < E) ? run : 0;
+    // expert totals, then the inclusive Hillis-Steele scan over 256 entries
+    int32_t total = 0;
+    if (part == 0) {
+        for (int p = 0; p < SCAN_PARTS; ++p) total += psum[p][e];
+        if (e < E) count[e] = total;
+        tot[e] = (e < E) ? total : 0;
+    }
     __syncthreads();
-    // inclusive Hillis-Steele scan over 256 entries
     for (int off = 1; off < 256; off <<= 1) {
-        const int32_t v = (e >= off) ? tot[e - off] : 0;
+        const int32_t v = (part == 0 && e >= off) ? tot[e - off] : 0;
         __syncthreads();
-        tot[e] += v;
+        if (part == 0) tot[e] += v;
         __syncthreads();
     }
-    if (e < E) group_offset[e] = tot[e] - run;   // exclusive
-    if (e == 0) {
-        group_offset[E] = tot[255];
-        if (include_shared) group_offset[E + 1] = tot[255] + (int32_t)T;
+    if (part == 0) {
+        if (e < E) group_offset[e] = tot[e] - total;   // exclusive
+        if (e == 0) {
+            group_offset[E] = tot[255];
+            if (include_shared) group_offset[E + 1] = tot[255] + (int32_t)T;
+        }
     }
 }
 
@@ -308,7 +336,7 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t T, int K, int E, int incl
     DispatchWs w = carve(ws, nchunk, E);
     hipLaunchKernelGGL(dispatch_hist_kernel, dim3((unsigned)nchunk), dim3(256), 0, st, idx, T, K,
                        E, w);
-    hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(256), 0, st, nchunk, T, K, E,
+    hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(256 * SCAN_PARTS), 0, st, nchunk, T, K, E,
                        include_shared, w, count, group_offset);
     hipLaunchKernelGGL(dispatch_scatter_kernel, dim3((unsigned)nchunk), dim3(256), 0, st, idx, T,
                        K, E, include_shared, w, group_offset, row_token, slot_row);
