@@ -1354,23 +1354,45 @@ __global__ __launch_bounds__(256) void gemm_tile_list_kernel(const int32_t* __re
 // a_sT[j][m] = a_s[am][j] with am = a_rows[m] (or m): the A scales gathered
 // into GEMM row order and made slice-major, so that the scales of one slice
 // for a tile's rows are contiguous.  One block per 64 rows, through LDS.
+// The slice-major copy of the A scales of rows m0 .. m0+63 (one 256-thread
+// block): four threads per row take the row's source index once and read its
+// ns scales (thread q of the row reads slices q, q+4, ...; all its loads go
+// out before its first LDS store), then the block writes each slice's 64
+// consecutive rows.
+__device__ __forceinline__ void gather_scales_64(const float* __restrict__ a_s, const int32_t* __restrict__ a_rows,
+                                                 int64_t M_total, int ns, float* __restrict__ a_sT, int64_t m0,
+                                                 float (*t)[MAX_SLICES + 1]) {
+    constexpr int PER_Q = MAX_SLICES / 4;
+    const int tid = threadIdx.x;
+    const int r = tid >> 2, qq = tid & 3;
+    const int64_t m = m0 + r;
+    const bool live = m < M_total;
+    const float* row = a_s + (live ? (a_rows ? (int64_t)a_rows[m] : m) : 0) * ns;
+    float v[PER_Q];
+#pragma unroll
+    for (int k = 0; k < PER_Q; ++k) {
+        const int j = qq + 4 * k;
+        v[k] = (live && j < ns) ? row[j] : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < PER_Q; ++k) {
+        const int j = qq + 4 * k;
+        if (j < ns) t[r][j] = v[k];
+    }
+    __syncthreads();
+    for (int i = tid; i < 64 * ns; i += 256) {
+        const int j = i >> 6, rr = i & 63;
+        const int64_t mm = m0 + rr;
+        if (mm < M_total) a_sT[j * M_total + mm] = t[rr][j];
+    }
+}
+
 __global__ __launch_bounds__(256) void gemm_scale_gather_kernel(const float* __restrict__ a_s,
                                                                 const int32_t* __restrict__ a_rows,
                                                                 int64_t M_total, int ns,
                                                                 float* __restrict__ a_sT) {
     __shared__ float t[64][MAX_SLICES + 1];
-    const int64_t m0 = (int64_t)blockIdx.x * 64;
-    for (int i = threadIdx.x; i < 64 * ns; i += 256) {
-        const int r = i / ns, j = i - r * ns;
-        const int64_t m = m0 + r;
-        if (m < M_total) t[r][j] = a_s[(a_rows ? (int64_t)a_rows[m] : m) * ns + j];
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < 64 * ns; i += 256) {
-        const int j = i >> 6, r = i & 63;
-        const int64_t m = m0 + r;
-        if (m < M_total) a_sT[j * M_total + m] = t[r][j];
-    }
+    gather_scales_64(a_s, a_rows, M_total, ns, a_sT, (int64_t)blockIdx.x * 64, t);
 }
 
 // The three preparation steps above in one launch, for G <= PREP_MAX_G (the
@@ -1391,30 +1413,7 @@ __global__ __launch_bounds__(256) void gemm_prep_kernel(const int32_t* __restric
     __shared__ int32_t part[256];
     __shared__ float t[64][MAX_SLICES + 1];
     if ((int)blockIdx.x >= nl) {
-        // every load of the thread is issued before the first LDS store (the
-        // gathered scales are a latency-bound handful per thread)
-        constexpr int PER_T = 64 * MAX_SLICES / 256;
-        const int64_t m0 = (int64_t)(blockIdx.x - nl) * 64;
-        float v[PER_T];
-#pragma unroll
-        for (int k = 0; k < PER_T; ++k) {
-            const int i = threadIdx.x + k * 256;
-            const int r = i / ns, j = i - r * ns;
-            const int64_t m = m0 + r;
-            v[k] = (i < 64 * ns && m < M_total) ? a_s[(a_rows ? (int64_t)a_rows[m] : m) * ns + j] : 0.0f;
-        }
-#pragma unroll
-        for (int k = 0; k < PER_T; ++k) {
-            const int i = threadIdx.x + k * 256;
-            const int r = i / ns, j = i - r * ns;
-            if (i < 64 * ns) t[r][j] = v[k];
-        }
-        __syncthreads();
-        for (int i = threadIdx.x; i < 64 * ns; i += 256) {
-            const int j = i >> 6, r = i & 63;
-            const int64_t m = m0 + r;
-            if (m < M_total) a_sT[j * M_total + m] = t[r][j];
-        }
+        gather_scales_64(a_s, a_rows, M_total, ns, a_sT, (int64_t)(blockIdx.x - nl) * 64, t);
         return;
     }
     // exclusive scan of ceil(rows_g / BM): thread i owns groups [i*c, i*c + c)
