@@ -22,7 +22,9 @@ namespace {
 // issued before any arithmetic so that QU loads per lane are in flight.
 constexpr int QU = 4;
 
-template <bool IN_F32>
+// IDX32: the tile count fits 31 bits, so a tile's row and column block come
+// from a 32-bit division (a 64-bit one is a long instruction sequence per tile)
+template <bool IN_F32, bool IDX32>
 __global__ __launch_bounds__(256) void quant_1x128_kernel(const void* __restrict__ x,
                                                           int64_t rows, int cols,
                                                           uint8_t* __restrict__ q,
@@ -41,8 +43,16 @@ __global__ __launch_bounds__(256) void quant_1x128_kernel(const void* __restrict
             live[u] = g < total;
             const int64_t tile = live[u] ? g >> 4 : 0;
             const int part = (int)(g & 15);
-            const int64_t row = tile / ntile;
-            const int tc = (int)(tile % ntile);
+            int64_t row;
+            int tc;
+            if constexpr (IDX32) {
+                const uint32_t t32 = (uint32_t)tile, r32 = t32 / (uint32_t)ntile;
+                row = r32;
+                tc = (int)(t32 - r32 * (uint32_t)ntile);
+            } else {
+                row = tile / ntile;
+                tc = (int)(tile % ntile);
+            }
             off[u] = row * cols + (int64_t)tc * 128 + part * 8;
             sidx[u] = part == 0 ? row * ntile + tc : -1;
             if (live[u]) {
@@ -142,12 +152,22 @@ hipError_t launch_quant_1x128(const void* x, int in_is_f32, int64_t rows, int co
     const int64_t threads = rows * (int64_t)(cols / 128) * 16;
     int64_t blocks = (threads + 256 * QU - 1) / (256 * QU);
     if (blocks > 65536) blocks = 65536;
-    if (in_is_f32)
-        hipLaunchKernelGGL(quant_1x128_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, st, x,
-                           rows, cols, q, scale);
-    else
-        hipLaunchKernelGGL(quant_1x128_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, st, x,
-                           rows, cols, q, scale);
+    const bool idx32 = rows * (int64_t)(cols / 128) < ((int64_t)1 << 31);
+    if (in_is_f32) {
+        if (idx32)
+            hipLaunchKernelGGL((quant_1x128_kernel<true, true>), dim3((unsigned)blocks), dim3(256), 0, st, x,
+                               rows, cols, q, scale);
+        else
+            hipLaunchKernelGGL((quant_1x128_kernel<true, false>), dim3((unsigned)blocks), dim3(256), 0, st, x,
+                               rows, cols, q, scale);
+    } else {
+        if (idx32)
+            hipLaunchKernelGGL((quant_1x128_kernel<false, true>), dim3((unsigned)blocks), dim3(256), 0, st, x,
+                               rows, cols, q, scale);
+        else
+            hipLaunchKernelGGL((quant_1x128_kernel<false, false>), dim3((unsigned)blocks), dim3(256), 0, st, x,
+                               rows, cols, q, scale);
+    }
     return hipGetLastError();
 }
 
