@@ -44,12 +44,19 @@ struct WgradSrc {
 
 __device__ __forceinline__ float sigm(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
-// the weight of row r's dY: its slot's gate (routed rows), 1 (shared rows)
+// the weight of row r's dY: its slot's gate (routed rows), 1 (shared rows).
+// The token's K slot rows (K <= 16) are loaded together, then the gate of the
+// first slot that holds r.
 __device__ __forceinline__ float row_weight(const WgradSrc& s, int64_t r, int64_t t) {
     if (s.shared_row0 >= 0 && r >= s.shared_row0) return 1.0f;
-    for (int k = 0; k < s.K; ++k)
-        if (s.slot_row[t * s.K + k] == r) return s.gate[t * s.K + k];
-    return 0.0f;
+    int32_t sr[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) sr[k] = k < s.K ? s.slot_row[t * s.K + k] : -1;
+    int hit = -1;
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+        if (hit < 0 && sr[k] == r) hit = k;
+    return hit >= 0 ? s.gate[t * s.K + hit] : 0.0f;
 }
 
 template <int SRC, bool BLOCK_SCALE>
@@ -92,43 +99,72 @@ __global__ __launch_bounds__(256) void wgrad_operand_kernel(WgradSrc s, const in
         s_w[tid] = w;
     }
     __syncthreads();
-    {   // values: thread = 4 columns c0 + 4 (tid & 31), rows (tid >> 5), +8, ...
+    {   // values: thread = 4 columns c0 + 4 (tid & 31), rows (tid >> 5) + 8 j.  The
+        // loads of NB rows go out before any of them is used, so NB loads per
+        // lane are in flight instead of one (the rows' arithmetic is unchanged)
         const int cq = (tid & 31) * 4, c = c0 + cq;
-        for (int i = tid >> 5; i < 128; i += 8) {
-            const int64_t r = rb + i;
-            float v[4] = {0.f, 0.f, 0.f, 0.f};
-            if (r < rend) {
-                if constexpr (SRC == SRC_DY) {
-                    const float4 x = *reinterpret_cast<const float4*>(s.dh + s_tok[i] * s.d + c);
-                    const float w = s_w[i];
-                    v[0] = w * x.x; v[1] = w * x.y; v[2] = w * x.z; v[3] = w * x.w;
-                } else if constexpr (SRC == SRC_X) {
-                    const uint2 x = *reinterpret_cast<const uint2*>(s.u + s_tok[i] * s.d + c);
-                    v[0] = bf16_lo(x.x); v[1] = bf16_hi(x.x); v[2] = bf16_lo(x.y); v[3] = bf16_hi(x.y);
-                } else if constexpr (SRC == SRC_H) {
-                    const float* zr = s.z + r * 2 * s.I + (c >> 7) * 256 + (c & 127);
-                    const float4 zg = *reinterpret_cast<const float4*>(zr);
-                    const float4 zu = *reinterpret_cast<const float4*>(zr + 128);
-                    const float g4[4] = {zg.x, zg.y, zg.z, zg.w}, u4[4] = {zu.x, zu.y, zu.z, zu.w};
+        const int i0 = tid >> 5;
+        // (every load reads a valid row -- rows past the group read the token
+        // of s_tok = 0, or the group's last row -- and such rows' values are
+        // zeroed below, so no load needs a condition)
+        constexpr int NB = (SRC == SRC_DY || SRC == SRC_X) ? 16 : 8;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) v[q] = g4[q] * sigm(g4[q]) * u4[q];
+        for (int b = 0; b < 16; b += NB) {
+            float4 la[NB], lb[NB], lc[NB];
+            uint2 lx[NB];
+#pragma unroll
+            for (int jj = 0; jj < NB; ++jj) {
+                const int i = i0 + 8 * (b + jj);
+                const int64_t rl = min(rb + i, rend - 1);
+                if constexpr (SRC == SRC_DY) {
+                    la[jj] = *reinterpret_cast<const float4*>(s.dh + s_tok[i] * s.d + c);
+                } else if constexpr (SRC == SRC_X) {
+                    lx[jj] = *reinterpret_cast<const uint2*>(s.u + s_tok[i] * s.d + c);
+                } else if constexpr (SRC == SRC_H) {
+                    const float* zr = s.z + rl * 2 * s.I + (c >> 7) * 256 + (c & 127);
+                    la[jj] = *reinterpret_cast<const float4*>(zr);
+                    lb[jj] = *reinterpret_cast<const float4*>(zr + 128);
                 } else {
                     const int j = c >> 8, w = c & 255, ic = j * 128 + (w & 127);
-                    const float* zr = s.z + r * 2 * s.I + j * 256 + (w & 127);
-                    const float4 zg = *reinterpret_cast<const float4*>(zr);
-                    const float4 zu = *reinterpret_cast<const float4*>(zr + 128);
-                    const float4 dh = *reinterpret_cast<const float4*>(s.dh_row + r * s.I + ic);
-                    const float g4[4] = {zg.x, zg.y, zg.z, zg.w}, u4[4] = {zu.x, zu.y, zu.z, zu.w};
-                    const float d4[4] = {dh.x, dh.y, dh.z, dh.w};
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const float sg = sigm(g4[q]);
-                        v[q] = (w < 128) ? d4[q] * u4[q] * sg * (1.0f + g4[q] * (1.0f - sg)) : d4[q] * (g4[q] * sg);
-                    }
+                    const float* zr = s.z + rl * 2 * s.I + j * 256 + (w & 127);
+                    la[jj] = *reinterpret_cast<const float4*>(zr);
+                    lb[jj] = *reinterpret_cast<const float4*>(zr + 128);
+                    lc[jj] = *reinterpret_cast<const float4*>(s.dh_row + rl * s.I + ic);
                 }
             }
 #pragma unroll
-            for (int q = 0; q < 4; ++q) tile[i][cq + q] = v[q];
+            for (int jj = 0; jj < NB; ++jj) {
+                const int i = i0 + 8 * (b + jj);
+                const int64_t r = rb + i;
+                float v[4] = {0.f, 0.f, 0.f, 0.f};
+                if (r < rend) {
+                    if constexpr (SRC == SRC_DY) {
+                        const float4 x = la[jj];
+                        const float w = s_w[i];
+                        v[0] = w * x.x; v[1] = w * x.y; v[2] = w * x.z; v[3] = w * x.w;
+                    } else if constexpr (SRC == SRC_X) {
+                        const uint2 x = lx[jj];
+                        v[0] = bf16_lo(x.x); v[1] = bf16_hi(x.x); v[2] = bf16_lo(x.y); v[3] = bf16_hi(x.y);
+                    } else if constexpr (SRC == SRC_H) {
+                        const float4 zg = la[jj], zu = lb[jj];
+                        const float g4[4] = {zg.x, zg.y, zg.z, zg.w}, u4[4] = {zu.x, zu.y, zu.z, zu.w};
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) v[q] = g4[q] * sigm(g4[q]) * u4[q];
+                    } else {
+                        const int w = c & 255;
+                        const float4 zg = la[jj], zu = lb[jj], dh = lc[jj];
+                        const float g4[4] = {zg.x, zg.y, zg.z, zg.w}, u4[4] = {zu.x, zu.y, zu.z, zu.w};
+                        const float d4[4] = {dh.x, dh.y, dh.z, dh.w};
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const float sg = sigm(g4[q]);
+                            v[q] = (w < 128) ? d4[q] * u4[q] * sg * (1.0f + g4[q] * (1.0f - sg)) : d4[q] * (g4[q] * sg);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) tile[i][cq + q] = v[q];
+            }
         }
     }
     __syncthreads();
