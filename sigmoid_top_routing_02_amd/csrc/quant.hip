@@ -36,6 +36,8 @@ __global__ __launch_bounds__(256) void quant_1x128_kernel(const void* __restrict
         float v[QU][8];
         int64_t off[QU], sidx[QU];
         bool live[QU];
+        float4 rf[QU][2];     // the raw 16-byte pieces, loaded for every u before any is used
+        uint4 rb[QU];
 #pragma unroll
         for (int u = 0; u < QU; ++u) {
             // every lane of a 16-lane group has the same `live` (total % 16 == 0)
@@ -55,14 +57,25 @@ __global__ __launch_bounds__(256) void quant_1x128_kernel(const void* __restrict
             }
             off[u] = row * cols + (int64_t)tc * 128 + part * 8;
             sidx[u] = part == 0 ? row * ntile + tc : -1;
+            // unconditional (a dead u reads tile 0, a valid address), so the
+            // QU loads are all in flight before the first value is used
+            if constexpr (IN_F32) {
+                const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(x) + off[u]);
+                rf[u][0] = p[0];
+                rf[u][1] = p[1];
+            } else {
+                rb[u] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + off[u]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < QU; ++u) {
             if (live[u]) {
                 if constexpr (IN_F32) {
-                    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(x) + off[u]);
-                    const float4 a = p[0], b = p[1];
+                    const float4 a = rf[u][0], b = rf[u][1];
                     v[u][0] = a.x; v[u][1] = a.y; v[u][2] = a.z; v[u][3] = a.w;
                     v[u][4] = b.x; v[u][5] = b.y; v[u][6] = b.z; v[u][7] = b.w;
                 } else {
-                    const uint4 a = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + off[u]);
+                    const uint4 a = rb[u];
                     v[u][0] = bf16_lo(a.x); v[u][1] = bf16_hi(a.x); v[u][2] = bf16_lo(a.y); v[u][3] = bf16_hi(a.y);
                     v[u][4] = bf16_lo(a.z); v[u][5] = bf16_hi(a.z); v[u][6] = bf16_lo(a.w); v[u][7] = bf16_hi(a.w);
                 }
