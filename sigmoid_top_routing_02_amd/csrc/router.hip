@@ -157,6 +157,150 @@ __global__ __launch_bounds__(NTHREADS) void router_scores_kernel(
     }
 }
 
+// Many tokens: the same chains on the matrix cores.  bf16 x bf16 products are
+// exact in FP32, so one step of a logit's chain is fl(acc + u_k e_k), and the
+// FP32 MFMA with K = 1 (v_mfma_f32_32x32x1_2b_f32: D = a (x) b + C for two
+// 32 x 32 blocks) performs exactly that step on every element, as long as
+// every product and partial sum stays in FP32's normal range (measured on
+// gfx950: bit-identical to the FMA chain on 2.3e8 steps of router-like data
+// and on large-by-tiny products; denormal products and overflow differ).  A
+// chain of such MFMAs in increasing k therefore gives the logits of the FMA
+// chain bit for bit.  The range is certified per block from the bf16 exponent
+// fields f (f' = max(f, 1)) gathered while the inputs are staged:
+//   every nonzero product's last bit is 2^(f'_u + f'_e - 268) >= 2^-126 when
+//   min f'_u + min f'_e >= 142, so every nonzero partial sum is normal;
+//   |sum| < d 2^(max f_u + max f_e - 252) <= 2^126 when
+//   max f_u + max f_e + ceil(log2 d) <= 378 (and no Inf/NaN input, f < 255).
+// A block whose inputs fail either bound recomputes its logits with the FMA
+// chain on the VALU, so every input gets the same result as the VALU kernels.
+//
+// Block: 64 tokens x 128 experts, 4 waves of 32 tokens x 64 experts (the two
+// MFMA blocks: experts 64 we + [0, 32) and + [32, 64)).  Lane l feeds token
+// 32 wt + l % 32 (both MFMA blocks share the tokens) and expert 64 we + l.
+// Chunks of MC k-values of the block's rows are widened to FP32 into LDS
+// (row pitch MC + 4 floats: the 16 lanes of a 16-byte read cover all banks),
+// double-buffered, the next chunk's global loads in flight during this one.
+constexpr int MB_T = 64, MB_E = 128, MC = 32, MP = MC + 4;
+
+__global__ __launch_bounds__(256) void router_scores_mfma_kernel(
+    const uint16_t* __restrict__ u, const uint16_t* __restrict__ e, int64_t T, int d, int E, int lg2d,
+    float* __restrict__ s) {
+    typedef float mv32 __attribute__((ext_vector_type(32)));
+    __shared__ __attribute__((aligned(16))) float us[2][MB_T][MP];
+    __shared__ __attribute__((aligned(16))) float es[2][MB_E][MP];
+    __shared__ int ex_stat[4];                 // min f'_u, max f_u, min f'_e, max f_e
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wt = w >> 1, we = w & 1;
+    const int64_t t0 = (int64_t)blockIdx.x * MB_T;
+    const int e0 = blockIdx.y * MB_E;
+    if (tid == 0) { ex_stat[0] = 1 << 20; ex_stat[1] = 0; ex_stat[2] = 1 << 20; ex_stat[3] = 0; }
+    // loaders: u piece tid (row tid / 4, 8 k-values at part tid % 4); e pieces
+    // tid and tid + 256.  Rows past T or E read the last row and are not stored.
+    const int ur = tid >> 2, up = tid & 3;
+    const uint4* ug = reinterpret_cast<const uint4*>(u + (int64_t)min(t0 + ur, T - 1) * d) + up;
+    const uint4* eg0 = reinterpret_cast<const uint4*>(e + (int64_t)min(e0 + (tid >> 2), E - 1) * d) + up;
+    const uint4* eg1 = reinterpret_cast<const uint4*>(e + (int64_t)min(e0 + 64 + (tid >> 2), E - 1) * d) + up;
+    int mn_u = 1 << 20, mx_u = 0, mn_e = 1 << 20, mx_e = 0;
+    auto stat = [](const uint4& v, int& mn, int& mx) {
+        const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t b = (wd[q] >> (16 * h)) & 0xFFFFu;
+                const int f = (int)((b >> 7) & 0xFFu);
+                mx = f > mx ? f : mx;
+                if (b & 0x7FFFu) {
+                    const int fp = f > 1 ? f : 1;
+                    mn = fp < mn ? fp : mn;
+                }
+            }
+    };
+    auto put = [](float* row, const uint4& v) {
+        reinterpret_cast<float4*>(row)[0] = float4{bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y)};
+        reinterpret_cast<float4*>(row)[1] = float4{bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+    };
+    const int nch = d / MC;
+    uint4 ru = ug[0], re0 = eg0[0], re1 = eg1[0];
+    __syncthreads();                           // ex_stat initialised
+    put(&us[0][ur][up * 8], ru);
+    put(&es[0][tid >> 2][up * 8], re0);
+    put(&es[0][64 + (tid >> 2)][up * 8], re1);
+    stat(ru, mn_u, mx_u);
+    stat(re0, mn_e, mx_e);
+    stat(re1, mn_e, mx_e);
+    __syncthreads();
+    mv32 acc = {};
+    const int tok_l = 32 * wt + (lane & 31), exp_l = 64 * we + lane;
+    for (int c = 0; c < nch; ++c) {
+        const int b = c & 1;
+        if (c + 1 < nch) {                     // the next chunk's loads, in flight during this one
+            const int off = (c + 1) * (MC / 8);
+            ru = ug[off];
+            re0 = eg0[off];
+            re1 = eg1[off];
+        }
+        const float* ua = &us[b][tok_l][0];
+        const float* eb = &es[b][exp_l][0];
+#pragma unroll
+        for (int kk = 0; kk < MC; kk += 4) {
+            const float4 av = *reinterpret_cast<const float4*>(ua + kk);
+            const float4 bv = *reinterpret_cast<const float4*>(eb + kk);
+            acc = __builtin_amdgcn_mfma_f32_32x32x1f32(av.x, bv.x, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x1f32(av.y, bv.y, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x1f32(av.z, bv.z, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x1f32(av.w, bv.w, acc, 0, 0, 0);
+        }
+        if (c + 1 < nch) {
+            // buffer b ^ 1 was last read in chunk c - 1, before the barrier that ended it
+            put(&us[b ^ 1][ur][up * 8], ru);
+            put(&es[b ^ 1][tid >> 2][up * 8], re0);
+            put(&es[b ^ 1][64 + (tid >> 2)][up * 8], re1);
+            stat(ru, mn_u, mx_u);
+            stat(re0, mn_e, mx_e);
+            stat(re1, mn_e, mx_e);
+        }
+        __syncthreads();
+    }
+    // the block's exponent extremes; rows past T or E repeat valid rows
+    atomicMin(&ex_stat[0], mn_u);
+    atomicMax(&ex_stat[1], mx_u);
+    atomicMin(&ex_stat[2], mn_e);
+    atomicMax(&ex_stat[3], mx_e);
+    __syncthreads();
+    const bool certified = ex_stat[0] + ex_stat[2] >= 142 && ex_stat[1] < 255 && ex_stat[3] < 255 &&
+                           ex_stat[1] + ex_stat[3] + lg2d <= 378;
+    if (certified) {
+        // D[i][j] of MFMA block bb sits in lane j + 32 ((i / 4) % 2), register
+        // 16 bb + (i % 4) + 4 (i / 8)
+#pragma unroll
+        for (int r = 0; r < 32; ++r) {
+            const int bb = r >> 4, rr = r & 15;
+            const int i = 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
+            const int64_t t = t0 + 32 * wt + i;
+            const int ex = e0 + 64 * we + 32 * bb + (lane & 31);
+            if (t < T && ex < E) s[t * E + ex] = sigmoid_fixed(acc[r]);
+        }
+    } else {
+        // the FMA chain on the VALU: thread = token tid / 4, experts 32 (tid % 4) + [0, 32)
+        const int64_t t = t0 + (tid >> 2);
+        const int xb = e0 + 32 * (tid & 3);
+        if (t < T) {
+            const uint16_t* urow = u + t * d;
+            for (int j = 0; j < 32; ++j) {
+                const int ex = xb + j;
+                if (ex >= E) break;
+                const uint16_t* erow = e + (int64_t)ex * d;
+                float a = 0.0f;
+                for (int k = 0; k < d; ++k)
+                    a = __builtin_fmaf(__uint_as_float((uint32_t)urow[k] << 16),
+                                       __uint_as_float((uint32_t)erow[k] << 16), a);
+                s[t * E + ex] = sigmoid_fixed(a);
+            }
+        }
+    }
+}
+
 // Few tokens, centroids shared: one block per (4 tokens, 64 experts), one
 // logit per lane (wave w = token, lane = expert).  Chunks of SM_KC k-values of
 // the block's 64 centroid rows and 4 token rows are loaded with coalesced
@@ -390,7 +534,14 @@ hipError_t launch_router_scores(const uint16_t* u, const uint16_t* e, int64_t T,
     // thread: measured faster at 8192 and 16384 tokens than 16 x 256 (2 x 8),
     // 32 x 256 (4 x 8, too few blocks below 16384 tokens) and 64 x 128 (8 x 4).
     if (E > 64) {
-        if (T >= 4096) return launch_scores<32, 128, 4, 4>(u, e, T, d, E, s, st);
+        if (T >= 4096) {
+            // the matrix-core chains (a K = 1 FP32 MFMA per step)
+            int lg2d = 0;
+            while ((1 << lg2d) < d) ++lg2d;
+            const dim3 grid((unsigned)((T + MB_T - 1) / MB_T), (unsigned)((E + MB_E - 1) / MB_E));
+            hipLaunchKernelGGL(router_scores_mfma_kernel, grid, dim3(256), 0, st, u, e, T, d, E, lg2d, s);
+            return hipGetLastError();
+        }
         if (T >= 1024) return launch_scores<16, 128, 2, 4>(u, e, T, d, E, s, st);
         // fewer tokens: one logit per lane, chunks of 256 k-values (128 when d
         // is an odd multiple of 128) fetched two ahead

@@ -33,9 +33,10 @@ ROUTER_CASES = [
     (300, 1024, 256, 8),      # full expert count, ragged T
     (1000, 384, 40, 6),       # E not a multiple of 64
     (1, 128, 8, 8),           # one token, K = E
-    (4096, 512, 256, 8),      # the 32 x 128 tile, fewest tokens
-    (16384, 256, 256, 8),     # the 32 x 128 tile, many blocks
-    (8200, 128, 256, 8),      # the 32 x 128 tile with a ragged last block
+    (4096, 512, 256, 8),      # the matrix-core chains (T >= 4096), fewest tokens
+    (16384, 256, 256, 8),     # the matrix-core chains, many blocks
+    (8200, 128, 256, 8),      # the matrix-core chains with a ragged last token block
+    (4100, 256, 200, 6),      # the matrix-core chains, E not a multiple of the 128-expert block
     (256, 7168, 256, 8),      # decode: blocks of 4 tokens x 64 experts, one logit per lane
     (50, 256, 200, 6),        # decode layout with idle lanes (E not a multiple of 64, T of 4)
     (3, 16512, 72, 4),        # decode layout, long rows, one token block
@@ -46,6 +47,29 @@ ROUTER_CASES = [
 def test_router_bit_exact(T, d, E, K):
     say(f"router T={T} d={d} E={E} K={K}")
     u, e, b = _inputs(T, d, E, seed=T * 7 + E, ties=True)
+    idx, gate, s = moe.moe_router_topk(u.to(dev()), e.to(dev()), b.to(dev()), K)
+    torch.cuda.synchronize()
+    s_ref = oracle.router_scores(u16(u), u16(e))
+    np.testing.assert_array_equal(np_(s).view(np.uint32), s_ref.view(np.uint32))
+    idx_ref, gate_ref = oracle.topk_from_scores(s_ref, b.numpy(), K)
+    np.testing.assert_array_equal(np_(idx), idx_ref)
+    np.testing.assert_array_equal(np_(gate).view(np.uint32), gate_ref.view(np.uint32))
+
+
+def test_router_mfma_certificate_fallback():
+    """The matrix-core router reproduces the FMA chain only while every product
+    and partial sum stays in FP32's normal range, which each block certifies
+    from its inputs' exponents; a block outside recomputes on the VALU.  Single
+    planted values push blocks outside: a 2^-100 token element (a product's
+    last bit below 2^-126), a 2^126 token element (the overflow bound) and a
+    2^-110 centroid element (every block of that expert block).  Scores,
+    indices and gates must still equal the oracle bit for bit everywhere."""
+    T, d, E, K = 4096, 256, 256, 8
+    u, e, b = _inputs(T, d, E, seed=99)
+    u[5, 17] = 2.0 ** -100
+    u[130, 40] = 2.0 ** 126
+    e[200, 3] = 2.0 ** -110
+    say("router certificate fallback")
     idx, gate, s = moe.moe_router_topk(u.to(dev()), e.to(dev()), b.to(dev()), K)
     torch.cuda.synchronize()
     s_ref = oracle.router_scores(u16(u), u16(e))
