@@ -6,13 +6,15 @@
 // expert i is in token t's set iff s[t,i] + b_i ranks among the token's K
 // largest; g = s / (sum of s over the set); b takes part in the ranking only.
 //
-// Affinity kernel: a register-tiled FP32 VALU GEMM.  Each output's dot product
-// is one FMA chain in increasing k (bf16 products are exact in FP32, so the
-// chain fixes the result bit for bit); MFMA is not used because its internal
-// summation order is unspecified and routing must be reproducible exactly.
-// Tiles of KC k-values of u and of the centroids are widened to FP32 into LDS
-// (double-buffered through registers); every thread owns TM tokens x EN
-// experts.
+// Affinity kernels: each output's dot product is one FP32 FMA chain in
+// increasing k (bf16 products are exact in FP32, so the chain fixes the result
+// bit for bit).  Three kernels keep that order: from 4096 tokens on, the chain
+// runs on the matrix cores as K = 1 FP32 MFMAs (one rounding per step, the
+// same as the FMA; MFMAs with K > 1 sum several products in an unspecified
+// order and are not used), with a per-block range certificate and a VALU
+// fallback; below that, a register-tiled VALU kernel (every thread owns TM
+// tokens x EN experts) and, for few tokens, one logit per lane.  Tiles of
+// k-values of u and of the centroids are widened to FP32 into LDS.
 //
 // Top-K kernel: one wavefront per token, 64-bit composite keys
 // (orderable(s+b) << 32 | ~expert) reduced with cross-lane shuffles, K rounds.
@@ -179,7 +181,10 @@ __global__ __launch_bounds__(NTHREADS) void router_scores_kernel(
 // 32 wt + l % 32 (both MFMA blocks share the tokens) and expert 64 we + l.
 // Chunks of MC k-values of the block's rows are widened to FP32 into LDS
 // (row pitch MC + 4 floats: the 16 lanes of a 16-byte read cover all banks),
-// double-buffered, the next chunk's global loads in flight during this one.
+// double-buffered; chunk c + 2's global loads are issued at the start of chunk
+// c, and chunk c + 1 is widened, checked and stored in pieces placed after
+// single MFMAs of chunk c, so that the VALU and LDS work of the staging
+// overlaps the matrix instructions instead of following them.
 constexpr int MB_T = 64, MB_E = 128, MC = 32, MP = MC + 4;
 
 __global__ __launch_bounds__(256) void router_scores_mfma_kernel(
@@ -200,28 +205,35 @@ __global__ __launch_bounds__(256) void router_scores_mfma_kernel(
     const uint4* ug = reinterpret_cast<const uint4*>(u + (int64_t)min(t0 + ur, T - 1) * d) + up;
     const uint4* eg0 = reinterpret_cast<const uint4*>(e + (int64_t)min(e0 + (tid >> 2), E - 1) * d) + up;
     const uint4* eg1 = reinterpret_cast<const uint4*>(e + (int64_t)min(e0 + 64 + (tid >> 2), E - 1) * d) + up;
-    int mn_u = 1 << 20, mx_u = 0, mn_e = 1 << 20, mx_e = 0;
-    auto stat = [](const uint4& v, int& mn, int& mx) {
+    // Exponent extremes as 16-bit magnitudes x = |bf16 bits|, two per word:
+    // the smallest nonzero x (kept as x - 1, so that a zero wraps to 0xFFFF
+    // and never wins the minimum) and the largest x.  f = x >> 7 is monotone
+    // in x, so min f' = max((min nonzero x) >> 7, 1) and max f = (max x) >> 7.
+    typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+    us2 mn_u = {0xFFFF, 0xFFFF}, mx_u = {0, 0}, mn_e = {0xFFFF, 0xFFFF}, mx_e = {0, 0};
+    auto stat = [](const uint4& v, us2& mn, us2& mx) {
         const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const uint32_t b = (wd[q] >> (16 * h)) & 0xFFFFu;
-                const int f = (int)((b >> 7) & 0xFFu);
-                mx = f > mx ? f : mx;
-                if (b & 0x7FFFu) {
-                    const int fp = f > 1 ? f : 1;
-                    mn = fp < mn ? fp : mn;
-                }
-            }
+        for (int q = 0; q < 4; ++q) {
+            const us2 x = __builtin_bit_cast(us2, wd[q] & 0x7FFF7FFFu);
+            mn = __builtin_elementwise_min(mn, x - (us2){1, 1});
+            mx = __builtin_elementwise_max(mx, x);
+        }
     };
     auto put = [](float* row, const uint4& v) {
         reinterpret_cast<float4*>(row)[0] = float4{bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y)};
         reinterpret_cast<float4*>(row)[1] = float4{bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
     };
-    const int nch = d / MC;
+    const int nch = d / MC;                    // even: d is a multiple of 128
+    // global offset of chunk c; past the end it re-reads the last chunk (the
+    // loads stay unconditional, and what they bring is never used)
+    auto goff = [nch](int c) { return (c < nch ? c : nch - 1) * (MC / 8); };
     uint4 ru = ug[0], re0 = eg0[0], re1 = eg1[0];
+    // two register sets alternate: during chunk c one holds chunk c + 1's rows
+    // (loaded during chunk c - 1), which are staged into LDS, while chunk c + 2's
+    // rows are loaded into the other
+    uint4 xu = ug[goff(1)], xe0 = eg0[goff(1)], xe1 = eg1[goff(1)];
+    uint4 yu, ye0, ye1;
     __syncthreads();                           // ex_stat initialised
     put(&us[0][ur][up * 8], ru);
     put(&es[0][tid >> 2][up * 8], re0);
@@ -232,41 +244,70 @@ __global__ __launch_bounds__(256) void router_scores_mfma_kernel(
     __syncthreads();
     mv32 acc = {};
     const int tok_l = 32 * wt + (lane & 31), exp_l = 64 * we + lane;
-    for (int c = 0; c < nch; ++c) {
-        const int b = c & 1;
-        if (c + 1 < nch) {                     // the next chunk's loads, in flight during this one
-            const int off = (c + 1) * (MC / 8);
-            ru = ug[off];
-            re0 = eg0[off];
-            re1 = eg1[off];
-        }
+    // k-groups of 4 are read one group ahead into two register slots
+    float4 av[2], bv[2];
+    av[0] = *reinterpret_cast<const float4*>(&us[0][tok_l][0]);
+    bv[0] = *reinterpret_cast<const float4*>(&es[0][exp_l][0]);
+    auto mfma = [&acc](float a, float bq) { acc = __builtin_amdgcn_mfma_f32_32x32x1f32(a, bq, acc, 0, 0, 0); };
+    auto chunk = [&](int c, int b, const uint4& su, const uint4& se0, const uint4& se1, uint4& lu,
+                     uint4& le0, uint4& le1) {
+        lu = ug[goff(c + 2)];
+        le0 = eg0[goff(c + 2)];
+        le1 = eg1[goff(c + 2)];
         const float* ua = &us[b][tok_l][0];
         const float* eb = &es[b][exp_l][0];
+        // buffer b ^ 1 was last read in chunk c - 1, before the barrier that
+        // ended it; after the last chunk this stages a repeat that nothing reads
+        float* wu = &us[b ^ 1][ur][up * 8];
+        float* we0 = &es[b ^ 1][tid >> 2][up * 8];
+        float* we1 = &es[b ^ 1][64 + (tid >> 2)][up * 8];
 #pragma unroll
-        for (int kk = 0; kk < MC; kk += 4) {
-            const float4 av = *reinterpret_cast<const float4*>(ua + kk);
-            const float4 bv = *reinterpret_cast<const float4*>(eb + kk);
-            acc = __builtin_amdgcn_mfma_f32_32x32x1f32(av.x, bv.x, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x1f32(av.y, bv.y, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x1f32(av.z, bv.z, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x1f32(av.w, bv.w, acc, 0, 0, 0);
-        }
-        if (c + 1 < nch) {
-            // buffer b ^ 1 was last read in chunk c - 1, before the barrier that ended it
-            put(&us[b ^ 1][ur][up * 8], ru);
-            put(&es[b ^ 1][tid >> 2][up * 8], re0);
-            put(&es[b ^ 1][64 + (tid >> 2)][up * 8], re1);
-            stat(ru, mn_u, mx_u);
-            stat(re0, mn_e, mx_e);
-            stat(re1, mn_e, mx_e);
+        for (int g = 0; g < MC / 4 - 1; ++g) {
+            av[(g + 1) & 1] = *reinterpret_cast<const float4*>(ua + 4 * (g + 1));
+            bv[(g + 1) & 1] = *reinterpret_cast<const float4*>(eb + 4 * (g + 1));
+            const float4 a = av[g & 1], bq = bv[g & 1];
+            mfma(a.x, bq.x);
+            // one piece of the staging in the shadow of each group's first MFMA
+            __builtin_amdgcn_sched_barrier(0);
+            switch (g) {
+                case 0: stat(su, mn_u, mx_u); break;
+                case 1: put(wu, su); break;
+                case 2: stat(se0, mn_e, mx_e); break;
+                case 3: put(we0, se0); break;
+                case 4: stat(se1, mn_e, mx_e); break;
+                case 5: put(we1, se1); break;
+                default: break;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            mfma(a.y, bq.y);
+            mfma(a.z, bq.z);
+            mfma(a.w, bq.w);
         }
         __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        // the next chunk's first group, then this chunk's last one
+        av[0] = *reinterpret_cast<const float4*>(&us[b ^ 1][tok_l][0]);
+        bv[0] = *reinterpret_cast<const float4*>(&es[b ^ 1][exp_l][0]);
+        mfma(av[1].x, bv[1].x);
+        mfma(av[1].y, bv[1].y);
+        mfma(av[1].z, bv[1].z);
+        mfma(av[1].w, bv[1].w);
+        __builtin_amdgcn_sched_barrier(0);
+        // keeps those two reads here, under the last group's MFMAs, rather
+        // than at the next chunk's start, where the first MFMA would wait on them
+        asm volatile("" : "+v"(av[0].x), "+v"(av[0].y), "+v"(av[0].z), "+v"(av[0].w),
+                          "+v"(bv[0].x), "+v"(bv[0].y), "+v"(bv[0].z), "+v"(bv[0].w));
+    };
+    for (int c = 0; c < nch; c += 2) {
+        chunk(c, 0, xu, xe0, xe1, yu, ye0, ye1);
+        chunk(c + 1, 1, yu, ye0, ye1, xu, xe0, xe1);
     }
     // the block's exponent extremes; rows past T or E repeat valid rows
-    atomicMin(&ex_stat[0], mn_u);
-    atomicMax(&ex_stat[1], mx_u);
-    atomicMin(&ex_stat[2], mn_e);
-    atomicMax(&ex_stat[3], mx_e);
+    const unsigned mnu = min(mn_u.x, mn_u.y), mne = min(mn_e.x, mn_e.y);
+    atomicMin(&ex_stat[0], mnu == 0xFFFFu ? 1 << 20 : max((int)((mnu + 1) >> 7), 1));
+    atomicMax(&ex_stat[1], (int)(max(mx_u.x, mx_u.y) >> 7));
+    atomicMin(&ex_stat[2], mne == 0xFFFFu ? 1 << 20 : max((int)((mne + 1) >> 7), 1));
+    atomicMax(&ex_stat[3], (int)(max(mx_e.x, mx_e.y) >> 7));
     __syncthreads();
     const bool certified = ex_stat[0] + ex_stat[2] >= 142 && ex_stat[1] < 255 && ex_stat[3] < 255 &&
                            ex_stat[1] + ex_stat[3] + lg2d <= 378;
