@@ -116,6 +116,12 @@ def layer_setup(sh):
         out=torch.empty(T, d, dtype=torch.float32, device=dev),
         dws=torch.empty(max(moe.moe_dispatch_workspace_bytes(T, E), 256), dtype=torch.uint8, device=dev),
         gws=torch.empty(max(moe.moe_gemm_workspace_bytes(E + 1, R, max(2 * I, d), max(I, d)), 256), dtype=torch.uint8, device=dev),
+        # the shared expert's FFN as launches of its own (two-stream step):
+        # one group of T rows, its own GEMM workspace, a second stream
+        go_shared=torch.tensor([0, T], dtype=torch.int32, device=dev),
+        gws_shared=torch.empty(max(moe.moe_gemm_workspace_bytes(1, T, max(2 * I, d), max(I, d)), 256), dtype=torch.uint8, device=dev),
+        stream_b=torch.cuda.Stream(),
+        ev_quant=torch.cuda.Event(), ev_shared=torch.cuda.Event(),
     )
     return st
 
@@ -147,6 +153,84 @@ def layer_step(sh, st, ev=None):
         for i, n in enumerate(names):
             ev.add(n, m[i], m[i + 1])
     st["count"] = count
+
+
+def layer_step_two_streams(sh, st, gev=None):
+    """The same layer step with the shared expert's FFN on a second stream.
+    The shared expert's rows (GEMM rows T*K .. T*K+T-1) need no routing, so
+    quant(u) goes first and the shared expert's GEMM1 and GEMM2 (one group of
+    T rows, through offset views of the same h and Y buffers) run on stream B
+    beside the router, dispatch and the routed experts' GEMMs (E groups, the
+    first T*K rows) on the main stream; the combine waits for both.  Every
+    output row is computed by the same tile arithmetic as in layer_step, so h'
+    is bit-identical (checked by a GPU test); the gain is the two GEMM chains
+    filling each other's partial last rounds of tiles.  The bias restore copy
+    of the benchmark runs on stream B too.  gev: optional marks around the
+    routed GEMMs (main stream)."""
+    T, d, E, K, I = sh.T, sh.d, sh.E, sh.K, sh.I
+    TK = T * K
+    w13q, w2q, w13s, w2s = st["views"]
+    A, B = torch.cuda.current_stream(), st["stream_b"]
+    moe.fp8_quant_1x128(st["u"], st["uq"], st["us"])
+    st["ev_quant"].record(A)
+    B.wait_event(st["ev_quant"])
+    with torch.cuda.stream(B):
+        st["b_next"].copy_(st["b"])
+        moe.grouped_gemm_fp8_blockscaled(st["uq"], st["us"], st["go_shared"], T, w13q[E:], w13s[E:],
+                                         epi=moe.MOE_EPI_SWIGLU_QUANT, out_q=st["hq"][TK:],
+                                         out_scale=st["hs"][TK:], ws=st["gws_shared"])
+        moe.grouped_gemm_fp8_blockscaled(st["hq"][TK:], st["hs"][TK:], st["go_shared"], T, w2q[E:], w2s[E:],
+                                         epi=moe.MOE_EPI_STORE_F32, out=st["y"][TK:], ws=st["gws_shared"])
+        st["ev_shared"].record(B)
+    moe.moe_router_topk(st["u"], st["e"], st["b"], K, st["scores"], st["idx"], st["gate"])
+    count, go, row_token, slot_row = moe.moe_dispatch(st["idx"], E, True, ws=st["dws"])
+    m = [gev.mark("gemm1")] if gev else None
+    moe.grouped_gemm_fp8_blockscaled(st["uq"], st["us"], go[:E + 1], TK, w13q[:E], w13s[:E],
+                                     epi=moe.MOE_EPI_SWIGLU_QUANT, a_row_index=row_token[:TK],
+                                     out_q=st["hq"][:TK], out_scale=st["hs"][:TK], ws=st["gws"])
+    if gev: m.append(gev.mark("gemm2"))
+    moe.grouped_gemm_fp8_blockscaled(st["hq"][:TK], st["hs"][:TK], go[:E + 1], TK, w2q[:E], w2s[:E],
+                                     epi=moe.MOE_EPI_STORE_F32, out=st["y"][:TK], ws=st["gws"])
+    if gev:
+        m.append(gev.mark("end"))
+        gev.add("gemm1_routed", m[0], m[1])
+        gev.add("gemm2_routed", m[1], m[2])
+    A.wait_event(st["ev_shared"])
+    moe.moe_combine(st["u"], st["y"], st["gate"], slot_row, shared_row0=TK, out=st["out"])
+    moe.moe_bias_update(st["b_next"], count, TK, sh.gamma)
+    st["count"] = count
+
+
+def layer_step_gemm_events(sh, st, gev):
+    """layer_step with HIP events around the two GEMM launches only (the
+    roofline's live kernel times; events between every launch cost the
+    decode step about 2%)."""
+    T, d, E, K, I = sh.T, sh.d, sh.E, sh.K, sh.I
+    R = T * K + T
+    w13q, w2q, w13s, w2s = st["views"]
+    moe.moe_router_topk(st["u"], st["e"], st["b"], K, st["scores"], st["idx"], st["gate"])
+    count, go, row_token, slot_row = moe.moe_dispatch(st["idx"], E, True, ws=st["dws"])
+    moe.fp8_quant_1x128(st["u"], st["uq"], st["us"])
+    m = [gev.mark("gemm1")]
+    moe.grouped_gemm_fp8_blockscaled(st["uq"], st["us"], go, R, w13q, w13s, epi=moe.MOE_EPI_SWIGLU_QUANT,
+                                     a_row_index=row_token, out_q=st["hq"], out_scale=st["hs"], ws=st["gws"])
+    m.append(gev.mark("gemm2"))
+    moe.grouped_gemm_fp8_blockscaled(st["hq"], st["hs"], go, R, w2q, w2s, epi=moe.MOE_EPI_STORE_F32,
+                                     out=st["y"], ws=st["gws"])
+    m.append(gev.mark("end"))
+    gev.add("gemm1", m[0], m[1])
+    gev.add("gemm2", m[1], m[2])
+    moe.moe_combine(st["u"], st["y"], st["gate"], slot_row, shared_row0=T * K, out=st["out"])
+    st["b_next"].copy_(st["b"])
+    moe.moe_bias_update(st["b_next"], count, T * K, sh.gamma)
+    st["count"] = count
+
+
+def two_stream_step(sh):
+    """Decode-shaped layers (T < 4096, weight streaming) time the two-stream
+    step; at prefill the shared expert's GEMMs are a large share of the GEMM
+    work and one stream keeps the GEMM pair's kernel times well defined."""
+    return sh.T < 4096
 
 
 def layer_flops(sh):
@@ -424,24 +508,35 @@ def run_layer(sh, steps, warmup, with_cpu):
     t = time.time()
     st = layer_setup(sh)
     log(f"[bench] inputs + packed weights ready in {time.time() - t:.1f}s")
+    two = two_stream_step(sh)
+    gev = Events()
+    # the timed step: two streams at decode (no events), one stream with
+    # events around the GEMM pair at prefill (the roofline's kernel times)
+    timed = (lambda: layer_step_two_streams(sh, st)) if two else (lambda: layer_step_gemm_events(sh, st, gev))
     for _ in range(warmup):
-        layer_step(sh, st)
+        timed()
     torch.cuda.synchronize()
+    gev.pairs.clear()
     log("[bench] warmup done")
-    ev = Events()
     clocks_before = gpu_clocks()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
-        layer_step(sh, st, ev)
+        timed()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     clocks_after = gpu_clocks()
     ms = wall * 1e3 / steps
     count = st["count"].cpu().numpy()
+    # stage times: a separate pass of the one-stream step with events between
+    # every launch (they lengthen the step, so they stay out of the timed loop)
+    ev = Events()
+    for _ in range(min(steps, 10)):
+        layer_step(sh, st, ev)
+    torch.cuda.synchronize()
     stages = {n: round(ev.avg_ms(n), 4) for n in ev.pairs}
     g1, g2 = layer_flops(sh)
-    g1_ms, g2_ms = ev.avg_ms("gemm1"), ev.avg_ms("gemm2")
+    g1_ms, g2_ms = (ev.avg_ms("gemm1"), ev.avg_ms("gemm2")) if two else (gev.avg_ms("gemm1"), gev.avg_ms("gemm2"))
     if sh.T >= 4096:
         # the grouped GEMM as the pair of launches one step makes (GEMM1 with
         # the SwiGLU + requant epilogue, GEMM2 with the FP32 store): their
@@ -467,16 +562,17 @@ def run_layer(sh, steps, warmup, with_cpu):
         achieved = nbytes["total"] / (ms * 1e-3) / 1e9
         b1 = gemm1_bytes(sh, count)
         a1 = b1 / (g1_ms * 1e-3) / 1e9
-        roof = {"kernel": "the whole layer step (all kernels, one stream)",
+        roof = {"kernel": "the whole layer step (all kernels; the shared expert's FFN on a second stream)",
                 "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
                 "algorithmic_per_launch": nbytes["total"], "avg_launch_ms": round(ms, 4),
                 "bytes": nbytes,
                 "gemm1": {"achieved": round(a1, 1), "frac": round(a1 / PEAK_HBM_GBS, 4),
                           "algorithmic_per_launch": b1, "avg_launch_ms": round(g1_ms, 4),
+                          "timing": "one-stream pass with events between launches, after the timed loop",
                           "traffic": traffic_for(f"gemm1_{sh.name}", "gemm.hip")}}
     log(f"[bench] {ms:.3f} ms/step; stages {stages}")
-    clk = sustained_clock(lambda: layer_step(sh, st))
+    clk = sustained_clock(timed)
     log(f"[bench] sustained shader clock under this step: {clk}")
     if roof["bound"] == "mfma":
         at_clock(roof, clk)
@@ -494,7 +590,10 @@ def run_layer(sh, steps, warmup, with_cpu):
                    "load_max_over_mean": round(float(count.max() / count.mean()), 3),
                    "parallelism": "single GPU"},
         "roofline": roof,
+        "timed_step": ("two streams (the shared expert's FFN beside the routing and the routed experts), "
+                       "no events") if two else "one stream, events around the two GEMM launches only",
         "stages_ms": stages,
+        "stages_note": "one-stream step with events between every launch, a separate pass after the timed loop",
         "gemm_tflops": {"gemm1": round(g1 / (ev.avg_ms("gemm1") * 1e-3) / 1e12, 1),
                         "gemm2": round(g2 / (ev.avg_ms("gemm2") * 1e-3) / 1e12, 1)},
         "gpu_clocks_mhz": {"before": clocks_before, "after": clocks_after, "sustained": clk},
@@ -877,8 +976,11 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None,
-                    help="timed steps (default 20; 200 for the dense GEMM, whose step is ~0.3 ms)")
-    ap.add_argument("--warmup", type=int, default=5)
+                    help="timed steps (default 20; 200 for the dense GEMM, whose step is ~0.3 ms, "
+                         "and for the decode and tiny layers, whose steps take ~1.2 ms and less)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps first (default 5; 200 for the decode and tiny layers: their "
+                         "short steps would otherwise be timed while the shader clock still ramps up)")
     ap.add_argument("--workload", default="prefill",
                     choices=["prefill", "decode", "tiny", "rdc", "dense", "dense16k",
                              "prefill_bwd", "decode_bwd", "tiny_bwd"])
@@ -899,8 +1001,11 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    short_step = args.workload in ("decode", "tiny")
     if args.steps is None:
-        args.steps = 200 if args.workload in ("dense", "dense16k") else 20
+        args.steps = 200 if args.workload in ("dense", "dense16k") or short_step else 20
+    if args.warmup is None:
+        args.warmup = 200 if short_step else 5
     moe.load_library()
     if args.with_copy:
         copy_calibration()

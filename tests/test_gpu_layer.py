@@ -118,8 +118,8 @@ def check_layer(sh, u, e, b, packed, g_out, token_sample=None, group_rows=None, 
 
     token_sample: the tokens whose output h' is checked (all of their K + 1
     GEMM rows are checked); None = every token.  group_rows: extra GEMM rows
-    to check, as {group: [rows]} (the survey's "at least one row of every
-    non-empty group").  quant_check: the experts whose packed weight codes and
+    to check, as {group: [rows]} (at least one row of every non-empty
+    group).  quant_check: the experts whose packed weight codes and
     scales are checked bit-exact against the oracle's quantiser of their FP32
     masters; None = every expert.  The oracle's GEMMs take the packed codes as
     operands (checked experts: the oracle's own codes, equal to them)."""

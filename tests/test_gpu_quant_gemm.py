@@ -422,7 +422,8 @@ def _zipf_sizes(n, total, rng):
     return s
 
 
-@pytest.mark.parametrize("kind", ["rows128_short_k", "rows128_long_k", "rows32", "rows32_long_k"])
+@pytest.mark.parametrize("kind", ["rows128_short_k", "rows128_k10", "rows128_k16", "rows128_long_k",
+                                  "rows32", "rows32_long_k"])
 def test_gemm_multi_tile_exact_pow2_scales(kind):
     """The persistent schedules over many more tiles than CUs (each block runs
     several tiles, so the tile-to-tile hand-over -- the next tile's DMAs
@@ -430,15 +431,20 @@ def test_gemm_multi_tile_exact_pow2_scales(kind):
     rows, the tile sequence of each XCD -- is exercised everywhere), with a
     gather and ragged, Zipf-sized groups, compared element by element with the
     oracle.  rows128_short_k: 26 groups, ~40k rows, 128-row tiles of 5 K
-    slices (the kernel whose DMA ring runs on across tiles); rows128_long_k:
-    the same groups with 18 K slices (the kernel that restarts its pipeline
-    per tile); rows32: 1500 groups of 0..60 rows (32-row tiles of 3 slices);
-    rows32_long_k: the same groups with 8 slices, through the SwiGLU
-    epilogues too."""
+    slices (the kernel whose DMA ring runs on across tiles; its FP32 tiles
+    carry part of their output into the next tile, and a 5-slice tile stores
+    the pieces it had no phase for at its end); rows128_k10 and rows128_k16:
+    the same with 10 and 16 slices (every carried piece stored in a phase of
+    the next tile, then phases with nothing to carry; 16 is the expert
+    down-projection's K = 2048); rows128_long_k: 18 K slices (the kernel that
+    restarts its pipeline per tile); rows32: 1500 groups of 0..60 rows
+    (32-row tiles of 3 slices); rows32_long_k: the same groups with 8 slices,
+    through the SwiGLU epilogues too."""
     rows32 = kind.startswith("rows32")
     rng = np.random.default_rng(8 if rows32 else 7)
     N = 512
-    K = {"rows128_short_k": 640, "rows128_long_k": 2304, "rows32": 384, "rows32_long_k": 1024}[kind]
+    K = {"rows128_short_k": 640, "rows128_k10": 1280, "rows128_k16": 2048, "rows128_long_k": 2304,
+         "rows32": 384, "rows32_long_k": 1024}[kind]
     if not rows32:
         sizes = _zipf_sizes(26, 40_000, rng)
     else:

@@ -1,0 +1,38 @@
+"""The benchmark's two-stream layer step (the shared expert's FFN on a second
+stream, as launches of its own: one group of T rows through offset views of
+the h and Y buffers, 128-row tiles) against the one-stream step that the
+layer parity tests check against the oracle: h', the h codes and scales, Y
+and the expert counts must be identical bit for bit, since every GEMM row is
+computed by the same per-slice arithmetic whatever launch or tile holds it."""
+import pytest
+import torch
+
+import bench
+import workloads
+from helpers import say
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("name", ["tiny", "decode"])
+def test_two_stream_step_equals_one_stream_step(name):
+    sh = workloads.SHAPES[name]
+    say(f"two-stream step, {name}: T={sh.T} E={sh.E} K={sh.K}")
+    st = bench.layer_setup(sh)
+    bench.layer_step(sh, st)
+    torch.cuda.synchronize()
+    ref = {k: st[k].clone() for k in ("out", "hq", "hs", "y")}
+    ref_count = st["count"].clone()
+    for k in ("out", "hq", "hs", "y"):
+        st[k].fill_(7)                    # stale values must not survive
+    for rep in range(2):                  # twice: nothing carries over from one step to the next
+        bench.layer_step_two_streams(sh, st)
+        torch.cuda.synchronize()
+        for k in ("out", "hq", "y"):
+            assert torch.equal(st[k], ref[k]), f"{k} differs (rep {rep})"
+        assert torch.equal(st["hs"].view(torch.int32), ref["hs"].view(torch.int32)), f"hs differs (rep {rep})"
+        assert torch.equal(st["count"], ref_count)
+    # the bias update ran on the restored bias in both steps
+    b1 = st["b_next"].clone()
+    bench.layer_step(sh, st)
+    torch.cuda.synchronize()
+    assert torch.equal(st["b_next"], b1)
