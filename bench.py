@@ -226,11 +226,16 @@ def layer_step_gemm_events(sh, st, gev):
     st["count"] = count
 
 
+ONE_STREAM = False     # --one-stream: time the one-stream step at every size
+
+
 def two_stream_step(sh):
     """Decode-shaped layers (T < 4096, weight streaming) time the two-stream
     step; at prefill the shared expert's GEMMs are a large share of the GEMM
-    work and one stream keeps the GEMM pair's kernel times well defined."""
-    return sh.T < 4096
+    work and one stream keeps the GEMM pair's kernel times well defined.
+    --one-stream times the one-stream step everywhere (counter profiles of
+    whole-GEMM launches)."""
+    return sh.T < 4096 and not ONE_STREAM
 
 
 def layer_flops(sh):
@@ -562,7 +567,8 @@ def run_layer(sh, steps, warmup, with_cpu):
         achieved = nbytes["total"] / (ms * 1e-3) / 1e9
         b1 = gemm1_bytes(sh, count)
         a1 = b1 / (g1_ms * 1e-3) / 1e9
-        roof = {"kernel": "the whole layer step (all kernels; the shared expert's FFN on a second stream)",
+        roof = {"kernel": "the whole layer step (all kernels" +
+                          ("; the shared expert's FFN on a second stream)" if two else ", one stream)"),
                 "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
                 "algorithmic_per_launch": nbytes["total"], "avg_launch_ms": round(ms, 4),
@@ -800,9 +806,13 @@ def cpu_model():
 def gpu_clocks():
     """Current GPU clocks in MHz as rocm-smi reports them (shader clock sclk,
     memory clock mclk, ...), or the reason they could not be read.  Read in a
-    child process; a failure never stops the benchmark."""
+    child process; a failure never stops the benchmark.  Skipped with
+    --no-clock (profiler runs, whose preloaded library would follow the
+    child process into rocm-smi)."""
     import re
     import subprocess
+    if CLOCK_SECONDS <= 0:
+        return {"skipped": "--no-clock"}
     try:
         r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=30)
         data = json.loads(r.stdout)
@@ -989,8 +999,15 @@ def main():
                     help="first run a plain 4 GiB copy kernel (moe_permute_rows with the identity "
                          "permutation) so a counter profile can calibrate FETCH_SIZE / WRITE_SIZE")
     ap.add_argument("--no-clock", action="store_true",
-                    help="skip the ~3 s sustained-clock reading after the timed region (profiler runs)")
+                    help="skip the clock readings (rocm-smi before and after the timed region, and the "
+                         "~3 s sustained-clock reading after it): profiler runs")
+    ap.add_argument("--one-stream", action="store_true",
+                    help="layer workloads: time the one-stream step also where the two-stream step is "
+                         "the default (decode, tiny), so every GEMM launch covers all rows")
     args = ap.parse_args()
+    if args.one_stream:
+        global ONE_STREAM
+        ONE_STREAM = True
     if args.no_clock:
         global CLOCK_SECONDS
         CLOCK_SECONDS = 0.0
