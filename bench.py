@@ -230,12 +230,14 @@ ONE_STREAM = False     # --one-stream: time the one-stream step at every size
 
 
 def two_stream_step(sh):
-    """Decode-shaped layers (T < 4096, weight streaming) time the two-stream
-    step; at prefill the shared expert's GEMMs are a large share of the GEMM
-    work and one stream keeps the GEMM pair's kernel times well defined.
-    --one-stream times the one-stream step everywhere (counter profiles of
-    whole-GEMM launches)."""
-    return sh.T < 4096 and not ONE_STREAM
+    """Decode-shaped layers (T < 4096 at the model's width d >= 4096, weight
+    streaming) time the two-stream step; at prefill the shared expert's GEMMs
+    are a large share of the GEMM work and one stream keeps the GEMM pair's
+    kernel times well defined, and a small layer (the tiny one: d = 512) is
+    launch-bound, where the extra launches and cross-stream waits cost more
+    than they hide (0.19 against 0.11 ms per step).  --one-stream times the
+    one-stream step everywhere (counter profiles of whole-GEMM launches)."""
+    return sh.T < 4096 and sh.d >= 4096 and not ONE_STREAM
 
 
 def layer_flops(sh):
