@@ -155,7 +155,7 @@ def layer_step(sh, st, ev=None):
     st["count"] = count
 
 
-def layer_step_two_streams(sh, st, gev=None):
+def layer_step_two_streams(sh, st):
     """The same layer step with the shared expert's FFN on a second stream.
     The shared expert's rows (GEMM rows T*K .. T*K+T-1) need no routing, so
     quant(u) goes first and the shared expert's GEMM1 and GEMM2 (one group of
@@ -165,8 +165,7 @@ def layer_step_two_streams(sh, st, gev=None):
     output row is computed by the same tile arithmetic as in layer_step, so h'
     is bit-identical (checked by a GPU test); the gain is the two GEMM chains
     filling each other's partial last rounds of tiles.  The bias restore copy
-    of the benchmark runs on stream B too.  gev: optional marks around the
-    routed GEMMs (main stream)."""
+    of the benchmark runs on stream B too."""
     T, d, E, K, I = sh.T, sh.d, sh.E, sh.K, sh.I
     TK = T * K
     w13q, w2q, w13s, w2s = st["views"]
@@ -184,17 +183,11 @@ def layer_step_two_streams(sh, st, gev=None):
         st["ev_shared"].record(B)
     moe.moe_router_topk(st["u"], st["e"], st["b"], K, st["scores"], st["idx"], st["gate"])
     count, go, row_token, slot_row = moe.moe_dispatch(st["idx"], E, True, ws=st["dws"])
-    m = [gev.mark("gemm1")] if gev else None
     moe.grouped_gemm_fp8_blockscaled(st["uq"], st["us"], go[:E + 1], TK, w13q[:E], w13s[:E],
                                      epi=moe.MOE_EPI_SWIGLU_QUANT, a_row_index=row_token[:TK],
                                      out_q=st["hq"][:TK], out_scale=st["hs"][:TK], ws=st["gws"])
-    if gev: m.append(gev.mark("gemm2"))
     moe.grouped_gemm_fp8_blockscaled(st["hq"][:TK], st["hs"][:TK], go[:E + 1], TK, w2q[:E], w2s[:E],
                                      epi=moe.MOE_EPI_STORE_F32, out=st["y"][:TK], ws=st["gws"])
-    if gev:
-        m.append(gev.mark("end"))
-        gev.add("gemm1_routed", m[0], m[1])
-        gev.add("gemm2_routed", m[1], m[2])
     A.wait_event(st["ev_shared"])
     moe.moe_combine(st["u"], st["y"], st["gate"], slot_row, shared_row0=TK, out=st["out"])
     moe.moe_bias_update(st["b_next"], count, TK, sh.gamma)
