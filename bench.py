@@ -165,7 +165,9 @@ def layer_step_two_streams(sh, st):
     output row is computed by the same tile arithmetic as in layer_step, so h'
     is bit-identical (checked by a GPU test); the gain is the two GEMM chains
     filling each other's partial last rounds of tiles.  The bias restore copy
-    of the benchmark runs on stream B too."""
+    of the benchmark runs on stream B too.  The views start at GEMM row T*K,
+    and the library takes 16-byte aligned buffers only: T*K*(I/128) must be a
+    multiple of 4 (the h scales' rows; see shared_views_aligned)."""
     T, d, E, K, I = sh.T, sh.d, sh.E, sh.K, sh.I
     TK = T * K
     w13q, w2q, w13s, w2s = st["views"]
@@ -222,6 +224,13 @@ def layer_step_gemm_events(sh, st, gev):
 ONE_STREAM = False     # --one-stream: time the one-stream step at every size
 
 
+def shared_views_aligned(sh):
+    """The two-stream step's views of h codes, h scales and Y start at row
+    T*K; each must start on a 16-byte boundary (d and I are multiples of 128,
+    so only the h scales, I/128 floats per row, can miss it)."""
+    return (sh.T * sh.K * (sh.I // 128)) % 4 == 0
+
+
 def two_stream_step(sh):
     """Decode-shaped layers (T < 4096 at the model's width d >= 4096, weight
     streaming) time the two-stream step; at prefill the shared expert's GEMMs
@@ -230,7 +239,7 @@ def two_stream_step(sh):
     launch-bound, where the extra launches and cross-stream waits cost more
     than they hide (0.19 against 0.11 ms per step).  --one-stream times the
     one-stream step everywhere (counter profiles of whole-GEMM launches)."""
-    return sh.T < 4096 and sh.d >= 4096 and not ONE_STREAM
+    return sh.T < 4096 and sh.d >= 4096 and shared_views_aligned(sh) and not ONE_STREAM
 
 
 def layer_flops(sh):

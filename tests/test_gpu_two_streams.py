@@ -12,10 +12,17 @@ import workloads
 from helpers import say
 
 
+RAGGED = workloads.custom_shape(T=37, d=640, E=12, K=4, I=384, outliers=True, name="custom")
+
+
 @pytest.mark.gpu
-@pytest.mark.parametrize("name", ["tiny", "decode"])
+@pytest.mark.parametrize("name", ["tiny", "decode", "ragged"])
 def test_two_stream_step_equals_one_stream_step(name):
-    sh = workloads.SHAPES[name]
+    """ragged: 37 tokens, 12 experts top-4, d = 640, I = 384 (the shared
+    expert's rows start at GEMM row 148, its h-scale view 148 * 3 floats into
+    the buffer: 16-byte aligned, which the library requires)."""
+    sh = RAGGED if name == "ragged" else workloads.SHAPES[name]
+    assert bench.shared_views_aligned(sh)
     say(f"two-stream step, {name}: T={sh.T} E={sh.E} K={sh.K}")
     st = bench.layer_setup(sh)
     bench.layer_step(sh, st)
