@@ -121,7 +121,7 @@ def layer_setup(sh):
         go_shared=torch.tensor([0, T], dtype=torch.int32, device=dev),
         gws_shared=torch.empty(max(moe.moe_gemm_workspace_bytes(1, T, max(2 * I, d), max(I, d)), 256), dtype=torch.uint8, device=dev),
         stream_b=torch.cuda.Stream(),
-        ev_quant=torch.cuda.Event(), ev_shared=torch.cuda.Event(),
+        ev_start=torch.cuda.Event(), ev_quant=torch.cuda.Event(), ev_shared=torch.cuda.Event(),
     )
     return st
 
@@ -196,16 +196,31 @@ def layer_step_two_streams(sh, st):
     st["count"] = count
 
 
-def layer_step_gemm_events(sh, st, gev):
+def layer_step_gemm_events(sh, st, gev, quant_beside_router=False):
     """layer_step with HIP events around the two GEMM launches only (the
     roofline's live kernel times; events between every launch cost the
-    decode step about 2%)."""
+    decode step about 2%).  quant_beside_router: quant(u), which needs no
+    routing, and the bias restore copy run on a second stream beside the
+    router and dispatch (the matrix-core router and the bandwidth-bound quant
+    share the chip; 9.455 -> 9.409 ms at prefill on one box), and GEMM1 waits
+    for them; every launch the events bracket stays on the main stream."""
     T, d, E, K, I = sh.T, sh.d, sh.E, sh.K, sh.I
     R = T * K + T
     w13q, w2q, w13s, w2s = st["views"]
+    if quant_beside_router:
+        A, B = torch.cuda.current_stream(), st["stream_b"]
+        st["ev_start"].record(A)           # the previous step no longer reads uq, us or b_next
+        B.wait_event(st["ev_start"])
+        with torch.cuda.stream(B):
+            moe.fp8_quant_1x128(st["u"], st["uq"], st["us"])
+            st["b_next"].copy_(st["b"])
+            st["ev_quant"].record(B)
     moe.moe_router_topk(st["u"], st["e"], st["b"], K, st["scores"], st["idx"], st["gate"])
     count, go, row_token, slot_row = moe.moe_dispatch(st["idx"], E, True, ws=st["dws"])
-    moe.fp8_quant_1x128(st["u"], st["uq"], st["us"])
+    if quant_beside_router:
+        A.wait_event(st["ev_quant"])
+    else:
+        moe.fp8_quant_1x128(st["u"], st["uq"], st["us"])
     m = [gev.mark("gemm1")]
     moe.grouped_gemm_fp8_blockscaled(st["uq"], st["us"], go, R, w13q, w13s, epi=moe.MOE_EPI_SWIGLU_QUANT,
                                      a_row_index=row_token, out_q=st["hq"], out_scale=st["hs"], ws=st["gws"])
@@ -216,7 +231,8 @@ def layer_step_gemm_events(sh, st, gev):
     gev.add("gemm1", m[0], m[1])
     gev.add("gemm2", m[1], m[2])
     moe.moe_combine(st["u"], st["y"], st["gate"], slot_row, shared_row0=T * K, out=st["out"])
-    st["b_next"].copy_(st["b"])
+    if not quant_beside_router:
+        st["b_next"].copy_(st["b"])
     moe.moe_bias_update(st["b_next"], count, T * K, sh.gamma)
     st["count"] = count
 
@@ -521,7 +537,9 @@ def run_layer(sh, steps, warmup, with_cpu):
     gev = Events()
     # the timed step: two streams at decode (no events), one stream with
     # events around the GEMM pair at prefill (the roofline's kernel times)
-    timed = (lambda: layer_step_two_streams(sh, st)) if two else (lambda: layer_step_gemm_events(sh, st, gev))
+    beside = sh.T >= 4096 and not ONE_STREAM   # prefill: quant(u) beside the router
+    timed = ((lambda: layer_step_two_streams(sh, st)) if two else
+             (lambda: layer_step_gemm_events(sh, st, gev, quant_beside_router=beside)))
     for _ in range(warmup):
         timed()
     torch.cuda.synchronize()
@@ -601,7 +619,10 @@ def run_layer(sh, steps, warmup, with_cpu):
                    "parallelism": "single GPU"},
         "roofline": roof,
         "timed_step": ("two streams (the shared expert's FFN beside the routing and the routed experts), "
-                       "no events") if two else "one stream, events around the two GEMM launches only",
+                       "no events") if two else
+                      ("quant(u) on a second stream beside the router; routing and the GEMMs on one stream, "
+                       "events around the two GEMM launches only") if beside else
+                      "one stream, events around the two GEMM launches only",
         "stages_ms": stages,
         "stages_note": "one-stream step with events between every launch, a separate pass after the timed loop",
         "gemm_tflops": {"gemm1": round(g1 / (ev.avg_ms("gemm1") * 1e-3) / 1e12, 1),

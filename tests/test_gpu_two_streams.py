@@ -43,3 +43,24 @@ def test_two_stream_step_equals_one_stream_step(name):
     bench.layer_step(sh, st)
     torch.cuda.synchronize()
     assert torch.equal(st["b_next"], b1)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("name", ["tiny", "ragged"])
+def test_quant_beside_router_step_equals_one_stream_step(name):
+    """The prefill benchmark's step: quant(u) and the bias restore copy on a
+    second stream beside the router and dispatch; h', h, Y and the updated
+    bias identical to the one-stream step's, over two steps in a row."""
+    sh = RAGGED if name == "ragged" else workloads.SHAPES[name]
+    say(f"quant beside the router, {name}: T={sh.T} E={sh.E} K={sh.K}")
+    st = bench.layer_setup(sh)
+    bench.layer_step(sh, st)
+    torch.cuda.synchronize()
+    ref = {k: st[k].clone() for k in ("out", "hq", "y", "b_next")}
+    for k in ("out", "hq", "y", "b_next", "uq"):
+        st[k].fill_(7)
+    for rep in range(2):
+        bench.layer_step_gemm_events(sh, st, bench.Events(), quant_beside_router=True)
+        torch.cuda.synchronize()
+        for k in ("out", "hq", "y", "b_next"):
+            assert torch.equal(st[k], ref[k]), f"{k} differs (rep {rep})"
